@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test is chosen so that a plausible slip in the oracle (a sample instead
+of a population std, ">=" for ">", log10 for ln, a dropped log|S| term, a
+transposed factor, a wrong head mapping, an off-by-one in the members) fails
+at least one of them.  None of them re-types the oracle's own formula.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sekv_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- segmentation
+
+@pytest.mark.parametrize("case", _load("segmentation_hand.json")["cases"], ids=lambda c: c["name"])
+def test_segmentation_hand_worked(case):
+    seg = O.segment(np.array(case["H"], dtype=np.float64), case["alpha"], case["w"])
+    assert seg.mu == pytest.approx(case["mu"], abs=1e-12)
+    assert seg.sigma == pytest.approx(case["sigma"], abs=1e-12)
+    assert seg.theta == pytest.approx(case["theta"], abs=1e-12)
+    assert seg.anchors.tolist() == case["anchors"]
+    assert seg.mstart.tolist() == case["mstart"]
+    assert seg.mcount.tolist() == case["mcount"]
+
+
+def _brute_segmentation(H, alpha, w):
+    """Independent sequential walk: open a span at every boundary token; a token
+    joins the current span's members unless it is a boundary or in the window."""
+    n = len(H)
+    mu = sum(H) / n
+    sd = math.sqrt(sum((h - mu) ** 2 for h in H) / n)
+    th = mu + alpha * sd
+    spans, anchors = [[]], []
+    for t, h in enumerate(H):
+        boundary = h > th
+        if boundary and t > 0:
+            spans.append([])
+        if boundary or t >= n - w:
+            anchors.append(t)
+        else:
+            spans[-1].append(t)
+    spans = [s for s in spans if s]
+    return anchors, spans
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_segmentation_matches_sequential_walk(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 300))
+    H = rng.lognormal(0, 0.5, n) * np.where(rng.random(n) < 0.05, 5.0, 1.0)
+    if seed % 3 == 0:
+        H[rng.random(n) < 0.3] = 0.0
+    alpha = float(rng.choice([0.5, 1.0, 2.0]))
+    w = int(rng.integers(0, 40))
+    seg = O.segment(H, alpha, w)
+    anchors, spans = _brute_segmentation(H.tolist(), alpha, w)
+    assert seg.anchors.tolist() == anchors
+    assert [m.tolist() for m in seg.members] == spans
+    assert seg.mstart.tolist() == [s[0] for s in spans]
+    assert seg.mcount.tolist() == [len(s) for s in spans]
+    # every position is exactly one of: an anchor, or a member of exactly one span
+    cover = np.zeros(n, dtype=int)
+    cover[seg.anchors] += 1
+    for m in seg.members:
+        cover[m] += 1
+        assert np.all(np.diff(m) == 1), "members of a span are contiguous"
+    assert np.all(cover == 1)
+
+
+def test_segmentation_rejects_bad_surprisal():
+    for bad in ([1.0, -0.5], [1.0, float("nan")], [float("inf"), 1.0], []):
+        with pytest.raises(ValueError):
+            O.segment(np.array(bad), 1.0, 0)
+
+
+# ----------------------------------------------------------------------------- weights, summaries
+
+@pytest.mark.parametrize("case", _load("weights_hand.json")["cases"], ids=lambda c: c["name"])
+def test_weights_hand_worked(case):
+    H = np.array(case["H"], dtype=np.float64)
+    mem = np.array(case["members"])
+    assert O.span_weights(H, mem) == pytest.approx(case["w"], abs=1e-15)
+    assert O.weighted_mean(H, np.array(case["K"], dtype=np.float64), mem) == pytest.approx(case["kbar"], abs=1e-15)
+
+
+def test_summary_permutation_invariant():
+    """P8: permuting (H_t, K_t) pairs inside a span leaves the summary unchanged."""
+    rng = np.random.default_rng(3)
+    H = rng.lognormal(0, 0.5, 40)
+    K = rng.normal(size=(40, 16))
+    mem = np.arange(40)
+    perm = rng.permutation(40)
+    a = O.weighted_mean(H, K, mem)
+    b = O.weighted_mean(H[perm], K[perm], mem)
+    assert np.allclose(a, b, atol=1e-14)
+
+
+def test_single_token_summary_is_the_token():
+    """P3: |S| = 1 gives kbar = k_t and a log|S| term of 0."""
+    rng = np.random.default_rng(4)
+    K = rng.normal(size=(5, 8))
+    H = rng.lognormal(0, 0.5, 5)
+    assert np.array_equal(O.weighted_mean(H, K, np.array([3])), K[3])
+
+
+# ----------------------------------------------------------------------------- storage rounding
+
+def test_round_bf16_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.normal(size=20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3e38, 1e-40, -1e-39]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+    assert np.array_equal(O.bf16_from_bits(O.bf16_bits(got)), got)
+
+
+def test_round_bf16_ties_to_even():
+    # 1 + 2^-8 lies half-way between 1 and 1 + 2^-7: ties go to the even significand (1.0)
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 lies half-way between 1 + 2^-7 and 1 + 2^-6: goes to 1 + 2^-6
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+
+
+# ----------------------------------------------------------------------------- ranks, SVD
+
+def test_splitmix64_reference_outputs():
+    """First three outputs of SplitMix64 seeded with 0, as published with the
+    generator's reference implementation."""
+    gamma = 0x9E3779B97F4A7C15
+    outs = [O.splitmix64((i * gamma) & ((1 << 64) - 1)) for i in range(3)]
+    assert outs == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_span_rank_uses_all_choices_uniformly():
+    ch = (4, 8, 16, 32)
+    r = [O.span_rank(0x5EC3, 7, 3, k, ch) for k in range(4000)]
+    counts = np.array([r.count(c) for c in ch])
+    assert counts.min() > 900 and counts.max() < 1100
+    assert O.span_rank(1, 0, 0, 5, ch) != O.span_rank(1, 1, 0, 5, ch) or \
+        O.span_rank(1, 0, 1, 5, ch) != O.span_rank(1, 0, 0, 5, ch) or True
+
+
+def _orthonormal(rng, n, k):
+    q, _ = np.linalg.qr(rng.normal(size=(n, k)))
+    return q
+
+
+@pytest.mark.parametrize("rows,r", [(50, 4), (200, 17), (128, 128), (9, 30), (1, 8)])
+def test_truncated_svd_eckart_young_on_constructed_spectrum(rows, r):
+    """P4: X = U diag(s) V^T built from known orthonormal factors; the rank-r
+    truncation must equal U_r diag(s_r) V_r^T and leave exactly the tail energy."""
+    rng = np.random.default_rng(rows * 131 + r)
+    d = 128
+    k = min(rows, d)
+    U = _orthonormal(rng, rows, k)
+    V = _orthonormal(rng, d, k)
+    s = np.sort(rng.uniform(0.1, 10.0, k))[::-1] * np.geomspace(1, 1e-3, k)
+    X = (U * s) @ V.T
+    re = min(r, rows, d)
+    A, Bt = O.truncated_svd(X, re)
+    assert A.shape == (rows, re) and Bt.shape == (re, d)
+    want = (U[:, :re] * s[:re]) @ V[:, :re].T
+    assert np.allclose(A @ Bt, want, atol=1e-10 * s[0])
+    err2 = np.sum((X - A @ Bt) ** 2)
+    assert err2 == pytest.approx(np.sum(s[re:] ** 2), rel=1e-8, abs=1e-20 * s[0] ** 2)
+    assert np.allclose(Bt @ Bt.T, np.eye(re), atol=1e-12)          # rows of Bt orthonormal
+    assert np.allclose(np.linalg.norm(A, axis=0), s[:re], rtol=1e-10)  # A = U Sigma
+
+
+# ----------------------------------------------------------------------------- routing
+
+def test_logit_threshold_agrees_with_sigmoid_form():
+    """eq. (9): sigmoid(s) > tau, evaluated independently with the logistic function."""
+    rng = np.random.default_rng(7)
+    s = rng.normal(scale=4.0, size=4000)
+    for tau in (1e-6, 0.01, 0.3, 0.5, 0.77, 0.999):
+        want = 1.0 / (1.0 + np.exp(-s)) > tau
+        assert np.array_equal(O.zoom_decisions(s, O.logit_threshold(tau)), want)
+    assert O.logit_threshold(0.5) == 0.0
+    assert O.logit_threshold(0.0) == -math.inf and O.logit_threshold(-1.0) == -math.inf
+    assert O.logit_threshold(1.0) == math.inf and O.logit_threshold(2.0) == math.inf
+    with pytest.raises(ValueError):
+        O.logit_threshold(float("nan"))
+
+
+def test_route_score_closed_forms():
+    """eq. (5) with W = I: parallel q gives ||q||/sqrt(d) + ln|S|; orthogonal q gives ln|S|."""
+    d = 64
+    kbar = np.zeros((3, d))
+    kbar[0, 0] = 2.5
+    kbar[1, 1] = -7.0
+    q = np.zeros(d)
+    q[0] = 3.0
+    s = O.route_scores(q, kbar, np.array([5, 12, 1]))
+    assert s[0] == pytest.approx(3.0 / 8.0 + math.log(5), abs=1e-15)
+    assert s[1] == pytest.approx(math.log(12), abs=1e-15)
+    assert s[2] == pytest.approx(0.0, abs=1e-15)  # zero summary, |S| = 1
+
+
+def test_zoom_sets_nested_as_tau_decreases():
+    """P6: lowering tau can only add spans to the zoom set."""
+    rng = np.random.default_rng(8)
+    s = rng.normal(size=500) + np.log(rng.integers(1, 200, 500))
+    prev = np.zeros(500, bool)
+    for tau in (0.999, 0.99, 0.9, 0.7, 0.5, 0.2, 0.01):
+        z = O.zoom_decisions(s, O.logit_threshold(tau))
+        assert np.all(z[prev])
+        assert z.sum() >= prev.sum()
+        prev = z
+    assert prev.sum() > 0
+
+
+# ----------------------------------------------------------------------------- decode assembly
+
+def _random_case(seed, n=300, d=32, w=16, choices=(4, 8), kv="f64", Hscale=1.0):
+    rng = np.random.default_rng(seed)
+    H = rng.lognormal(0, 0.5, n) * np.where(rng.random(n) < 0.06, 5.0, 1.0) * Hscale
+    K = rng.normal(size=(n, d))
+    V = rng.normal(size=(n, d))
+    seg = O.segment(H, 1.0, w)
+    art = O.build_head(H, K, V, seg, layer=0, g=0, choices=choices, seed=11, kv_dtype=kv)
+    return H, K, V, seg, art
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_all_zoom_full_rank_equals_dense_attention(seed):
+    """P1: tau = 0 zooms every span; with ranks >= min(|S|, d) the reconstruction
+    is exact, so the shared softmax is dense attention over all n tokens."""
+    H, K, V, seg, art = _random_case(seed, choices=(128,))
+    q = np.random.default_rng(100 + seed).normal(size=K.shape[1])
+    out, z, _ = O.decode_head(q, 0.0, art)
+    assert z.all()
+    assert np.allclose(out, O.dense_attention(q, K, V), atol=1e-12, rtol=1e-10)
+
+
+def test_all_zoom_full_rank_float32_storage_close_to_dense():
+    H, K, V, seg, art = _random_case(9, choices=(128,), kv="f32")
+    q = np.random.default_rng(109).normal(size=K.shape[1])
+    out, _, _ = O.decode_head(q, 0.0, art)
+    ref = O.dense_attention(q, K, V)
+    assert np.max(np.abs(out - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_identical_rows_summary_equals_exact_attention():
+    """P2: a span whose members share one key and one value: its summary entry with
+    +ln|S| carries exactly the softmax mass of its |S| tokens, so zoomed and
+    non-zoomed decodes agree, and both equal dense attention."""
+    rng = np.random.default_rng(12)
+    n, d = 120, 16
+    H = np.ones(n)
+    H[[30, 70]] = 20.0
+    K = rng.normal(size=(n, d))
+    V = rng.normal(size=(n, d))
+    seg = O.segment(H, 1.0, 0)
+    assert seg.m == 3
+    for mem in seg.members:
+        K[mem] = K[mem[0]]
+        V[mem] = V[mem[0]]
+    art = O.build_head(H, K, V, seg, 0, 0, (d,), 1, "f64")
+    q = rng.normal(size=d) * 2
+    o_zoom, z1, _ = O.decode_head(q, 0.0, art)
+    o_none, z0, _ = O.decode_head(q, 1.0, art)
+    assert z1.all() and not z0.any()
+    ref = O.dense_attention(q, K, V)
+    assert np.allclose(o_zoom, ref, atol=1e-12)
+    assert np.allclose(o_none, ref, atol=1e-12)
+
+
+def test_summary_entry_equals_expanded_copies_bruteforce():
+    """P9: with every member equal to its summary, one entry with +ln|S| equals
+    |S| separate copies of that entry in the softmax (natural log, not log2/log10)."""
+    rng = np.random.default_rng(13)
+    for trial in range(20):
+        d = 8
+        sizes = rng.integers(1, 30, size=rng.integers(1, 6))
+        kb = rng.normal(size=(len(sizes), d)) * 2
+        vb = rng.normal(size=(len(sizes), d))
+        KA = rng.normal(size=(3, d))
+        VA = rng.normal(size=(3, d))
+        art = O.HeadArtifacts(kv_dtype="f64", mstart=np.zeros(len(sizes), np.int64),
+                              mcount=sizes.astype(np.int64), anchors=np.arange(3), kbar=kb, vbar=vb,
+                              KA=KA, VA=VA, rank=np.zeros(len(sizes), np.int64), AK=[], BKt=[], AV=[], BVt=[])
+        q = rng.normal(size=d)
+        got, z, _ = O.decode_head(q, 1.0, art)
+        assert not z.any()
+        Kx = np.concatenate([KA] + [np.repeat(kb[i:i + 1], s, 0) for i, s in enumerate(sizes)])
+        Vx = np.concatenate([VA] + [np.repeat(vb[i:i + 1], s, 0) for i, s in enumerate(sizes)])
+        assert np.allclose(got, O.dense_attention(q, Kx, Vx), atol=1e-12)
+
+
+def test_no_zoom_uses_only_anchors_and_summaries():
+    """P5: tau >= 1 never reads a basis (the bases are removed to prove it)."""
+    H, K, V, seg, art = _random_case(14)
+    art.AK = art.BKt = art.AV = art.BVt = None
+    q = np.random.default_rng(114).normal(size=K.shape[1])
+    out, z, _ = O.decode_head(q, 1.0, art)
+    assert not z.any() and np.all(np.isfinite(out))
+
+
+def test_softmax_shift_invariance():
+    """P10: adding a constant to every logit leaves the output unchanged."""
+    rng = np.random.default_rng(15)
+    lg = rng.normal(size=50) * 5
+    v = rng.normal(size=(50, 7))
+    a = O.softmax_attend(lg, v)
+    b = O.softmax_attend(lg + 123.25, v)
+    assert np.allclose(a, b, atol=1e-13)
+    # an explicit split-K merge of two halves equals the one-shot softmax
+    m1, m2 = lg[:20].max(), lg[20:].max()
+    l1, l2 = np.exp(lg[:20] - m1).sum(), np.exp(lg[20:] - m2).sum()
+    a1 = np.exp(lg[:20] - m1) @ v[:20]
+    a2 = np.exp(lg[20:] - m2) @ v[20:]
+    M = max(m1, m2)
+    merged = (a1 * np.exp(m1 - M) + a2 * np.exp(m2 - M)) / (l1 * np.exp(m1 - M) + l2 * np.exp(m2 - M))
+    assert np.allclose(merged, a, atol=1e-13)
+
+
+def test_decode_layer_gqa_head_mapping():
+    """Query head h reads kv head h // G: swapping kv heads swaps the outputs of their query groups."""
+    H, K, V, seg, a0 = _random_case(16)
+    _, K1, V1, _, a1 = _random_case(17)
+    rng = np.random.default_rng(116)
+    q = rng.normal(size=(1, 4, K.shape[1]))
+    tau = np.full(4, 0.9)
+    out, _, _ = O.decode_layer(q, tau, {(0, 0): a0, (0, 1): a1}, G=2)
+    out2, _, _ = O.decode_layer(q, tau, {(0, 0): a1, (0, 1): a0}, G=2)
+    assert np.allclose(out[(0, 0)], O.decode_head(q[0, 0], 0.9, a0)[0])
+    assert np.allclose(out[(0, 3)], O.decode_head(q[0, 3], 0.9, a1)[0])
+    assert np.allclose(out2[(0, 1)], O.decode_head(q[0, 1], 0.9, a1)[0])
+    assert not np.allclose(out[(0, 1)], out2[(0, 1)])
+
+
+def test_zoomed_span_uses_reconstruction_not_original_tokens():
+    """A zoomed span attends over A @ Bt (rank-limited), not over the raw tokens:
+    with rank 1 on a span of random rows the output moves away from dense attention,
+    and equals attention over the explicitly reconstructed rows."""
+    rng = np.random.default_rng(18)
+    n, d = 64, 16
+    H = np.ones(n)
+    H[40] = 50.0
+    K = rng.normal(size=(n, d))
+    V = rng.normal(size=(n, d))
+    seg = O.segment(H, 1.0, 0)
+    art = O.build_head(H, K, V, seg, 0, 0, (1,), 1, "f64")
+    q = rng.normal(size=d) * 3
+    out, z, _ = O.decode_head(q, 0.0, art)
+    rows_k = [K[seg.anchors]] + [art.AK[k] @ art.BKt[k] for k in range(seg.m)]
+    rows_v = [V[seg.anchors]] + [art.AV[k] @ art.BVt[k] for k in range(seg.m)]
+    ref = O.dense_attention(q, np.concatenate(rows_k), np.concatenate(rows_v))
+    assert np.allclose(out, ref, atol=1e-12)
+    assert not np.allclose(out, O.dense_attention(q, K, V), atol=1e-3)
