@@ -1,0 +1,983 @@
+// Host runtime and C ABI of the SeKV library (see include/sekv.h).
+//
+// Owns the span tables, per-layer artefacts (summaries, anchors, packed SVD
+// bases in device memory or in a pinned host store), decode scratch (split-K
+// partials, arrival tickets), the zoom fetch path (pinned tables, device
+// staging, a side stream) and launches the HIP kernels.
+#include "sekv.h"
+#include "sekv_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace sekv;
+
+namespace {
+
+std::string g_create_err;
+
+uint64_t splitmix64(uint64_t x) {
+  // SplitMix64 output for state x (Steele, Lea, Flood 2014).
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  int v = std::atoi(s);
+  return std::min(hi, std::max(lo, v));
+}
+
+struct LayerState {
+  bool ready = false;      // every head has artefacts
+  bool allocated = false;  // layout fixed, buffers allocated
+  void* kbar = nullptr;
+  void* vbar = nullptr;
+  void* KA = nullptr;
+  void* VA = nullptr;
+  int32_t* rank_d = nullptr;
+  int64_t* boff_d = nullptr;
+  void* bases_d = nullptr;  // DEVICE home (and build scratch for HOST home)
+  void* bases_h = nullptr;  // HOST home: pinned store
+  int64_t basis_elems = 0;
+  std::vector<int32_t> rank_h;     // [B*Hkv*m_max]
+  std::vector<int64_t> boff_h;     // [B*Hkv*m_max], relative to the layer store
+  std::vector<int64_t> head_base;  // [B*Hkv + 1]
+  std::vector<uint8_t> head_set;   // [B*Hkv]
+};
+
+}  // namespace
+
+struct sekv_ctx {
+  sekv_config cfg{};
+  int G = 1;
+  size_t esz = 4;
+  bool bf16 = false;
+  std::string err;
+
+  // spans
+  bool spans_ready = false;
+  bool spans_built = false;
+  double alpha = 0.0;
+  std::vector<float> H_first;
+  int m_max = 0, na_max = 0;
+  std::vector<int32_t> m_b, na_b;
+  std::vector<std::vector<int32_t>> mstart, mcount, anchors;
+  std::vector<uint8_t> pend;  // imported span tables pending per sequence
+  int32_t* m_b_d = nullptr;
+  int32_t* na_b_d = nullptr;
+  int32_t* mstart_d = nullptr;
+  int32_t* mcount_d = nullptr;
+  int32_t* anchors_d = nullptr;
+  float* logS_d = nullptr;
+  int32_t* prob_d[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  int n_prob[5] = {0, 0, 0, 0, 0};
+
+  // build scratch
+  int32_t* seg_i = nullptr;   // [4][B][n] flagpos, mstart, mcount, anchors
+  int32_t* seg_counts = nullptr;
+  double* seg_stats = nullptr;
+  float* H_d_tmp = nullptr;
+
+  std::vector<LayerState> layers;
+
+  // decode scratch
+  float* part_ml = nullptr;
+  float* part_acc = nullptr;
+  size_t parts_cap = 0;  // partial slots
+  uint32_t* counters = nullptr;
+
+  // HOST-home fetch path
+  int32_t* zlist_d = nullptr;
+  int32_t* zcount_d = nullptr;
+  int32_t* zlist_h = nullptr;   // pinned [B*Hkv][m_max]
+  int32_t* zcount_h = nullptr;  // pinned [B*Hkv]
+  int32_t* zent_h = nullptr;    // pinned [B*Hkv*m_max]
+  int64_t* zoff_h = nullptr;
+  int32_t* zbase_h = nullptr;   // pinned [B*Hkv + 1]
+  int32_t* zent_d = nullptr;
+  int64_t* zoff_d = nullptr;
+  int32_t* zbase_d = nullptr;
+  size_t zcap = 0;              // entries capacity of the tables above
+  void* staging = nullptr;
+  int64_t staging_cap = 0;      // elements
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fetch = nullptr;
+
+  sekv_stats stats{};
+  int anchor_chunk = 256, span_chunk = 64, zoom_chunks = 8;
+};
+
+namespace {
+
+sekv_status fail(sekv_ctx* c, sekv_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  else g_create_err = msg;
+  return s;
+}
+
+#define HIPCHK(ctx, call)                                                                  \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) {                                                                \
+      (void)hipGetLastError();                                                             \
+      return fail(ctx, e_ == hipErrorOutOfMemory ? SEKV_ERR_OOM : SEKV_ERR_HIP,            \
+                  std::string(#call) + ": " + hipGetErrorString(e_));                      \
+    }                                                                                      \
+  } while (0)
+
+#define TRY(x)                      \
+  do {                              \
+    sekv_status s_ = (x);           \
+    if (s_ != SEKV_OK) return s_;   \
+  } while (0)
+
+struct DevGuard {
+  int prev = -1;
+  explicit DevGuard(int d) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != d) (void)hipSetDevice(d);
+  }
+  ~DevGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename P>
+sekv_status dalloc(sekv_ctx* c, P** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, e == hipErrorOutOfMemory ? SEKV_ERR_OOM : SEKV_ERR_HIP,
+                "hipMalloc(" + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  }
+  *p = static_cast<P*>(q);
+  return SEKV_OK;
+}
+
+template <typename P>
+sekv_status halloc(sekv_ctx* c, P** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  const char* f = std::getenv("SEKV_FAULT");
+  if (f && std::strcmp(f, "pinned_oom") == 0)
+    return fail(c, SEKV_ERR_OOM, "pinned host allocation refused (SEKV_FAULT=pinned_oom)");
+  void* q = nullptr;
+  hipError_t e = hipHostMalloc(&q, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, SEKV_ERR_OOM, "hipHostMalloc(" + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  }
+  *p = static_cast<P*>(q);
+  return SEKV_OK;
+}
+
+template <typename P>
+void dfree(P*& p) {
+  if (p) (void)hipFree((void*)p);
+  p = nullptr;
+}
+template <typename P>
+void hfree(P*& p) {
+  if (p) (void)hipHostFree((void*)p);
+  p = nullptr;
+}
+
+void free_layer(LayerState& L) {
+  dfree(L.kbar);
+  dfree(L.vbar);
+  dfree(L.KA);
+  dfree(L.VA);
+  dfree(L.rank_d);
+  dfree(L.boff_d);
+  dfree(L.bases_d);
+  hfree(L.bases_h);
+  L = LayerState();
+}
+
+int64_t span_elems(int c, int r, int d) {
+  return 2 * pad8((int64_t)c * r) + 2 * pad8((int64_t)r * d);
+}
+
+// Install span tables (host vectors already filled); uploads device copies
+// and the SVD problem buckets.
+sekv_status install_spans(sekv_ctx* c) {
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads;
+  c->m_b.assign(B, 0);
+  c->na_b.assign(B, 0);
+  int mm = 1, nm = 1;
+  for (int b = 0; b < B; ++b) {
+    c->m_b[b] = (int)c->mstart[b].size();
+    c->na_b[b] = (int)c->anchors[b].size();
+    mm = std::max(mm, c->m_b[b]);
+    nm = std::max(nm, c->na_b[b]);
+  }
+  c->m_max = mm;
+  c->na_max = nm;
+  dfree(c->m_b_d);
+  dfree(c->na_b_d);
+  dfree(c->mstart_d);
+  dfree(c->mcount_d);
+  dfree(c->anchors_d);
+  dfree(c->logS_d);
+  TRY(dalloc(c, &c->m_b_d, sizeof(int32_t) * B));
+  TRY(dalloc(c, &c->na_b_d, sizeof(int32_t) * B));
+  TRY(dalloc(c, &c->mstart_d, sizeof(int32_t) * B * mm));
+  TRY(dalloc(c, &c->mcount_d, sizeof(int32_t) * B * mm));
+  TRY(dalloc(c, &c->anchors_d, sizeof(int32_t) * B * nm));
+  TRY(dalloc(c, &c->logS_d, sizeof(float) * B * mm));
+  std::vector<int32_t> ms((size_t)B * mm, 0), mc((size_t)B * mm, 0), an((size_t)B * nm, 0);
+  std::vector<float> ls((size_t)B * mm, 0.f);
+  for (int b = 0; b < B; ++b) {
+    for (int k = 0; k < c->m_b[b]; ++k) {
+      ms[(size_t)b * mm + k] = c->mstart[b][k];
+      mc[(size_t)b * mm + k] = c->mcount[b][k];
+      ls[(size_t)b * mm + k] = (float)std::log((double)c->mcount[b][k]);
+    }
+    for (int i = 0; i < c->na_b[b]; ++i) an[(size_t)b * nm + i] = c->anchors[b][i];
+  }
+  HIPCHK(c, hipMemcpy(c->m_b_d, c->m_b.data(), sizeof(int32_t) * B, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->na_b_d, c->na_b.data(), sizeof(int32_t) * B, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->mstart_d, ms.data(), ms.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->mcount_d, mc.data(), mc.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->anchors_d, an.data(), an.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->logS_d, ls.data(), ls.size() * 4, hipMemcpyHostToDevice));
+
+  // SVD problem buckets by member count
+  std::vector<int32_t> pr[5];
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g)
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        const int cnt = c->mcount[b][k];
+        const int bk = cnt <= 16 ? 0 : cnt <= 32 ? 1 : cnt <= 64 ? 2 : cnt <= 128 ? 3 : 4;
+        for (int w = 0; w < 2; ++w) {
+          pr[bk].push_back(b * Hkv + g);
+          pr[bk].push_back(k);
+          pr[bk].push_back(w);
+        }
+      }
+  for (int i = 0; i < 5; ++i) {
+    dfree(c->prob_d[i]);
+    c->n_prob[i] = (int)(pr[i].size() / 3);
+    TRY(dalloc(c, &c->prob_d[i], pr[i].size() * 4));
+    if (!pr[i].empty())
+      HIPCHK(c, hipMemcpy(c->prob_d[i], pr[i].data(), pr[i].size() * 4, hipMemcpyHostToDevice));
+  }
+  c->spans_ready = true;
+  return SEKV_OK;
+}
+
+// Fix the layout of a layer from per-(b, g, k) ranks and allocate its buffers.
+sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank) {
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  LayerState& L = c->layers[layer];
+  free_layer(L);
+  const int mm = c->m_max, nm = c->na_max;
+  L.rank_h = rank;
+  L.boff_h.assign((size_t)B * Hkv * mm, 0);
+  L.head_base.assign((size_t)B * Hkv + 1, 0);
+  L.head_set.assign((size_t)B * Hkv, 0);
+  int64_t off = 0;
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      const size_t bg = (size_t)b * Hkv + g;
+      L.head_base[bg] = off;
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        L.boff_h[bg * mm + k] = off;
+        off += span_elems(c->mcount[b][k], rank[bg * mm + k], d);
+      }
+    }
+  L.head_base[(size_t)B * Hkv] = off;
+  L.basis_elems = off;
+  const size_t rows_m = (size_t)B * Hkv * mm, rows_a = (size_t)B * Hkv * nm;
+  TRY(dalloc(c, &L.kbar, rows_m * d * c->esz));
+  TRY(dalloc(c, &L.vbar, rows_m * d * c->esz));
+  TRY(dalloc(c, &L.KA, rows_a * d * c->esz));
+  TRY(dalloc(c, &L.VA, rows_a * d * c->esz));
+  TRY(dalloc(c, &L.rank_d, rows_m * 4));
+  TRY(dalloc(c, &L.boff_d, rows_m * 8));
+  HIPCHK(c, hipMemset(L.kbar, 0, rows_m * d * c->esz));
+  HIPCHK(c, hipMemset(L.vbar, 0, rows_m * d * c->esz));
+  HIPCHK(c, hipMemset(L.KA, 0, rows_a * d * c->esz));
+  HIPCHK(c, hipMemset(L.VA, 0, rows_a * d * c->esz));
+  HIPCHK(c, hipMemcpy(L.rank_d, L.rank_h.data(), rows_m * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(L.boff_d, L.boff_h.data(), rows_m * 8, hipMemcpyHostToDevice));
+  TRY(dalloc(c, &L.bases_d, (size_t)off * c->esz));
+  if (c->cfg.basis_home == SEKV_BASES_HOST) TRY(halloc(c, &L.bases_h, (size_t)off * c->esz));
+  L.allocated = true;
+  return SEKV_OK;
+}
+
+sekv_status ensure_parts(sekv_ctx* c, size_t slots) {
+  if (slots <= c->parts_cap) return SEKV_OK;
+  dfree(c->part_ml);
+  dfree(c->part_acc);
+  c->parts_cap = 0;
+  TRY(dalloc(c, &c->part_ml, slots * 2 * sizeof(float)));
+  TRY(dalloc(c, &c->part_acc, slots * c->cfg.d_head * sizeof(float)));
+  c->parts_cap = slots;
+  return SEKV_OK;
+}
+
+sekv_status ensure_fetch_tables(sekv_ctx* c) {
+  const int BH = c->cfg.batch * c->cfg.n_kv_heads;
+  const size_t need = (size_t)BH * c->m_max;
+  if (need <= c->zcap && c->zlist_d) return SEKV_OK;
+  dfree(c->zlist_d);
+  dfree(c->zcount_d);
+  dfree(c->zent_d);
+  dfree(c->zoff_d);
+  dfree(c->zbase_d);
+  hfree(c->zlist_h);
+  hfree(c->zcount_h);
+  hfree(c->zent_h);
+  hfree(c->zoff_h);
+  hfree(c->zbase_h);
+  c->zcap = 0;
+  TRY(dalloc(c, &c->zlist_d, need * 4));
+  TRY(dalloc(c, &c->zcount_d, (size_t)BH * 4));
+  TRY(dalloc(c, &c->zent_d, need * 4));
+  TRY(dalloc(c, &c->zoff_d, need * 8));
+  TRY(dalloc(c, &c->zbase_d, ((size_t)BH + 1) * 4));
+  TRY(halloc(c, &c->zlist_h, need * 4));
+  TRY(halloc(c, &c->zcount_h, (size_t)BH * 4));
+  TRY(halloc(c, &c->zent_h, need * 4));
+  TRY(halloc(c, &c->zoff_h, need * 8));
+  TRY(halloc(c, &c->zbase_h, ((size_t)BH + 1) * 4));
+  c->zcap = need;
+  return SEKV_OK;
+}
+
+sekv_status check_layer(sekv_ctx* c, int layer) {
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(c, SEKV_ERR_INVALID, "layer " + std::to_string(layer) + " out of range");
+  if (!c->spans_ready) return fail(c, SEKV_ERR_STATE, "no span table: build or import first");
+  if (!c->layers[layer].ready)
+    return fail(c, SEKV_ERR_STATE, "layer " + std::to_string(layer) + " has no artefacts");
+  return SEKV_OK;
+}
+
+void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
+  std::memset(&a, 0, sizeof(a));
+  a.B = c->cfg.batch;
+  a.Hq = c->cfg.n_q_heads;
+  a.Hkv = c->cfg.n_kv_heads;
+  a.G = c->G;
+  a.m_max = c->m_max;
+  a.na_max = c->na_max;
+  a.m_b = c->m_b_d;
+  a.na_b = c->na_b_d;
+  a.mcount = c->mcount_d;
+  a.logS = c->logS_d;
+  a.kbar = L.kbar;
+  a.vbar = L.vbar;
+  a.KA = L.KA;
+  a.VA = L.VA;
+  a.rank = L.rank_d;
+  a.boff = L.boff_d;
+  a.bases = L.bases_d;
+  int na_any = 0;
+  for (int v : c->na_b) na_any = std::max(na_any, v);
+  int m_any = 0;
+  for (int v : c->m_b) m_any = std::max(m_any, v);
+  a.anchor_chunk = c->anchor_chunk;
+  a.n_anchor_chunks = (na_any + c->anchor_chunk - 1) / c->anchor_chunk;
+  a.span_chunk = c->span_chunk;
+  a.n_span_chunks = (m_any + c->span_chunk - 1) / c->span_chunk;
+  a.n_zoom_chunks = c->zoom_chunks;
+  a.counters = c->counters;
+}
+
+sekv_status thetas(sekv_ctx* c, const float* tau, DecodeArgs& a) {
+  if (!tau) return fail(c, SEKV_ERR_INVALID, "tau is NULL");
+  for (int h = 0; h < c->cfg.n_q_heads; ++h) {
+    const double t = (double)tau[h];
+    if (std::isnan(t)) return fail(c, SEKV_ERR_INVALID, "tau[" + std::to_string(h) + "] is NaN");
+    if (t <= 0.0) a.theta[h] = -INFINITY;
+    else if (t >= 1.0) a.theta[h] = INFINITY;
+    else a.theta[h] = std::log(t) - std::log1p(-t);
+  }
+  return SEKV_OK;
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+
+extern "C" {
+
+const char* sekv_last_error(const sekv_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_create_err.c_str();
+}
+
+sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
+  if (!cfg || !out) return fail(nullptr, SEKV_ERR_INVALID, "NULL argument");
+  *out = nullptr;
+  const sekv_config& k = *cfg;
+  if (k.n_layers < 1 || k.batch < 1 || k.n_ctx < 1 || k.n_q_heads < 1 || k.n_kv_heads < 1)
+    return fail(nullptr, SEKV_ERR_INVALID, "sizes must be >= 1");
+  if (k.n_q_heads % k.n_kv_heads != 0)
+    return fail(nullptr, SEKV_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  const int G = k.n_q_heads / k.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(nullptr, SEKV_ERR_INVALID, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+  if (k.n_q_heads > kMaxHq) return fail(nullptr, SEKV_ERR_INVALID, "at most 64 query heads");
+  if (k.d_head != 64 && k.d_head != 128) return fail(nullptr, SEKV_ERR_INVALID, "d_head must be 64 or 128");
+  if (k.kv_dtype != SEKV_F32 && k.kv_dtype != SEKV_BF16) return fail(nullptr, SEKV_ERR_INVALID, "bad kv_dtype");
+  if (k.local_window < 0) return fail(nullptr, SEKV_ERR_INVALID, "local_window must be >= 0");
+  if (k.basis_home != SEKV_BASES_HOST && k.basis_home != SEKV_BASES_DEVICE)
+    return fail(nullptr, SEKV_ERR_INVALID, "bad basis_home");
+  if (k.n_ctx >= (1 << 24)) return fail(nullptr, SEKV_ERR_INVALID, "n_ctx must be < 2^24");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || k.device < 0 || k.device >= ndev) {
+    (void)hipGetLastError();
+    return fail(nullptr, SEKV_ERR_HIP, "HIP device " + std::to_string(k.device) + " not available");
+  }
+  DevGuard dg(k.device);
+  sekv_ctx* c = new sekv_ctx();
+  c->cfg = k;
+  c->G = G;
+  c->bf16 = k.kv_dtype == SEKV_BF16;
+  c->esz = c->bf16 ? 2 : 4;
+  c->layers.resize(k.n_layers);
+  c->pend.assign(k.batch, 0);
+  c->mstart.assign(k.batch, {});
+  c->mcount.assign(k.batch, {});
+  c->anchors.assign(k.batch, {});
+  c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
+  c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
+  c->zoom_chunks = env_int("SEKV_ZOOM_CHUNKS", 8, 1, 1024);
+  sekv_status s = dalloc(c, &c->counters, sizeof(uint32_t) * k.batch * k.n_kv_heads);
+  if (s == SEKV_OK && hipMemset(c->counters, 0, sizeof(uint32_t) * k.batch * k.n_kv_heads) != hipSuccess)
+    s = fail(c, SEKV_ERR_HIP, "hipMemset(counters)");
+  if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess)
+    s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side)");
+  if (s == SEKV_OK && hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming) != hipSuccess)
+    s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
+  if (s != SEKV_OK) {
+    g_create_err = c->err;
+    sekv_destroy(c);
+    return s;
+  }
+  const int64_t full = 2ll * k.n_layers * k.batch * k.n_kv_heads * (int64_t)k.n_ctx * k.d_head * c->esz;
+  c->stats.full_kv_bytes = full;
+  *out = c;
+  return SEKV_OK;
+}
+
+void sekv_destroy(sekv_ctx* c) {
+  if (!c) return;
+  DevGuard dg(c->cfg.device);
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  for (auto& L : c->layers) free_layer(L);
+  dfree(c->m_b_d);
+  dfree(c->na_b_d);
+  dfree(c->mstart_d);
+  dfree(c->mcount_d);
+  dfree(c->anchors_d);
+  dfree(c->logS_d);
+  for (auto& p : c->prob_d) dfree(p);
+  dfree(c->seg_i);
+  dfree(c->seg_counts);
+  dfree(c->seg_stats);
+  dfree(c->part_ml);
+  dfree(c->part_acc);
+  dfree(c->counters);
+  dfree(c->zlist_d);
+  dfree(c->zcount_d);
+  dfree(c->zent_d);
+  dfree(c->zoff_d);
+  dfree(c->zbase_d);
+  hfree(c->zlist_h);
+  hfree(c->zcount_h);
+  hfree(c->zent_h);
+  hfree(c->zoff_h);
+  hfree(c->zbase_h);
+  dfree(c->staging);
+  if (c->ev_fetch) (void)hipEventDestroy(c->ev_fetch);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  delete c;
+}
+
+// ---------------------------------------------------------------------------- build
+
+sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K, const void* V,
+                       double alpha, const int32_t* rank_choices, int32_t n_choices,
+                       uint64_t rank_seed, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, n = c->cfg.n_ctx, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SEKV_ERR_INVALID, "layer out of range");
+  if (!H || !K || !V) return fail(c, SEKV_ERR_INVALID, "NULL H, K or V");
+  if (!std::isfinite(alpha)) return fail(c, SEKV_ERR_INVALID, "alpha must be finite");
+  if (!rank_choices || n_choices < 1) return fail(c, SEKV_ERR_INVALID, "rank choices missing");
+  for (int i = 0; i < n_choices; ++i)
+    if (rank_choices[i] < 1) return fail(c, SEKV_ERR_INVALID, "rank choice < 1");
+
+  // 1. segmentation
+  if (!c->seg_i) {
+    TRY(dalloc(c, &c->seg_i, sizeof(int32_t) * 4 * (size_t)B * n));
+    TRY(dalloc(c, &c->seg_counts, sizeof(int32_t) * 4 * B));
+    TRY(dalloc(c, &c->seg_stats, sizeof(double) * 3 * B));
+  }
+  SegmentArgs sa;
+  sa.H = H;
+  sa.B = B;
+  sa.n = n;
+  sa.w = c->cfg.local_window;
+  sa.alpha = alpha;
+  sa.flagpos = c->seg_i;
+  sa.mstart = c->seg_i + (size_t)B * n;
+  sa.mcount = c->seg_i + 2 * (size_t)B * n;
+  sa.anchors = c->seg_i + 3 * (size_t)B * n;
+  sa.counts = c->seg_counts;
+  sa.stats = c->seg_stats;
+  launch_segment(sa, stream);
+  HIPCHK(c, hipGetLastError());
+  std::vector<int32_t> counts(4 * B);
+  HIPCHK(c, hipMemcpyAsync(counts.data(), c->seg_counts, counts.size() * 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(c, hipStreamSynchronize(stream));
+  for (int b = 0; b < B; ++b)
+    if (counts[4 * b + 2]) return fail(c, SEKV_ERR_INVALID, "surprisal must be finite and >= 0");
+  std::vector<std::vector<int32_t>> ms(B), mc(B), an(B);
+  for (int b = 0; b < B; ++b) {
+    ms[b].resize(counts[4 * b + 0]);
+    mc[b].resize(counts[4 * b + 0]);
+    an[b].resize(counts[4 * b + 1]);
+    HIPCHK(c, hipMemcpy(ms[b].data(), sa.mstart + (size_t)b * n, ms[b].size() * 4, hipMemcpyDeviceToHost));
+    HIPCHK(c, hipMemcpy(mc[b].data(), sa.mcount + (size_t)b * n, mc[b].size() * 4, hipMemcpyDeviceToHost));
+    HIPCHK(c, hipMemcpy(an[b].data(), sa.anchors + (size_t)b * n, an[b].size() * 4, hipMemcpyDeviceToHost));
+  }
+  if (c->spans_ready) {
+    bool same = true;
+    for (int b = 0; b < B && same; ++b)
+      same = ms[b] == c->mstart[b] && mc[b] == c->mcount[b] && an[b] == c->anchors[b];
+    if (!same) return fail(c, SEKV_ERR_STATE, "surprisal or alpha differ from the span table in use");
+  } else {
+    c->mstart = ms;
+    c->mcount = mc;
+    c->anchors = an;
+    TRY(install_spans(c));
+    c->spans_built = true;
+    c->alpha = alpha;
+  }
+
+  // 2. ranks and layout
+  const int mm = c->m_max;
+  std::vector<int32_t> rank((size_t)B * Hkv * mm, 0);
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g)
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        const uint64_t key = rank_seed ^ ((uint64_t)layer << 40) ^ ((uint64_t)g << 32) ^ (uint64_t)k;
+        int r = rank_choices[splitmix64(key) % (uint64_t)n_choices];
+        r = std::min(r, std::min(c->mcount[b][k], d));
+        rank[((size_t)b * Hkv + g) * mm + k] = r;
+      }
+  TRY(alloc_layer(c, layer, rank));
+  LayerState& L = c->layers[layer];
+
+  // 3. summaries and anchors
+  SummaryArgs su;
+  su.H = H;
+  su.K = K;
+  su.V = V;
+  su.B = B;
+  su.Hkv = Hkv;
+  su.n = n;
+  su.m_max = mm;
+  su.na_max = c->na_max;
+  su.m_b = c->m_b_d;
+  su.mstart = c->mstart_d;
+  su.mcount = c->mcount_d;
+  su.na_b = c->na_b_d;
+  su.anchors = c->anchors_d;
+  su.kbar = L.kbar;
+  su.vbar = L.vbar;
+  su.KA = L.KA;
+  su.VA = L.VA;
+  su.span_chunk = 16;
+  su.n_span_chunks = (mm + su.span_chunk - 1) / su.span_chunk;
+  su.anchor_chunk = 256;
+  su.n_anchor_chunks = (c->na_max + su.anchor_chunk - 1) / su.anchor_chunk;
+  launch_summaries(d, c->bf16, su, stream);
+  HIPCHK(c, hipGetLastError());
+
+  // 4. truncated SVD of every span, K and V, straight into the packed store
+  SvdArgs sv;
+  sv.K = K;
+  sv.V = V;
+  sv.Hkv = Hkv;
+  sv.n = n;
+  sv.m_max = mm;
+  sv.mstart = c->mstart_d;
+  sv.mcount = c->mcount_d;
+  sv.rank = L.rank_d;
+  sv.boff = L.boff_d;
+  sv.bases = L.bases_d;
+  const int cmax[5] = {16, 32, 64, 128, 0};
+  for (int i = 0; i < 5; ++i) {
+    sv.problems = c->prob_d[i];
+    sv.n_problems = c->n_prob[i];
+    launch_svd(cmax[i], d, c->bf16, sv, stream);
+    HIPCHK(c, hipGetLastError());
+  }
+  // 5. HOST home: move the store to pinned memory
+  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+    HIPCHK(c, hipMemcpyAsync(L.bases_h, L.bases_d, (size_t)L.basis_elems * c->esz, hipMemcpyDeviceToHost,
+                             stream));
+  }
+  HIPCHK(c, hipStreamSynchronize(stream));
+  if (c->cfg.basis_home == SEKV_BASES_HOST) dfree(L.bases_d);
+  std::fill(L.head_set.begin(), L.head_set.end(), 1);
+  L.ready = true;
+  return SEKV_OK;
+}
+
+sekv_status sekv_get_spans(const sekv_ctx* cc, int32_t b, int32_t* m, int32_t* n_anchors, int32_t* m_max,
+                           int32_t* mstart, int32_t* mcount, int32_t* anchors) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  if (!c->spans_ready) return fail(c, SEKV_ERR_STATE, "no span table yet");
+  if (b < 0 || b >= c->cfg.batch) return fail(c, SEKV_ERR_INVALID, "b out of range");
+  if (m) *m = c->m_b[b];
+  if (n_anchors) *n_anchors = c->na_b[b];
+  if (m_max) *m_max = c->m_max;
+  if (mstart) std::memcpy(mstart, c->mstart[b].data(), c->mstart[b].size() * 4);
+  if (mcount) std::memcpy(mcount, c->mcount[b].data(), c->mcount[b].size() * 4);
+  if (anchors) std::memcpy(anchors, c->anchors[b].data(), c->anchors[b].size() * 4);
+  return SEKV_OK;
+}
+
+sekv_status sekv_get_bases_layout(const sekv_ctx* cc, int32_t layer, int32_t b, int32_t g, int32_t* rank,
+                                  int64_t* basis_off, int64_t* basis_elems) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= c->cfg.batch || g < 0 || g >= c->cfg.n_kv_heads)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  LayerState& L = c->layers[layer];
+  if (!L.allocated) return fail(c, SEKV_ERR_STATE, "layer has no layout");
+  const size_t bg = (size_t)b * c->cfg.n_kv_heads + g;
+  const int m = c->m_b[b];
+  for (int k = 0; k < m; ++k) {
+    if (rank) rank[k] = L.rank_h[bg * c->m_max + k];
+    if (basis_off) basis_off[k] = L.boff_h[bg * c->m_max + k] - L.head_base[bg];
+  }
+  if (basis_elems) *basis_elems = L.head_base[bg + 1] - L.head_base[bg];
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------------------- decode
+
+sekv_status sekv_zoom_fetch(sekv_ctx* c, int32_t layer, const int32_t* entries, const int32_t* counts,
+                            hipStream_t side, hipEvent_t done) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  TRY(check_layer(c, layer));
+  if (c->cfg.basis_home != SEKV_BASES_HOST) return fail(c, SEKV_ERR_STATE, "bases are device-resident");
+  if (!entries || !counts) return fail(c, SEKV_ERR_INVALID, "NULL entries or counts");
+  TRY(ensure_fetch_tables(c));
+  LayerState& L = c->layers[layer];
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, mm = c->m_max;
+  // sizing pass and validation (entries copied to the pinned table and sorted per (b, g))
+  int64_t need = 0;
+  size_t ne = 0;
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      const size_t bg = (size_t)b * Hkv + g;
+      const int cnt = counts[bg];
+      if (cnt < 0 || cnt > c->m_b[b]) return fail(c, SEKV_ERR_INVALID, "zoom count out of range");
+      c->zbase_h[bg] = (int32_t)ne;
+      int32_t* z = c->zent_h + ne;
+      if (entries != c->zent_h) std::memcpy(z, entries + bg * mm, (size_t)cnt * 4);
+      std::sort(z, z + cnt, [](int32_t x, int32_t y) { return (x & 0xffffff) < (y & 0xffffff); });
+      for (int i = 0; i < cnt; ++i) {
+        const int k = z[i] & 0xffffff;
+        if (k >= c->m_b[b]) return fail(c, SEKV_ERR_INVALID, "zoom entry: span id out of range");
+        if (i > 0 && k == (z[i - 1] & 0xffffff)) return fail(c, SEKV_ERR_INVALID, "zoom entry: duplicate span");
+        need += span_elems(c->mcount[b][k], L.rank_h[bg * mm + k], d);
+      }
+      ne += cnt;
+    }
+  c->zbase_h[(size_t)B * Hkv] = (int32_t)ne;
+  if (need > c->staging_cap) {
+    dfree(c->staging);
+    c->staging_cap = 0;
+    const int64_t cap = std::max<int64_t>(need, std::min<int64_t>(L.basis_elems, need * 2));
+    TRY(dalloc(c, &c->staging, (size_t)cap * c->esz));
+    c->staging_cap = cap;
+  }
+  const char* f = std::getenv("SEKV_FAULT");
+  if (f && std::strcmp(f, "fetch") == 0) return fail(c, SEKV_ERR_HIP, "fetch failure forced (SEKV_FAULT=fetch)");
+  // copies, runs of adjacent spans coalesced
+  const char* hsrc = static_cast<const char*>(L.bases_h);
+  char* dst = static_cast<char*>(c->staging);
+  int64_t pos = 0;
+  uint64_t ncopies = 0;
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      const size_t bg = (size_t)b * Hkv + g;
+      int64_t run_src = -1, run_dst = 0, run_len = 0;
+      for (int i = c->zbase_h[bg]; i < c->zbase_h[bg + 1]; ++i) {
+        const int k = c->zent_h[i] & 0xffffff;
+        const int64_t off = L.boff_h[bg * mm + k];
+        const int64_t sz = span_elems(c->mcount[b][k], L.rank_h[bg * mm + k], d);
+        c->zoff_h[i] = pos;
+        if (run_src >= 0 && off == run_src + run_len) {
+          run_len += sz;
+        } else {
+          if (run_src >= 0) {
+            HIPCHK(c, hipMemcpyAsync(dst + run_dst * c->esz, hsrc + run_src * c->esz, run_len * c->esz,
+                                     hipMemcpyHostToDevice, side));
+            ++ncopies;
+          }
+          run_src = off;
+          run_dst = pos;
+          run_len = sz;
+        }
+        pos += sz;
+      }
+      if (run_src >= 0) {
+        HIPCHK(c, hipMemcpyAsync(dst + run_dst * c->esz, hsrc + run_src * c->esz, run_len * c->esz,
+                                 hipMemcpyHostToDevice, side));
+        ++ncopies;
+      }
+    }
+  if (ne) {
+    HIPCHK(c, hipMemcpyAsync(c->zent_d, c->zent_h, ne * 4, hipMemcpyHostToDevice, side));
+    HIPCHK(c, hipMemcpyAsync(c->zoff_d, c->zoff_h, ne * 8, hipMemcpyHostToDevice, side));
+  }
+  HIPCHK(c, hipMemcpyAsync(c->zbase_d, c->zbase_h, ((size_t)B * Hkv + 1) * 4, hipMemcpyHostToDevice, side));
+  if (done) HIPCHK(c, hipEventRecord(done, side));
+  c->stats.fetch_calls++;
+  c->stats.spans_fetched += ne;
+  c->stats.bytes_fetched += (uint64_t)pos * c->esz;
+  c->stats.memcpy_calls += ncopies;
+  return SEKV_OK;
+}
+
+sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
+                             uint8_t* zoom_mask, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  TRY(check_layer(c, layer));
+  if (!q || !out) return fail(c, SEKV_ERR_INVALID, "NULL q or out");
+  LayerState& L = c->layers[layer];
+  DecodeArgs a;
+  fill_decode_geometry(c, L, a);
+  TRY(thetas(c, tau, a));
+  a.q = q;
+  a.out = out;
+  a.mask = zoom_mask;
+  const bool host = c->cfg.basis_home == SEKV_BASES_HOST;
+  const int nc1 = a.n_anchor_chunks + a.n_span_chunks;
+  a.n_parts = nc1 + (host ? a.n_zoom_chunks : 0);
+  TRY(ensure_parts(c, (size_t)a.B * a.Hq * a.n_parts));
+  a.part_ml = c->part_ml;
+  a.part_acc = c->part_acc;
+  c->stats.decode_calls++;
+  if (!host) {
+    launch_decode_main(0, c->cfg.d_head, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
+    return SEKV_OK;
+  }
+  TRY(ensure_fetch_tables(c));
+  const int BH = a.B * a.Hkv;
+  a.zlist = c->zlist_d;
+  a.zcount = c->zcount_d;
+  HIPCHK(c, hipMemsetAsync(c->zcount_d, 0, (size_t)BH * 4, stream));
+  launch_decode_main(1, c->cfg.d_head, c->bf16, a, stream);
+  HIPCHK(c, hipGetLastError());
+  HIPCHK(c, hipMemcpyAsync(c->zcount_h, c->zcount_d, (size_t)BH * 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(c, hipMemcpyAsync(c->zlist_h, c->zlist_d, (size_t)BH * c->m_max * 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(c, hipStreamSynchronize(stream));
+  TRY(sekv_zoom_fetch(c, layer, c->zlist_h, c->zcount_h, c->side, c->ev_fetch));
+  HIPCHK(c, hipStreamWaitEvent(stream, c->ev_fetch, 0));
+  a.zent = c->zent_d;
+  a.zoff = c->zoff_d;
+  a.zbase = c->zbase_d;
+  a.staging = c->staging;
+  launch_decode_staged_zoom(c->cfg.d_head, c->bf16, a, stream);
+  HIPCHK(c, hipGetLastError());
+  return SEKV_OK;
+}
+
+sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float* scores, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  TRY(check_layer(c, layer));
+  if (!q || !scores) return fail(c, SEKV_ERR_INVALID, "NULL q or scores");
+  LayerState& L = c->layers[layer];
+  DecodeArgs a;
+  fill_decode_geometry(c, L, a);
+  for (int h = 0; h < kMaxHq; ++h) a.theta[h] = INFINITY;
+  a.q = q;
+  a.scores = scores;
+  launch_decode_main(2, c->cfg.d_head, c->bf16, a, stream);
+  HIPCHK(c, hipGetLastError());
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------------------- artefact exchange
+
+sekv_status sekv_import_spans(sekv_ctx* c, int32_t b, int32_t m, const int32_t* mstart, const int32_t* mcount,
+                              int32_t n_anchors, const int32_t* anchors) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  if (c->spans_built) return fail(c, SEKV_ERR_STATE, "span table fixed by sekv_build");
+  const int n = c->cfg.n_ctx;
+  if (b < 0 || b >= c->cfg.batch) return fail(c, SEKV_ERR_INVALID, "b out of range");
+  if (m < 0 || n_anchors < 0 || m + n_anchors > n) return fail(c, SEKV_ERR_INVALID, "bad sizes");
+  if ((m && (!mstart || !mcount)) || (n_anchors && !anchors)) return fail(c, SEKV_ERR_INVALID, "NULL arrays");
+  std::vector<uint8_t> used(n, 0);
+  int prev_end = 0;
+  for (int k = 0; k < m; ++k) {
+    if (mcount[k] < 1 || mstart[k] < prev_end || (int64_t)mstart[k] + mcount[k] > n)
+      return fail(c, SEKV_ERR_INVALID, "spans must be non-empty, ascending, disjoint, inside [0, n)");
+    for (int t = mstart[k]; t < mstart[k] + mcount[k]; ++t) used[t] = 1;
+    prev_end = mstart[k] + mcount[k];
+  }
+  for (int i = 0; i < n_anchors; ++i) {
+    if (anchors[i] < 0 || anchors[i] >= n || (i && anchors[i] <= anchors[i - 1]) || used[anchors[i]])
+      return fail(c, SEKV_ERR_INVALID, "anchors must be ascending, inside [0, n) and not members");
+  }
+  if (c->spans_ready) {
+    // re-import invalidates the layers
+    for (auto& L : c->layers) free_layer(L);
+    c->spans_ready = false;
+  }
+  c->mstart[b].assign(mstart, mstart + m);
+  c->mcount[b].assign(mcount, mcount + m);
+  c->anchors[b].assign(anchors, anchors + n_anchors);
+  c->pend[b] = 1;
+  for (int i = 0; i < c->cfg.batch; ++i)
+    if (!c->pend[i]) return SEKV_OK;
+  return install_spans(c);
+}
+
+sekv_status sekv_import_layout(sekv_ctx* c, int32_t layer, const int32_t* rank) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SEKV_ERR_INVALID, "layer out of range");
+  if (!c->spans_ready) return fail(c, SEKV_ERR_STATE, "import or build the span tables first");
+  if (!rank) return fail(c, SEKV_ERR_INVALID, "NULL rank");
+  const int mm = c->m_max;
+  std::vector<int32_t> rk((size_t)B * Hkv * mm, 0);
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g)
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        const size_t i = ((size_t)b * Hkv + g) * mm + k;
+        if (rank[i] < 1 || rank[i] > std::min(c->mcount[b][k], d))
+          return fail(c, SEKV_ERR_INVALID, "rank out of range");
+        rk[i] = rank[i];
+      }
+  TRY(alloc_layer(c, layer, rk));
+  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+    LayerState& L = c->layers[layer];
+    std::memset(L.bases_h, 0, (size_t)L.basis_elems * c->esz);
+    dfree(L.bases_d);
+  }
+  return SEKV_OK;
+}
+
+sekv_status sekv_import_head(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, const void* kbar, const void* vbar,
+                             const void* KA, const void* VA, const int32_t* rank, const void* bases,
+                             int64_t basis_elems) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= B || g < 0 || g >= Hkv)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  if (!c->spans_ready) return fail(c, SEKV_ERR_STATE, "import or build the span tables first");
+  const int m = c->m_b[b], na = c->na_b[b], mm = c->m_max;
+  if ((m && (!kbar || !vbar || !rank || !bases)) || (na && (!KA || !VA)))
+    return fail(c, SEKV_ERR_INVALID, "NULL arrays");
+  for (int k = 0; k < m; ++k)
+    if (rank[k] < 1 || rank[k] > std::min(c->mcount[b][k], d))
+      return fail(c, SEKV_ERR_INVALID, "rank out of range at span " + std::to_string(k));
+  LayerState& L = c->layers[layer];
+  const size_t bg = (size_t)b * Hkv + g;
+  if (!L.allocated) return fail(c, SEKV_ERR_STATE, "layer has no layout (sekv_import_layout)");
+  for (int k = 0; k < m; ++k)
+    if (L.rank_h[bg * mm + k] != rank[k])
+      return fail(c, SEKV_ERR_INVALID, "ranks differ from the layer's layout");
+  const int64_t he = L.head_base[bg + 1] - L.head_base[bg];
+  if (basis_elems != he)
+    return fail(c, SEKV_ERR_INVALID, "basis_elems " + std::to_string(basis_elems) + " != layout " + std::to_string(he));
+  const size_t es = c->esz;
+  if (m) {
+    HIPCHK(c, hipMemcpy((char*)L.kbar + bg * mm * d * es, kbar, (size_t)m * d * es, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy((char*)L.vbar + bg * mm * d * es, vbar, (size_t)m * d * es, hipMemcpyHostToDevice));
+  }
+  if (na) {
+    HIPCHK(c, hipMemcpy((char*)L.KA + bg * c->na_max * d * es, KA, (size_t)na * d * es, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy((char*)L.VA + bg * c->na_max * d * es, VA, (size_t)na * d * es, hipMemcpyHostToDevice));
+  }
+  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+    std::memcpy((char*)L.bases_h + L.head_base[bg] * es, bases, (size_t)he * es);
+  } else {
+    HIPCHK(c, hipMemcpy((char*)L.bases_d + L.head_base[bg] * es, bases, (size_t)he * es, hipMemcpyHostToDevice));
+  }
+  L.head_set[bg] = 1;
+  L.ready = std::all_of(L.head_set.begin(), L.head_set.end(), [](uint8_t x) { return x != 0; });
+  return SEKV_OK;
+}
+
+sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32_t g, void* kbar, void* vbar,
+                             void* KA, void* VA, int32_t* rank, void* bases) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= B || g < 0 || g >= Hkv)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  LayerState& L = c->layers[layer];
+  const size_t bg = (size_t)b * Hkv + g;
+  if (!L.allocated || !L.head_set[bg]) return fail(c, SEKV_ERR_STATE, "head has no artefacts");
+  const int m = c->m_b[b], na = c->na_b[b], mm = c->m_max;
+  const size_t es = c->esz;
+  if (kbar && m) HIPCHK(c, hipMemcpy(kbar, (char*)L.kbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
+  if (vbar && m) HIPCHK(c, hipMemcpy(vbar, (char*)L.vbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
+  if (KA && na) HIPCHK(c, hipMemcpy(KA, (char*)L.KA + bg * c->na_max * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
+  if (VA && na) HIPCHK(c, hipMemcpy(VA, (char*)L.VA + bg * c->na_max * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
+  if (rank) std::memcpy(rank, L.rank_h.data() + bg * mm, (size_t)m * 4);
+  if (bases) {
+    const int64_t he = L.head_base[bg + 1] - L.head_base[bg];
+    if (c->cfg.basis_home == SEKV_BASES_HOST)
+      std::memcpy(bases, (char*)L.bases_h + L.head_base[bg] * es, (size_t)he * es);
+    else
+      HIPCHK(c, hipMemcpy(bases, (char*)L.bases_d + L.head_base[bg] * es, (size_t)he * es, hipMemcpyDeviceToHost));
+  }
+  return SEKV_OK;
+}
+
+sekv_status sekv_get_stats(const sekv_ctx* cc, sekv_stats* out) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c || !out) return fail(c, SEKV_ERR_INVALID, "NULL argument");
+  sekv_stats s = c->stats;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  int64_t dev = 0, host = 0;
+  for (auto& L : c->layers) {
+    if (!L.allocated) continue;
+    dev += (int64_t)2 * B * Hkv * (c->m_max + c->na_max) * d * c->esz;  // summaries + anchors
+    dev += (int64_t)B * Hkv * c->m_max * 12;                              // rank + offset tables
+    if (c->cfg.basis_home == SEKV_BASES_DEVICE) dev += L.basis_elems * c->esz;
+    else host += L.basis_elems * c->esz;
+  }
+  s.device_resident_bytes = dev;
+  s.host_basis_bytes = host;
+  *out = s;
+  return SEKV_OK;
+}
+
+}  // extern "C"

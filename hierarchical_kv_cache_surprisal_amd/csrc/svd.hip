@@ -1,0 +1,374 @@
+// Batched truncated SVD of SeKV span matrices for gfx950.
+//
+// For every (sequence, kv head, span, K-or-V) the member rows X (c x d) are
+// factorised and the top r = r_eff singular triplets are stored as
+// A = U_r Sigma_r (c x r) and B^T = V_r^T (r x d), the truncated SVD of the
+// span's key / value matrix (long-form summary page, section 2.2, eq. (6) with
+// every rank gate on).
+//
+// Short spans (c <= 128): one-sided Jacobi (Hestenes) on the c rows of X held
+// in LDS: plane rotations of row pairs until all pairs are orthogonal, with the
+// rotations accumulated in J (c x c), so X = J X' with orthogonal rows x'_i.
+// Then U = J, sigma_i = |x'_i|, V_i = x'_i / sigma_i.
+//
+// Tall spans (c > 128): the d x d Gram matrix X^T X is accumulated in fp64,
+// factored by Cholesky (R^T R, semidefinite pivots dropped) and one-sided
+// Jacobi orthogonalises the columns of R (R J = N); then V = J,
+// sigma_i = |N_i| and A = X V_r is streamed from X.  fp64 for the Gram and the
+// factorisation keeps the squared condition number away from fp32 rounding.
+//
+// Rotations are applied to disjoint pairs in parallel (round-robin tournament
+// ordering), one group of 512/PMAX threads per pair.
+#include "sekv_device.h"
+
+namespace sekv {
+
+namespace {
+
+// One-sided Jacobi on p vectors (length D, stride XS) with the rotations applied
+// to p companion vectors (length p, stride JS).  All threads of the workgroup.
+template <int D, int PMAX>
+__device__ void jacobi_sweeps(float* Xv, int XS, float* Jv, int JS, int p, int* s_rot) {
+  constexpr int TPP = 512 / PMAX;
+  const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
+  const int pe = p + (p & 1);
+  const float tol = (float)pe * 1.1920929e-7f;
+  if (p < 2) return;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    if (threadIdx.x == 0) *s_rot = 0;
+    __syncthreads();
+    for (int t = 0; t < pe - 1; ++t) {
+      int i = -1, j = -1;
+      if (pi < pe / 2) {
+        if (pi == 0) {
+          i = pe - 1;
+          j = t;
+        } else {
+          i = (t + pi) % (pe - 1);
+          j = (t - pi + pe - 1) % (pe - 1);
+        }
+      }
+      const bool act = i >= 0 && i < p && j < p;
+      float al = 0.f, be = 0.f, ga = 0.f;
+      if (act) {
+        const float* xi = Xv + i * XS;
+        const float* xj = Xv + j * XS;
+        for (int e = li; e < D; e += TPP) {
+          const float u = xi[e], v = xj[e];
+          al += u * u;
+          be += v * v;
+          ga += u * v;
+        }
+      }
+      al = group_sum<TPP>(al);
+      be = group_sum<TPP>(be);
+      ga = group_sum<TPP>(ga);
+      if (act && al > 0.f && be > 0.f && fabsf(ga) > tol * sqrtf(al) * sqrtf(be)) {
+        const float zeta = (be - al) / (2.f * ga);
+        const float az = fabsf(zeta);
+        const float tt = (az > 1e15f) ? 0.5f / zeta
+                                     : copysignf(1.f, zeta) / (az + sqrtf(1.f + zeta * zeta));
+        const float cs = 1.f / sqrtf(1.f + tt * tt);
+        const float sn = cs * tt;
+        float* xi = Xv + i * XS;
+        float* xj = Xv + j * XS;
+        for (int e = li; e < D; e += TPP) {
+          const float u = xi[e], v = xj[e];
+          xi[e] = cs * u - sn * v;
+          xj[e] = sn * u + cs * v;
+        }
+        float* ji = Jv + i * JS;
+        float* jj = Jv + j * JS;
+        for (int e = li; e < p; e += TPP) {
+          const float u = ji[e], v = jj[e];
+          ji[e] = cs * u - sn * v;
+          jj[e] = sn * u + cs * v;
+        }
+        if (li == 0) *s_rot = 1;
+      }
+      __syncthreads();
+    }
+    const int rot = *s_rot;
+    __syncthreads();
+    if (!rot) break;
+  }
+}
+
+// sigma_i = |v_i| for p vectors, and order[kk] = index of the kk-th largest (kk < r).
+__device__ void rank_by_norm(const float* Xv, int XS, int len, int p, int r, float* sig, int* order) {
+  for (int i = threadIdx.x; i < p; i += kThreads) {
+    float s = 0.f;
+    for (int e = 0; e < len; ++e) s += Xv[i * XS + e] * Xv[i * XS + e];
+    sig[i] = sqrtf(s);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p; i += kThreads) {
+    const float si = sig[i];
+    int rk = 0;
+    for (int j = 0; j < p; ++j) rk += (sig[j] > si || (sig[j] == si && j < i)) ? 1 : 0;
+    if (rk < r) order[rk] = i;
+  }
+  __syncthreads();
+}
+
+struct Prob {
+  int bg, b, k, which, c, r, ms;
+  int64_t off;
+};
+
+__device__ Prob load_prob(const SvdArgs& a, int Hkv) {
+  Prob p;
+  const int32_t* e = a.problems + 3 * (size_t)blockIdx.x;
+  p.bg = e[0];
+  p.k = e[1];
+  p.which = e[2];
+  p.b = p.bg / Hkv;
+  p.ms = a.mstart[(size_t)p.b * a.m_max + p.k];
+  p.c = a.mcount[(size_t)p.b * a.m_max + p.k];
+  p.r = a.rank[(size_t)p.bg * a.m_max + p.k];
+  p.off = a.boff[(size_t)p.bg * a.m_max + p.k];
+  return p;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt) {
+  T* base = reinterpret_cast<T*>(a.bases) + p.off;
+  const int64_t ca = pad8((int64_t)p.c * p.r), rb = pad8((int64_t)p.r * D);
+  if (p.which) base += ca + rb;
+  return bt ? base + ca : base;
+}
+
+// ---------------------------------------------------------------- short spans
+
+template <int D, typename T, int PMAX>
+__global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
+  extern __shared__ float smem[];
+  constexpr int XS = D + 1, JS = PMAX + 1;
+  float* X = smem;                 // [PMAX][XS]
+  float* Jv = smem + PMAX * XS;    // [PMAX][JS]
+  __shared__ float sig[PMAX];
+  __shared__ int order[PMAX];
+  __shared__ int s_rot;
+
+  const Prob p = load_prob(a, a.Hkv);
+  const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
+  for (int idx = threadIdx.x; idx < p.c * D; idx += kThreads) {
+    const int t = idx / D, e = idx % D;
+    X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
+  }
+  for (int idx = threadIdx.x; idx < p.c * p.c; idx += kThreads) {
+    const int i = idx / p.c, t = idx % p.c;
+    Jv[i * JS + t] = (i == t) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  jacobi_sweeps<D, PMAX>(X, XS, Jv, JS, p.c, &s_rot);
+  __syncthreads();
+  rank_by_norm(X, XS, D, p.c, p.r, sig, order);
+
+  T* A = block_ptr<T, D>(a, p, false);
+  const int na = (int)pad8((int64_t)p.c * p.r);
+  for (int idx = threadIdx.x; idx < na; idx += kThreads) {
+    float v = 0.f;
+    if (idx < p.c * p.r) {
+      const int t = idx / p.r, kk = idx % p.r;
+      const int i = order[kk];
+      v = Jv[i * JS + t] * sig[i];
+    }
+    A[idx] = Elem<T>::from_f(v);
+  }
+  T* Bt = block_ptr<T, D>(a, p, true);
+  for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
+    const int kk = idx / D, e = idx % D;
+    const int i = order[kk];
+    const float s = sig[i];
+    Bt[idx] = Elem<T>::from_f(s > 0.f ? X[i * XS + e] / s : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------- tall spans
+
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
+  extern __shared__ double smd[];
+  constexpr int GS = D + 1;       // Gram row stride (doubles)
+  constexpr int XS = D + 1;       // float vector stride
+  constexpr int ROWS = 32;        // X rows staged per step
+  constexpr int NB = D / 8;       // 8x8 Gram blocks per dimension
+  double* Gm = smd;                                       // [D][GS]
+  float* Xs = reinterpret_cast<float*>(smd + D * GS);     // [ROWS][D]
+  __shared__ float sig[D];
+  __shared__ int order[D];
+  __shared__ int s_rot;
+  __shared__ double s_rkk, s_tol;
+
+  const Prob p = load_prob(a, a.Hkv);
+  const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
+
+  // 1. Gram matrix in fp64
+  const int bi = threadIdx.x / NB, bj = threadIdx.x % NB;
+  const bool gact = threadIdx.x < NB * NB;
+  double gacc[8][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) gacc[u][v] = 0.0;
+  for (int t0 = 0; t0 < p.c; t0 += ROWS) {
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
+      const int t = idx / D, e = idx % D;
+      Xs[idx] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
+    }
+    __syncthreads();
+    if (gact) {
+      for (int t = 0; t < ROWS; ++t) {
+        double xa[8], xb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          xa[u] = (double)Xs[t * D + bi * 8 + u];
+          xb[u] = (double)Xs[t * D + bj * 8 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) gacc[u][v] = fma(xa[u], xb[v], gacc[u][v]);
+      }
+    }
+    __syncthreads();
+  }
+  if (gact) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) Gm[(bi * 8 + u) * GS + bj * 8 + v] = gacc[u][v];
+  }
+  __syncthreads();
+
+  // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped
+  if (threadIdx.x == 0) {
+    double mx = 0.0;
+    for (int i = 0; i < D; ++i) mx = fmax(mx, Gm[i * GS + i]);
+    s_tol = mx * (double)D * 4.440892098500626e-16;
+  }
+  __syncthreads();
+  const double tolc = s_tol;
+  for (int kc = 0; kc < D; ++kc) {
+    if (threadIdx.x == 0) {
+      const double piv = Gm[kc * GS + kc];
+      s_rkk = piv > tolc ? sqrt(piv) : 0.0;
+    }
+    __syncthreads();
+    const double rkk = s_rkk;
+    for (int j = kc + threadIdx.x; j < D; j += kThreads)
+      Gm[kc * GS + j] = rkk > 0.0 ? (j == kc ? rkk : Gm[kc * GS + j] / rkk) : 0.0;
+    __syncthreads();
+    const int w = D - kc - 1;
+    for (int idx = threadIdx.x; idx < w * w; idx += kThreads) {
+      const int i = kc + 1 + idx / w, j = kc + 1 + idx % w;
+      if (j >= i) Gm[i * GS + j] -= Gm[kc * GS + i] * Gm[kc * GS + j];
+    }
+    __syncthreads();
+  }
+
+  // 3. columns of R (fp32) and J = I
+  constexpr int PER = D * D / kThreads;
+  float rv[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = threadIdx.x + u * kThreads;
+    const int col = idx / D, row = idx % D;
+    rv[u] = row <= col ? (float)Gm[row * GS + col] : 0.f;
+  }
+  __syncthreads();
+  float* Rc = reinterpret_cast<float*>(smd);  // [D][XS]: vector col = column col of R
+  float* Jv = Rc + D * XS;                    // [D][XS]
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = threadIdx.x + u * kThreads;
+    const int col = idx / D, row = idx % D;
+    Rc[col * XS + row] = rv[u];
+    Jv[col * XS + row] = (row == col) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  jacobi_sweeps<D, D>(Rc, XS, Jv, XS, D, &s_rot);
+  __syncthreads();
+  const int r = p.r;
+  rank_by_norm(Rc, XS, D, D, r, sig, order);
+
+  // 4. B^T rows = chosen columns of V = J
+  T* Bt = block_ptr<T, D>(a, p, true);
+  for (int idx = threadIdx.x; idx < r * D; idx += kThreads) {
+    const int kk = idx / D, e = idx % D;
+    Bt[idx] = Elem<T>::from_f(sig[order[kk]] > 0.f ? Jv[order[kk] * XS + e] : 0.f);
+  }
+  // 5. A = X V_r, streamed (R no longer needed: reuse its LDS for X rows)
+  T* A = block_ptr<T, D>(a, p, false);
+  float* Xr = Rc;  // [ROWS][XS]
+  for (int t0 = 0; t0 < p.c; t0 += ROWS) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
+      const int t = idx / D, e = idx % D;
+      Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * r; idx += kThreads) {
+      const int t = idx / r, kk = idx % r;
+      if (t0 + t >= p.c) continue;
+      const int i = order[kk];
+      float s = 0.f;
+      if (sig[i] > 0.f)
+        for (int e = 0; e < D; ++e) s += Xr[t * XS + e] * Jv[i * XS + e];
+      A[(size_t)(t0 + t) * r + kk] = Elem<T>::from_f(s);
+    }
+  }
+  const int64_t na = pad8((int64_t)p.c * r);
+  for (int64_t idx = (int64_t)p.c * r + threadIdx.x; idx < na; idx += kThreads) A[idx] = Elem<T>::from_f(0.f);
+}
+
+template <int D, typename T, int PMAX>
+void launch_rows(const SvdArgs& a, hipStream_t s) {
+  const size_t lds = sizeof(float) * (PMAX * (D + 1) + PMAX * (PMAX + 1));
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(kThreads), lds, s, a);
+}
+
+template <int D, typename T>
+void launch_tall(const SvdArgs& a, hipStream_t s) {
+  const size_t lds = sizeof(double) * D * (D + 1) + sizeof(float) * 32 * D;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_svd_tall<D, T>), dim3(a.n_problems), dim3(kThreads), lds, s, a);
+}
+
+template <int D, typename T>
+void launch_svd_t(int cmax, const SvdArgs& a, hipStream_t s) {
+  switch (cmax) {
+    case 16: launch_rows<D, T, 16>(a, s); break;
+    case 32: launch_rows<D, T, 32>(a, s); break;
+    case 64: launch_rows<D, T, 64>(a, s); break;
+    case 128: launch_rows<D, T, 128>(a, s); break;
+    default: launch_tall<D, T>(a, s); break;
+  }
+}
+
+}  // namespace
+
+void launch_svd(int cmax, int d, int kv_bf16, const SvdArgs& a, hipStream_t s) {
+  if (a.n_problems <= 0) return;
+  if (d == 128) {
+    if (kv_bf16) launch_svd_t<128, bf16_t>(cmax, a, s);
+    else launch_svd_t<128, float>(cmax, a, s);
+  } else {
+    if (kv_bf16) launch_svd_t<64, bf16_t>(cmax, a, s);
+    else launch_svd_t<64, float>(cmax, a, s);
+  }
+}
+
+}  // namespace sekv

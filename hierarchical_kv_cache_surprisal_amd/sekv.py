@@ -1,0 +1,286 @@
+"""Thin Python binding of the SeKV C ABI (include/sekv.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Functions keep the C names (sekv_create, sekv_build, sekv_decode_attn, ...);
+device buffers are torch tensors on the context's device (PyTorch is used as
+the allocator and stream source), host buffers are numpy arrays.
+
+The library is loaded from this package directory (libsekv.so, built by
+build_lib.py).  There is no fallback: if it is missing, importing works but
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsekv.so")
+
+SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_OOM, SEKV_ERR_HIP, SEKV_ERR_STATE = range(5)
+SEKV_F32, SEKV_BF16 = 0, 1
+SEKV_BASES_HOST, SEKV_BASES_DEVICE = 0, 1
+_STATUS = {0: "OK", 1: "INVALID", 2: "OOM", 3: "HIP", 4: "STATE"}
+
+EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sekv_get_spans",
+            "sekv_get_bases_layout", "sekv_decode_attn", "sekv_route_scores", "sekv_zoom_fetch",
+            "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
+            "sekv_get_stats"]
+
+
+class SekvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sekv status {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class sekv_config(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("batch", C.c_int32), ("n_ctx", C.c_int32),
+                ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("d_head", C.c_int32),
+                ("kv_dtype", C.c_int32), ("local_window", C.c_int32), ("basis_home", C.c_int32),
+                ("device", C.c_int32)]
+
+
+class sekv_stats(C.Structure):
+    _fields_ = [("decode_calls", C.c_uint64), ("fetch_calls", C.c_uint64),
+                ("spans_fetched", C.c_uint64), ("bytes_fetched", C.c_uint64),
+                ("memcpy_calls", C.c_uint64), ("device_resident_bytes", C.c_int64),
+                ("host_basis_bytes", C.c_int64), ("full_kv_bytes", C.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsekv.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          f"`python -m hierarchical_kv_cache_surprisal_amd.build_lib`")
+    lib = C.CDLL(path)
+    P, I32, I64, U64, D = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_double
+    pI32, pI64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+    sig = {
+        "sekv_create": (I32, [C.POINTER(sekv_config), C.POINTER(P)]),
+        "sekv_destroy": (None, [P]),
+        "sekv_last_error": (C.c_char_p, [P]),
+        "sekv_build": (I32, [P, I32, P, P, P, D, pI32, I32, U64, P]),
+        "sekv_get_spans": (I32, [P, I32, pI32, pI32, pI32, pI32, pI32, pI32]),
+        "sekv_get_bases_layout": (I32, [P, I32, I32, I32, pI32, pI64, pI64]),
+        "sekv_decode_attn": (I32, [P, I32, P, C.POINTER(C.c_float), P, P, P]),
+        "sekv_route_scores": (I32, [P, I32, P, P, P]),
+        "sekv_zoom_fetch": (I32, [P, I32, pI32, pI32, P, P]),
+        "sekv_import_spans": (I32, [P, I32, I32, pI32, pI32, I32, pI32]),
+        "sekv_import_layout": (I32, [P, I32, pI32]),
+        "sekv_import_head": (I32, [P, I32, I32, I32, P, P, P, P, pI32, P, I64]),
+        "sekv_export_head": (I32, [P, I32, I32, I32, P, P, P, P, pI32, P]),
+        "sekv_get_stats": (I32, [P, C.POINTER(sekv_stats)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, ctx) -> None:
+    if status != SEKV_OK:
+        msg = load_library().sekv_last_error(ctx)
+        raise SekvError(status, (msg or b"").decode())
+
+
+def _i32(a) -> "C.POINTER(C.c_int32)":
+    return a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _i64(a) -> "C.POINTER(C.c_int64)":
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+def _dptr(t) -> Optional[int]:
+    """Device pointer of a contiguous torch tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _hbuf(a) -> int:
+    return a.ctypes.data
+
+
+# ----------------------------------------------------------------------------- C-named wrappers
+
+def sekv_create(n_layers: int, batch: int, n_ctx: int, n_q_heads: int, n_kv_heads: int, d_head: int,
+                kv_dtype: int, local_window: int, basis_home: int, device: int = 0) -> int:
+    lib = load_library()
+    cfg = sekv_config(n_layers, batch, n_ctx, n_q_heads, n_kv_heads, d_head, kv_dtype,
+                      local_window, basis_home, device)
+    out = C.c_void_p()
+    _check(lib.sekv_create(C.byref(cfg), C.byref(out)), None)
+    return out.value
+
+
+def sekv_destroy(ctx: int) -> None:
+    load_library().sekv_destroy(ctx)
+
+
+def sekv_build(ctx, layer, H, K, V, alpha, rank_choices: Sequence[int], rank_seed: int, stream=None):
+    ch = np.ascontiguousarray(rank_choices, dtype=np.int32)
+    _check(load_library().sekv_build(ctx, layer, _dptr(H), _dptr(K), _dptr(V), float(alpha), _i32(ch),
+                                      len(ch), int(rank_seed) & ((1 << 64) - 1), _stream(stream)), ctx)
+
+
+def sekv_get_spans(ctx, b: int):
+    lib = load_library()
+    m, na, mm = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib.sekv_get_spans(ctx, b, C.byref(m), C.byref(na), C.byref(mm), None, None, None), ctx)
+    ms = np.zeros(m.value, np.int32)
+    mc = np.zeros(m.value, np.int32)
+    an = np.zeros(na.value, np.int32)
+    _check(lib.sekv_get_spans(ctx, b, None, None, None, _i32(ms), _i32(mc), _i32(an)), ctx)
+    return ms, mc, an, mm.value
+
+
+def sekv_get_bases_layout(ctx, layer: int, b: int, g: int, m: int):
+    rank = np.zeros(m, np.int32)
+    off = np.zeros(m, np.int64)
+    tot = np.zeros(1, np.int64)
+    _check(load_library().sekv_get_bases_layout(ctx, layer, b, g, _i32(rank), _i64(off), _i64(tot)), ctx)
+    return rank, off, int(tot[0])
+
+
+def sekv_decode_attn(ctx, layer: int, q, tau, out, zoom_mask=None, stream=None):
+    t = np.ascontiguousarray(tau, dtype=np.float32)
+    _check(load_library().sekv_decode_attn(ctx, layer, _dptr(q), t.ctypes.data_as(C.POINTER(C.c_float)),
+                                           _dptr(out), _dptr(zoom_mask), _stream(stream)), ctx)
+
+
+def sekv_route_scores(ctx, layer: int, q, scores, stream=None):
+    _check(load_library().sekv_route_scores(ctx, layer, _dptr(q), _dptr(scores), _stream(stream)), ctx)
+
+
+def sekv_zoom_fetch(ctx, layer: int, entries: np.ndarray, counts: np.ndarray, side=None, done=None):
+    e = np.ascontiguousarray(entries, dtype=np.int32)
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    _check(load_library().sekv_zoom_fetch(ctx, layer, _i32(e), _i32(c), _stream(side) if side else None,
+                                          done), ctx)
+
+
+def sekv_import_spans(ctx, b: int, mstart, mcount, anchors):
+    ms = np.ascontiguousarray(mstart, dtype=np.int32)
+    mc = np.ascontiguousarray(mcount, dtype=np.int32)
+    an = np.ascontiguousarray(anchors, dtype=np.int32)
+    _check(load_library().sekv_import_spans(ctx, b, len(ms), _i32(ms), _i32(mc), len(an), _i32(an)), ctx)
+
+
+def sekv_import_layout(ctx, layer: int, rank):
+    r = np.ascontiguousarray(rank, dtype=np.int32)
+    _check(load_library().sekv_import_layout(ctx, layer, _i32(r)), ctx)
+
+
+def sekv_import_head(ctx, layer, b, g, kbar, vbar, KA, VA, rank, bases):
+    """Host numpy arrays in the KV dtype's storage (float32, or uint16 bf16 bits)."""
+    arrs = [np.ascontiguousarray(x) for x in (kbar, vbar, KA, VA, bases)]
+    r = np.ascontiguousarray(rank, dtype=np.int32)
+    _check(load_library().sekv_import_head(ctx, layer, b, g, *[_hbuf(x) for x in arrs[:4]], _i32(r),
+                                           _hbuf(arrs[4]), arrs[4].size), ctx)
+
+
+def sekv_export_head(ctx, layer, b, g, m, n_a, d, basis_elems, storage_dtype):
+    kbar = np.zeros((m, d), storage_dtype)
+    vbar = np.zeros((m, d), storage_dtype)
+    KA = np.zeros((n_a, d), storage_dtype)
+    VA = np.zeros((n_a, d), storage_dtype)
+    rank = np.zeros(m, np.int32)
+    bases = np.zeros(basis_elems, storage_dtype)
+    _check(load_library().sekv_export_head(ctx, layer, b, g, _hbuf(kbar), _hbuf(vbar), _hbuf(KA), _hbuf(VA),
+                                           _i32(rank), _hbuf(bases)), ctx)
+    return kbar, vbar, KA, VA, rank, bases
+
+
+def sekv_get_stats(ctx) -> dict:
+    s = sekv_stats()
+    _check(load_library().sekv_get_stats(ctx, C.byref(s)), ctx)
+    return {f: getattr(s, f) for f, _ in sekv_stats._fields_}
+
+
+# ----------------------------------------------------------------------------- convenience object
+
+class Context:
+    """Owns one sekv_ctx; methods forward to the C-named wrappers above."""
+
+    def __init__(self, n_layers, batch, n_ctx, n_q_heads, n_kv_heads, d_head, kv_dtype="bf16",
+                 local_window=512, basis_home="device", device=0):
+        self.kv_dtype = kv_dtype
+        self.d = d_head
+        self.B, self.Hq, self.Hkv, self.L, self.n = batch, n_q_heads, n_kv_heads, n_layers, n_ctx
+        dt = {"f32": SEKV_F32, "bf16": SEKV_BF16}[kv_dtype]
+        home = {"host": SEKV_BASES_HOST, "device": SEKV_BASES_DEVICE}[basis_home]
+        self.ptr = sekv_create(n_layers, batch, n_ctx, n_q_heads, n_kv_heads, d_head, dt, local_window,
+                               home, device)
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            sekv_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def storage_dtype(self):
+        return np.float32 if self.kv_dtype == "f32" else np.uint16
+
+    def build(self, layer, H, K, V, alpha, rank_choices, rank_seed, stream=None):
+        sekv_build(self.ptr, layer, H, K, V, alpha, rank_choices, rank_seed, stream)
+
+    def spans(self, b):
+        return sekv_get_spans(self.ptr, b)
+
+    def m_max(self):
+        return sekv_get_spans(self.ptr, 0)[3]
+
+    def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None):
+        sekv_decode_attn(self.ptr, layer, q, tau, out, zoom_mask, stream)
+
+    def route_scores(self, layer, q, scores, stream=None):
+        sekv_route_scores(self.ptr, layer, q, scores, stream)
+
+    def bases_layout(self, layer, b, g):
+        m = len(self.spans(b)[0])
+        return sekv_get_bases_layout(self.ptr, layer, b, g, m)
+
+    def export_head(self, layer, b, g):
+        ms, mc, an, _ = self.spans(b)
+        _, _, tot = self.bases_layout(layer, b, g)
+        return sekv_export_head(self.ptr, layer, b, g, len(ms), len(an), self.d, tot, self.storage_dtype)
+
+    def import_spans(self, b, mstart, mcount, anchors):
+        sekv_import_spans(self.ptr, b, mstart, mcount, anchors)
+
+    def import_layout(self, layer, rank):
+        sekv_import_layout(self.ptr, layer, rank)
+
+    def import_head(self, layer, b, g, kbar, vbar, KA, VA, rank, bases):
+        sekv_import_head(self.ptr, layer, b, g, kbar, vbar, KA, VA, rank, bases)
+
+    def stats(self):
+        return sekv_get_stats(self.ptr)

@@ -1,0 +1,241 @@
+/*
+ * sekv.h -- C ABI of the SeKV mixed-resolution decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (SeKV, "Resolution-Adaptive KV Cache with Hierarchical Semantic
+ * Memory"):
+ *   prefill  -- cut each sequence into spans where token surprisal exceeds
+ *               mu + alpha*sigma, keep the boundary tokens (and a local window)
+ *               as full-resolution anchors, summarise every span by the
+ *               surprisal-weighted mean of its keys and values, and store a
+ *               truncated SVD of each span's key and value matrices.
+ *               [long-form summary page "SeKV：面向长上下文推理的分辨率自适应
+ *               KV Cache 与层级语义记忆", sections 2.1-2.2, eqs. (1), (2), (6)]
+ *   decode   -- score the query against every span summary, zoom into spans
+ *               whose sigmoid score exceeds a per-(layer, head) threshold,
+ *               rebuild their tokens from the SVD bases, and run one softmax
+ *               over anchors, zoomed tokens and the log|S|-corrected summaries
+ *               of the other spans.
+ *               [same page, section 2.3, eqs. (5), (9), Figure 2; review page
+ *               "SeKV：支持分层语义记忆的分辨率自适应KV缓存…", workflow paragraph]
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   mu/sigma are the population mean/std in fp64; both rules use a strict '>';
+ *   members of a span = its positions minus anchors; empty spans are dropped;
+ *   |S| = member count, natural log; the learned routing projection is the
+ *   identity, so the routing score is q.kbar/(|kbar| sqrt(d)) + ln|S|; the
+ *   trained rank gate is a hard rank r_S = choices[splitmix64(seed ^ layer<<40
+ *   ^ g<<32 ^ k) mod n_choices], r_eff = min(r_S, |S|, d); a zoomed span adds
+ *   only its rebuilt tokens, a non-zoomed span one entry with logit
+ *   q.kbar/sqrt(d) + ln|S|; query head h reads kv head h / (Hq/Hkv).
+ *
+ * Conventions
+ *   * Every call returns sekv_status (0 = OK); no C++ exception crosses the ABI.
+ *     On error the text of the failure is kept in sekv_last_error(ctx).
+ *   * "dev" pointers are HIP device memory on the context's device, "host"
+ *     pointers ordinary host memory.  The caller owns every pointer it passes.
+ *   * All device work is stream-ordered on the stream passed in (NULL = the
+ *     legacy default stream).  Calls on one context are not thread-safe and
+ *     must not overlap on different streams: they share internal buffers.
+ *   * KV tensors are row-major [B][H_kv][n][d] in the context's KV dtype
+ *     (float32 or bfloat16 bit patterns); q and outputs are float32.
+ */
+#ifndef SEKV_H
+#define SEKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sekv_status {
+  SEKV_OK = 0,
+  SEKV_ERR_INVALID = 1, /* bad argument: shape, NaN/negative surprisal, NaN tau, ... */
+  SEKV_ERR_OOM = 2,     /* device or pinned-host allocation failed */
+  SEKV_ERR_HIP = 3,     /* a HIP runtime call failed; see sekv_last_error */
+  SEKV_ERR_STATE = 4    /* call out of order (layer not built, ...) */
+} sekv_status;
+
+typedef enum sekv_dtype { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
+
+/* Where the per-span SVD bases live between decode steps.
+ * HOST   -- pinned host memory (the pages' CPU tier): every decode step copies
+ *           the zoomed spans' bases into a device staging buffer on a side
+ *           stream before the zoomed segment runs (one host sync per step).
+ * DEVICE -- device memory (the whole store fits in HBM on MI355X at 128K
+ *           context): the decode step is fully device-side, one kernel. */
+typedef enum sekv_basis_home { SEKV_BASES_HOST = 0, SEKV_BASES_DEVICE = 1 } sekv_basis_home;
+
+typedef struct sekv_config {
+  int32_t n_layers;     /* L >= 1 */
+  int32_t batch;        /* B >= 1 independent sequences */
+  int32_t n_ctx;        /* n >= 1 tokens per sequence */
+  int32_t n_q_heads;    /* H_q, a multiple of n_kv_heads, H_q/H_kv <= 8 */
+  int32_t n_kv_heads;   /* H_kv >= 1 */
+  int32_t d_head;       /* 64 or 128 */
+  int32_t kv_dtype;     /* sekv_dtype */
+  int32_t local_window; /* w >= 0: the last w positions are anchors */
+  int32_t basis_home;   /* sekv_basis_home */
+  int32_t device;       /* HIP device ordinal */
+} sekv_config;
+
+typedef struct sekv_ctx sekv_ctx;
+
+/* Create a context.  Allocates the span tables and per-layer bookkeeping;
+ * per-layer artefacts are allocated by sekv_build / sekv_import_head.
+ * Errors: INVALID (shape rules above), OOM, HIP. */
+sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out);
+
+/* Free everything the context owns.  NULL is accepted. */
+void sekv_destroy(sekv_ctx* ctx);
+
+/* Text of the last failure on this context ("" if none).  Valid until the
+ * next call on the context.  NULL ctx returns the text of the last failed
+ * sekv_create in this process. */
+const char* sekv_last_error(const sekv_ctx* ctx);
+
+/* ------------------------------------------------------------------ build */
+
+/* Prefill builder for one layer [summary page 2.1-2.2, eqs. (1), (2), (6)].
+ *   H      dev float32 [B][n]       per-token surprisal, finite and >= 0
+ *   K, V   dev KV dtype [B][H_kv][n][d]
+ *   alpha  boundary sensitivity (finite)
+ *   rank_choices host int32 [n_choices] (each >= 1), rank_seed: the hard
+ *          per-span rank r_S described above.
+ * Steps: segmentation (on the first build of the context; later layers must
+ * present the same H and alpha, which is checked), weighted-mean summaries,
+ * anchor gather, batched one-sided-Jacobi truncated SVD of each span's key
+ * and value member rows, basis packing (and, for SEKV_BASES_HOST, a copy into
+ * the pinned host store).  The call synchronises `stream` once (after the
+ * segmentation) and again before returning; H, K, V may be freed on return.
+ * Errors: INVALID (NaN/Inf/negative H, alpha not finite, bad rank choice,
+ * layer out of range), STATE (H or alpha differ from the first build), OOM, HIP. */
+sekv_status sekv_build(sekv_ctx* ctx, int32_t layer, const float* H, const void* K, const void* V,
+                       double alpha, const int32_t* rank_choices, int32_t n_choices,
+                       uint64_t rank_seed, hipStream_t stream);
+
+/* Span table of sequence b (shared by every layer and head).
+ *   m, n_anchors, m_max (max over sequences) are written when non-NULL.
+ *   mstart/mcount host int32 [m]: first member position and member count of
+ *   each kept span, in position order.  anchors host int32 [n_anchors],
+ *   ascending.  Pass NULL arrays to query sizes only.
+ * Errors: STATE before the first build/import, INVALID (b out of range). */
+sekv_status sekv_get_spans(const sekv_ctx* ctx, int32_t b, int32_t* m, int32_t* n_anchors,
+                           int32_t* m_max, int32_t* mstart, int32_t* mcount, int32_t* anchors);
+
+/* Packed basis layout of one (layer, b, kv head g).  For span k with c = mcount[k]
+ * and r = rank[k] the store holds, from element offset basis_off[k], four
+ * row-major blocks A_K [c][r], B_K^T [r][d], A_V [c][r], B_V^T [r][d]
+ * (A = U_r Sigma_r, B^T = V_r^T of the span's member rows), each block padded
+ * to a multiple of 8 elements; spans follow each other in span order.
+ *   rank host int32 [m], basis_off host int64 [m] (elements), basis_elems
+ *   total elements; any may be NULL.
+ * Errors: STATE (layer not built), INVALID. */
+sekv_status sekv_get_bases_layout(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g,
+                                  int32_t* rank, int64_t* basis_off, int64_t* basis_elems);
+
+/* ----------------------------------------------------------------- decode */
+
+/* One decode step of one layer for every sequence and query head.
+ *   q         dev float32 [B][H_q][d]
+ *   tau       host float32 [H_q]: zoom thresholds of this layer, on the
+ *             probability scale of eq. (9); tau <= 0 zooms every span,
+ *             tau >= 1 none.  NaN -> INVALID.
+ *   out       dev float32 [B][H_q][d]: attention output
+ *   zoom_mask dev uint8 [B][H_q][m_max] or NULL: 1 where the head zoomed the
+ *             span; entries at or beyond the sequence's m are left untouched.
+ * DEVICE bases: fully asynchronous on `stream` (one kernel).
+ * HOST bases: route kernel, then the zoomed spans' bases are copied from the
+ * pinned store to device staging on the context's side stream (see
+ * sekv_zoom_fetch), then the zoomed-segment kernel; synchronises `stream`
+ * once, after routing.
+ * Errors: STATE (layer not built), INVALID, HIP. */
+sekv_status sekv_decode_attn(sekv_ctx* ctx, int32_t layer, const float* q, const float* tau,
+                             float* out, uint8_t* zoom_mask, hipStream_t stream);
+
+/* Stage-1 routing scores only [eq. (5) with the identity projection]:
+ *   scores dev float32 [B][H_q][m_max] = q.kbar/(|kbar| sqrt(d)) + ln|S|
+ * (ln|S| alone when kbar = 0).  Entries beyond a sequence's m are untouched.
+ * A diagnostic / calibration entry point; asynchronous on `stream`. */
+sekv_status sekv_route_scores(sekv_ctx* ctx, int32_t layer, const float* q, float* scores,
+                              hipStream_t stream);
+
+/* Copy the bases of selected spans from the pinned host store into the
+ * context's device staging buffer (HOST bases only) [the asynchronous CPU
+ * fetch of zoomed spans, summary page Figure 2].
+ *   entries host int32 [B*H_kv][m_max]: for each (b, g) the first counts[b*H_kv+g]
+ *           entries are span ids k (0 <= k < m_b) in the low 24 bits and a bit
+ *           mask of the group's zooming query heads in bits 24..31 (bit i =
+ *           query head g*G+i).  Each span id at most once per (b, g).
+ *   counts  host int32 [B*H_kv]
+ * The copies are issued on `side` (runs of adjacent spans coalesced into one
+ * hipMemcpyAsync each), followed by the upload of the staging table, and
+ * `done` (may be NULL) is recorded on `side` after the last copy.  The staging
+ * table describes exactly these spans until the next fetch; the decode entry
+ * point calls this itself.  The host arrays may be reused after `done`.
+ * Errors: STATE (DEVICE bases, layer not built), INVALID (bad id, duplicate),
+ * OOM (staging too small), HIP. */
+sekv_status sekv_zoom_fetch(sekv_ctx* ctx, int32_t layer, const int32_t* entries,
+                            const int32_t* counts, hipStream_t side, hipEvent_t done);
+
+/* ------------------------------------------------------ artefact exchange */
+
+/* Install a span table for sequence b instead of building one (test hook:
+ * lets a decode run on artefacts built elsewhere).  All sequences must be
+ * imported before any sekv_import_head.  Host int32 arrays as in
+ * sekv_get_spans; spans must be disjoint, ascending, inside [0, n), and the
+ * anchors ascending and disjoint from the members.
+ * Errors: INVALID, STATE (a build already fixed the table), OOM, HIP. */
+sekv_status sekv_import_spans(sekv_ctx* ctx, int32_t b, int32_t m, const int32_t* mstart,
+                              const int32_t* mcount, int32_t n_anchors, const int32_t* anchors);
+
+/* Fix the packed-basis layout of a layer that is not built here (test hook):
+ *   rank host int32 [B][H_kv][m_max]: r_eff of every (b, g, span); entries at
+ *   or beyond a sequence's m are ignored; 1 <= rank <= min(mcount, d).
+ * Allocates the layer's summaries, anchors and basis store (zero-filled);
+ * sekv_import_head then fills them head by head.  A layer produced by
+ * sekv_build already has its layout and needs no call.
+ * Errors: INVALID, STATE (span table not set), OOM, HIP. */
+sekv_status sekv_import_layout(sekv_ctx* ctx, int32_t layer, const int32_t* rank);
+
+/* Install the artefacts of one (layer, b, kv head g) from host memory:
+ *   kbar, vbar host KV dtype [m][d]; KA, VA host KV dtype [n_anchors][d];
+ *   rank host int32 [m] (1 <= rank[k] <= min(mcount[k], d));
+ *   bases host KV dtype, packed as described at sekv_get_bases_layout,
+ *   basis_elems elements.
+ * The layer needs a layout (sekv_build or sekv_import_layout) and the ranks
+ * must equal that layout's; imports are synchronous.  The layer is decodable
+ * once every (b, g) has artefacts (all of them, after a build).
+ * Errors: INVALID, STATE (no layout), OOM, HIP. */
+sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, const void* kbar,
+                             const void* vbar, const void* KA, const void* VA, const int32_t* rank,
+                             const void* bases, int64_t basis_elems);
+
+/* Copy the artefacts of one (layer, b, g) to host memory (same layouts as
+ * sekv_import_head; any pointer may be NULL).  Synchronous.
+ * Errors: STATE (layer not built), INVALID, HIP. */
+sekv_status sekv_export_head(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* kbar,
+                             void* vbar, void* KA, void* VA, int32_t* rank, void* bases);
+
+/* ------------------------------------------------------------- diagnostics */
+
+typedef struct sekv_stats {
+  uint64_t decode_calls;          /* sekv_decode_attn calls */
+  uint64_t fetch_calls;           /* sekv_zoom_fetch calls */
+  uint64_t spans_fetched;         /* (b, g, span) bases copied to staging */
+  uint64_t bytes_fetched;         /* bytes copied host -> staging */
+  uint64_t memcpy_calls;          /* hipMemcpyAsync calls issued by fetches */
+  int64_t device_resident_bytes;  /* anchors + summaries + tables (+ bases if DEVICE) */
+  int64_t host_basis_bytes;       /* pinned store (HOST) */
+  int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
+} sekv_stats;
+
+sekv_status sekv_get_stats(const sekv_ctx* ctx, sekv_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEKV_H */

@@ -1,0 +1,155 @@
+"""Shared test helpers: marshal oracle artefacts into the C ABI's packed layout,
+place zoom thresholds away from ties, and compare results.
+
+Test infrastructure (may use the oracle); never imported by the product path.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+from oracle import sekv_oracle as O
+
+
+def pad8(x: int) -> int:
+    return (x + 7) & ~7
+
+
+def storage(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """float64 values exactly representable in the KV dtype -> storage array."""
+    if kv_dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return O.bf16_bits(x)
+
+
+def from_storage(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    if kv_dtype == "f32":
+        return np.asarray(x, dtype=np.float64)
+    return O.bf16_from_bits(x)
+
+
+def pack_bases(art: O.HeadArtifacts, kv_dtype: str, d: int) -> np.ndarray:
+    """The packed layout documented at sekv_get_bases_layout: per span
+    [A_K | B_K^T | A_V | B_V^T], each block padded to 8 elements."""
+    parts = []
+    for k in range(art.m):
+        c, r = int(art.mcount[k]), int(art.rank[k])
+        for blk, n in ((art.AK[k], c * r), (art.BKt[k], r * d), (art.AV[k], c * r), (art.BVt[k], r * d)):
+            flat = np.zeros(pad8(n))
+            flat[:n] = np.asarray(blk, dtype=np.float64).reshape(-1)
+            parts.append(flat)
+    flat = np.concatenate(parts) if parts else np.zeros(0)
+    return storage(flat, kv_dtype)
+
+
+def unpack_bases(flat_storage: np.ndarray, mcount, rank, kv_dtype: str, d: int):
+    """Inverse of pack_bases: lists AK, BKt, AV, BVt (float64)."""
+    flat = from_storage(flat_storage, kv_dtype)
+    AK, BKt, AV, BVt = [], [], [], []
+    pos = 0
+    for c, r in zip(mcount, rank):
+        c, r = int(c), int(r)
+        out = []
+        for shape in ((c, r), (r, d), (c, r), (r, d)):
+            n = shape[0] * shape[1]
+            out.append(flat[pos:pos + n].reshape(shape))
+            pos += pad8(n)
+        AK.append(out[0]); BKt.append(out[1]); AV.append(out[2]); BVt.append(out[3])
+    return AK, BKt, AV, BVt
+
+
+def import_oracle_layer(ctx, layer: int, segs: Sequence[O.Segmentation],
+                        arts: Dict[Tuple[int, int], O.HeadArtifacts], B: int, Hkv: int, d: int,
+                        kv_dtype: str, set_spans: bool = True, set_layout: bool = True):
+    """Install the oracle's artefacts of one layer into a library context."""
+    if set_spans:
+        for b in range(B):
+            ctx.import_spans(b, segs[b].mstart, segs[b].mcount, segs[b].anchors)
+    m_max = max(1, max(s.m for s in segs))
+    if set_layout:
+        rank = np.ones((B, Hkv, m_max), np.int32)
+        for (b, g), a in arts.items():
+            rank[b, g, :a.m] = a.rank
+        ctx.import_layout(layer, rank)
+    for (b, g), a in arts.items():
+        ctx.import_head(layer, b, g, storage(a.kbar, kv_dtype), storage(a.vbar, kv_dtype),
+                        storage(a.KA, kv_dtype), storage(a.VA, kv_dtype), a.rank.astype(np.int32),
+                        pack_bases(a, kv_dtype, d))
+
+
+# ----------------------------------------------------------------------------- thresholds
+
+def route_band(q: np.ndarray, kbar: np.ndarray, mcount: np.ndarray) -> np.ndarray:
+    """Half-width of the region around a routing score inside which fp32
+    evaluation on the GPU may decide differently from the fp64 oracle:
+    4 * gamma_d * (sum_i |q_i kbar_i| / (|kbar| sqrt(d)) + ln|S|), with
+    gamma_d = d u / (1 - d u), u = 2^-24 (a standard dot-product error bound),
+    plus a few ulps for the norm, the square root and the final add."""
+    d = q.size
+    u = 2.0 ** -24
+    gam = d * u / (1 - d * u)
+    nrm = np.sqrt(np.einsum("ij,ij->i", kbar, kbar))
+    mag = np.abs(kbar) @ np.abs(q)
+    cos_mag = np.where(nrm > 0, mag / np.maximum(nrm, 1e-300) / math.sqrt(d), 0.0)
+    return 4 * gam * (cos_mag + np.log(mcount)) + 16 * u * (cos_mag + np.log(mcount) + 1)
+
+
+def place_theta(scores: np.ndarray, rate: float, band_max: float) -> float:
+    """theta at the midpoint of the widest gap between sorted scores near the
+    target zoom quantile (scores: all steps pooled); the gap must clear the band."""
+    s = np.sort(scores.reshape(-1))[::-1]
+    N = s.size
+    target = rate * N
+    lo = max(1, int(target * 0.6))
+    hi = min(N - 1, max(lo + 1, int(math.ceil(target * 1.4)) + 1))
+    gaps = s[lo - 1:hi - 1] - s[lo:hi]
+    i = int(np.argmax(gaps))
+    th = 0.5 * (s[lo - 1 + i] + s[lo + i])
+    assert gaps[i] > 8 * band_max, f"no gap wide enough near the target rate: {gaps[i]} vs band {band_max}"
+    return th
+
+
+def tau_from_theta(theta: float) -> float:
+    """float32 tau whose logit is within rounding of theta."""
+    if theta == -math.inf:
+        return 0.0
+    if theta == math.inf:
+        return 1.0
+    return float(np.float32(1.0 / (1.0 + math.exp(-theta))))
+
+
+def thresholds_for(q_steps: np.ndarray, arts, G: int, rates: np.ndarray, B: int) -> np.ndarray:
+    """Per query head tau (float32) such that no decision of any step falls in the tie band."""
+    steps, _, Hq, d = q_steps.shape
+    taus = np.zeros(Hq, np.float32)
+    for h in range(Hq):
+        if rates[h] >= 1.0:
+            taus[h] = 0.0
+            continue
+        sc, bands = [], []
+        for b in range(B):
+            a = arts[(b, h // G)]
+            for t in range(steps):
+                sc.append(O.route_scores(q_steps[t, b, h], a.kbar, a.mcount))
+                bands.append(route_band(q_steps[t, b, h], a.kbar, a.mcount))
+        sc = np.concatenate(sc)
+        bm = float(np.concatenate(bands).max())
+        taus[h] = tau_from_theta(place_theta(sc, rates[h], bm))
+    return taus
+
+
+def assert_no_ties(q: np.ndarray, tau: float, a: O.HeadArtifacts):
+    th = O.logit_threshold(tau)
+    if not math.isfinite(th):
+        return
+    s = O.route_scores(q, a.kbar, a.mcount)
+    bd = route_band(q, a.kbar, a.mcount)
+    close = np.abs(s - th) <= bd
+    assert not close.any(), f"{close.sum()} routing decisions inside the fp32 tie band"
+
+
+def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """||o - o_ref||_inf / max(||o_ref||_inf, 1e-6)."""
+    return float(np.max(np.abs(out - ref)) / max(float(np.max(np.abs(ref))), 1e-6))

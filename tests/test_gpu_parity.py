@@ -1,0 +1,314 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Decode parity runs on identical artefacts (the oracle's, imported), so routing
+masks must match bit for bit (every decision is checked to lie outside the
+fp32 tie band) and outputs within 1e-4 relative (fp32 accumulation on the same
+bf16/fp32 data; tighter than the 2e-2 / 1e-4 bounds the workload set fixes).
+Builder parity: span tables and anchors bit-exact; summaries within one bf16
+ulp of the row maximum (or 1e-6 for fp32); SVD factors by reconstruction error
+against the Eckart-Young optimum, never by sign.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import sekv_oracle as O
+from tests import sekv_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _lib():
+    from hierarchical_kv_cache_surprisal_amd import sekv
+    sekv.load_library()
+    return sekv
+
+
+def _ctx(s, home, L=None):
+    sekv = _lib()
+    return sekv.Context(L or s.L, s.B, s.n, s.Hq, s.Hkv, s.d, s.kv_dtype, s.w, home)
+
+
+def _inputs(s, layer=0, device="cpu"):
+    H = synth.surprisal_batch(s)
+    K, V = synth.kv_layer(s, layer, device=device)
+    return H, K, V
+
+
+def _to_np64(t):
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def _oracle_layer(s, H, K, V, layer=0, heads=None):
+    Kn = _to_np64(K)
+    Vn = _to_np64(V)
+    return O.build_layer(H, Kn, Vn, s.alpha, s.w, layer, s.rank_choices, s.rank_seed, s.kv_dtype,
+                         heads=heads)
+
+
+def _check_margins(s, H, segs):
+    for b in range(s.B):
+        th = segs[b].theta
+        assert np.min(np.abs(H[b].astype(np.float64) - th)) > 1e-12 * max(1.0, abs(th))
+
+
+def _decode_compare(s, ctx, arts, layer, steps, taus, heads=None, tol=1e-4):
+    """Decode `steps` queries on the GPU and compare every (b, h) with the oracle."""
+    m_max = ctx.m_max()
+    worst = 0.0
+    nz = 0
+    for t in range(steps):
+        q = synth.queries(s, layer, t)
+        qd = q.to(DEV)
+        out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+        mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
+        ctx.decode_attn(layer, qd, taus, out, mask)
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy().astype(np.float64)
+        mask_h = mask.cpu().numpy()
+        qn = q.numpy().astype(np.float64)
+        for b in range(s.B):
+            for h in range(s.Hq):
+                if heads is not None and h not in heads:
+                    continue
+                a = arts[(b, h // s.G)]
+                T.assert_no_ties(qn[b, h], float(taus[h]), a)
+                o_ref, z_ref, _ = O.decode_head(qn[b, h], float(taus[h]), a)
+                assert np.array_equal(mask_h[b, h, :a.m].astype(bool), z_ref), \
+                    f"zoom mask differs at step {t} b {b} h {h}"
+                assert np.all(mask_h[b, h, a.m:] == 7), "mask written beyond m"
+                e = T.rel_err(out_h[b, h], o_ref)
+                worst = max(worst, e)
+                nz += int(z_ref.sum())
+                assert e <= tol, f"step {t} b {b} h {h}: rel err {e}"
+    return worst, nz
+
+
+def _q_steps(s, layer, steps):
+    return np.stack([synth.queries(s, layer, t).numpy().astype(np.float64) for t in range(steps)])
+
+
+def _check_build(s, ctx, segs, arts, layer, H, K, V, heads=None, span_sample=None):
+    """GPU-built artefacts of `heads` against the oracle's."""
+    for b in range(s.B):
+        ms, mc, an, _ = ctx.spans(b)
+        assert np.array_equal(ms, segs[b].mstart), "span starts differ"
+        assert np.array_equal(mc, segs[b].mcount), "member counts differ"
+        assert np.array_equal(an, segs[b].anchors), "anchors differ"
+    Kh = K.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+    Vh = V.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+    hs = list(range(s.Hkv)) if heads is None else list(heads)
+    rng = np.random.default_rng(7)
+    for (b, g), a in arts.items():
+        i = hs.index(g)
+        kb, vb, KA, VA, rank, bases = ctx.export_head(layer, b, g)
+        assert np.array_equal(rank, a.rank), "ranks differ"
+        assert np.array_equal(T.from_storage(KA, s.kv_dtype), a.KA)
+        assert np.array_equal(T.from_storage(VA, s.kv_dtype), a.VA)
+        for got, ref in ((kb, a.kbar), (vb, a.vbar)):
+            g64 = T.from_storage(got, s.kv_dtype)
+            rowmax = np.max(np.abs(ref), axis=1, keepdims=True)
+            tol = (2.0 ** -7 if s.kv_dtype == "bf16" else 2e-6) * rowmax + 1e-30
+            assert np.all(np.abs(g64 - ref) <= tol), f"summary mismatch {np.max(np.abs(g64 - ref) / tol)}"
+        AK, BKt, AV, BVt = T.unpack_bases(bases, a.mcount, a.rank, s.kv_dtype, s.d)
+        ks = range(a.m) if span_sample is None else sorted(set(rng.choice(a.m, min(a.m, span_sample), replace=False)) | {int(np.argmax(a.mcount))})
+        for k in ks:
+            mem = np.arange(a.mstart[k], a.mstart[k] + a.mcount[k])
+            for X, A, Bt in ((Kh[b, i][mem], AK[k], BKt[k]), (Vh[b, i][mem], AV[k], BVt[k])):
+                sv = np.linalg.svd(X, compute_uv=False)
+                r = int(a.rank[k])
+                e_opt = math.sqrt(float(np.sum(sv[r:] ** 2)))
+                nx = float(np.linalg.norm(X))
+                e = float(np.linalg.norm(X - A @ Bt))
+                if s.kv_dtype == "bf16":
+                    assert e <= e_opt + 2.0 ** -7 * nx, (k, e, e_opt, nx)
+                    assert np.allclose(np.linalg.norm(A, axis=0), sv[:r], atol=2.0 ** -7 * sv[0])
+                else:
+                    assert e <= e_opt * (1 + 1e-3) + 1e-5 * nx, (k, e, e_opt, nx)
+                    assert np.allclose(np.linalg.norm(A, axis=0), sv[:r], atol=1e-4 * sv[0])
+                    assert np.max(np.abs(Bt @ Bt.T - np.eye(r))) <= 1e-4
+
+
+# ============================================================================ tiny
+
+@pytest.mark.parametrize("home", ["device", "host"])
+def test_tiny_fp32_all_zoom(home):
+    s = synth.spec("tiny")
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    _check_margins(s, H, segs)
+    # decode on the oracle's artefacts
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    taus = np.zeros(s.Hq, np.float32)   # tau = 0: every span zoomed
+    worst, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert nz == s.steps * segs[0].m
+    # the builder
+    ctx2 = _ctx(s, home)
+    ctx2.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    _check_build(s, ctx2, segs, arts, 0, H, K, V)
+    # end to end (GPU build -> GPU decode) vs the oracle: tiny SVD differences only
+    q = synth.queries(s, 0, 0)
+    out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+    ctx2.decode_attn(0, q.to(DEV), taus, out)
+    o_ref, _, _ = O.decode_head(q[0, 0].double().numpy(), 0.0, arts[(0, 0)])
+    assert T.rel_err(out[0, 0].cpu().double().numpy(), o_ref) < 1e-3
+
+
+def test_dense_equivalence_full_rank_fp32_d128():
+    """P1 on the GPU: tau = 0 and ranks >= min(|S|, d) make the mixed softmax
+    dense attention over all n tokens (GPU-built SVD, fp32 storage)."""
+    s = synth.spec("tiny").replace(d=128, n=1500, Hq=2, Hkv=2, w=64, rank_choices=(128,))
+    H, K, V = _inputs(s)
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    q = synth.queries(s, 0, 0)
+    out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+    ctx.decode_attn(0, q.to(DEV), np.zeros(s.Hq, np.float32), out)
+    torch.cuda.synchronize()
+    for h in range(s.Hq):
+        ref = O.dense_attention(q[0, h].double().numpy(), K[0, h].double().numpy(), V[0, h].double().numpy())
+        assert T.rel_err(out[0, h].cpu().double().numpy(), ref) <= 1e-4
+
+
+# ============================================================================ bf16, several heads
+
+def _small_bf16():
+    return synth.spec("single_layer_32k").replace(n=4096, Hq=8, Hkv=8, steps=6)
+
+
+@pytest.mark.parametrize("home", ["device", "host"])
+def test_small_bf16_decode_on_oracle_artefacts(home):
+    s = _small_bf16()
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    _check_margins(s, H, segs)
+    qs = _q_steps(s, 0, s.steps)
+    rates = np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1])
+    taus = T.thresholds_for(qs, arts, s.G, rates, s.B)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    worst, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert nz > 0
+    if home == "host":
+        st = ctx.stats()
+        assert st["spans_fetched"] > 0 and st["bytes_fetched"] > 0 and st["host_basis_bytes"] > 0
+
+
+def test_small_bf16_no_zoom_and_all_zoom():
+    s = _small_bf16().replace(steps=2)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    ctx = _ctx(s, "device")
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    taus = np.array([1.0, 2.0, 0.0, -1.0, 1.0, 0.0, 1.0, 0.0], np.float32)
+    _decode_compare(s, ctx, arts, 0, s.steps, taus)
+
+
+def test_small_bf16_build_parity():
+    s = _small_bf16()
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    _check_build(s, ctx, segs, arts, 0, H, K, V)
+
+
+# ============================================================================ GQA, ragged batch
+
+def _gqa_small():
+    return synth.spec("gqa_batch8_128k").replace(B=3, Hq=8, Hkv=2, n=6000, steps=3)
+
+
+@pytest.mark.parametrize("home", ["device", "host"])
+def test_gqa_ragged_batch_decode_and_build(home):
+    s = _gqa_small()
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    assert len({sg.m for sg in segs}) > 1, "sequences should have different span counts"
+    _check_margins(s, H, segs)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.01, 0.05, 0.15, 0.3, 0.3, 0.15, 0.05, 0.5]), s.B)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    ctx2 = _ctx(s, home)
+    ctx2.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    _check_build(s, ctx2, segs, arts, 0, H, K, V)
+
+
+# ============================================================================ edge cases
+
+def test_window_covers_everything_no_spans():
+    s = synth.spec("tiny").replace(n=300, w=400, Hq=2, Hkv=1)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    assert segs[0].m == 0 and segs[0].anchors.size == 300
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    q = synth.queries(s, 0, 0)
+    out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+    ctx.decode_attn(0, q.to(DEV), np.full(s.Hq, 0.5, np.float32), out)
+    torch.cuda.synchronize()
+    for h in range(s.Hq):
+        ref = O.dense_attention(q[0, h].double().numpy(), K[0, 0].double().numpy(), V[0, 0].double().numpy())
+        assert T.rel_err(out[0, h].cpu().double().numpy(), ref) <= 1e-5
+
+
+def test_single_token_context():
+    s = synth.spec("tiny").replace(n=1, w=0)
+    H = np.array([[1.5]], np.float32)
+    K = torch.randn(1, 1, 1, s.d)
+    V = torch.randn(1, 1, 1, s.d)
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), 1.0, (8,), 1)
+    ms, mc, an, _ = ctx.spans(0)
+    assert ms.tolist() == [0] and mc.tolist() == [1] and an.size == 0
+    out = torch.zeros(1, 1, s.d, device=DEV)
+    for tau in (0.0, 1.0):
+        ctx.decode_attn(0, torch.randn(1, 1, s.d, device=DEV), np.array([tau], np.float32), out)
+        torch.cuda.synchronize()
+        # a single entry: the output is that token's value (summary, or rank-1 rebuild)
+        assert torch.allclose(out[0, 0].cpu(), V[0, 0, 0], atol=1e-5)
+
+
+def test_error_paths_return_status():
+    sekv = _lib()
+    s = synth.spec("tiny").replace(n=256)
+    ctx = _ctx(s, "device")
+    H = torch.ones(1, 256, device=DEV)
+    H[0, 5] = -1.0
+    K = torch.randn(1, 1, 256, s.d, device=DEV)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.build(0, H, K, K, 1.0, (8,), 1)
+    assert ei.value.status == sekv.SEKV_ERR_INVALID
+    H[0, 5] = float("nan")
+    with pytest.raises(sekv.SekvError):
+        ctx.build(0, H, K, K, 1.0, (8,), 1)
+    out = torch.zeros(1, 1, s.d, device=DEV)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.decode_attn(0, torch.randn(1, 1, s.d, device=DEV), np.zeros(1, np.float32), out)
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    H = torch.rand(1, 256, device=DEV) + 0.5
+    ctx.build(0, H, K, K, 1.0, (8,), 1)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.decode_attn(0, torch.randn(1, 1, s.d, device=DEV), np.array([np.nan], np.float32), out)
+    assert ei.value.status == sekv.SEKV_ERR_INVALID
+    # a second build with another surprisal is refused (the span table is shared by all layers)
+    s2 = s.replace(L=2)
+    ctx2 = _ctx(s2, "device")
+    ctx2.build(0, H, K, K, 1.0, (8,), 1)
+    H2 = H.clone()
+    H2[0, 7] = 50.0
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx2.build(1, H2, K, K, 1.0, (8,), 1)
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    ctx2.build(1, H, K, K, 1.0, (8,), 1)
