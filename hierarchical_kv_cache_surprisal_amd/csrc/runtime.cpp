@@ -35,6 +35,31 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   return std::min(hi, std::max(lo, v));
 }
 
+// Work schedule of one layer's route kernel: one task per workgroup.  Zoom-heavy
+// (sequence, kv head) rows get smaller span chunks, so that no workgroup holds
+// more than a few zoomed spans, and go first; the zoom load of each row is
+// measured by the kernels (cumulative counters) and read back without a sync.
+struct LayerSched {
+  bool valid = false;
+  std::vector<int4> tasks;        // (bg | anchor << 31, first row, rows, partial slot)
+  int n_span_tasks = 0;           // span tasks come first
+  std::vector<int32_t> parts_n;   // [B*Hkv]
+  std::vector<int32_t> chunk;     // [B*Hkv] span rows per task
+  int max_parts = 0;
+  int4* tasks_d = nullptr;
+  int32_t* parts_d = nullptr;
+  size_t tasks_cap = 0;
+  int4* tasks_pin = nullptr;      // pinned staging of the uploads
+  int32_t* parts_pin = nullptr;
+  int32_t* zstat_d = nullptr;     // [B*Hkv] cumulative zoomed spans (device)
+  int32_t* stat_pin = nullptr;    // pinned copy
+  hipEvent_t ev = nullptr;        // recorded after the last statistics copy
+  bool pending = false;
+  uint64_t calls = 0, calls_at_copy = 0, calls_at_read = 0;
+  std::vector<int32_t> prev;      // cumulative counts at the last read
+  std::vector<double> est;        // zoomed spans per call, per row
+};
+
 struct LayerState {
   bool ready = false;      // every head has artefacts
   bool allocated = false;  // layout fixed, buffers allocated
@@ -44,6 +69,7 @@ struct LayerState {
   void* VA = nullptr;
   int32_t* rank_d = nullptr;
   int64_t* boff_d = nullptr;
+  int2* smeta_d = nullptr;  // [B*Hkv*m_max] {boff / 8, rank | count << 8} for the decode kernels
   void* bases_d = nullptr;  // DEVICE home (and build scratch for HOST home)
   void* bases_h = nullptr;  // HOST home: pinned store
   int64_t basis_elems = 0;
@@ -51,6 +77,7 @@ struct LayerState {
   std::vector<int64_t> boff_h;     // [B*Hkv*m_max], relative to the layer store
   std::vector<int64_t> head_base;  // [B*Hkv + 1]
   std::vector<uint8_t> head_set;   // [B*Hkv]
+  LayerSched sched;
 };
 
 }  // namespace
@@ -92,27 +119,34 @@ struct sekv_ctx {
   float* part_ml = nullptr;
   float* part_acc = nullptr;
   size_t parts_cap = 0;  // partial slots
-  uint32_t* counters = nullptr;
+
+  // zoom list and per-(span, head) partials
+  int4* zlist_d = nullptr;      // [B*Hkv*m_max] written by the route kernel
+  int32_t* zcounter_d = nullptr;
+  float* zpart_ml = nullptr;    // [B*Hq*m_max][2]
+  float* zpart_acc = nullptr;   // [B*Hq*m_max][d]
+  uint8_t* mask_d = nullptr;    // [B*Hq*m_max] used when the caller passes no mask
+  size_t zcap = 0;              // spans capacity B*Hkv*m_max of the buffers above
 
   // HOST-home fetch path
-  int32_t* zlist_d = nullptr;
-  int32_t* zcount_d = nullptr;
-  int32_t* zlist_h = nullptr;   // pinned [B*Hkv][m_max]
-  int32_t* zcount_h = nullptr;  // pinned [B*Hkv]
-  int32_t* zent_h = nullptr;    // pinned [B*Hkv*m_max]
+  int4* zlist_h = nullptr;      // pinned copy of the zoom list
+  int32_t* zcount_h = nullptr;  // pinned
+  int4* zitems_h = nullptr;     // pinned, sorted by (b, g, span)
   int64_t* zoff_h = nullptr;
-  int32_t* zbase_h = nullptr;   // pinned [B*Hkv + 1]
-  int32_t* zent_d = nullptr;
+  int32_t* zn_h = nullptr;
+  int4* zitems_d = nullptr;
   int64_t* zoff_d = nullptr;
-  int32_t* zbase_d = nullptr;
-  size_t zcap = 0;              // entries capacity of the tables above
+  int32_t* zn_d = nullptr;
   void* staging = nullptr;
   int64_t staging_cap = 0;      // elements
   hipStream_t side = nullptr;
   hipEvent_t ev_fetch = nullptr;
+  // anchor segment on a second stream, concurrent with routing and zoom
+  hipStream_t side2 = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
   sekv_stats stats{};
-  int anchor_chunk = 256, span_chunk = 64, zoom_chunks = 8;
+  int anchor_chunk = 256, span_chunk = 64, zoom_wgs = 512;
 };
 
 namespace {
@@ -200,13 +234,22 @@ void free_layer(LayerState& L) {
   dfree(L.VA);
   dfree(L.rank_d);
   dfree(L.boff_d);
+  dfree(L.smeta_d);
   dfree(L.bases_d);
   hfree(L.bases_h);
+  dfree(L.sched.tasks_d);
+  dfree(L.sched.parts_d);
+  dfree(L.sched.zstat_d);
+  hfree(L.sched.tasks_pin);
+  hfree(L.sched.parts_pin);
+  hfree(L.sched.stat_pin);
+  if (L.sched.ev) (void)hipEventDestroy(L.sched.ev);
   L = LayerState();
 }
 
+// Elements of one span's packed bases: A_K^T [r][c8], B_K^T [r][d], A_V^T, B_V^T.
 int64_t span_elems(int c, int r, int d) {
-  return 2 * pad8((int64_t)c * r) + 2 * pad8((int64_t)r * d);
+  return 2 * (int64_t)r * (pad8(c) + d);
 }
 
 // Install span tables (host vectors already filled); uploads device copies
@@ -299,6 +342,8 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
     }
   L.head_base[(size_t)B * Hkv] = off;
   L.basis_elems = off;
+  if ((off >> 3) >= ((int64_t)1 << 32))
+    return fail(c, SEKV_ERR_INVALID, "basis store of one layer exceeds 2^35 elements");
   const size_t rows_m = (size_t)B * Hkv * mm, rows_a = (size_t)B * Hkv * nm;
   TRY(dalloc(c, &L.kbar, rows_m * d * c->esz));
   TRY(dalloc(c, &L.vbar, rows_m * d * c->esz));
@@ -306,12 +351,29 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   TRY(dalloc(c, &L.VA, rows_a * d * c->esz));
   TRY(dalloc(c, &L.rank_d, rows_m * 4));
   TRY(dalloc(c, &L.boff_d, rows_m * 8));
+  TRY(dalloc(c, &L.smeta_d, rows_m * sizeof(int2)));
+  TRY(dalloc(c, &L.sched.zstat_d, (size_t)B * Hkv * 4));
+  HIPCHK(c, hipMemset(L.sched.zstat_d, 0, (size_t)B * Hkv * 4));
+  TRY(halloc(c, &L.sched.stat_pin, (size_t)B * Hkv * 4));
+  HIPCHK(c, hipEventCreateWithFlags(&L.sched.ev, hipEventDisableTiming));
+  L.sched.prev.assign((size_t)B * Hkv, 0);
+  L.sched.est.assign((size_t)B * Hkv, 0.0);
   HIPCHK(c, hipMemset(L.kbar, 0, rows_m * d * c->esz));
   HIPCHK(c, hipMemset(L.vbar, 0, rows_m * d * c->esz));
   HIPCHK(c, hipMemset(L.KA, 0, rows_a * d * c->esz));
   HIPCHK(c, hipMemset(L.VA, 0, rows_a * d * c->esz));
   HIPCHK(c, hipMemcpy(L.rank_d, L.rank_h.data(), rows_m * 4, hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(L.boff_d, L.boff_h.data(), rows_m * 8, hipMemcpyHostToDevice));
+  {
+    std::vector<int2> meta(rows_m, make_int2(0, 0));
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < Hkv; ++g)
+        for (int k = 0; k < c->m_b[b]; ++k) {
+          const size_t i = ((size_t)b * Hkv + g) * mm + k;
+          meta[i] = make_int2((int)(uint32_t)(L.boff_h[i] >> 3), L.rank_h[i] | (c->mcount[b][k] << 8));
+        }
+    HIPCHK(c, hipMemcpy(L.smeta_d, meta.data(), rows_m * sizeof(int2), hipMemcpyHostToDevice));
+  }
   TRY(dalloc(c, &L.bases_d, (size_t)off * c->esz));
   if (c->cfg.basis_home == SEKV_BASES_HOST) TRY(halloc(c, &L.bases_h, (size_t)off * c->esz));
   L.allocated = true;
@@ -329,32 +391,219 @@ sekv_status ensure_parts(sekv_ctx* c, size_t slots) {
   return SEKV_OK;
 }
 
-sekv_status ensure_fetch_tables(sekv_ctx* c) {
-  const int BH = c->cfg.batch * c->cfg.n_kv_heads;
-  const size_t need = (size_t)BH * c->m_max;
-  if (need <= c->zcap && c->zlist_d) return SEKV_OK;
+sekv_status ensure_zoom_buffers(sekv_ctx* c) {
+  const size_t spans = (size_t)c->cfg.batch * c->cfg.n_kv_heads * c->m_max;
+  if (spans <= c->zcap && c->zlist_d) return SEKV_OK;
   dfree(c->zlist_d);
-  dfree(c->zcount_d);
-  dfree(c->zent_d);
+  dfree(c->zpart_ml);
+  dfree(c->zpart_acc);
+  dfree(c->mask_d);
+  dfree(c->zitems_d);
   dfree(c->zoff_d);
-  dfree(c->zbase_d);
   hfree(c->zlist_h);
-  hfree(c->zcount_h);
-  hfree(c->zent_h);
+  hfree(c->zitems_h);
   hfree(c->zoff_h);
-  hfree(c->zbase_h);
   c->zcap = 0;
-  TRY(dalloc(c, &c->zlist_d, need * 4));
-  TRY(dalloc(c, &c->zcount_d, (size_t)BH * 4));
-  TRY(dalloc(c, &c->zent_d, need * 4));
-  TRY(dalloc(c, &c->zoff_d, need * 8));
-  TRY(dalloc(c, &c->zbase_d, ((size_t)BH + 1) * 4));
-  TRY(halloc(c, &c->zlist_h, need * 4));
-  TRY(halloc(c, &c->zcount_h, (size_t)BH * 4));
-  TRY(halloc(c, &c->zent_h, need * 4));
-  TRY(halloc(c, &c->zoff_h, need * 8));
-  TRY(halloc(c, &c->zbase_h, ((size_t)BH + 1) * 4));
-  c->zcap = need;
+  const size_t heads = spans * c->G;
+  TRY(dalloc(c, &c->zlist_d, spans * sizeof(int4)));
+  TRY(dalloc(c, &c->zpart_ml, heads * 2 * sizeof(float)));
+  TRY(dalloc(c, &c->zpart_acc, heads * c->cfg.d_head * sizeof(float)));
+  TRY(dalloc(c, &c->mask_d, heads));
+  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+    TRY(dalloc(c, &c->zitems_d, spans * sizeof(int4)));
+    TRY(dalloc(c, &c->zoff_d, spans * 8));
+    TRY(halloc(c, &c->zlist_h, spans * sizeof(int4)));
+    TRY(halloc(c, &c->zitems_h, spans * sizeof(int4)));
+    TRY(halloc(c, &c->zoff_h, spans * 8));
+  }
+  c->zcap = spans;
+  return SEKV_OK;
+}
+
+// Copy the bases of the listed spans (items: bg | head bits << 24, span id)
+// from the pinned store into staging on `side`, runs of adjacent spans
+// coalesced, and upload the sorted item list, staging offsets and count.
+sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hipStream_t side,
+                        hipEvent_t done) {
+  LayerState& L = c->layers[layer];
+  const int Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, mm = c->m_max;
+  int4* z = c->zitems_h;
+  if (items != z) std::memcpy(z, items, (size_t)count * sizeof(int4));
+  std::sort(z, z + count, [](const int4& x, const int4& y) {
+    const int bx = x.x & 0xffffff, by = y.x & 0xffffff;
+    return bx != by ? bx < by : x.y < y.y;
+  });
+  int64_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    const int bg = z[i].x & 0xffffff, k = z[i].y, b = bg / Hkv;
+    if (bg >= c->cfg.batch * Hkv || k < 0 || k >= c->m_b[b])
+      return fail(c, SEKV_ERR_INVALID, "zoom entry out of range");
+    if (i > 0 && bg == (z[i - 1].x & 0xffffff) && k == z[i - 1].y)
+      return fail(c, SEKV_ERR_INVALID, "zoom entry: duplicate span");
+    z[i].w = L.rank_h[(size_t)bg * mm + k] | (c->mcount[b][k] << 8);
+    need += span_elems(c->mcount[b][k], L.rank_h[(size_t)bg * mm + k], d);
+  }
+  if (need > c->staging_cap) {
+    dfree(c->staging);
+    c->staging_cap = 0;
+    const int64_t cap = std::max<int64_t>(need, std::min<int64_t>(L.basis_elems, need * 2));
+    TRY(dalloc(c, &c->staging, (size_t)cap * c->esz));
+    c->staging_cap = cap;
+  }
+  const char* f = std::getenv("SEKV_FAULT");
+  if (f && std::strcmp(f, "fetch") == 0) return fail(c, SEKV_ERR_HIP, "fetch failure forced (SEKV_FAULT=fetch)");
+  const char* hsrc = static_cast<const char*>(L.bases_h);
+  char* dst = static_cast<char*>(c->staging);
+  int64_t pos = 0, run_src = -1, run_dst = 0, run_len = 0;
+  uint64_t ncopies = 0;
+  for (int i = 0; i <= count; ++i) {
+    int64_t off = -1, sz = 0;
+    if (i < count) {
+      const int bg = z[i].x & 0xffffff, k = z[i].y;
+      off = L.boff_h[(size_t)bg * mm + k];
+      sz = span_elems(c->mcount[bg / Hkv][k], L.rank_h[(size_t)bg * mm + k], d);
+      c->zoff_h[i] = pos;
+    }
+    if (i < count && run_src >= 0 && off == run_src + run_len) {
+      run_len += sz;
+    } else {
+      if (run_src >= 0) {
+        HIPCHK(c, hipMemcpyAsync(dst + run_dst * c->esz, hsrc + run_src * c->esz, run_len * c->esz,
+                                 hipMemcpyHostToDevice, side));
+        ++ncopies;
+      }
+      run_src = off;
+      run_dst = pos;
+      run_len = sz;
+    }
+    pos += sz;
+  }
+  *c->zn_h = count;
+  if (count) {
+    HIPCHK(c, hipMemcpyAsync(c->zitems_d, z, (size_t)count * sizeof(int4), hipMemcpyHostToDevice, side));
+    HIPCHK(c, hipMemcpyAsync(c->zoff_d, c->zoff_h, (size_t)count * 8, hipMemcpyHostToDevice, side));
+  }
+  HIPCHK(c, hipMemcpyAsync(c->zn_d, c->zn_h, 4, hipMemcpyHostToDevice, side));
+  if (done) HIPCHK(c, hipEventRecord(done, side));
+  c->stats.fetch_calls++;
+  c->stats.spans_fetched += count;
+  c->stats.bytes_fetched += (uint64_t)pos * c->esz;
+  c->stats.memcpy_calls += ncopies;
+  return SEKV_OK;
+}
+
+// Task table of a layer from the per-row zoom estimates.
+void plan_tasks(sekv_ctx* c, LayerSched& S) {
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
+  const int base = env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, 1024);
+  const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
+  const int zpw = env_int("SEKV_ZOOM_PER_WG", 4, 1, 1024);
+  S.chunk.assign(BH, base);
+  S.parts_n.assign(BH, 0);
+  std::vector<int> nspan(BH), nanch(BH), anch(BH, ach);
+  std::vector<std::pair<double, int>> order;
+  for (int bg = 0; bg < BH; ++bg) {
+    const int m = c->m_b[bg / Hkv], na = c->na_b[bg / Hkv];
+    int n = std::max((m + base - 1) / base, (int)std::ceil(S.est[bg] / zpw));
+    n = std::max(1, std::min(n, std::max(1, (m + 15) / 16)));
+    int ch = m > 0 ? ((m + n - 1) / n + 15) / 16 * 16 : 16;
+    int a = ach;
+    auto parts = [&]() { return (m + ch - 1) / ch + (na + a - 1) / a; };
+    while (parts() > kMaxParts) {
+      if (ch < 1024) ch *= 2;
+      else a *= 2;
+    }
+    S.chunk[bg] = ch;
+    anch[bg] = a;
+    nspan[bg] = (m + ch - 1) / ch;
+    nanch[bg] = (na + a - 1) / a;
+    S.parts_n[bg] = nspan[bg] + nanch[bg];
+    order.push_back({-(S.est[bg] / std::max(1, nspan[bg])), bg});
+  }
+  std::stable_sort(order.begin(), order.end());
+  S.tasks.clear();
+  S.max_parts = 1;
+  for (int bg = 0; bg < BH; ++bg) S.max_parts = std::max(S.max_parts, S.parts_n[bg]);
+  for (auto& o : order) {  // span chunks, the most zoom-heavy rows first
+    const int bg = o.second, m = c->m_b[bg / Hkv];
+    for (int j = 0; j < nspan[bg]; ++j) S.tasks.push_back(make_int4(bg, j * S.chunk[bg], S.chunk[bg], j));
+  }
+  S.n_span_tasks = (int)S.tasks.size();
+  int amax = 0;
+  for (int bg = 0; bg < BH; ++bg) amax = std::max(amax, nanch[bg]);
+  for (int j = 0; j < amax; ++j)  // anchor chunks, interleaved over the rows
+    for (int bg = 0; bg < BH; ++bg)
+      if (j < nanch[bg])
+        S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg], anch[bg], nspan[bg] + j));
+}
+
+// Refresh a layer's schedule before a launch on `stream`.  `pending` means a
+// statistics copy (and any table upload queued before it) is in flight, with
+// S.ev recorded after it.  When that event has completed the counts are read,
+// the per-row estimates updated and the tables replanned; new tables are
+// uploaded from pinned staging that no copy in flight still reads.  While the
+// stream is being captured into a graph nothing changes and nothing is copied.
+sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capturing) {
+  LayerSched& S = c->layers[layer].sched;
+  const int BH = c->cfg.batch * c->cfg.n_kv_heads;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIPCHK(c, hipStreamIsCapturing(stream, &cs));
+  *capturing = cs != hipStreamCaptureStatusNone;
+  if (*capturing) {
+    if (!S.valid) return fail(c, SEKV_ERR_STATE, "decode a layer once before capturing it into a graph");
+    return SEKV_OK;
+  }
+  bool replan = !S.valid;
+  if (S.pending && hipEventQuery(S.ev) == hipSuccess) {
+    S.pending = false;
+    const uint64_t dc = S.calls_at_copy - S.calls_at_read;
+    if (dc > 0) {
+      for (int bg = 0; bg < BH; ++bg) {
+        const double per = (double)(S.stat_pin[bg] - S.prev[bg]) / (double)dc;
+        S.est[bg] = S.calls_at_read == 0 ? per : 0.5 * S.est[bg] + 0.5 * per;
+        S.prev[bg] = S.stat_pin[bg];
+      }
+      S.calls_at_read = S.calls_at_copy;
+      replan = true;
+    }
+  }
+  if (!replan || S.pending) return SEKV_OK;
+  const std::vector<int4> old_tasks = S.tasks;
+  plan_tasks(c, S);
+  if (S.valid && old_tasks.size() == S.tasks.size() &&
+      std::memcmp(old_tasks.data(), S.tasks.data(), S.tasks.size() * sizeof(int4)) == 0)
+    return SEKV_OK;
+  if (S.tasks.size() > S.tasks_cap) {
+    dfree(S.tasks_d);
+    hfree(S.tasks_pin);
+    S.tasks_cap = 0;
+    TRY(dalloc(c, &S.tasks_d, S.tasks.size() * sizeof(int4)));
+    TRY(halloc(c, &S.tasks_pin, S.tasks.size() * sizeof(int4)));
+    S.tasks_cap = S.tasks.size();
+  }
+  if (!S.parts_d) {
+    TRY(dalloc(c, &S.parts_d, (size_t)BH * 4));
+    TRY(halloc(c, &S.parts_pin, (size_t)BH * 4));
+  }
+  std::memcpy(S.tasks_pin, S.tasks.data(), S.tasks.size() * sizeof(int4));
+  std::memcpy(S.parts_pin, S.parts_n.data(), (size_t)BH * 4);
+  HIPCHK(c, hipMemcpyAsync(S.tasks_d, S.tasks_pin, S.tasks.size() * sizeof(int4), hipMemcpyHostToDevice, stream));
+  HIPCHK(c, hipMemcpyAsync(S.parts_d, S.parts_pin, (size_t)BH * 4, hipMemcpyHostToDevice, stream));
+  S.valid = true;
+  return SEKV_OK;
+}
+
+// After the kernels of a call: start a statistics copy if none is in flight.
+sekv_status finish_sched(sekv_ctx* c, int layer, hipStream_t stream, bool capturing) {
+  LayerSched& S = c->layers[layer].sched;
+  if (capturing) return SEKV_OK;
+  S.calls++;
+  if (S.pending) return SEKV_OK;
+  const int BH = c->cfg.batch * c->cfg.n_kv_heads;
+  HIPCHK(c, hipMemcpyAsync(S.stat_pin, S.zstat_d, (size_t)BH * 4, hipMemcpyDeviceToHost, stream));
+  HIPCHK(c, hipEventRecord(S.ev, stream));
+  S.pending = true;
+  S.calls_at_copy = S.calls;
   return SEKV_OK;
 }
 
@@ -385,17 +634,19 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.VA = L.VA;
   a.rank = L.rank_d;
   a.boff = L.boff_d;
+  a.smeta = L.smeta_d;
   a.bases = L.bases_d;
-  int na_any = 0;
-  for (int v : c->na_b) na_any = std::max(na_any, v);
-  int m_any = 0;
-  for (int v : c->m_b) m_any = std::max(m_any, v);
-  a.anchor_chunk = c->anchor_chunk;
-  a.n_anchor_chunks = (na_any + c->anchor_chunk - 1) / c->anchor_chunk;
-  a.span_chunk = c->span_chunk;
-  a.n_span_chunks = (m_any + c->span_chunk - 1) / c->span_chunk;
-  a.n_zoom_chunks = c->zoom_chunks;
-  a.counters = c->counters;
+  a.tasks = L.sched.tasks_d;
+  a.n_tasks = (int)L.sched.tasks.size();
+  a.n_span_tasks = L.sched.n_span_tasks;
+  a.parts_n = L.sched.parts_d;
+  a.max_parts = L.sched.max_parts;
+  a.zstat = L.sched.zstat_d;
+  a.n_zoom_wgs = env_int("SEKV_ZOOM_WGS", c->zoom_wgs, 1, 65536);
+  a.zlist = c->zlist_d;
+  a.zcounter = c->zcounter_d;
+  a.zpart_ml = c->zpart_ml;
+  a.zpart_acc = c->zpart_acc;
 }
 
 sekv_status thetas(sekv_ctx* c, const float* tau, DecodeArgs& a) {
@@ -432,6 +683,8 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(nullptr, SEKV_ERR_INVALID, "n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
   if (k.n_q_heads > kMaxHq) return fail(nullptr, SEKV_ERR_INVALID, "at most 64 query heads");
+  if ((int64_t)k.batch * k.n_kv_heads > kMaxBg)
+    return fail(nullptr, SEKV_ERR_INVALID, "batch * n_kv_heads must be <= 512");
   if (k.d_head != 64 && k.d_head != 128) return fail(nullptr, SEKV_ERR_INVALID, "d_head must be 64 or 128");
   if (k.kv_dtype != SEKV_F32 && k.kv_dtype != SEKV_BF16) return fail(nullptr, SEKV_ERR_INVALID, "bad kv_dtype");
   if (k.local_window < 0) return fail(nullptr, SEKV_ERR_INVALID, "local_window must be >= 0");
@@ -456,13 +709,20 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->anchors.assign(k.batch, {});
   c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
   c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
-  c->zoom_chunks = env_int("SEKV_ZOOM_CHUNKS", 8, 1, 1024);
-  sekv_status s = dalloc(c, &c->counters, sizeof(uint32_t) * k.batch * k.n_kv_heads);
-  if (s == SEKV_OK && hipMemset(c->counters, 0, sizeof(uint32_t) * k.batch * k.n_kv_heads) != hipSuccess)
-    s = fail(c, SEKV_ERR_HIP, "hipMemset(counters)");
+  c->zoom_wgs = env_int("SEKV_ZOOM_WGS", 512, 1, 65536);
+  sekv_status s = dalloc(c, &c->zcounter_d, 4);
+  if (s == SEKV_OK) s = dalloc(c, &c->zn_d, 4);
+  if (s == SEKV_OK) s = halloc(c, &c->zcount_h, 4);
+  if (s == SEKV_OK) s = halloc(c, &c->zn_h, 4);
+  if (s == SEKV_OK && hipMemset(c->zcounter_d, 0, 4) != hipSuccess) s = fail(c, SEKV_ERR_HIP, "hipMemset");
   if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess)
     s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side)");
   if (s == SEKV_OK && hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming) != hipSuccess)
+    s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
+  if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side2, hipStreamNonBlocking) != hipSuccess)
+    s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side2)");
+  if (s == SEKV_OK && (hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess))
     s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
   if (s != SEKV_OK) {
     g_create_err = c->err;
@@ -492,20 +752,26 @@ void sekv_destroy(sekv_ctx* c) {
   dfree(c->seg_stats);
   dfree(c->part_ml);
   dfree(c->part_acc);
-  dfree(c->counters);
   dfree(c->zlist_d);
-  dfree(c->zcount_d);
-  dfree(c->zent_d);
+  dfree(c->zcounter_d);
+  dfree(c->zpart_ml);
+  dfree(c->zpart_acc);
+  dfree(c->mask_d);
+  dfree(c->zitems_d);
   dfree(c->zoff_d);
-  dfree(c->zbase_d);
+  dfree(c->zn_d);
   hfree(c->zlist_h);
   hfree(c->zcount_h);
-  hfree(c->zent_h);
+  hfree(c->zitems_h);
   hfree(c->zoff_h);
-  hfree(c->zbase_h);
+  hfree(c->zn_h);
   dfree(c->staging);
+  if (c->side2) (void)hipStreamSynchronize(c->side2);
   if (c->ev_fetch) (void)hipEventDestroy(c->ev_fetch);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->side2) (void)hipStreamDestroy(c->side2);
   delete c;
 }
 
@@ -685,84 +951,18 @@ sekv_status sekv_zoom_fetch(sekv_ctx* c, int32_t layer, const int32_t* entries, 
   TRY(check_layer(c, layer));
   if (c->cfg.basis_home != SEKV_BASES_HOST) return fail(c, SEKV_ERR_STATE, "bases are device-resident");
   if (!entries || !counts) return fail(c, SEKV_ERR_INVALID, "NULL entries or counts");
-  TRY(ensure_fetch_tables(c));
-  LayerState& L = c->layers[layer];
-  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, mm = c->m_max;
-  // sizing pass and validation (entries copied to the pinned table and sorted per (b, g))
-  int64_t need = 0;
-  size_t ne = 0;
-  for (int b = 0; b < B; ++b)
-    for (int g = 0; g < Hkv; ++g) {
-      const size_t bg = (size_t)b * Hkv + g;
-      const int cnt = counts[bg];
-      if (cnt < 0 || cnt > c->m_b[b]) return fail(c, SEKV_ERR_INVALID, "zoom count out of range");
-      c->zbase_h[bg] = (int32_t)ne;
-      int32_t* z = c->zent_h + ne;
-      if (entries != c->zent_h) std::memcpy(z, entries + bg * mm, (size_t)cnt * 4);
-      std::sort(z, z + cnt, [](int32_t x, int32_t y) { return (x & 0xffffff) < (y & 0xffffff); });
-      for (int i = 0; i < cnt; ++i) {
-        const int k = z[i] & 0xffffff;
-        if (k >= c->m_b[b]) return fail(c, SEKV_ERR_INVALID, "zoom entry: span id out of range");
-        if (i > 0 && k == (z[i - 1] & 0xffffff)) return fail(c, SEKV_ERR_INVALID, "zoom entry: duplicate span");
-        need += span_elems(c->mcount[b][k], L.rank_h[bg * mm + k], d);
-      }
-      ne += cnt;
+  TRY(ensure_zoom_buffers(c));
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, mm = c->m_max;
+  int n = 0;
+  for (int bg = 0; bg < B * Hkv; ++bg) {
+    const int cnt = counts[bg];
+    if (cnt < 0 || cnt > c->m_b[bg / Hkv]) return fail(c, SEKV_ERR_INVALID, "zoom count out of range");
+    for (int i = 0; i < cnt; ++i) {
+      const int32_t e = entries[(size_t)bg * mm + i];
+      c->zitems_h[n++] = make_int4(bg | (int)((uint32_t)e & 0xff000000u), e & 0xffffff, 0, 0);
     }
-  c->zbase_h[(size_t)B * Hkv] = (int32_t)ne;
-  if (need > c->staging_cap) {
-    dfree(c->staging);
-    c->staging_cap = 0;
-    const int64_t cap = std::max<int64_t>(need, std::min<int64_t>(L.basis_elems, need * 2));
-    TRY(dalloc(c, &c->staging, (size_t)cap * c->esz));
-    c->staging_cap = cap;
   }
-  const char* f = std::getenv("SEKV_FAULT");
-  if (f && std::strcmp(f, "fetch") == 0) return fail(c, SEKV_ERR_HIP, "fetch failure forced (SEKV_FAULT=fetch)");
-  // copies, runs of adjacent spans coalesced
-  const char* hsrc = static_cast<const char*>(L.bases_h);
-  char* dst = static_cast<char*>(c->staging);
-  int64_t pos = 0;
-  uint64_t ncopies = 0;
-  for (int b = 0; b < B; ++b)
-    for (int g = 0; g < Hkv; ++g) {
-      const size_t bg = (size_t)b * Hkv + g;
-      int64_t run_src = -1, run_dst = 0, run_len = 0;
-      for (int i = c->zbase_h[bg]; i < c->zbase_h[bg + 1]; ++i) {
-        const int k = c->zent_h[i] & 0xffffff;
-        const int64_t off = L.boff_h[bg * mm + k];
-        const int64_t sz = span_elems(c->mcount[b][k], L.rank_h[bg * mm + k], d);
-        c->zoff_h[i] = pos;
-        if (run_src >= 0 && off == run_src + run_len) {
-          run_len += sz;
-        } else {
-          if (run_src >= 0) {
-            HIPCHK(c, hipMemcpyAsync(dst + run_dst * c->esz, hsrc + run_src * c->esz, run_len * c->esz,
-                                     hipMemcpyHostToDevice, side));
-            ++ncopies;
-          }
-          run_src = off;
-          run_dst = pos;
-          run_len = sz;
-        }
-        pos += sz;
-      }
-      if (run_src >= 0) {
-        HIPCHK(c, hipMemcpyAsync(dst + run_dst * c->esz, hsrc + run_src * c->esz, run_len * c->esz,
-                                 hipMemcpyHostToDevice, side));
-        ++ncopies;
-      }
-    }
-  if (ne) {
-    HIPCHK(c, hipMemcpyAsync(c->zent_d, c->zent_h, ne * 4, hipMemcpyHostToDevice, side));
-    HIPCHK(c, hipMemcpyAsync(c->zoff_d, c->zoff_h, ne * 8, hipMemcpyHostToDevice, side));
-  }
-  HIPCHK(c, hipMemcpyAsync(c->zbase_d, c->zbase_h, ((size_t)B * Hkv + 1) * 4, hipMemcpyHostToDevice, side));
-  if (done) HIPCHK(c, hipEventRecord(done, side));
-  c->stats.fetch_calls++;
-  c->stats.spans_fetched += ne;
-  c->stats.bytes_fetched += (uint64_t)pos * c->esz;
-  c->stats.memcpy_calls += ncopies;
-  return SEKV_OK;
+  return fetch_items(c, layer, c->zitems_h, n, side, done);
 }
 
 sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
@@ -772,43 +972,68 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   TRY(check_layer(c, layer));
   if (!q || !out) return fail(c, SEKV_ERR_INVALID, "NULL q or out");
   LayerState& L = c->layers[layer];
+  TRY(ensure_zoom_buffers(c));
   DecodeArgs a;
-  fill_decode_geometry(c, L, a);
-  TRY(thetas(c, tau, a));
+  TRY(thetas(c, tau, a));  // validates tau before anything is queued
+  bool capturing = false;
+  TRY(prepare_sched(c, layer, stream, &capturing));
+  {
+    double th[kMaxHq];
+    std::memcpy(th, a.theta, sizeof(th));
+    fill_decode_geometry(c, L, a);
+    std::memcpy(a.theta, th, sizeof(th));
+  }
   a.q = q;
   a.out = out;
-  a.mask = zoom_mask;
-  const bool host = c->cfg.basis_home == SEKV_BASES_HOST;
-  const int nc1 = a.n_anchor_chunks + a.n_span_chunks;
-  a.n_parts = nc1 + (host ? a.n_zoom_chunks : 0);
-  TRY(ensure_parts(c, (size_t)a.B * a.Hq * a.n_parts));
+  a.mask = zoom_mask ? zoom_mask : c->mask_d;
+  if (capturing && (size_t)a.B * a.Hq * a.max_parts > c->parts_cap)
+    return fail(c, SEKV_ERR_STATE, "partial buffers would grow during graph capture: decode once first");
+  TRY(ensure_parts(c, (size_t)a.B * a.Hq * a.max_parts));
   a.part_ml = c->part_ml;
   a.part_acc = c->part_acc;
   c->stats.decode_calls++;
-  if (!host) {
-    launch_decode_main(0, c->cfg.d_head, c->bf16, a, stream);
-    HIPCHK(c, hipGetLastError());
-    return SEKV_OK;
+  const int d = c->cfg.d_head;
+  // anchor tasks on the second stream, joined before the combine
+  const int nspan = a.n_span_tasks, ntask = a.n_tasks;
+  HIPCHK(c, hipEventRecord(c->ev_fork, stream));
+  HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_fork, 0));
+  launch_decode_route(false, nspan, ntask, d, c->bf16, a, c->side2);
+  HIPCHK(c, hipGetLastError());
+  HIPCHK(c, hipEventRecord(c->ev_join, c->side2));
+  // span tasks: routing, summaries, the zoom list
+  launch_decode_route(false, 0, nspan, d, c->bf16, a, stream);
+  HIPCHK(c, hipGetLastError());
+  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
+    a.zitems = c->zlist_d;
+    a.zn = c->zcounter_d;
+    launch_decode_zoom(false, d, c->bf16, a, stream);
+  } else {
+    // HOST home: learn the zoom list, fetch the bases, then the zoomed segment
+    if (capturing) return fail(c, SEKV_ERR_STATE, "host-resident bases need a host sync: not capturable");
+    HIPCHK(c, hipMemcpyAsync(c->zcount_h, c->zcounter_d, 4, hipMemcpyDeviceToHost, stream));
+    HIPCHK(c, hipStreamSynchronize(stream));
+    const int nz = *c->zcount_h;
+    if (nz) {
+      HIPCHK(c, hipMemcpyAsync(c->zlist_h, c->zlist_d, (size_t)nz * sizeof(int4), hipMemcpyDeviceToHost, stream));
+      HIPCHK(c, hipStreamSynchronize(stream));
+    }
+    sekv_status fs = fetch_items(c, layer, c->zlist_h, nz, c->side, c->ev_fetch);
+    if (fs != SEKV_OK) {
+      (void)hipStreamWaitEvent(stream, c->ev_join, 0);
+      (void)hipMemsetAsync(c->zcounter_d, 0, 4, stream);  // leave an empty list for the next call
+      return fs;
+    }
+    HIPCHK(c, hipStreamWaitEvent(stream, c->ev_fetch, 0));
+    a.zitems = c->zitems_d;
+    a.zn = c->zn_d;
+    a.zoff = c->zoff_d;
+    a.staging = c->staging;
+    launch_decode_zoom(true, d, c->bf16, a, stream);
   }
-  TRY(ensure_fetch_tables(c));
-  const int BH = a.B * a.Hkv;
-  a.zlist = c->zlist_d;
-  a.zcount = c->zcount_d;
-  HIPCHK(c, hipMemsetAsync(c->zcount_d, 0, (size_t)BH * 4, stream));
-  launch_decode_main(1, c->cfg.d_head, c->bf16, a, stream);
+  HIPCHK(c, hipStreamWaitEvent(stream, c->ev_join, 0));
+  launch_decode_combine(d, a, stream);
   HIPCHK(c, hipGetLastError());
-  HIPCHK(c, hipMemcpyAsync(c->zcount_h, c->zcount_d, (size_t)BH * 4, hipMemcpyDeviceToHost, stream));
-  HIPCHK(c, hipMemcpyAsync(c->zlist_h, c->zlist_d, (size_t)BH * c->m_max * 4, hipMemcpyDeviceToHost, stream));
-  HIPCHK(c, hipStreamSynchronize(stream));
-  TRY(sekv_zoom_fetch(c, layer, c->zlist_h, c->zcount_h, c->side, c->ev_fetch));
-  HIPCHK(c, hipStreamWaitEvent(stream, c->ev_fetch, 0));
-  a.zent = c->zent_d;
-  a.zoff = c->zoff_d;
-  a.zbase = c->zbase_d;
-  a.staging = c->staging;
-  launch_decode_staged_zoom(c->cfg.d_head, c->bf16, a, stream);
-  HIPCHK(c, hipGetLastError());
-  return SEKV_OK;
+  return finish_sched(c, layer, stream, capturing);
 }
 
 sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float* scores, hipStream_t stream) {
@@ -817,12 +1042,14 @@ sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float*
   TRY(check_layer(c, layer));
   if (!q || !scores) return fail(c, SEKV_ERR_INVALID, "NULL q or scores");
   LayerState& L = c->layers[layer];
+  bool capturing = false;
+  TRY(prepare_sched(c, layer, stream, &capturing));
   DecodeArgs a;
   fill_decode_geometry(c, L, a);
   for (int h = 0; h < kMaxHq; ++h) a.theta[h] = INFINITY;
   a.q = q;
   a.scores = scores;
-  launch_decode_main(2, c->cfg.d_head, c->bf16, a, stream);
+  launch_decode_route(true, 0, a.n_span_tasks, c->cfg.d_head, c->bf16, a, stream);
   HIPCHK(c, hipGetLastError());
   return SEKV_OK;
 }

@@ -8,8 +8,11 @@
 namespace sekv {
 
 constexpr int kMaxHq = 64;        // query heads per layer supported by the decode kernels
+constexpr int kMaxBg = 512;       // sequences x kv heads supported by the decode kernels
 constexpr int kThreads = 256;     // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
+constexpr int kMaxParts = 512;  // split-K partial slots per (sequence, query head)
+constexpr int kCombineThreads = 1024;
 
 // Every packed basis block starts on a multiple of 8 elements (16 bytes for
 // bf16), so wide loads stay aligned.
@@ -29,33 +32,39 @@ struct DecodeArgs {
   const void* VA;
   const int32_t* rank;    // [B][Hkv][m_max]
   const int64_t* boff;    // [B][Hkv][m_max] element offset of each span's packed bases
+  const int2* smeta;      // [B][Hkv][m_max] {boff / 8, rank | member count << 8}
   const void* bases;      // device basis store of the layer (DEVICE home)
   const float* q;         // [B][Hq][d]
   float* out;             // [B][Hq][d]
-  uint8_t* mask;          // [B][Hq][m_max] or null
-  float* scores;          // [B][Hq][m_max] or null (route-only mode)
-  int n_anchor_chunks, anchor_chunk;  // anchor rows per workgroup
-  int n_span_chunks, span_chunk;      // spans per workgroup
-  int n_zoom_chunks;                  // workgroups per (b, g) of the staged-zoom kernel
-  int n_parts;                        // partial slots per (b, h)
-  float* part_ml;         // [B][Hq][n_parts][2] (running max in log2 units, sum)
-  float* part_acc;        // [B][Hq][n_parts][d]
-  uint32_t* counters;     // [B][Hkv] arrival tickets, self-resetting
-  int32_t* zlist;         // [B][Hkv][m_max] zoom list (HOST home), unordered
-  int32_t* zcount;        // [B][Hkv]
-  const int32_t* zent;    // staged zoom entries, sorted per (b, g)
-  const int64_t* zoff;    // staging element offset per entry
-  const int32_t* zbase;   // [B*Hkv + 1] first entry of each (b, g)
-  const void* staging;    // device staging buffer
+  uint8_t* mask;          // [B][Hq][m_max] zoom decisions (always written)
+  float* scores;          // [B][Hq][m_max] (routing-scores mode)
+  const int4* tasks;      // one per route workgroup: (bg | anchor kind << 31, first row, rows, partial slot)
+  int n_tasks, n_span_tasks;  // span tasks first, then anchor tasks
+  const int32_t* parts_n; // [B*Hkv] partial slots used by each (sequence, kv head)
+  int max_parts;          // partial slots per (sequence, query head) in the buffers below
+  int32_t* zstat;         // [B*Hkv] cumulative zoomed spans of this layer (scheduling statistics)
+  float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
+  float* part_acc;        // [B][Hq][max_parts][d]
+  int4* zlist;            // zoom list: (bg | head bits << 24, span, boff / 8, rank | count << 8)
+  int32_t* zcounter;      // its length (atomic; reset by the combine kernel)
+  const int4* zitems;     // spans the zoom kernel processes (zlist, or the sorted staged list)
+  const int32_t* zn;      // their count (device)
+  const int64_t* zoff;    // staging element offset per staged item (HOST home)
+  const void* staging;    // device staging buffer (HOST home)
+  int n_zoom_wgs;         // workgroups of the zoom kernel
+  float* zpart_ml;        // [B][Hkv][m_max][G][2] partial of each zoomed (span, head)
+  float* zpart_acc;       // [B][Hkv][m_max][G][d]
   double theta[kMaxHq];   // logit(tau) per query head
 };
 
-// mode 0: anchors + routing + summaries + zoomed spans from the device store, in-kernel combine
-// mode 1: anchors + routing + summaries; zoomed spans appended to the zoom list
-// mode 2: routing scores only
-void launch_decode_main(int mode, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
-// zoomed spans from the staging buffer, then the combine over all partial slots
-void launch_decode_staged_zoom(int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// route-kernel tasks [t0, t1) of the table: anchors, routing and summaries, zoomed spans
+// appended to the list (scores_only: routing scores into `scores`, nothing else)
+void launch_decode_route(bool scores_only, int t0, int t1, int d, int kv_bf16, const DecodeArgs& a,
+                         hipStream_t s);
+// zoomed spans of the list, bases in the device store or (staged) the staging buffer
+void launch_decode_zoom(bool staged, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// log-sum-exp merge of every (sequence, query head) into out; empties the zoom list
+void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- build
 

@@ -130,10 +130,11 @@ __device__ Prob load_prob(const SvdArgs& a, int Hkv) {
   return p;
 }
 
+// Packed blocks of a span: A_K^T [r][c8] | B_K^T [r][D] | A_V^T [r][c8] | B_V^T [r][D].
 template <typename T, int D>
 __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt) {
   T* base = reinterpret_cast<T*>(a.bases) + p.off;
-  const int64_t ca = pad8((int64_t)p.c * p.r), rb = pad8((int64_t)p.r * D);
+  const int64_t ca = (int64_t)p.r * pad8(p.c), rb = (int64_t)p.r * D;
   if (p.which) base += ca + rb;
   return bt ? base + ca : base;
 }
@@ -165,16 +166,13 @@ __global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
   __syncthreads();
   rank_by_norm(X, XS, D, p.c, p.r, sig, order);
 
-  T* A = block_ptr<T, D>(a, p, false);
-  const int na = (int)pad8((int64_t)p.c * p.r);
-  for (int idx = threadIdx.x; idx < na; idx += kThreads) {
-    float v = 0.f;
-    if (idx < p.c * p.r) {
-      const int t = idx / p.r, kk = idx % p.r;
-      const int i = order[kk];
-      v = Jv[i * JS + t] * sig[i];
-    }
-    A[idx] = Elem<T>::from_f(v);
+  // A^T [r][c8]: row kk = sigma_i * (column i of J), zero beyond c
+  T* At = block_ptr<T, D>(a, p, false);
+  const int c8 = (int)pad8(p.c);
+  for (int idx = threadIdx.x; idx < p.r * c8; idx += kThreads) {
+    const int kk = idx / c8, t = idx % c8;
+    const int i = order[kk];
+    At[idx] = Elem<T>::from_f(t < p.c ? Jv[i * JS + t] * sig[i] : 0.f);
   }
   T* Bt = block_ptr<T, D>(a, p, true);
   for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
@@ -299,8 +297,9 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
     const int kk = idx / D, e = idx % D;
     Bt[idx] = Elem<T>::from_f(sig[order[kk]] > 0.f ? Jv[order[kk] * XS + e] : 0.f);
   }
-  // 5. A = X V_r, streamed (R no longer needed: reuse its LDS for X rows)
-  T* A = block_ptr<T, D>(a, p, false);
+  // 5. A = X V_r, streamed (R no longer needed: reuse its LDS for X rows), stored as A^T [r][c8]
+  T* At = block_ptr<T, D>(a, p, false);
+  const int c8 = (int)pad8(p.c);
   float* Xr = Rc;  // [ROWS][XS]
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     __syncthreads();
@@ -316,11 +315,13 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
       float s = 0.f;
       if (sig[i] > 0.f)
         for (int e = 0; e < D; ++e) s += Xr[t * XS + e] * Jv[i * XS + e];
-      A[(size_t)(t0 + t) * r + kk] = Elem<T>::from_f(s);
+      At[(size_t)kk * c8 + t0 + t] = Elem<T>::from_f(s);
     }
   }
-  const int64_t na = pad8((int64_t)p.c * r);
-  for (int64_t idx = (int64_t)p.c * r + threadIdx.x; idx < na; idx += kThreads) A[idx] = Elem<T>::from_f(0.f);
+  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kThreads) {
+    const int kk = idx / (c8 - p.c), t = p.c + idx % (c8 - p.c);
+    At[(size_t)kk * c8 + t] = Elem<T>::from_f(0.f);
+  }
 }
 
 template <int D, typename T, int PMAX>

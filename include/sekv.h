@@ -125,11 +125,15 @@ sekv_status sekv_build(sekv_ctx* ctx, int32_t layer, const float* H, const void*
 sekv_status sekv_get_spans(const sekv_ctx* ctx, int32_t b, int32_t* m, int32_t* n_anchors,
                            int32_t* m_max, int32_t* mstart, int32_t* mcount, int32_t* anchors);
 
-/* Packed basis layout of one (layer, b, kv head g).  For span k with c = mcount[k]
- * and r = rank[k] the store holds, from element offset basis_off[k], four
- * row-major blocks A_K [c][r], B_K^T [r][d], A_V [c][r], B_V^T [r][d]
- * (A = U_r Sigma_r, B^T = V_r^T of the span's member rows), each block padded
- * to a multiple of 8 elements; spans follow each other in span order.
+/* Packed basis layout of one (layer, b, kv head g).  For span k with c = mcount[k],
+ * c8 = c rounded up to a multiple of 8, and r = rank[k], the store holds from
+ * element offset basis_off[k] four row-major blocks
+ *     A_K^T [r][c8] | B_K^T [r][d] | A_V^T [r][c8] | B_V^T [r][d]
+ * where A = U_r Sigma_r (c x r) and B^T = V_r^T (r x d) are the truncated SVD
+ * factors of the span's member rows (X ~ A B^T); A is stored transposed
+ * (rank-major, one row per singular component) with columns c..c8-1 zero, so
+ * every block starts on a 16-byte boundary.  A span takes 2*r*(c8 + d)
+ * elements; spans follow each other in span order.
  *   rank host int32 [m], basis_off host int64 [m] (elements), basis_elems
  *   total elements; any may be NULL.
  * Errors: STATE (layer not built), INVALID. */

@@ -32,30 +32,36 @@ def from_storage(x: np.ndarray, kv_dtype: str) -> np.ndarray:
 
 def pack_bases(art: O.HeadArtifacts, kv_dtype: str, d: int) -> np.ndarray:
     """The packed layout documented at sekv_get_bases_layout: per span
-    [A_K | B_K^T | A_V | B_V^T], each block padded to 8 elements."""
+    [A_K^T (r x c8) | B_K^T (r x d) | A_V^T (r x c8) | B_V^T (r x d)],
+    c8 = c rounded up to 8, A stored transposed with zero columns c..c8-1."""
     parts = []
     for k in range(art.m):
         c, r = int(art.mcount[k]), int(art.rank[k])
-        for blk, n in ((art.AK[k], c * r), (art.BKt[k], r * d), (art.AV[k], c * r), (art.BVt[k], r * d)):
-            flat = np.zeros(pad8(n))
-            flat[:n] = np.asarray(blk, dtype=np.float64).reshape(-1)
-            parts.append(flat)
+        c8 = pad8(c)
+        for A, Bt in ((art.AK[k], art.BKt[k]), (art.AV[k], art.BVt[k])):
+            at = np.zeros((r, c8))
+            at[:, :c] = np.asarray(A, dtype=np.float64).T
+            parts.append(at.reshape(-1))
+            parts.append(np.asarray(Bt, dtype=np.float64).reshape(-1))
     flat = np.concatenate(parts) if parts else np.zeros(0)
     return storage(flat, kv_dtype)
 
 
 def unpack_bases(flat_storage: np.ndarray, mcount, rank, kv_dtype: str, d: int):
-    """Inverse of pack_bases: lists AK, BKt, AV, BVt (float64)."""
+    """Inverse of pack_bases: lists AK (c x r), BKt (r x d), AV, BVt (float64)."""
     flat = from_storage(flat_storage, kv_dtype)
     AK, BKt, AV, BVt = [], [], [], []
     pos = 0
     for c, r in zip(mcount, rank):
         c, r = int(c), int(r)
+        c8 = pad8(c)
         out = []
-        for shape in ((c, r), (r, d), (c, r), (r, d)):
-            n = shape[0] * shape[1]
-            out.append(flat[pos:pos + n].reshape(shape))
-            pos += pad8(n)
+        for _ in range(2):
+            at = flat[pos:pos + r * c8].reshape(r, c8)
+            pos += r * c8
+            bt = flat[pos:pos + r * d].reshape(r, d)
+            pos += r * d
+            out += [at[:, :c].T.copy(), bt]
         AK.append(out[0]); BKt.append(out[1]); AV.append(out[2]); BVt.append(out[3])
     return AK, BKt, AV, BVt
 

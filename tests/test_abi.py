@@ -82,7 +82,7 @@ def test_pack_unpack_roundtrip():
     seg = O.segment(H, 1.0, 10)
     art = O.build_head(H, K, V, seg, 0, 0, (3, 5, 8), 1, "f32")
     flat = pack_bases(art, "f32", 64)
-    want = sum(2 * pad8(c * r) + 2 * pad8(r * 64) for c, r in zip(art.mcount, art.rank))
+    want = sum(2 * r * (pad8(c) + 64) for c, r in zip(art.mcount, art.rank))
     assert flat.size == want
     AK, BKt, AV, BVt = unpack_bases(flat, art.mcount, art.rank, "f32", 64)
     for k in range(art.m):
