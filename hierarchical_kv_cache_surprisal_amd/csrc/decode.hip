@@ -10,32 +10,41 @@
 //   zoomed span      its tokens rebuilt from the truncated SVD (eq. (6)),
 //                    K^ = A_K B_K^T, V^ = A_V B_V^T, scored in rank space:
 //                    p = B_K^T q, logit_t = A_K[t].p / sqrt(d),
-//                    c = sum_t e_t A_V[t], contribution c . B_V^T.
+//                    w = sum_t e_t A_V[t], contribution w . B_V^T.
 //
-// Per layer-step (split-K over the context):
-//   k_route    one workgroup per task of the runtime's table.  Anchor tasks:
-//              exact tokens.  Span tasks: routing scores, zoom decisions
-//              (written to the zoom mask) and the summaries of the spans each
-//              head does not zoom; every span zoomed by some head of the group
-//              is appended to one global list.  One partial per task.  The
-//              anchor tasks run as a separate launch on a second stream,
-//              concurrently with the span tasks and the zoom kernel.
-//   k_zoom     one wave per listed span, balanced over all heads and
-//              sequences: the span's tokens in rank space, one partial per
-//              (span, zooming head).
-//   k_combine  one workgroup per (sequence, query head): log-sum-exp merge of
-//              its task partials and, in span order, of the partials of the
-//              spans its mask row marks.
+// A layer-step is split over the context into tasks, each writing one partial
+// (running max in log2 units, sum, d-vector accumulator) per query head into
+// a slot of its own, in three kernels:
+//   k_route    one workgroup per span task: routing scores of a chunk of
+//              spans, the zoom decisions (zoom mask), the summary entries of
+//              the spans a head does not zoom, and the chunk's zoomed spans
+//              listed in span order (device-resident bases: one entry per
+//              token tile, a "unit", in the task's range of a table;
+//              host-resident: appended to a flat list for the host fetch).
+//   k_attend   zoom workgroups first, then one workgroup per anchor task
+//              (the exact tokens of a chunk of anchors).  Device store: the
+//              units of the whole layer-step, balanced over the zoom
+//              workgroups (each forms the prefix of the per-task unit counts
+//              and takes a contiguous range), one partial per unit.  Staged
+//              bases: one workgroup per fetched span task, into the task's
+//              second slot.  The anchor stream hides the latency of the zoom
+//              chain (unit list, then bases).
+//   k_combine  log-sum-exp merge of every (sequence, query head)'s slots and
+//              units, in a fixed order.
+// No workgroup waits for another and no atomic shares an address across the
+// grid: kernel boundaries order the phases.
 // Lanes are grouped in "row slots" of d*elem/16 lanes, each slot streaming
-// whole 16-byte row pieces with its own online-softmax state (max in log2
-// units, sum, d-slice of the accumulator) for the G query heads of the kv
-// head.  The path is HBM-bound (about one flop per byte per query head), so
-// no MFMA is used.
+// whole 16-byte row pieces.  The path is HBM-bound (about one flop per byte per
+// query head), so no MFMA is used.
 #include "sekv_device.h"
+
+#include <type_traits>
 
 namespace sekv {
 
 namespace {
+
+typedef unsigned long long u64;
 
 template <int G>
 struct SoftState {
@@ -56,14 +65,11 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float* acc, float 
   m = mn;
 }
 
-// ------------------------------------------------------------------ zoomed span, one wave
-
-// A raw N-element piece of T as loaded (converted to float at use, so a batch of
-// pieces in flight costs N*sizeof(T)/4 registers each).
-template <typename T, int N>
+// A raw 16-byte piece of T as loaded (converted to float at use).
+template <typename T>
 struct Raw;
 template <>
-struct Raw<bf16_t, 8> {
+struct Raw<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
   __device__ __forceinline__ float get(int e) const {
@@ -72,279 +78,259 @@ struct Raw<bf16_t, 8> {
   }
 };
 template <>
-struct Raw<bf16_t, 4> {
-  uint2 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ float get(int e) const {
-    const uint32_t w = e < 2 ? v.x : v.y;
-    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-  }
-};
-template <>
-struct Raw<float, 4> {
+struct Raw<float> {
   float4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 };
-template <>
-struct Raw<float, 8> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
-  }
-  __device__ __forceinline__ float get(int e) const {
-    const float4& v = e < 4 ? a : b;
-    const int k = e & 3;
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-  }
+
+// Lane geometry for head dimension D and element type T.
+template <int D, typename T>
+struct Geo {
+  static constexpr int EPL = Elem<T>::kPer16;  // elements per 16-byte piece
+  static constexpr int LPR = D / EPL;          // lanes per D-row: one row slot
+  static constexpr int RPW = 64 / LPR;         // row slots per wave
+  // zoomed spans: lane = rank group (its row slot) x token group (its lane in the slot)
+  static constexpr int TILE = LPR * EPL;       // tokens per tile (= D)
+  static constexpr int RB = ((int)sizeof(T) == 2 ? 32 : 16) / RPW;  // rank rows per lane per batch
+  static constexpr int RBATCH = RB * RPW;
 };
 
-template <int D, typename T, int G>
-struct ZoomCfg {
-  static constexpr int EPL = Elem<T>::kPer16;
-  static constexpr int RPW = 64 / (D / EPL);  // B rows per wave per load
-  static constexpr int TPL = G >= 4 ? 4 : 8;  // tokens per lane in a token tile
-  static constexpr int TILE = 64 * TPL;
-  // rank components whose A pieces are in flight together: 64 registers of raw data
-  static constexpr int BATCH = 64 / (TPL * (int)sizeof(T) / 4);
-  // spans with r <= FAST_R and c <= TILE load everything in one round
-  static constexpr int FAST_R = BATCH < 4 * RPW ? BATCH : 4 * RPW;
-};
+// Sum over the row slots of a wave (lanes with the same position in their slot).
+template <int LPR>
+__device__ __forceinline__ float slots_sum(float x) {
+#pragma unroll
+  for (int s = LPR; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
+  return x;
+}
 
 template <int G>
 struct ZoomLds {
   float P[G][128];  // p = B_K^T q, pre-scaled by log2(e)/sqrt(d); zero beyond r
-  float C[G][128];  // c = sum_t e_t A_V[t]
+  float W[G][128];  // w = sum_t e_t A_V[t]; zero beyond r
 };
 
-// One zoomed span (c tokens, rank r) of one kv head, in rank space, by one wave.
+// ------------------------------------------------------------------ zoomed span tile, one wave
+
+// One unit of a zoomed span (c tokens, rank r <= D) of one kv head: the
+// tokens [t0, min(c, t0 + TILE)), in rank space.  Units of one span are
+// independent entries of the softmax and merge by log-sum-exp.
 //   base: the span's packed bases A_K^T [r][c8] | B_K^T [r][D] | A_V^T [r][c8] | B_V^T [r][D]
-// Lanes cover TPL consecutive tokens of a token tile for A_K^T / A_V^T (wide
-// pieces of each rank component's row) and row slots for B_K^T / B_V^T.  All
-// loads use clamped, always-valid addresses (no load sits behind a branch),
-// and spans with r <= FAST_R, c <= TILE issue every load in one round.
-// Out: per head the span's softmax max sm (log2 units) and sum sl, and the
-// output c . B_V^T split over the row slots (slot j holds rows i = j mod RPW).
+// Lane (rank group rg = its row slot, token group tg = its lane in the slot)
+// holds rank rows j = rg + RPW*u: for B_K^T / B_V^T the 16-byte piece at column
+// tg*EPL, for A_K^T / A_V^T the piece of EPL tokens starting at t0 + tg*EPL.
+// p_j lands, after the reduction inside the row slot, exactly in the lanes
+// that hold row j of A_K^T, and w_j in those holding row j of B_V^T, so no
+// data moves between the four products.  Addresses are clamped to valid rows
+// and tokens (no load sits behind a branch).  With r <= RBATCH every load of
+// the unit is issued in one round; larger ranks go in rank batches with p and
+// w in LDS.
+// Out, per head: softmax max sm (log2 units), sum sl, and the output slice
+// o[e] of column tg*EPL + e (the same in every row slot).
 template <int D, typename T, int G>
-__device__ void zoom_span(const T* __restrict__ base, int c, int r, const float (&qr)[G][Elem<T>::kPer16],
-                          ZoomLds<G>& z, float c2, int lane, int slot, int sub, float (&sm)[G], float (&sl)[G],
+__device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, const float (&qr)[G][Elem<T>::kPer16],
+                          ZoomLds<G>& z, float c2, int rg, int tg, float (&sm)[G], float (&sl)[G],
                           float (&o)[G][Elem<T>::kPer16]) {
-  using Cfg = ZoomCfg<D, T, G>;
-  constexpr int EPL = Cfg::EPL, RPW = Cfg::RPW, LPR = D / EPL;
-  constexpr int TPL = Cfg::TPL, TILE = Cfg::TILE, BATCH = Cfg::BATCH, FAST_R = Cfg::FAST_R;
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr int RB = Gm::RB, RBATCH = Gm::RBATCH;
   const int c8 = (c + 7) & ~7;
   const T* AKt = base;
   const T* BKt = AKt + (size_t)r * c8;
   const T* AVt = BKt + (size_t)r * D;
   const T* BVt = AVt + (size_t)r * c8;
   const int rl = r - 1;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    sm[h] = kNegInf;
-    sl[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-  }
+  const int tok = t0 + tg * EPL;
+  const int tokc = tok < c8 ? tok : t0;  // t0 < c: a valid piece
 
-  if (r <= FAST_R && c <= TILE) {
-    // ---------------- one round: every piece of the span in flight together
-    const int tb = lane * TPL;
-    const bool act = tb < c;
-    const int tbl = act ? tb : 0;
-    Raw<T, EPL> fb[4], fw[4];
-    Raw<T, TPL> fa[FAST_R], fv[FAST_R];
+  if (r <= RBATCH) {
+    // ---------------- one rank batch: everything in registers, one round
+    Raw<T> bk[RB], ak[RB], av[RB], bv[RB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = min(u * RPW + slot, rl);
-      fb[u].load(BKt + (size_t)i * D + sub * EPL);
-      fw[u].load(BVt + (size_t)i * D + sub * EPL);
+    for (int u = 0; u < RB; ++u) {
+      const int j = min(rg + RPW * u, rl);
+      bk[u].load(BKt + (size_t)j * D + tg * EPL);
+      ak[u].load(AKt + (size_t)j * c8 + tokc);
+      av[u].load(AVt + (size_t)j * c8 + tokc);
+      bv[u].load(BVt + (size_t)j * D + tg * EPL);
     }
-#pragma unroll
-    for (int u = 0; u < FAST_R; ++u) {
-      const int i = min(u, rl);
-      fa[u].load(AKt + (size_t)i * c8 + tbl);
-      fv[u].load(AVt + (size_t)i * c8 + tbl);
-    }
-    // p (zero beyond r)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float dp = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * fb[u].get(e);
-        dp = group_sum<LPR>(dp);
-        const int i = u * RPW + slot;
-        if (sub == 0 && i < FAST_R) z.P[h][i] = i < r ? dp * c2 : 0.f;
-      }
-    wave_lds_sync();
-    float ew[G][TPL];
+    float lg[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float lg[TPL];
+      float p[RB];
 #pragma unroll
-      for (int e = 0; e < TPL; ++e) lg[e] = 0.f;
+      for (int u = 0; u < RB; ++u) {
+        float dp = 0.f;
 #pragma unroll
-      for (int u = 0; u < FAST_R; ++u) {
-        const float pv = z.P[h][u];
-#pragma unroll
-        for (int e = 0; e < TPL; ++e) lg[e] += fa[u].get(e) * pv;
+        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * bk[u].get(e);
+        dp = group_sum<LPR>(dp);
+        p[u] = (rg + RPW * u < r) ? dp * c2 : 0.f;
       }
-      float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < TPL; ++e) {
-        if (tb + e >= c) lg[e] = kNegInf;
-        mx = fmaxf(mx, lg[e]);
-      }
-      mx = wave_max(mx);
-      float ssum = 0.f;
-#pragma unroll
-      for (int e = 0; e < TPL; ++e) {
-        ew[h][e] = fast_exp2(lg[e] - mx);
-        ssum += ew[h][e];
-      }
-      sm[h] = mx;
-      sl[h] = wave_sum(ssum);
-    }
-    // c[i] = sum_t e_t A_V^T[i][t]
-#pragma unroll
-    for (int u = 0; u < FAST_R; ++u)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int e = 0; e < EPL; ++e) {
         float x = 0.f;
 #pragma unroll
-        for (int e = 0; e < TPL; ++e) x += ew[h][e] * fv[u].get(e);
-        x = wave_sum(x);
-        if (lane == 0) z.C[h][u] = x;
-      }
-    wave_lds_sync();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = u * RPW + slot;
-      if (i < r) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float cv = z.C[h][i];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[h][e] += cv * fw[u].get(e);
-        }
+        for (int u = 0; u < RB; ++u) x += p[u] * ak[u].get(e);
+        lg[h][e] = x;
       }
     }
-    wave_lds_sync();  // P and C are rewritten by the next span
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = slots_sum<LPR>(lg[h][e]);
+        x = (tok + e < c) ? x : kNegInf;
+        lg[h][e] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = group_max<LPR>(mx);  // finite: token t0 is valid
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        lg[h][e] = fast_exp2(lg[h][e] - mx);
+        s += lg[h][e];
+      }
+      sm[h] = mx;
+      sl[h] = group_sum<LPR>(s);
+      float w[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x += lg[h][e] * av[u].get(e);
+        x = group_sum<LPR>(x);
+        w[u] = (rg + RPW * u < r) ? x : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int u = 0; u < RB; ++u) x += w[u] * bv[u].get(e);
+        o[h][e] = slots_sum<LPR>(x);
+      }
+    }
     return;
   }
 
-  // ---------------- general spans: rank in batches, tokens in tiles
-  for (int j0 = 0; j0 < r; j0 += 4 * RPW) {
-    Raw<T, EPL> fb[4];
+  // ---------------- larger ranks: rank batches, p and w in LDS
+  const int rpad = (r + RBATCH - 1) / RBATCH * RBATCH;
+  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
+    Raw<T> bk[RB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fb[u].load(BKt + (size_t)min(j0 + u * RPW + slot, rl) * D + sub * EPL);
+    for (int u = 0; u < RB; ++u) bk[u].load(BKt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < RB; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * fb[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * bk[u].get(e);
         dp = group_sum<LPR>(dp);
-        const int i = j0 + u * RPW + slot;
-        if (sub == 0 && i < r) z.P[h][i] = dp * c2;
+        const int j = j0 + rg + RPW * u;
+        if (tg == 0) z.P[h][j] = j < r ? dp * c2 : 0.f;
       }
   }
-  const int rpad = (r + BATCH - 1) / BATCH * BATCH;
-  for (int i = r + lane; i < rpad; i += 64)
-#pragma unroll
-    for (int h = 0; h < G; ++h) z.P[h][i] = 0.f;
   wave_lds_sync();
-  for (int t0 = 0; t0 < c; t0 += TILE) {
-    const int tb = t0 + lane * TPL;
-    const bool act = tb < c;
-    const int tbl = act ? tb : t0;
-    float lg[G][TPL];
+  float lg[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) lg[h][e] = 0.f;
+  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
+    Raw<T> ak[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) ak[u].load(AKt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < TPL; ++e) lg[h][e] = 0.f;
-    for (int i0 = 0; i0 < r; i0 += BATCH) {
-      Raw<T, TPL> fa[BATCH];
+      for (int u = 0; u < RB; ++u) {
+        const float pv = z.P[h][j0 + rg + RPW * u];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) fa[u].load(AKt + (size_t)min(i0 + u, rl) * c8 + tbl);
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pv = z.P[h][i0 + u];
-#pragma unroll
-          for (int e = 0; e < TPL; ++e) lg[h][e] += fa[u].get(e) * pv;
-        }
-    }
-    float ew[G][TPL], sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < TPL; ++e) {
-        if (tb + e >= c) lg[h][e] = kNegInf;
-        mx = fmaxf(mx, lg[h][e]);
+        for (int e = 0; e < EPL; ++e) lg[h][e] += pv * ak[u].get(e);
       }
-      mx = wave_max(mx);
-      const float mn = fmaxf(sm[h], mx);  // finite: the tile holds a token
-      sc[h] = fast_exp2(sm[h] - mn);
-      float ssum = 0.f;
+  }
 #pragma unroll
-      for (int e = 0; e < TPL; ++e) {
-        ew[h][e] = fast_exp2(lg[h][e] - mn);
-        ssum += ew[h][e];
+  for (int h = 0; h < G; ++h) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = slots_sum<LPR>(lg[h][e]);
+      x = (tok + e < c) ? x : kNegInf;
+      lg[h][e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = group_max<LPR>(mx);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      lg[h][e] = fast_exp2(lg[h][e] - mx);
+      s += lg[h][e];
+    }
+    sm[h] = mx;
+    sl[h] = group_sum<LPR>(s);
+  }
+  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
+    Raw<T> av[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) av[u].load(AVt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x += lg[h][e] * av[u].get(e);
+        x = group_sum<LPR>(x);
+        const int j = j0 + rg + RPW * u;
+        if (tg == 0) z.W[h][j] = j < r ? x : 0.f;
       }
-      sl[h] = sl[h] * sc[h] + wave_sum(ssum);
-      sm[h] = mn;
-    }
-    for (int i0 = 0; i0 < r; i0 += BATCH) {
-      Raw<T, TPL> fv[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) fv[u].load(AVt + (size_t)min(i0 + u, rl) * c8 + tbl);
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float x = 0.f;
-#pragma unroll
-          for (int e = 0; e < TPL; ++e) x += ew[h][e] * fv[u].get(e);
-          x = wave_sum(x);
-          const int i = i0 + u;
-          if (lane == 0 && i < r) z.C[h][i] = (t0 == 0 ? 0.f : z.C[h][i] * sc[h]) + x;
-        }
-    }
   }
   wave_lds_sync();
-  for (int j0 = 0; j0 < r; j0 += 4 * RPW) {
-    Raw<T, EPL> fw[4];
+  float acc[G][EPL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fw[u].load(BVt + (size_t)min(j0 + u * RPW + slot, rl) * D + sub * EPL);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = j0 + u * RPW + slot;
-      if (i < r) {
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
+    Raw<T> bv[RB];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float cv = z.C[h][i];
+    for (int u = 0; u < RB; ++u) bv[u].load(BVt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[h][e] += cv * fw[u].get(e);
-        }
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const float wv = z.W[h][j0 + rg + RPW * u];  // zero beyond r
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] += wv * bv[u].get(e);
       }
-    }
   }
-  wave_lds_sync();  // P and C are rewritten by the next span
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = slots_sum<LPR>(acc[h][e]);
+  wave_lds_sync();  // P and W are rewritten by the next unit
 }
 
-// ------------------------------------------------------------------ workgroup merge
+// ------------------------------------------------------------------ workgroup state and merges
 
 template <int D, int G>
 struct MergeLds {
   float m[kWaves][G];
   float l[kWaves][G];
   float acc[kWaves][G][D];
+};
+
+template <int D, int G>
+struct Smem {
+  MergeLds<D, G> ml;
+  ZoomLds<G> zw[kWaves];
+  uint8_t zb[kMaxSpanChunk];     // zoom head bits of each row of a span chunk
+  int2 zmeta[kMaxSpanChunk];     // their basis metadata (rows with zoom bits only)
+  int3 zit[kMaxSpanChunk];       // a span task's zoomed spans
+  int ustart[kMaxSpanChunk + 1]; // their first work unit (token tile)
+  int wcount[kWaves];
+  int s_int[4];
 };
 
 // Butterfly over the row slots of each wave, then one record per wave in LDS.
@@ -377,7 +363,7 @@ __device__ void slots_to_lds(SoftState<G>& st, float (&acc)[G][EPL], MergeLds<D,
   }
 }
 
-// Merge the per-wave records into one partial per head and store it.
+// Merge the per-wave records into one partial per head and store it in `part`.
 template <int D, int G>
 __device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int b, int g, int part) {
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
@@ -393,10 +379,20 @@ __device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int
       L += ml.l[r][h] * w;
       A += ml.acc[r][h][j] * w;
     }
-    const int hq = g * G + h;
-    const size_t slot = ((size_t)b * a.Hq + hq) * a.max_parts + part;
+    const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
     a.part_acc[slot * D + j] = A;
     if (j == 0) reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(M, L);
+  }
+}
+
+// An empty partial (no entries) for every head of the group.
+template <int D, int G>
+__device__ void store_empty(const DecodeArgs& a, int b, int g, int part) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, j = idx % D;
+    const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
+    a.part_acc[slot * D + j] = 0.f;
+    if (j == 0) reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(kNegInf, 0.f);
   }
 }
 
@@ -410,45 +406,52 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int su
       Elem<float>::load16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * EPL + e, qr[h] + e);
 }
 
-// ------------------------------------------------------------------ k_route
+// ------------------------------------------------------------------ zoomed spans of one span task
 
-// One pipeline stage of a row slot: U rows of keys (or summaries) and values.
-template <typename T, int U>
-struct Stage {
-  Raw<T, Elem<T>::kPer16> k[U], v[U];
-  float ls[U];
-  int2 meta[U];  // span rows: packed {basis offset / 8, rank | count << 8}
-};
+static_assert(kMaxSpanChunk <= kThreads, "one thread per zoomed span of a task");
 
-// SCORES: routing scores only.  Otherwise zoomed spans are appended to the
-// global list for the zoom kernel.  Workgroup i runs task task_base + i.
-template <int D, typename T, int G, bool SCORES>
-__global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base) {
-  constexpr int EPL = Elem<T>::kPer16;  // elements per 16-byte load
-  constexpr int LPR = D / EPL;          // lanes per row
-  constexpr int RPW = 64 / LPR;         // rows per wave per load
-  constexpr int U = 4;                  // rows per lane slot per stage
-  constexpr int STEP = kWaves * RPW * U;
-
-  __shared__ MergeLds<D, G> ml_s;
-  __shared__ int4 list_s[1024];  // (bg | head bits << 24, span, packed basis offset, rank | count << 8)
-  __shared__ int list_n, s_base;
-
+// The zc zoomed spans of one span task, cut into units of one token tile, the
+// units spread over the waves (wave w takes units w, w + 4, ...), merged into
+// one partial per query head stored in `part` (heads that zoom none of the
+// spans get an empty one).  item(j) -> (head bits, basis offset / 8,
+// rank | count << 8) is called by thread j < zc only, with j = its index.
+template <int D, typename T, int G, class Item>
+__device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item item, const T* __restrict__ src,
+                           Smem<D, G>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, TILE = Gm::TILE;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane / LPR, sub = lane % LPR;
-  // rows of the grid in the host's order (most zoom-prone kv heads first);
-  // span chunks come before anchor chunks in each row
-  // one task per workgroup, in the runtime's order (the busiest first)
-  const int4 task = a.tasks[task_base + blockIdx.x];
-  const int bg = task.x & 0x7fffffff;
-  const bool is_anchor_chunk = task.x < 0;
-  const int t_start = task.y, t_count = task.z, part = task.w;
+  const int rg = lane / LPR, tg = lane % LPR;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
-  if (SCORES && is_anchor_chunk) return;
-  if (threadIdx.x == 0) list_n = 0;
-  const float c2 = kLog2e * rsqrtf((float)D);  // logit scale in log2 units
-  const float inv_sqrt_d = rsqrtf((float)D);
-
+  const float c2 = kLog2e * rsqrtf((float)D);
+  // unit table: tiles of span j start at ustart[j] (exclusive scan over the threads)
+  {
+    const int i = threadIdx.x;
+    int nt = 0;
+    if (i < zc) {
+      const int3 it = item(i);
+      sh.zit[i] = it;
+      nt = ((int)((uint32_t)it.z >> 8) + TILE - 1) / TILE;
+    }
+    int incl = nt;
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) {
+      const int y = __shfl_up(incl, sft, 64);
+      if (lane >= sft) incl += y;
+    }
+    if (lane == 63) sh.wcount[wave] = incl;
+    __syncthreads();
+    int before = incl - nt, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) before += sh.wcount[w];
+      total += sh.wcount[w];
+    }
+    if (i < zc) sh.ustart[i] = before;
+    if (i == 0) sh.ustart[zc] = total;  // zc <= kMaxSpanChunk
+    __syncthreads();
+  }
+  const int units = sh.ustart[zc];
   SoftState<G> st;
   float acc[G][EPL];
 #pragma unroll
@@ -458,13 +461,108 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  // fold U rows with logits lg[h][u] (log2 units, -inf = skip) and values vf into the state
-  auto fold = [&](const float (&lg)[G][U], const Raw<T, EPL>(&vf)[U]) {
+  if (wave < units) {
+    float qr[G][EPL];
+    load_q<D, G, T>(a, b, g, tg, qr);
+    int j = 0;
+    for (int u = wave; u < units; u += kWaves) {
+      while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
+      const int3 it = sh.zit[j];
+      const uint32_t hb = (uint32_t)it.x;
+      const int r = it.z & 0xff, cnt = (int)((uint32_t)it.z >> 8);
+      float sm[G], sl[G], o[G][EPL];
+      zoom_unit<D, T, G>(src + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, qr, sh.zw[wave], c2,
+                         rg, tg, sm, sl, o);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (hb & (1u << h)) lse_merge<EPL>(st.m[h], st.l[h], acc[h], sm[h], sl[h], o[h]);
+    }
+  }
+  // every row slot holds the same state: slot 0 writes the wave's record
+  if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      sh.ml.m[wave][h] = st.m[h];
+      sh.ml.l[wave][h] = st.l[h];
+    }
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sh.ml.acc[wave][h][tg * EPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  store_partial<D, G>(sh.ml, a, b, g, part);
+}
+
+// ------------------------------------------------------------------ anchor task
+
+// Rows per row slot per pipeline stage of the streaming tasks; two stages are
+// in flight.  Span tasks (one round each, with d = 128 bf16: 32 rows of
+// summaries and values per stage) run in a lean kernel; anchor tasks share
+// the attend kernel's register budget with the zoom and use deeper stages.
+constexpr int kSpanStageRows = 2;
+constexpr int kAnchorStageRows = 4;
+
+// One pipeline stage of a row slot: U rows of keys (or summaries) and values.
+template <typename T, int U>
+struct Stage {
+  Raw<T> k[U], v[U];
+  float ls[U];
+  int2 meta[U];  // span rows: {basis offset / 8, rank | count << 8}
+};
+
+template <int D, typename T, int G>
+__device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr int U = kAnchorStageRows;
+  constexpr int STEP = kWaves * RPW * U;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const int bg = task.x & 0x7fffffff;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const float c2 = kLog2e * rsqrtf((float)D);
+  SoftState<G> st;
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = kNegInf;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  const int na = a.na_b[b];
+  const int r0 = task.y;
+  const int r1 = min(na, r0 + task.z);
+  const T* Kb = reinterpret_cast<const T*>(a.KA) + (size_t)bg * a.na_max * D + sub * EPL;
+  const T* Vb = reinterpret_cast<const T*>(a.VA) + (size_t)bg * a.na_max * D + sub * EPL;
+  auto load = [&](Stage<T, U>& sg, int bs) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = bs + u * RPW + slot;
+      const int rr = row < r1 ? row : r0;
+      sg.k[u].load(Kb + (size_t)rr * D);
+      sg.v[u].load(Vb + (size_t)rr * D);
+    }
+  };
+  float qr[G][EPL];
+  auto consume = [&](const Stage<T, U>& sg, int bs) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float lg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * sg.k[u].get(e);
+        dp = group_sum<LPR>(dp);
+        lg[u] = (bs + u * RPW + slot < r1) ? dp * c2 : kNegInf;
+      }
       float mx = st.m[h];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, lg[h][u]);
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, lg[u]);
       const float ms = (mx == kNegInf) ? 0.f : mx;
       const float sc = fast_exp2(st.m[h] - ms);
       float ls = st.l[h] * sc;
@@ -472,70 +570,63 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
       for (int e = 0; e < EPL; ++e) acc[h][e] *= sc;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = fast_exp2(lg[h][u] - ms);
+        const float p = fast_exp2(lg[u] - ms);
         ls += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[u].get(e);
+        for (int e = 0; e < EPL; ++e) acc[h][e] += p * sg.v[u].get(e);
       }
       st.l[h] = ls;
       st.m[h] = mx;
     }
   };
-
-  if (is_anchor_chunk) {
-    // ---------------- anchor segment: exact tokens, two stages in flight
-    const int na = a.na_b[b];
-    const int r0 = t_start;
-    const int r1 = min(na, r0 + t_count);
-    const T* Kb = reinterpret_cast<const T*>(a.KA) + (size_t)bg * a.na_max * D + sub * EPL;
-    const T* Vb = reinterpret_cast<const T*>(a.VA) + (size_t)bg * a.na_max * D + sub * EPL;
-    auto load = [&](Stage<T, U>& sg, int bs) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = bs + u * RPW + slot;
-        const int rr = row < r1 ? row : r0;
-        sg.k[u].load(Kb + (size_t)rr * D);
-        sg.v[u].load(Vb + (size_t)rr * D);
-      }
-    };
-    float qr[G][EPL];
-    auto consume = [&](const Stage<T, U>& sg, int bs) {
-      float lg[G][U];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float dp = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) dp += qr[h][e] * sg.k[u].get(e);
-          dp = group_sum<LPR>(dp);
-          lg[h][u] = (bs + u * RPW + slot < r1) ? dp * c2 : kNegInf;
-        }
-      fold(lg, sg.v);
-    };
-    int bs = r0 + wave * RPW * U;
-    if (bs < r1) {
-      Stage<T, U> A, B;
-      load(A, bs);
-      load_q<D, G, T>(a, b, g, sub, qr);
-      for (; bs < r1; bs += 2 * STEP) {
-        load(B, bs + STEP);
-        consume(A, bs);
-        if (bs + STEP >= r1) break;
-        load(A, bs + 2 * STEP);
-        consume(B, bs + STEP);
-      }
+  int bs = r0 + wave * RPW * U;
+  if (bs < r1) {
+    Stage<T, U> A, B;
+    load(A, bs);
+    load_q<D, G, T>(a, b, g, sub, qr);
+    for (; bs < r1; bs += 2 * STEP) {
+      load(B, bs + STEP);
+      consume(A, bs);
+      if (bs + STEP >= r1) break;
+      load(A, bs + 2 * STEP);
+      consume(B, bs + STEP);
     }
-    slots_to_lds<D, G, EPL, LPR>(st, acc, ml_s, lane, wave, slot, sub);
-    __syncthreads();
-    store_partial<D, G>(ml_s, a, b, g, part);
-    return;
   }
+  slots_to_lds<D, G, EPL, LPR>(st, acc, ml, lane, wave, slot, sub);
+  __syncthreads();
+  store_partial<D, G>(ml, a, b, g, task.w);
+}
 
-  // ---------------- span chunk: routing, zoom decisions, summaries of non-zoomed spans
+// ------------------------------------------------------------------ span task
+
+// MODE 0: zoomed spans listed in the chunk's rows of the dense table.
+// MODE 1: zoomed spans appended to the flat list for the host fetch.
+// MODE 2: routing scores only.
+template <int D, typename T, int G, int MODE>
+__device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr int U = kSpanStageRows;
+  constexpr int STEP = kWaves * RPW * U;
+  constexpr bool SCORES = MODE == 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const int bg = task.x;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const float c2 = kLog2e * rsqrtf((float)D);
+  const float inv_sqrt_d = rsqrtf((float)D);
+  SoftState<G> st;
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = kNegInf;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
   const int m = a.m_b[b];
-  const int k0 = t_start;
-  const int k1 = min(m, k0 + t_count);
+  const int k0 = task.y;
+  const int k1 = min(m, k0 + task.z);
   const T* Kb = reinterpret_cast<const T*>(a.kbar) + (size_t)bg * a.m_max * D + sub * EPL;
   const T* Vb = reinterpret_cast<const T*>(a.vbar) + (size_t)bg * a.m_max * D + sub * EPL;
   const float* lS = a.logS + (size_t)b * a.m_max;
@@ -547,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
       sg.k[u].load(Kb + (size_t)kk * D);
       if (!SCORES) sg.v[u].load(Vb + (size_t)kk * D);
       sg.ls[u] = lS[kk];
-      if (!SCORES) sg.meta[u] = a.smeta[(size_t)bg * a.m_max + kk];
+      if (!SCORES) sg.meta[u] = sub == 0 ? a.smeta[(size_t)bg * a.m_max + kk] : make_int2(0, 0);
     }
   };
   float qr[G][EPL];
@@ -560,12 +651,12 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
       for (int e = 0; e < EPL; ++e) s2 += sg.k[u].get(e) * sg.k[u].get(e);
       nrm[u] = group_sum<LPR>(s2);
     }
-    float lg[G][U];
     uint32_t zbits[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) zbits[u] = 0u;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      float lg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float dp = 0.f;
@@ -582,22 +673,39 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
           else a.mask[mi] = zoom ? 1 : 0;
         }
         if (zoom) zbits[u] |= 1u << h;
-        lg[h][u] = (ok && !zoom) ? dp * c2 + sg.ls[u] * kLog2e : kNegInf;
+        lg[u] = (ok && !zoom) ? dp * c2 + sg.ls[u] * kLog2e : kNegInf;
       }
-    if (SCORES) return;
-    fold(lg, sg.v);
-    if (sub == 0) {
+      if (!SCORES) {
+        float mx = st.m[h];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, lg[u]);
+        const float ms = (mx == kNegInf) ? 0.f : mx;
+        const float sc = fast_exp2(st.m[h] - ms);
+        float ls = st.l[h] * sc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = fast_exp2(lg[u] - ms);
+          ls += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] += p * sg.v[u].get(e);
+        }
+        st.l[h] = ls;
+        st.m[h] = mx;
+      }
+    }
+    if (!SCORES && sub == 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = bs + u * RPW + slot;
-        if (k < k1 && zbits[u]) {
-          const int pos = atomicAdd(&list_n, 1);
-          list_s[pos] = make_int4(bg | (int)(zbits[u] << 24), k, sg.meta[u].x, sg.meta[u].y);
+        if (k < k1) {
+          sh.zb[k - k0] = (uint8_t)zbits[u];
+          if (zbits[u]) sh.zmeta[k - k0] = sg.meta[u];
         }
       }
     }
   };
-  __syncthreads();  // list_n
   int bs = k0 + wave * RPW * U;
   if (bs < k1) {
     Stage<T, U> A, B;
@@ -612,173 +720,310 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a, int task_base)
     }
   }
   if (SCORES) return;
-  slots_to_lds<D, G, EPL, LPR>(st, acc, ml_s, lane, wave, slot, sub);
-  __syncthreads();  // list_s and the records complete
-  if (threadIdx.x == 0) {
-    s_base = list_n ? atomicAdd(a.zcounter, list_n) : 0;
-    if (list_n) atomicAdd(&a.zstat[bg], list_n);
-  }
-  store_partial<D, G>(ml_s, a, b, g, part);
+  slots_to_lds<D, G, EPL, LPR>(st, acc, sh.ml, lane, wave, slot, sub);
+  __syncthreads();  // zoom bits and records complete
+
+  // the chunk's zoomed spans, compacted in span order
+  const int cnt = max(0, k1 - k0);
+  const int i = threadIdx.x;
+  const uint32_t hb = i < cnt ? sh.zb[i] : 0u;
+  const u64 bal = __ballot(hb != 0);
+  int pos = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) sh.wcount[wave] = __popcll(bal);
+  store_partial<D, G>(sh.ml, a, b, g, task.w);
   __syncthreads();
-  for (int i = threadIdx.x; i < list_n; i += kThreads) a.zlist[s_base + i] = list_s[i];
+  int zc = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) pos += sh.wcount[w];
+    zc += sh.wcount[w];
+  }
+  if (MODE == 0) {
+    // one unit entry per token tile of each zoomed span, in span order, in the
+    // task's own range of the unit table
+    constexpr int TILE = Gm::TILE;
+    int2 meta = make_int2(0, 0);
+    int nt = 0;
+    if (hb) {
+      meta = sh.zmeta[i];
+      nt = ((int)((uint32_t)meta.y >> 8) + TILE - 1) / TILE;
+    }
+    int incl = nt;
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) {
+      const int y = __shfl_up(incl, sft, 64);
+      if (lane >= sft) incl += y;
+    }
+    __syncthreads();  // wcount reads above are done
+    if (lane == 63) sh.wcount[wave] = incl;
+    __syncthreads();
+    int before = incl - nt, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) before += sh.wcount[w];
+      total += sh.wcount[w];
+    }
+    int4* ue = a.uent + a.uoff[t] + before;
+    for (int tt = 0; tt < nt; ++tt) ue[tt] = make_int4((int)hb, meta.x, meta.y, tt * TILE);
+    if (threadIdx.x == 0) {
+      a.zunits[t] = total;
+      if (total) atomicAdd(&a.zstat[bg], total);
+    }
+    return;
+  }
+  if (zc == 0) store_empty<D, G>(a, b, g, task.w + 1);  // the zoom slot, when nothing fills it
+  if (threadIdx.x == 0 && zc) atomicAdd(&a.zstat[bg], zc);
+  // MODE 1: list for the host fetch
+  if (zc) {
+    if (threadIdx.x == 0) sh.s_int[0] = atomicAdd(a.zcounter, zc);
+    __syncthreads();
+    if (hb) {
+      const int2 meta = sh.zmeta[i];
+      a.zlist[sh.s_int[0] + pos] = make_int4(bg | (int)(hb << 24), k0 + i, meta.x, meta.y);
+    }
+  }
 }
 
-// ------------------------------------------------------------------ k_zoom
+// ------------------------------------------------------------------ kernels
 
-// One wave per listed span, over the whole grid.  STAGED: bases in the staging
-// buffer at zoff[i] (HOST home); otherwise in the device store at boff.
-template <int D, typename T, int G, bool STAGED>
-__global__ __launch_bounds__(kThreads) void k_zoom(DecodeArgs a) {
-  constexpr int EPL = Elem<T>::kPer16;
-  constexpr int LPR = D / EPL;
-  __shared__ ZoomLds<G> zl_s[kWaves];
+template <int D, typename T, int G, int MODE>
+__global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
+  __shared__ Smem<D, G> sh;
+  span_task<D, T, G, MODE>(a, (int)blockIdx.x, a.tasks[blockIdx.x], sh);
+}
+
+// Staged bases: zoom workgroup i takes group i (span task, first item, items)
+// of the fetch, into the task's second slot.
+template <int D, typename T, int G>
+__device__ void staged_group(const DecodeArgs& a, int i, Smem<D, G>& sh) {
+  const int4 grp = a.zgroups[i];
+  const int4 task = a.tasks[grp.x];
+  const int4* items = a.zitems + grp.y;
+  auto item = [&](int j) -> int3 {
+    const int4 it = items[j];
+    return make_int3((int)((uint32_t)it.x >> 24), it.z, it.w);
+  };
+  zoom_group<D, T, G>(a, task.x, task.w + 1, grp.z, item, reinterpret_cast<const T*>(a.staging), sh);
+}
+
+
+template <int D, int G>
+struct AttendLds {
+  union {
+    MergeLds<D, G> ml;  // anchor tasks
+    struct {
+      ZoomLds<G> zw[kWaves];
+      int pre[kMaxSpanTasks + 1];  // units before each span task
+      int wsum[kWaves];
+    };
+  };
+};
+
+// Device store: the zoom units of the whole layer-step, balanced over the
+// n_wgs zoom workgroups.  Each reads the units of every span task (a few KB,
+// from L2) and forms their prefix; wave W takes the contiguous units
+// [W * per, (W + 1) * per) and writes one partial per unit and query head
+// (empty for heads that do not zoom the span).  Zoom workgroup 0 stores the
+// prefix for the combine kernel.
+template <int D, typename T, int G>
+__device__ void unit_pass(const DecodeArgs& a, int wg, int n_wgs, AttendLds<D, G>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane / LPR, sub = lane % LPR;
+  const int rg = lane / LPR, tg = lane % LPR;
+  const int n = a.n_span_tasks;  // <= kMaxSpanTasks
+  constexpr int PER_T = (kMaxSpanTasks + kThreads) / kThreads;  // covers indices 0..n
+  {
+    // each thread sums a contiguous run of tasks; scan of the runs
+    const int t0 = threadIdx.x * PER_T;
+    int v[PER_T];
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < PER_T; ++j) {
+      v[j] = (t0 + j < n) ? a.zunits[t0 + j] : 0;
+      run += v[j];
+    }
+    int incl = run;
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) {
+      const int y = __shfl_up(incl, sft, 64);
+      if (lane >= sft) incl += y;
+    }
+    if (lane == 63) sh.wsum[wave] = incl;
+    __syncthreads();
+    int before = incl - run;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (w < wave) before += sh.wsum[w];
+#pragma unroll
+    for (int j = 0; j < PER_T; ++j) {
+      if (t0 + j <= n) sh.pre[t0 + j] = before;
+      before += v[j];
+    }
+    __syncthreads();
+    if (wg == 0)
+      for (int t = threadIdx.x; t <= n; t += kThreads) a.upre[t] = sh.pre[t];
+  }
+  const int units = sh.pre[n];
+  const int nw = n_wgs * kWaves;
+  const int per = (units + nw - 1) / nw;
+  const int u0 = (wg * kWaves + wave) * per;
+  const int u1 = min(units, u0 + per);
+  if (u0 >= u1) return;
+  // task of the first unit: last t with pre[t] <= u0
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sh.pre[mid] <= u0) lo = mid;
+    else hi = mid - 1;
+  }
+  int t = lo;
   const float c2 = kLog2e * rsqrtf((float)D);
-  const int total = *a.zn;
-  const int stride = gridDim.x * kWaves;
-  int i = blockIdx.x * kWaves + wave;
-  if (i >= total) return;
-  const T* src = reinterpret_cast<const T*>(STAGED ? a.staging : a.bases);
-  int4 ent = a.zitems[i];
-  while (true) {
-    const int inext = i + stride;
-    const int4 ent_next = a.zitems[inext < total ? inext : i];  // prefetch
-    const int bg = ent.x & 0xffffff;
-    const uint32_t hb = (uint32_t)ent.x >> 24;
-    const int k = ent.y;
+  const T* src = reinterpret_cast<const T*>(a.bases);
+  // the entries (and tasks) of the first units in one round
+  constexpr int PF = 4;
+  int4 pe[PF];
+  int pbg[PF];
+  {
+    int tt = t;
+#pragma unroll
+    for (int x = 0; x < PF; ++x) {
+      const int u = min(u0 + x, u1 - 1);
+      while (sh.pre[tt + 1] <= u) ++tt;
+      pe[x] = a.uent[a.uoff[tt] + (u - sh.pre[tt])];
+      pbg[x] = a.tasks[tt].x;
+    }
+  }
+  for (int u = u0; u < u1; ++u) {
+    while (sh.pre[t + 1] <= u) ++t;
+    int4 e;
+    int bg;
+    if (u - u0 < PF) {
+      e = pe[0];
+      bg = pbg[0];
+#pragma unroll
+      for (int x = 1; x < PF; ++x)
+        if (u - u0 == x) {
+          e = pe[x];
+          bg = pbg[x];
+        }
+    } else {
+      e = a.uent[a.uoff[t] + (u - sh.pre[t])];
+      bg = a.tasks[t].x;
+    }
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const size_t ti = (size_t)bg * a.m_max + k;
-    const int64_t off = STAGED ? a.zoff[i] : (int64_t)(uint32_t)ent.z << 3;
-    const int r = ent.w & 0xff;
-    const int cnt = (int)((uint32_t)ent.w >> 8);
     float qr[G][EPL];
-    load_q<D, G, T>(a, b, g, sub, qr);
+    load_q<D, G, T>(a, b, g, tg, qr);
+    const uint32_t hb = (uint32_t)e.x;
+    const int r = e.z & 0xff, cnt = (int)((uint32_t)e.z >> 8);
     float sm[G], sl[G], o[G][EPL];
-    zoom_span<D, T, G>(src + off, cnt, r, qr, zl_s[wave], c2, lane, slot, sub, sm, sl, o);
-    // add up the slots' output parts (they share the span's max)
+    zoom_unit<D, T, G>(src + ((int64_t)(uint32_t)e.y << 3), cnt, r, e.w, qr, sh.zw[wave], c2, rg, tg, sm, sl, o);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      for (int sh = LPR; sh < 64; sh <<= 1) {
+      const bool z = (hb >> h) & 1u;
+      const size_t slot = (size_t)u * G + h;
+      if (rg == 0) {
+        float ov[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], sh, 64);
-      }
-      if (hb & (1u << h)) {
-        const size_t zi = ti * G + h;
-        if (slot == 0) {
+        for (int x = 0; x < EPL; ++x) ov[x] = z ? o[h][x] : 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; e += 4) Elem<float>::store16(a.zpart_acc + zi * D + sub * EPL + e, o[h] + e);
-        }
-        if (lane == 0) reinterpret_cast<float2*>(a.zpart_ml)[zi] = make_float2(sm[h], sl[h]);
+        for (int x = 0; x < EPL; x += 4) Elem<float>::store16(a.upart_acc + slot * D + tg * EPL + x, ov + x);
       }
+      if (lane == 0) reinterpret_cast<float2*>(a.upart_ml)[slot] = z ? make_float2(sm[h], sl[h]) : make_float2(kNegInf, 0.f);
     }
-    if (inext >= total) break;
-    i = inext;
-    ent = ent_next;
   }
 }
 
-// ------------------------------------------------------------------ k_combine
+// Workgroups [0, n_zoom_wgs): zoom (STAGED: one per fetched group; else the
+// unit pass); then one workgroup per anchor task.
+template <int D, typename T, int G, bool STAGED>
+__global__ __launch_bounds__(kThreads) void k_attend(DecodeArgs a) {
+  __shared__ typename std::conditional<STAGED, Smem<D, G>, AttendLds<D, G>>::type sh;
+  const int i = (int)blockIdx.x - a.n_zoom_wgs;
+  if (i >= 0) {
+    anchor_task<D, T, G>(a, a.tasks[a.n_span_tasks + i], sh.ml);
+    return;
+  }
+  if constexpr (STAGED) staged_group<D, T, G>(a, blockIdx.x, sh);
+  else unit_pass<D, T, G>(a, blockIdx.x, a.n_zoom_wgs, sh);
+}
 
-// One workgroup per (sequence, query head): merges its partials and the
-// partials of the zoomed spans its mask row marks, in span order, so the result
-// does not depend on the order of the zoom list.  Each thread (group pg, float4
-// column c4) keeps an online log-sum-exp over its share of the entries; the
-// groups are merged at the end.
+// One workgroup per (sequence, query head): log-sum-exp merge of its slots in
+// slot order.  Thread (group pg, float4 column c4) merges slots pg, pg + PG, ...
+// with 8 in flight; the groups are merged at the end.  Also empties the flat
+// zoom list for the next launch.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   constexpr int NT = kCombineThreads;
-  constexpr int NW = NT / 64;
-  constexpr int C4 = D / 4;     // float4 columns of a partial accumulator
-  constexpr int PG = NT / C4;   // entry groups
-  constexpr int SPT = 4;        // mask bytes scanned per thread per round
-  constexpr int ROUND = SPT * NT;
-  __shared__ int zid_s[ROUND];
-  __shared__ int cnt_s[NW];
+  constexpr int C4 = D / 4;
+  constexpr int PG = NT / C4;
+  constexpr int UN = 8;
   __shared__ float gm_s[PG], gl_s[PG];
   __shared__ float4 ga_s[PG][C4];
-  const int bh = blockIdx.x;  // b * Hq + hq
+  const int bh = blockIdx.x;
   const int b = bh / a.Hq, hq = bh % a.Hq;
-  const int g = hq / a.G, h = hq % a.G;
-  const size_t bg = (size_t)b * a.Hkv + g;
-  const int np = a.parts_n[bg], m = a.m_b[b];
-  const uint8_t* mrow = a.mask + (size_t)bh * a.m_max;
-  const float2* zml = reinterpret_cast<const float2*>(a.zpart_ml);
+  const int g = hq / a.G;
+  const int np = a.parts_n[(size_t)b * a.Hkv + g];
   const int pg = threadIdx.x / C4, c4 = threadIdx.x % C4;
-
   float M = kNegInf, L = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto merge = [&](float mo, float lo, float4 v) {
-    const float mn = fmaxf(M, mo);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    const float x = fast_exp2(M - ms), y = fast_exp2(mo - ms);
-    L = L * x + lo * y;
-    A.x = A.x * x + v.x * y;
-    A.y = A.y * x + v.y * y;
-    A.z = A.z * x + v.z * y;
-    A.w = A.w * x + v.w * y;
-    M = mn;
-  };
-  // stream partials, 8 entries in flight per thread
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)bh * a.max_parts;
   const float4* pa = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * a.max_parts * D) + c4;
-  for (int p0 = pg; p0 < np; p0 += 8 * PG) {
-    float2 ml[8];
-    float4 v[8];
+  for (int p0 = pg; p0 < np; p0 += UN * PG) {
+    float2 ml[UN];
+    float4 v[UN];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < UN; ++u) {
       const int p = min(p0 + u * PG, np - 1);
       ml[u] = pml[p];
       v[u] = pa[(size_t)p * C4];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (p0 + u * PG < np) merge(ml[u].x, ml[u].y, v[u]);
+    for (int u = 0; u < UN; ++u) {
+      if (p0 + u * PG < np) {
+        const float mn = fmaxf(M, ml[u].x);
+        const float ms = (mn == kNegInf) ? 0.f : mn;
+        const float x = fast_exp2(M - ms), y = fast_exp2(ml[u].x - ms);
+        L = L * x + ml[u].y * y;
+        A.x = A.x * x + v[u].x * y;
+        A.y = A.y * x + v[u].y * y;
+        A.z = A.z * x + v[u].z * y;
+        A.w = A.w * x + v[u].w * y;
+        M = mn;
+      }
+    }
   }
-  // zoomed spans, in span order (HOST home: their partials come from the zoom kernel)
-  for (int k0 = 0; a.zpart_ml && k0 < m; k0 += ROUND) {
-    uint8_t mb[SPT];
-    int n = 0;
-    const int kb = k0 + threadIdx.x * SPT;
+  if (a.upart_ml) {
+    // zoom units of the (sequence, kv head)'s span tasks: one contiguous range
+    const int2 bt = a.bg_tasks[(size_t)b * a.Hkv + g];
+    const int v0 = a.upre[bt.x], v1 = a.upre[bt.x + bt.y];
+    const int h = hq % a.G;
+    const float2* uml = reinterpret_cast<const float2*>(a.upart_ml);
+    for (int p0 = v0 + pg; p0 < v1; p0 += UN * PG) {
+      float2 ml[UN];
+      float4 v[UN];
 #pragma unroll
-    for (int e = 0; e < SPT; ++e) {
-      mb[e] = (kb + e < m) ? mrow[kb + e] : 0;
-      n += mb[e] ? 1 : 0;
-    }
-    // exclusive prefix of n over the workgroup: shuffle scan in each wave, then wave offsets
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = n;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const int y = __shfl_up(incl, sh, 64);
-      if (lane >= sh) incl += y;
-    }
-    if (lane == 63) cnt_s[wave] = incl;
-    __syncthreads();
-    int pos = incl - n;
-    for (int w = 0; w < wave; ++w) pos += cnt_s[w];
-    int nz = 0;
-    for (int w = 0; w < NW; ++w) nz += cnt_s[w];
-#pragma unroll
-    for (int e = 0; e < SPT; ++e)
-      if (mb[e]) zid_s[pos++] = kb + e;
-    __syncthreads();
-    for (int j0 = pg; j0 < nz; j0 += 8 * PG) {
-      float2 ml[8];
-      float4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const size_t zi = (bg * a.m_max + zid_s[min(j0 + u * PG, nz - 1)]) * a.G + h;
-        ml[u] = zml[zi];
-        v[u] = reinterpret_cast<const float4*>(a.zpart_acc + zi * D)[c4];
+      for (int u = 0; u < UN; ++u) {
+        const size_t sl = (size_t)min(p0 + u * PG, v1 - 1) * a.G + h;
+        ml[u] = uml[sl];
+        v[u] = reinterpret_cast<const float4*>(a.upart_acc + sl * D)[c4];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u * PG < nz) merge(ml[u].x, ml[u].y, v[u]);
+      for (int u = 0; u < UN; ++u) {
+        if (p0 + u * PG < v1) {
+          const float mn = fmaxf(M, ml[u].x);
+          const float ms = (mn == kNegInf) ? 0.f : mn;
+          const float x = fast_exp2(M - ms), y = fast_exp2(ml[u].x - ms);
+          L = L * x + ml[u].y * y;
+          A.x = A.x * x + v[u].x * y;
+          A.y = A.y * x + v[u].y * y;
+          A.z = A.z * x + v[u].z * y;
+          A.w = A.w * x + v[u].w * y;
+          M = mn;
+        }
+      }
     }
-    __syncthreads();
   }
-  // merge the groups
   if (c4 == 0) {
     gm_s[pg] = M;
     gl_s[pg] = L;
@@ -804,57 +1049,49 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
     reinterpret_cast<float4*>(a.out + (size_t)bh * D)[threadIdx.x] =
         make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
   }
-  if (bh == 0 && threadIdx.x == 0 && a.zcounter) *a.zcounter = 0;  // the zoom list is empty again
+  if (bh == 0 && threadIdx.x == 0 && a.zcounter) *a.zcounter = 0;
 }
 
 template <int D, typename T, int G>
-void launch_route_t(bool scores, int t0, int t1, const DecodeArgs& a, hipStream_t s) {
-  if (t1 <= t0) return;
-  dim3 grid(t1 - t0);
-  if (scores) hipLaunchKernelGGL((k_route<D, T, G, true>), grid, dim3(kThreads), 0, s, a, t0);
-  else hipLaunchKernelGGL((k_route<D, T, G, false>), grid, dim3(kThreads), 0, s, a, t0);
-}
-
-template <int D, typename T, int G>
-void launch_zoom_t(bool staged, const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.n_zoom_wgs);
-  if (staged) hipLaunchKernelGGL((k_zoom<D, T, G, true>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_zoom<D, T, G, false>), grid, dim3(kThreads), 0, s, a);
+void launch_t(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  if (grid <= 0) return;
+  const dim3 gd(grid), bd(kThreads);
+  if (which == 0) {
+    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0>), gd, bd, 0, s, a);
+    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_route<D, T, G, 2>), gd, bd, 0, s, a);
+  } else {
+    if (mode) hipLaunchKernelGGL((k_attend<D, T, G, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_attend<D, T, G, false>), gd, bd, 0, s, a);
+  }
 }
 
 template <int D, typename T>
-void launch_g(int which, int flag, int t0, int t1, const DecodeArgs& a, hipStream_t s) {
+void launch_g(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
   switch (a.G) {
-#define SEKV_CASE(GG)                                                    \
-  case GG:                                                               \
-    if (which == 0) launch_route_t<D, T, GG>(flag != 0, t0, t1, a, s);   \
-    else launch_zoom_t<D, T, GG>(flag != 0, a, s);                       \
-    break;
-    SEKV_CASE(1)
-    SEKV_CASE(2)
-    SEKV_CASE(4)
-    SEKV_CASE(8)
-#undef SEKV_CASE
+    case 1: launch_t<D, T, 1>(which, mode, grid, a, s); break;
+    case 2: launch_t<D, T, 2>(which, mode, grid, a, s); break;
+    case 4: launch_t<D, T, 4>(which, mode, grid, a, s); break;
+    case 8: launch_t<D, T, 8>(which, mode, grid, a, s); break;
   }
 }
 
 template <int D>
-void launch_d(int which, int kv_bf16, int flag, int t0, int t1, const DecodeArgs& a, hipStream_t s) {
-  if (kv_bf16) launch_g<D, bf16_t>(which, flag, t0, t1, a, s);
-  else launch_g<D, float>(which, flag, t0, t1, a, s);
+void launch_d(int which, int kv_bf16, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  if (kv_bf16) launch_g<D, bf16_t>(which, mode, grid, a, s);
+  else launch_g<D, float>(which, mode, grid, a, s);
 }
 
 }  // namespace
 
-void launch_decode_route(bool scores_only, int t0, int t1, int d, int kv_bf16, const DecodeArgs& a,
-                         hipStream_t s) {
-  if (d == 128) launch_d<128>(0, kv_bf16, scores_only, t0, t1, a, s);
-  else launch_d<64>(0, kv_bf16, scores_only, t0, t1, a, s);
+void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
+  if (d == 128) launch_d<128>(0, kv_bf16, mode, grid, a, s);
+  else launch_d<64>(0, kv_bf16, mode, grid, a, s);
 }
 
-void launch_decode_zoom(bool staged, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
-  if (d == 128) launch_d<128>(1, kv_bf16, staged, 0, 0, a, s);
-  else launch_d<64>(1, kv_bf16, staged, 0, 0, a, s);
+void launch_decode_attend(bool staged, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
+  if (d == 128) launch_d<128>(1, kv_bf16, staged ? 1 : 0, grid, a, s);
+  else launch_d<64>(1, kv_bf16, staged ? 1 : 0, grid, a, s);
 }
 
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s) {

@@ -35,19 +35,27 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   return std::min(hi, std::max(lo, v));
 }
 
-// Work schedule of one layer's route kernel: one task per workgroup.  Zoom-heavy
-// (sequence, kv head) rows get smaller span chunks, so that no workgroup holds
-// more than a few zoomed spans, and go first; the zoom load of each row is
-// measured by the kernels (cumulative counters) and read back without a sync.
+// Work schedule of one layer's attend kernel: one task per workgroup.
+// Zoom-heavy (sequence, kv head) rows get smaller span chunks, so that a span
+// task holds about one zoomed span per wave, and go first; the zoom load of
+// each row is measured by the kernels (cumulative counters) and read back
+// without a sync.
 struct LayerSched {
   bool valid = false;
   std::vector<int4> tasks;        // (bg | anchor << 31, first row, rows, partial slot)
   int n_span_tasks = 0;           // span tasks come first
   std::vector<int32_t> parts_n;   // [B*Hkv]
   std::vector<int32_t> chunk;     // [B*Hkv] span rows per task
+  std::vector<int32_t> first_span_task;  // [B*Hkv]
+  std::vector<int32_t> uoff;             // [span tasks] first unit entry (device store)
+  std::vector<int2> bg_tasks;            // [B*Hkv] (first span task, span tasks)
+  int64_t n_units_cap = 0;               // unit entries the span tasks can write
+  int unit_wgs = 64;                     // grid of the unit pass
   int max_parts = 0;
   int4* tasks_d = nullptr;
   int32_t* parts_d = nullptr;
+  int32_t* uoff_d = nullptr;      // [tasks_cap]
+  int2* bg_tasks_d = nullptr;     // [B*Hkv]
   size_t tasks_cap = 0;
   int4* tasks_pin = nullptr;      // pinned staging of the uploads
   int32_t* parts_pin = nullptr;
@@ -120,33 +128,34 @@ struct sekv_ctx {
   float* part_acc = nullptr;
   size_t parts_cap = 0;  // partial slots
 
-  // zoom list and per-(span, head) partials
-  int4* zlist_d = nullptr;      // [B*Hkv*m_max] written by the route kernel
-  int32_t* zcounter_d = nullptr;
-  float* zpart_ml = nullptr;    // [B*Hq*m_max][2]
-  float* zpart_acc = nullptr;   // [B*Hq*m_max][d]
   uint8_t* mask_d = nullptr;    // [B*Hq*m_max] used when the caller passes no mask
+  // device-store unit pass (sized for the largest schedule so far)
+  int4* uent_d = nullptr;
+  float* upart_ml = nullptr;
+  float* upart_acc = nullptr;
+  size_t units_cap = 0;
+  int32_t* zunits_d = nullptr;
+  int32_t* upre_d = nullptr;
+  size_t ztasks_cap = 0;
   size_t zcap = 0;              // spans capacity B*Hkv*m_max of the buffers above
 
-  // HOST-home fetch path
+  // HOST-home fetch path: flat list, staged items, groups per span task
+  int4* zlist_d = nullptr;      // [B*Hkv*m_max] written by the attend kernel
+  int32_t* zcounter_d = nullptr;
   int4* zlist_h = nullptr;      // pinned copy of the zoom list
   int32_t* zcount_h = nullptr;  // pinned
   int4* zitems_h = nullptr;     // pinned, sorted by (b, g, span)
-  int64_t* zoff_h = nullptr;
-  int32_t* zn_h = nullptr;
+  int4* zgroups_h = nullptr;    // pinned
   int4* zitems_d = nullptr;
-  int64_t* zoff_d = nullptr;
-  int32_t* zn_d = nullptr;
+  int4* zgroups_d = nullptr;
+  int n_fetched = 0;            // items of the last fetch
   void* staging = nullptr;
   int64_t staging_cap = 0;      // elements
   hipStream_t side = nullptr;
   hipEvent_t ev_fetch = nullptr;
-  // anchor segment on a second stream, concurrent with routing and zoom
-  hipStream_t side2 = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
   sekv_stats stats{};
-  int anchor_chunk = 256, span_chunk = 64, zoom_wgs = 512;
+  int anchor_chunk = 256, span_chunk = 64;
 };
 
 namespace {
@@ -238,6 +247,8 @@ void free_layer(LayerState& L) {
   dfree(L.bases_d);
   hfree(L.bases_h);
   dfree(L.sched.tasks_d);
+  dfree(L.sched.uoff_d);
+  dfree(L.sched.bg_tasks_d);
   dfree(L.sched.parts_d);
   dfree(L.sched.zstat_d);
   hfree(L.sched.tasks_pin);
@@ -393,28 +404,23 @@ sekv_status ensure_parts(sekv_ctx* c, size_t slots) {
 
 sekv_status ensure_zoom_buffers(sekv_ctx* c) {
   const size_t spans = (size_t)c->cfg.batch * c->cfg.n_kv_heads * c->m_max;
-  if (spans <= c->zcap && c->zlist_d) return SEKV_OK;
-  dfree(c->zlist_d);
-  dfree(c->zpart_ml);
-  dfree(c->zpart_acc);
+  if (spans <= c->zcap && c->mask_d) return SEKV_OK;
   dfree(c->mask_d);
+  dfree(c->zlist_d);
   dfree(c->zitems_d);
-  dfree(c->zoff_d);
+  dfree(c->zgroups_d);
   hfree(c->zlist_h);
   hfree(c->zitems_h);
-  hfree(c->zoff_h);
+  hfree(c->zgroups_h);
   c->zcap = 0;
-  const size_t heads = spans * c->G;
-  TRY(dalloc(c, &c->zlist_d, spans * sizeof(int4)));
-  TRY(dalloc(c, &c->zpart_ml, heads * 2 * sizeof(float)));
-  TRY(dalloc(c, &c->zpart_acc, heads * c->cfg.d_head * sizeof(float)));
-  TRY(dalloc(c, &c->mask_d, heads));
+  TRY(dalloc(c, &c->mask_d, spans * c->G));
   if (c->cfg.basis_home == SEKV_BASES_HOST) {
+    TRY(dalloc(c, &c->zlist_d, spans * sizeof(int4)));
     TRY(dalloc(c, &c->zitems_d, spans * sizeof(int4)));
-    TRY(dalloc(c, &c->zoff_d, spans * 8));
+    TRY(dalloc(c, &c->zgroups_d, spans * sizeof(int4)));
     TRY(halloc(c, &c->zlist_h, spans * sizeof(int4)));
     TRY(halloc(c, &c->zitems_h, spans * sizeof(int4)));
-    TRY(halloc(c, &c->zoff_h, spans * 8));
+    TRY(halloc(c, &c->zgroups_h, spans * sizeof(int4)));
   }
   c->zcap = spans;
   return SEKV_OK;
@@ -422,9 +428,12 @@ sekv_status ensure_zoom_buffers(sekv_ctx* c) {
 
 // Copy the bases of the listed spans (items: bg | head bits << 24, span id)
 // from the pinned store into staging on `side`, runs of adjacent spans
-// coalesced, and upload the sorted item list, staging offsets and count.
+// coalesced, and upload the item list sorted by (bg, span) with each item's
+// staging offset / 8 and rank | count << 8.  `groups` (optional, host) gets
+// one (span task, first item, items) per span task of the layer's schedule
+// holding listed spans; their upload follows the items.
 sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hipStream_t side,
-                        hipEvent_t done) {
+                        hipEvent_t done, int* n_groups) {
   LayerState& L = c->layers[layer];
   const int Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, mm = c->m_max;
   int4* z = c->zitems_h;
@@ -443,6 +452,7 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
     z[i].w = L.rank_h[(size_t)bg * mm + k] | (c->mcount[b][k] << 8);
     need += span_elems(c->mcount[b][k], L.rank_h[(size_t)bg * mm + k], d);
   }
+  if ((need >> 3) >= ((int64_t)1 << 31)) return fail(c, SEKV_ERR_INVALID, "zoomed bases exceed the staging limit");
   if (need > c->staging_cap) {
     dfree(c->staging);
     c->staging_cap = 0;
@@ -462,7 +472,7 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
       const int bg = z[i].x & 0xffffff, k = z[i].y;
       off = L.boff_h[(size_t)bg * mm + k];
       sz = span_elems(c->mcount[bg / Hkv][k], L.rank_h[(size_t)bg * mm + k], d);
-      c->zoff_h[i] = pos;
+      z[i].z = (int)(pos >> 3);  // every span's element count is a multiple of 16
     }
     if (i < count && run_src >= 0 && off == run_src + run_len) {
       run_len += sz;
@@ -478,13 +488,23 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
     }
     pos += sz;
   }
-  *c->zn_h = count;
-  if (count) {
-    HIPCHK(c, hipMemcpyAsync(c->zitems_d, z, (size_t)count * sizeof(int4), hipMemcpyHostToDevice, side));
-    HIPCHK(c, hipMemcpyAsync(c->zoff_d, c->zoff_h, (size_t)count * 8, hipMemcpyHostToDevice, side));
+  if (count) HIPCHK(c, hipMemcpyAsync(c->zitems_d, z, (size_t)count * sizeof(int4), hipMemcpyHostToDevice, side));
+  if (n_groups) {
+    const LayerSched& S = L.sched;
+    int ng = 0;
+    for (int i = 0; i < count;) {
+      const int bg = z[i].x & 0xffffff;
+      const int t = S.first_span_task[bg] + z[i].y / S.chunk[bg];
+      int j = i + 1;
+      while (j < count && (z[j].x & 0xffffff) == bg && S.first_span_task[bg] + z[j].y / S.chunk[bg] == t) ++j;
+      c->zgroups_h[ng++] = make_int4(t, i, j - i, 0);
+      i = j;
+    }
+    if (ng) HIPCHK(c, hipMemcpyAsync(c->zgroups_d, c->zgroups_h, (size_t)ng * sizeof(int4), hipMemcpyHostToDevice, side));
+    *n_groups = ng;
   }
-  HIPCHK(c, hipMemcpyAsync(c->zn_d, c->zn_h, 4, hipMemcpyHostToDevice, side));
   if (done) HIPCHK(c, hipEventRecord(done, side));
+  c->n_fetched = count;
   c->stats.fetch_calls++;
   c->stats.spans_fetched += count;
   c->stats.bytes_fetched += (uint64_t)pos * c->esz;
@@ -494,47 +514,80 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
 
 // Task table of a layer from the per-row zoom estimates.
 void plan_tasks(sekv_ctx* c, LayerSched& S) {
-  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
-  const int base = env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, 1024);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv, d = c->cfg.d_head;
+  const bool dev = c->cfg.basis_home == SEKV_BASES_DEVICE;
+  int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
   const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
-  const int zpw = env_int("SEKV_ZOOM_PER_WG", 4, 1, 1024);
+  const double zpw = env_int("SEKV_ZOOM_PER_TASK", 4, 1, 256);
+  // device store: the unit pass balances the zoom work, one slot per span task;
+  // host store: a span task's zoomed spans go to its second slot, and zoom-heavy
+  // rows get smaller chunks
+  const int per_span = dev ? 1 : 2;
+  {
+    int64_t ntask = 0;
+    for (int bg = 0; bg < BH; ++bg) ntask += (c->m_b[bg / Hkv] + base - 1) / base;
+    while (dev && ntask > kMaxSpanTasks && base < kMaxSpanChunk) {
+      base = std::min(kMaxSpanChunk, base * 2);
+      ntask = 0;
+      for (int bg = 0; bg < BH; ++bg) ntask += (c->m_b[bg / Hkv] + base - 1) / base;
+    }
+  }
   S.chunk.assign(BH, base);
   S.parts_n.assign(BH, 0);
+  S.first_span_task.assign(BH, 0);
   std::vector<int> nspan(BH), nanch(BH), anch(BH, ach);
   std::vector<std::pair<double, int>> order;
   for (int bg = 0; bg < BH; ++bg) {
     const int m = c->m_b[bg / Hkv], na = c->na_b[bg / Hkv];
-    int n = std::max((m + base - 1) / base, (int)std::ceil(S.est[bg] / zpw));
+    int n = (m + base - 1) / base;
+    if (!dev) n = std::max(n, (int)std::ceil(S.est[bg] / zpw));
     n = std::max(1, std::min(n, std::max(1, (m + 15) / 16)));
     int ch = m > 0 ? ((m + n - 1) / n + 15) / 16 * 16 : 16;
     int a = ach;
-    auto parts = [&]() { return (m + ch - 1) / ch + (na + a - 1) / a; };
+    auto parts = [&]() { return per_span * ((m + ch - 1) / ch) + (na + a - 1) / a; };
     while (parts() > kMaxParts) {
-      if (ch < 1024) ch *= 2;
+      if (ch < kMaxSpanChunk) ch = std::min(kMaxSpanChunk, ch * 2);
       else a *= 2;
     }
     S.chunk[bg] = ch;
     anch[bg] = a;
-    nspan[bg] = (m + ch - 1) / ch;
+    nspan[bg] = m > 0 ? (m + ch - 1) / ch : 0;
     nanch[bg] = (na + a - 1) / a;
-    S.parts_n[bg] = nspan[bg] + nanch[bg];
+    S.parts_n[bg] = per_span * nspan[bg] + nanch[bg];
     order.push_back({-(S.est[bg] / std::max(1, nspan[bg])), bg});
   }
   std::stable_sort(order.begin(), order.end());
   S.tasks.clear();
+  S.uoff.clear();
+  S.bg_tasks.assign(BH, make_int2(0, 0));
   S.max_parts = 1;
   for (int bg = 0; bg < BH; ++bg) S.max_parts = std::max(S.max_parts, S.parts_n[bg]);
+  int64_t ucap = 0;
   for (auto& o : order) {  // span chunks, the most zoom-heavy rows first
-    const int bg = o.second, m = c->m_b[bg / Hkv];
-    for (int j = 0; j < nspan[bg]; ++j) S.tasks.push_back(make_int4(bg, j * S.chunk[bg], S.chunk[bg], j));
+    const int bg = o.second, b = bg / Hkv;
+    S.first_span_task[bg] = (int)S.tasks.size();
+    S.bg_tasks[bg] = make_int2((int)S.tasks.size(), nspan[bg]);
+    for (int j = 0; j < nspan[bg]; ++j) {
+      const int k0 = j * S.chunk[bg], k1 = std::min(c->m_b[b], k0 + S.chunk[bg]);
+      S.tasks.push_back(make_int4(bg, k0, S.chunk[bg], per_span * j));
+      S.uoff.push_back((int32_t)ucap);
+      for (int k = k0; k < k1; ++k) ucap += (c->mcount[b][k] + d - 1) / d;  // token tiles of d tokens
+    }
   }
+  S.n_units_cap = ucap;
   S.n_span_tasks = (int)S.tasks.size();
   int amax = 0;
   for (int bg = 0; bg < BH; ++bg) amax = std::max(amax, nanch[bg]);
   for (int j = 0; j < amax; ++j)  // anchor chunks, interleaved over the rows
     for (int bg = 0; bg < BH; ++bg)
       if (j < nanch[bg])
-        S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg], anch[bg], nspan[bg] + j));
+        S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg], anch[bg], per_span * nspan[bg] + j));
+  // unit-pass grid: about one unit per wave at the measured zoom load
+  double est_units = 0.0;
+  for (int bg = 0; bg < BH; ++bg) est_units += S.est[bg];
+  const double upw = env_int("SEKV_UNITS_PER_WAVE", 1, 1, 64);
+  S.unit_wgs = std::max(64, std::min(env_int("SEKV_UNIT_WGS_MAX", 2048, 1, 65536),
+                                     (int)std::ceil(est_units / (upw * kWaves))));
 }
 
 // Refresh a layer's schedule before a launch on `stream`.  `pending` means a
@@ -570,16 +623,42 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   if (!replan || S.pending) return SEKV_OK;
   const std::vector<int4> old_tasks = S.tasks;
   plan_tasks(c, S);
+  // the slot counts follow from the tasks: both tables change together
   if (S.valid && old_tasks.size() == S.tasks.size() &&
       std::memcmp(old_tasks.data(), S.tasks.data(), S.tasks.size() * sizeof(int4)) == 0)
     return SEKV_OK;
   if (S.tasks.size() > S.tasks_cap) {
     dfree(S.tasks_d);
+    dfree(S.uoff_d);
     hfree(S.tasks_pin);
     S.tasks_cap = 0;
     TRY(dalloc(c, &S.tasks_d, S.tasks.size() * sizeof(int4)));
+    TRY(dalloc(c, &S.uoff_d, S.tasks.size() * sizeof(int32_t)));
     TRY(halloc(c, &S.tasks_pin, S.tasks.size() * sizeof(int4)));
     S.tasks_cap = S.tasks.size();
+  }
+  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
+    if (S.n_span_tasks > kMaxSpanTasks) return fail(c, SEKV_ERR_INVALID, "too many span tasks for the zoom unit pass");
+    if ((size_t)S.n_span_tasks + 1 > c->ztasks_cap) {
+      dfree(c->zunits_d);
+      dfree(c->upre_d);
+      c->ztasks_cap = 0;
+      TRY(dalloc(c, &c->zunits_d, ((size_t)S.n_span_tasks + 1) * 4));
+      TRY(dalloc(c, &c->upre_d, ((size_t)S.n_span_tasks + 1) * 4));
+      c->ztasks_cap = (size_t)S.n_span_tasks + 1;
+    }
+    if ((size_t)S.n_units_cap > c->units_cap || !c->uent_d) {
+      dfree(c->uent_d);
+      dfree(c->upart_ml);
+      dfree(c->upart_acc);
+      c->units_cap = 0;
+      const size_t cap = (size_t)S.n_units_cap;
+      TRY(dalloc(c, &c->uent_d, cap * sizeof(int4)));
+      TRY(dalloc(c, &c->upart_ml, cap * c->G * 2 * sizeof(float)));
+      TRY(dalloc(c, &c->upart_acc, cap * c->G * c->cfg.d_head * sizeof(float)));
+      c->units_cap = cap;
+    }
+    if (!S.bg_tasks_d) TRY(dalloc(c, &S.bg_tasks_d, (size_t)BH * sizeof(int2)));
   }
   if (!S.parts_d) {
     TRY(dalloc(c, &S.parts_d, (size_t)BH * 4));
@@ -588,6 +667,11 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   std::memcpy(S.tasks_pin, S.tasks.data(), S.tasks.size() * sizeof(int4));
   std::memcpy(S.parts_pin, S.parts_n.data(), (size_t)BH * 4);
   HIPCHK(c, hipMemcpyAsync(S.tasks_d, S.tasks_pin, S.tasks.size() * sizeof(int4), hipMemcpyHostToDevice, stream));
+  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
+    // small static tables: synchronous copies (no pinned staging kept for them)
+    if (!S.uoff.empty()) HIPCHK(c, hipMemcpy(S.uoff_d, S.uoff.data(), S.uoff.size() * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(S.bg_tasks_d, S.bg_tasks.data(), (size_t)BH * sizeof(int2), hipMemcpyHostToDevice));
+  }
   HIPCHK(c, hipMemcpyAsync(S.parts_d, S.parts_pin, (size_t)BH * 4, hipMemcpyHostToDevice, stream));
   S.valid = true;
   return SEKV_OK;
@@ -626,27 +710,27 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.na_max = c->na_max;
   a.m_b = c->m_b_d;
   a.na_b = c->na_b_d;
-  a.mcount = c->mcount_d;
   a.logS = c->logS_d;
   a.kbar = L.kbar;
   a.vbar = L.vbar;
   a.KA = L.KA;
   a.VA = L.VA;
-  a.rank = L.rank_d;
-  a.boff = L.boff_d;
   a.smeta = L.smeta_d;
   a.bases = L.bases_d;
+  a.basis_elems = L.basis_elems;
   a.tasks = L.sched.tasks_d;
   a.n_tasks = (int)L.sched.tasks.size();
   a.n_span_tasks = L.sched.n_span_tasks;
   a.parts_n = L.sched.parts_d;
   a.max_parts = L.sched.max_parts;
   a.zstat = L.sched.zstat_d;
-  a.n_zoom_wgs = env_int("SEKV_ZOOM_WGS", c->zoom_wgs, 1, 65536);
   a.zlist = c->zlist_d;
   a.zcounter = c->zcounter_d;
-  a.zpart_ml = c->zpart_ml;
-  a.zpart_acc = c->zpart_acc;
+  a.uoff = L.sched.uoff_d;
+  a.uent = c->uent_d;
+  a.zunits = c->zunits_d;
+  a.upre = c->upre_d;
+  a.bg_tasks = L.sched.bg_tasks_d;
 }
 
 sekv_status thetas(sekv_ctx* c, const float* tau, DecodeArgs& a) {
@@ -709,20 +793,12 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->anchors.assign(k.batch, {});
   c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
   c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
-  c->zoom_wgs = env_int("SEKV_ZOOM_WGS", 512, 1, 65536);
   sekv_status s = dalloc(c, &c->zcounter_d, 4);
-  if (s == SEKV_OK) s = dalloc(c, &c->zn_d, 4);
   if (s == SEKV_OK) s = halloc(c, &c->zcount_h, 4);
-  if (s == SEKV_OK) s = halloc(c, &c->zn_h, 4);
   if (s == SEKV_OK && hipMemset(c->zcounter_d, 0, 4) != hipSuccess) s = fail(c, SEKV_ERR_HIP, "hipMemset");
   if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess)
     s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side)");
   if (s == SEKV_OK && hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming) != hipSuccess)
-    s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
-  if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side2, hipStreamNonBlocking) != hipSuccess)
-    s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side2)");
-  if (s == SEKV_OK && (hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
-                       hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess))
     s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
   if (s != SEKV_OK) {
     g_create_err = c->err;
@@ -754,24 +830,21 @@ void sekv_destroy(sekv_ctx* c) {
   dfree(c->part_acc);
   dfree(c->zlist_d);
   dfree(c->zcounter_d);
-  dfree(c->zpart_ml);
-  dfree(c->zpart_acc);
   dfree(c->mask_d);
+  dfree(c->uent_d);
+  dfree(c->upart_ml);
+  dfree(c->upart_acc);
+  dfree(c->zunits_d);
+  dfree(c->upre_d);
   dfree(c->zitems_d);
-  dfree(c->zoff_d);
-  dfree(c->zn_d);
+  dfree(c->zgroups_d);
   hfree(c->zlist_h);
   hfree(c->zcount_h);
   hfree(c->zitems_h);
-  hfree(c->zoff_h);
-  hfree(c->zn_h);
+  hfree(c->zgroups_h);
   dfree(c->staging);
-  if (c->side2) (void)hipStreamSynchronize(c->side2);
   if (c->ev_fetch) (void)hipEventDestroy(c->ev_fetch);
-  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->side) (void)hipStreamDestroy(c->side);
-  if (c->side2) (void)hipStreamDestroy(c->side2);
   delete c;
 }
 
@@ -962,7 +1035,7 @@ sekv_status sekv_zoom_fetch(sekv_ctx* c, int32_t layer, const int32_t* entries, 
       c->zitems_h[n++] = make_int4(bg | (int)((uint32_t)e & 0xff000000u), e & 0xffffff, 0, 0);
     }
   }
-  return fetch_items(c, layer, c->zitems_h, n, side, done);
+  return fetch_items(c, layer, c->zitems_h, n, side, done, nullptr);
 }
 
 sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
@@ -993,23 +1066,24 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   a.part_acc = c->part_acc;
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
-  // anchor tasks on the second stream, joined before the combine
-  const int nspan = a.n_span_tasks, ntask = a.n_tasks;
-  HIPCHK(c, hipEventRecord(c->ev_fork, stream));
-  HIPCHK(c, hipStreamWaitEvent(c->side2, c->ev_fork, 0));
-  launch_decode_route(false, nspan, ntask, d, c->bf16, a, c->side2);
-  HIPCHK(c, hipGetLastError());
-  HIPCHK(c, hipEventRecord(c->ev_join, c->side2));
-  // span tasks: routing, summaries, the zoom list
-  launch_decode_route(false, 0, nspan, d, c->bf16, a, stream);
-  HIPCHK(c, hipGetLastError());
   if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
-    a.zitems = c->zlist_d;
-    a.zn = c->zcounter_d;
-    launch_decode_zoom(false, d, c->bf16, a, stream);
+    // span tasks; then the zoom units, balanced over the zoom workgroups, and the anchor tasks
+    if ((size_t)L.sched.n_units_cap > c->units_cap || (size_t)a.n_span_tasks + 1 > c->ztasks_cap)
+      return fail(c, SEKV_ERR_STATE, "zoom unit buffers smaller than the schedule");
+    a.upart_ml = c->upart_ml;  // written by the unit pass, read by the combine
+    a.upart_acc = c->upart_acc;
+    if (!a.upart_ml || !a.upart_acc || !a.uent || !a.zunits || !a.upre || !a.uoff || !a.bg_tasks)
+      return fail(c, SEKV_ERR_STATE, "zoom unit buffers missing");
+    launch_decode_route(0, a.n_span_tasks, d, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
+    a.n_zoom_wgs = L.sched.unit_wgs;
+    launch_decode_attend(false, a.n_zoom_wgs + (a.n_tasks - a.n_span_tasks), d, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
   } else {
     // HOST home: learn the zoom list, fetch the bases, then the zoomed segment
     if (capturing) return fail(c, SEKV_ERR_STATE, "host-resident bases need a host sync: not capturable");
+    launch_decode_route(1, a.n_span_tasks, d, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
     HIPCHK(c, hipMemcpyAsync(c->zcount_h, c->zcounter_d, 4, hipMemcpyDeviceToHost, stream));
     HIPCHK(c, hipStreamSynchronize(stream));
     const int nz = *c->zcount_h;
@@ -1017,20 +1091,20 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
       HIPCHK(c, hipMemcpyAsync(c->zlist_h, c->zlist_d, (size_t)nz * sizeof(int4), hipMemcpyDeviceToHost, stream));
       HIPCHK(c, hipStreamSynchronize(stream));
     }
-    sekv_status fs = fetch_items(c, layer, c->zlist_h, nz, c->side, c->ev_fetch);
+    int ng = 0;
+    sekv_status fs = fetch_items(c, layer, c->zlist_h, nz, c->side, c->ev_fetch, &ng);
     if (fs != SEKV_OK) {
-      (void)hipStreamWaitEvent(stream, c->ev_join, 0);
       (void)hipMemsetAsync(c->zcounter_d, 0, 4, stream);  // leave an empty list for the next call
       return fs;
     }
     HIPCHK(c, hipStreamWaitEvent(stream, c->ev_fetch, 0));
     a.zitems = c->zitems_d;
-    a.zn = c->zn_d;
-    a.zoff = c->zoff_d;
+    a.zgroups = c->zgroups_d;
     a.staging = c->staging;
-    launch_decode_zoom(true, d, c->bf16, a, stream);
+    a.n_zoom_wgs = ng;
+    launch_decode_attend(true, ng + (a.n_tasks - a.n_span_tasks), d, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
   }
-  HIPCHK(c, hipStreamWaitEvent(stream, c->ev_join, 0));
   launch_decode_combine(d, a, stream);
   HIPCHK(c, hipGetLastError());
   return finish_sched(c, layer, stream, capturing);
@@ -1049,7 +1123,7 @@ sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float*
   for (int h = 0; h < kMaxHq; ++h) a.theta[h] = INFINITY;
   a.q = q;
   a.scores = scores;
-  launch_decode_route(true, 0, a.n_span_tasks, c->cfg.d_head, c->bf16, a, stream);
+  launch_decode_route(2, a.n_span_tasks, c->cfg.d_head, c->bf16, a, stream);
   HIPCHK(c, hipGetLastError());
   return SEKV_OK;
 }

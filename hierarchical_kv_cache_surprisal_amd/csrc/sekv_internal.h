@@ -12,7 +12,9 @@ constexpr int kMaxBg = 512;       // sequences x kv heads supported by the decod
 constexpr int kThreads = 256;     // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxParts = 512;  // split-K partial slots per (sequence, query head)
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreads = 512;
+constexpr int kMaxSpanChunk = 256;  // span rows per span task
+constexpr int kMaxSpanTasks = 8192; // span tasks per layer (device-store zoom units)
 
 // Every packed basis block starts on a multiple of 8 elements (16 bytes for
 // bf16), so wide loads stay aligned.
@@ -24,46 +26,54 @@ struct DecodeArgs {
   int B, Hq, Hkv, G, m_max, na_max;
   const int32_t* m_b;     // [B] spans per sequence
   const int32_t* na_b;    // [B] anchors per sequence
-  const int32_t* mcount;  // [B][m_max] member counts
   const float* logS;      // [B][m_max] ln(member count)
   const void* kbar;       // [B][Hkv][m_max][d]
   const void* vbar;
   const void* KA;         // [B][Hkv][na_max][d]
   const void* VA;
-  const int32_t* rank;    // [B][Hkv][m_max]
-  const int64_t* boff;    // [B][Hkv][m_max] element offset of each span's packed bases
-  const int2* smeta;      // [B][Hkv][m_max] {boff / 8, rank | member count << 8}
+  const int2* smeta;      // [B][Hkv][m_max] {basis offset / 8, rank | member count << 8}
   const void* bases;      // device basis store of the layer (DEVICE home)
+  int64_t basis_elems;    // its size in elements
   const float* q;         // [B][Hq][d]
   float* out;             // [B][Hq][d]
   uint8_t* mask;          // [B][Hq][m_max] zoom decisions (always written)
   float* scores;          // [B][Hq][m_max] (routing-scores mode)
-  const int4* tasks;      // one per route workgroup: (bg | anchor kind << 31, first row, rows, partial slot)
-  int n_tasks, n_span_tasks;  // span tasks first, then anchor tasks
+  // tasks: span (bg, first span, spans, partial slot; with host-resident bases
+  // the next slot holds its zoomed spans) then anchor (bg | 1 << 31, first
+  // anchor, anchors, slot)
+  const int4* tasks;
+  int n_tasks, n_span_tasks;
   const int32_t* parts_n; // [B*Hkv] partial slots used by each (sequence, kv head)
   int max_parts;          // partial slots per (sequence, query head) in the buffers below
   int32_t* zstat;         // [B*Hkv] cumulative zoomed spans of this layer (scheduling statistics)
   float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
   float* part_acc;        // [B][Hq][max_parts][d]
-  int4* zlist;            // zoom list: (bg | head bits << 24, span, boff / 8, rank | count << 8)
-  int32_t* zcounter;      // its length (atomic; reset by the combine kernel)
-  const int4* zitems;     // spans the zoom kernel processes (zlist, or the sorted staged list)
-  const int32_t* zn;      // their count (device)
-  const int64_t* zoff;    // staging element offset per staged item (HOST home)
-  const void* staging;    // device staging buffer (HOST home)
-  int n_zoom_wgs;         // workgroups of the zoom kernel
-  float* zpart_ml;        // [B][Hkv][m_max][G][2] partial of each zoomed (span, head)
-  float* zpart_acc;       // [B][Hkv][m_max][G][d]
+  // device store: zoom units (one token tile of a zoomed span each)
+  const int32_t* uoff;     // [n_span_tasks] first entry of each span task in uent
+  int4* uent;              // unit entries (head bits, basis offset / 8, rank | count << 8, first token)
+  int32_t* zunits;         // [n_span_tasks] units of each span task
+  int32_t* upre;           // [n_span_tasks + 1] units before each span task (from the units kernel)
+  float* upart_ml;         // [units][G][2] partial of each unit and head (NULL: no unit pass)
+  float* upart_acc;        // [units][G][d]
+  const int2* bg_tasks;    // [B*Hkv] (first span task, span tasks) of each (sequence, kv head)
+  int n_zoom_wgs;          // zoom workgroups at the front of the attend grid
+  // host fetch path: flat list (bg | head bits << 24, span, basis offset / 8, rank | count << 8)
+  int4* zlist;
+  int32_t* zcounter;      // its length (reset by the combine kernel)
+  const int4* zitems;     // staged items: (bg | head bits << 24, span, staging offset / 8, rank | count << 8)
+  const int4* zgroups;    // (span task, first item, items)
+  const void* staging;
   double theta[kMaxHq];   // logit(tau) per query head
 };
 
-// route-kernel tasks [t0, t1) of the table: anchors, routing and summaries, zoomed spans
-// appended to the list (scores_only: routing scores into `scores`, nothing else)
-void launch_decode_route(bool scores_only, int t0, int t1, int d, int kv_bf16, const DecodeArgs& a,
-                         hipStream_t s);
-// zoomed spans of the list, bases in the device store or (staged) the staging buffer
-void launch_decode_zoom(bool staged, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
-// log-sum-exp merge of every (sequence, query head) into out; empties the zoom list
+// span tasks, grid = span tasks.  mode 0: zoom units to the task table
+// (DEVICE bases); 1: zoomed spans to the flat list (HOST bases); 2: routing
+// scores only
+void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// n_zoom_wgs zoom workgroups (staged: one per fetched group; else the unit
+// pass, n_zoom_wgs >= 1), then the anchor tasks; grid = n_zoom_wgs + anchor tasks
+void launch_decode_attend(bool staged, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// log-sum-exp merge of every (sequence, query head) into out; resets the counters
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- build
