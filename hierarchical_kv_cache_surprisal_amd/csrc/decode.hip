@@ -415,7 +415,7 @@ static_assert(kMaxSpanChunk <= kThreads, "one thread per zoomed span of a task")
 // one partial per query head stored in `part` (heads that zoom none of the
 // spans get an empty one).  item(j) -> (head bits, basis offset / 8,
 // rank | count << 8) is called by thread j < zc only, with j = its index.
-template <int D, typename T, int G, class Item>
+template <int D, typename T, int G, bool MERGE, class Item>
 __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item item, const T* __restrict__ src,
                            Smem<D, G>& sh) {
   using Gm = Geo<D, T>;
@@ -478,7 +478,30 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
         if (hb & (1u << h)) lse_merge<EPL>(st.m[h], st.l[h], acc[h], sm[h], sl[h], o[h]);
     }
   }
-  // every row slot holds the same state: slot 0 writes the wave's record
+  // every row slot holds the same state: slot 0 writes the wave's record, or
+  // (MERGE) folds it into the record the wave already holds
+  if (MERGE) {
+    if (wave < units) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mr = sh.ml.m[wave][h], lr = sh.ml.l[wave][h];
+        float ar[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ar[e] = sh.ml.acc[wave][h][tg * EPL + e];
+        lse_merge<EPL>(mr, lr, ar, st.m[h], st.l[h], acc[h]);
+        wave_lds_sync();  // every lane has read the record before it is rewritten
+        if (lane == 0) {
+          sh.ml.m[wave][h] = mr;
+          sh.ml.l[wave][h] = lr;
+        }
+        if (rg == 0) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) sh.ml.acc[wave][h][tg * EPL + e] = ar[e];
+        }
+      }
+    }
+    return;
+  }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -730,7 +753,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
   const u64 bal = __ballot(hb != 0);
   int pos = __popcll(bal & ((1ull << lane) - 1ull));
   if (lane == 0) sh.wcount[wave] = __popcll(bal);
-  store_partial<D, G>(sh.ml, a, b, g, task.w);
+  if (MODE != 0) store_partial<D, G>(sh.ml, a, b, g, task.w);
   __syncthreads();
   int zc = 0;
 #pragma unroll
@@ -739,36 +762,17 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     zc += sh.wcount[w];
   }
   if (MODE == 0) {
-    // one unit entry per token tile of each zoomed span, in span order, in the
-    // task's own range of the unit table
-    constexpr int TILE = Gm::TILE;
-    int2 meta = make_int2(0, 0);
-    int nt = 0;
-    if (hb) {
-      meta = sh.zmeta[i];
-      nt = ((int)((uint32_t)meta.y >> 8) + TILE - 1) / TILE;
+    // zoomed spans in place: token-tile units over the waves, folded into the
+    // wave records, then the task's one partial
+    if (zc) {
+      if (hb) sh.zit[pos] = make_int3((int)hb, sh.zmeta[i].x, sh.zmeta[i].y);
+      if (threadIdx.x == 0) atomicAdd(&a.zstat[bg], zc);
+      __syncthreads();
+      auto item = [&](int j) -> int3 { return sh.zit[j]; };
+      zoom_group<D, T, G, true>(a, bg, task.w, zc, item, reinterpret_cast<const T*>(a.bases), sh);
+      __syncthreads();
     }
-    int incl = nt;
-#pragma unroll
-    for (int sft = 1; sft < 64; sft <<= 1) {
-      const int y = __shfl_up(incl, sft, 64);
-      if (lane >= sft) incl += y;
-    }
-    __syncthreads();  // wcount reads above are done
-    if (lane == 63) sh.wcount[wave] = incl;
-    __syncthreads();
-    int before = incl - nt, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) before += sh.wcount[w];
-      total += sh.wcount[w];
-    }
-    int4* ue = a.uent + a.uoff[t] + before;
-    for (int tt = 0; tt < nt; ++tt) ue[tt] = make_int4((int)hb, meta.x, meta.y, tt * TILE);
-    if (threadIdx.x == 0) {
-      a.zunits[t] = total;
-      if (total) atomicAdd(&a.zstat[bg], total);
-    }
+    store_partial<D, G>(sh.ml, a, b, g, task.w);
     return;
   }
   if (zc == 0) store_empty<D, G>(a, b, g, task.w + 1);  // the zoom slot, when nothing fills it
@@ -789,7 +793,12 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
 template <int D, typename T, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
-  span_task<D, T, G, MODE>(a, (int)blockIdx.x, a.tasks[blockIdx.x], sh);
+  const int4 task = a.tasks[blockIdx.x];
+  if (task.x < 0) {  // anchor tasks: MODE 0 only (the attend kernel runs them otherwise)
+    if (MODE == 0) anchor_task<D, T, G>(a, task, sh.ml);
+    return;
+  }
+  span_task<D, T, G, MODE>(a, (int)blockIdx.x, task, sh);
 }
 
 // Staged bases: zoom workgroup i takes group i (span task, first item, items)
@@ -803,7 +812,7 @@ __device__ void staged_group(const DecodeArgs& a, int i, Smem<D, G>& sh) {
     const int4 it = items[j];
     return make_int3((int)((uint32_t)it.x >> 24), it.z, it.w);
   };
-  zoom_group<D, T, G>(a, task.x, task.w + 1, grp.z, item, reinterpret_cast<const T*>(a.staging), sh);
+  zoom_group<D, T, G, false>(a, task.x, task.w + 1, grp.z, item, reinterpret_cast<const T*>(a.staging), sh);
 }
 
 

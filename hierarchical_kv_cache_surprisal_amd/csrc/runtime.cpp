@@ -540,7 +540,7 @@ void plan_tasks(sekv_ctx* c, LayerSched& S) {
   for (int bg = 0; bg < BH; ++bg) {
     const int m = c->m_b[bg / Hkv], na = c->na_b[bg / Hkv];
     int n = (m + base - 1) / base;
-    if (!dev) n = std::max(n, (int)std::ceil(S.est[bg] / zpw));
+    n = std::max(n, (int)std::ceil(S.est[bg] / zpw));
     n = std::max(1, std::min(n, std::max(1, (m + 15) / 16)));
     int ch = m > 0 ? ((m + n - 1) / n + 15) / 16 * 16 : 16;
     int a = ach;
@@ -1067,17 +1067,8 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
   if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
-    // span tasks; then the zoom units, balanced over the zoom workgroups, and the anchor tasks
-    if ((size_t)L.sched.n_units_cap > c->units_cap || (size_t)a.n_span_tasks + 1 > c->ztasks_cap)
-      return fail(c, SEKV_ERR_STATE, "zoom unit buffers smaller than the schedule");
-    a.upart_ml = c->upart_ml;  // written by the unit pass, read by the combine
-    a.upart_acc = c->upart_acc;
-    if (!a.upart_ml || !a.upart_acc || !a.uent || !a.zunits || !a.upre || !a.uoff || !a.bg_tasks)
-      return fail(c, SEKV_ERR_STATE, "zoom unit buffers missing");
-    launch_decode_route(0, a.n_span_tasks, d, c->bf16, a, stream);
-    HIPCHK(c, hipGetLastError());
-    a.n_zoom_wgs = L.sched.unit_wgs;
-    launch_decode_attend(false, a.n_zoom_wgs + (a.n_tasks - a.n_span_tasks), d, c->bf16, a, stream);
+    // span tasks with their zoomed spans in place, and the anchor tasks
+    launch_decode_route(0, a.n_tasks, d, c->bf16, a, stream);
     HIPCHK(c, hipGetLastError());
   } else {
     // HOST home: learn the zoom list, fetch the bases, then the zoomed segment
