@@ -8,10 +8,15 @@ SVD of every span into a device-resident basis store), then decode steps are
 timed: one step = one decode-attention pass over all 32 layers.
 
 Reported metric: key positions per second per layer-step (B*n / t_layer_step),
-plus achieved HBM bandwidth of the decode kernel from the algorithmic bytes
-of each layer-step (anchors, summaries, zoomed spans' bases, q/out/mask).
+plus achieved HBM bandwidth of one layer-step (the route kernel, which does the
+work, and the small combine kernel) from the algorithmic bytes of each
+layer-step (anchors, summaries, zoomed spans' bases, q/out/mask), timed with
+HIP events around a graph replay of every step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --home host ...          # bases in pinned host memory: PCIe-inclusive rate
+    python bench.py --copy-calibration ...   # also runs a 1 GiB device copy (counter scaling)
+    python bench.py --traffic-from FETCH_DIR WRITE_DIR   # rocprofv3 --pmc runs -> profiles/decode_traffic.json
 """
 from __future__ import annotations
 
@@ -43,8 +48,12 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-baseline sample")
+    p.add_argument("--cpu-heads", type=int, default=4, help="kv heads in the CPU-baseline sample")
+    p.add_argument("--cpu-steps", type=int, default=160, help="decode steps in the CPU-baseline sample")
     p.add_argument("--calib-steps", type=int, default=8)
+    p.add_argument("--home", choices=("device", "host"), default="device")
+    p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args()
 
 
@@ -71,8 +80,78 @@ def load_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
+def decode_kernel(name: str):
+    """The decode kernels of a device-resident layer-step: the route kernel in
+    its decode mode (last template argument 0; mode 2 is the routing-scores
+    pass used to calibrate thresholds) and the combine kernel."""
+    import re
+    if re.search(r"k_route<[^>]*,\s*0>", name):
+        return "k_route"
+    if "k_combine<" in name:
+        return "k_combine"
+    return None
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, counter value) per dispatch from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_from(fetch_dir, write_dir):
+    """HBM bytes per layer-step of the decode kernels from two rocprofv3 --pmc
+    runs of `bench.py --no-graph --copy-calibration` (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter reads
+    for the 1 GiB device copy (read once, written once).  Writes
+    profiles/decode_traffic.json keyed by workload, with the kernel-source hash."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        copy = [v for k, v in rows if "elementwise" in k.lower()]
+        if not copy:
+            raise SystemExit(f"no copy-kernel dispatch with {counter} in {d}")
+        kib_copy = max(copy)  # the 1 GiB copy is the largest copy dispatch
+        scale = COPY_BYTES / (kib_copy * 1024.0)
+        per = {}
+        for k, v in rows:
+            name = decode_kernel(k)
+            if name:
+                per.setdefault(name, []).append(v * 1024.0 * scale)
+        res[counter] = {"scale": scale, "copy_kib": kib_copy,
+                        "kernels": {n: {"dispatches": len(v), "bytes_mean": sum(v) / len(v)} for n, v in per.items()}}
+    fetch = sum(e["bytes_mean"] for e in res["FETCH_SIZE"]["kernels"].values())
+    write = sum(e["bytes_mean"] for e in res["WRITE_SIZE"]["kernels"].values())
+    out = {"kernel_hash": kernel_source_hash(), "bytes_per_launch": fetch + write,
+           "fetch_bytes": fetch, "write_bytes": write, "detail": res,
+           "note": "one launch = one layer-step (k_route + k_combine): mean over dispatches"}
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    try:
+        with open(path) as f:
+            allw = json.load(f)
+    except (OSError, ValueError):
+        allw = {}
+    allw["layers32_128k"] = out
+    with open(path, "w") as f:
+        json.dump(allw, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               f"(the decode path has no multi-GPU split in this build).", file=sys.stderr)
@@ -95,7 +174,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     # ------------------------------------------------------------------ build every layer
-    ctx = sekv.Context(L, B, n, Hq, Hkv, d, s.kv_dtype, s.w, "device")
+    ctx = sekv.Context(L, B, n, Hq, Hkv, d, s.kv_dtype, s.w, args.home)
     H = torch.from_numpy(synth.surprisal_batch(s)).to(dev)
     t_gen = t_build = 0.0
     for l in range(L):
@@ -190,7 +269,7 @@ def main():
 
     # ------------------------------------------------------------------ timed region
     graph = None
-    if not args.no_graph:
+    if not args.no_graph and args.home == "device":  # host-resident bases sync each call: no graph
         try:
             g = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()
@@ -230,10 +309,20 @@ def main():
     log(f"timed {args.steps} steps x {L} layers: {t_ms:.3f} ms (wall {wall*1e3:.1f} ms), "
         f"t_layer_step {t_ls*1e6:.2f} us, {kps:.3e} KP/s, {gbs:.0f} GB/s = {100*gbs/PEAK_HBM_GBS:.1f}% of peak")
 
+    if args.copy_calibration:
+        # a device copy of known size, for scaling the HBM byte counters
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 3 x {COPY_BYTES >> 20} MiB device copy")
+
     # ------------------------------------------------------------------ CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(s, ctx, H, taus, qs, args.cpu_heads)
+        cpu = cpu_baseline(s, ctx, H, taus, args.cpu_heads, args.cpu_steps)
 
     traffic = load_traffic(s.name)
     res = {
@@ -251,12 +340,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{s.name}: {L} layers x {Hq} q-heads / {Hkv} kv-heads, d={d}, n={n}, "
                                f"{s.kv_dtype} KV, batch {B}, {args.steps} decode steps, zoom 0.5-20% per head, "
-                               f"bases device-resident",
+                               f"bases {args.home}-resident",
                    "layers": L, "q_heads": Hq, "kv_heads": Hkv, "d_head": d, "ctx": n, "batch": B,
-                   "spans": m_tot, "anchors": n_a, "graph": graph is not None},
+                   "spans": m_tot, "anchors": n_a, "graph": graph is not None, "bases": args.home},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
-                     "traffic": traffic},
+                     "traffic": traffic if args.home == "device" else None,
+                     "kernel": "one layer-step: k_route (the work) + k_combine"},
         "cpu_baseline": cpu,
         "t_layer_step_us": t_ls * 1e6,
         "algorithmic_bytes_per_layer_step": bytes_per_ls,
@@ -269,12 +359,11 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(s, ctx, H, taus, qs, n_heads):
+def cpu_baseline(s, ctx, H, taus, n_heads, steps):
     """The oracle (numpy fp64, untuned) on a bounded sample: build the artefacts
     of `n_heads` kv heads of layer 0 (not timed), then time the decode of those
-    heads for two steps, scaled to one full layer-step."""
+    heads for `steps` queries (about 10 s), scaled to one full layer-step."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_limits
 
     import synth
@@ -291,22 +380,22 @@ def cpu_baseline(s, ctx, H, taus, qs, n_heads):
         segs, arts = O.build_layer(Hn, Kh, Vh, s.alpha, s.w, 0, s.rank_choices, s.rank_seed, s.kv_dtype,
                                    heads=heads)
         t_build = time.perf_counter() - t0
-        steps = 2
+        qh = [synth.queries(s, 0, t).numpy().astype(np.float64) for t in range(steps)]
         t0 = time.perf_counter()
         for t in range(steps):
-            q = qs[0, t].cpu().numpy().astype(np.float64)
             for b in range(s.B):
                 for g in heads:
                     for h in range(g * s.G, (g + 1) * s.G):
-                        O.decode_head(q[b, h], float(taus[0, h]), arts[(b, g)])
+                        O.decode_head(qh[t][b, h], float(taus[0, h]), arts[(b, g)])
         t_dec = time.perf_counter() - t0
     per_head = t_dec / (steps * s.B * len(heads) * s.G)
     t_ls = per_head * s.Hq * s.B  # one layer-step: every query head of every sequence
     kps = s.B * s.n / t_ls
-    log(f"cpu oracle: {per_head*1e3:.1f} ms per head-step -> {kps:.3e} KP/s (build sample {t_build:.1f}s)")
+    log(f"cpu oracle: {t_dec:.1f}s for {steps * s.B * len(heads) * s.G} head-steps, {per_head*1e3:.1f} ms per "
+        f"head-step -> {kps:.3e} KP/s (artefact build of the sample {t_build:.1f}s, not timed)")
     return {"value": kps, "unit": "key-positions/s", "cores": 1, "kind": "oracle",
             "sample": f"numpy fp64 oracle, 1 thread: decode of {len(heads)} kv heads x {s.G} q-heads of layer 0 "
-                      f"for 2 steps at the same thresholds, scaled to a {s.Hq}-head layer-step "
+                      f"for {steps} steps ({t_dec:.1f}s) at the same thresholds, scaled to a {s.Hq}-head layer-step "
                       f"(oracle artefact build of the sample: {t_build:.1f}s, not timed)"}
 
 

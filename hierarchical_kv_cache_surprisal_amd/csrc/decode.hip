@@ -14,31 +14,29 @@
 //
 // A layer-step is split over the context into tasks, each writing one partial
 // (running max in log2 units, sum, d-vector accumulator) per query head into
-// a slot of its own, in three kernels:
-//   k_route    one workgroup per span task: routing scores of a chunk of
-//              spans, the zoom decisions (zoom mask), the summary entries of
-//              the spans a head does not zoom, and the chunk's zoomed spans
-//              listed in span order (device-resident bases: one entry per
-//              token tile, a "unit", in the task's range of a table;
-//              host-resident: appended to a flat list for the host fetch).
-//   k_attend   zoom workgroups first, then one workgroup per anchor task
-//              (the exact tokens of a chunk of anchors).  Device store: the
-//              units of the whole layer-step, balanced over the zoom
-//              workgroups (each forms the prefix of the per-task unit counts
-//              and takes a contiguous range), one partial per unit.  Staged
-//              bases: one workgroup per fetched span task, into the task's
-//              second slot.  The anchor stream hides the latency of the zoom
-//              chain (unit list, then bases).
-//   k_combine  log-sum-exp merge of every (sequence, query head)'s slots and
-//              units, in a fixed order.
+// a slot of its own:
+//   k_route    one workgroup per task.  Span task: routing scores of a chunk
+//              of spans, the zoom decisions (zoom mask) and the summary
+//              entries of the spans a head does not zoom; then its zoomed
+//              spans, cut into units of one token tile each (independent
+//              entries of the softmax), spread over the waves and folded into
+//              the same partial (device-resident bases), or listed for the
+//              host fetch (host-resident bases).  Anchor task (device-resident
+//              bases): the exact tokens of a chunk of anchors.  The runtime
+//              sizes the span chunks of each (sequence, kv head) from the zoom
+//              counts of earlier steps, so that a chunk holds about one zoomed
+//              span per wave.
+//   k_attend   (host-resident bases) one workgroup per fetched span task, its
+//              zoomed spans from the staged bases into the task's second slot,
+//              then one workgroup per anchor task.
+//   k_combine  log-sum-exp merge of every (sequence, query head)'s slots, in
+//              slot order.
 // No workgroup waits for another and no atomic shares an address across the
 // grid: kernel boundaries order the phases.
 // Lanes are grouped in "row slots" of d*elem/16 lanes, each slot streaming
 // whole 16-byte row pieces.  The path is HBM-bound (about one flop per byte per
 // query head), so no MFMA is used.
 #include "sekv_device.h"
-
-#include <type_traits>
 
 namespace sekv {
 
@@ -816,145 +814,17 @@ __device__ void staged_group(const DecodeArgs& a, int i, Smem<D, G>& sh) {
 }
 
 
-template <int D, int G>
-struct AttendLds {
-  union {
-    MergeLds<D, G> ml;  // anchor tasks
-    struct {
-      ZoomLds<G> zw[kWaves];
-      int pre[kMaxSpanTasks + 1];  // units before each span task
-      int wsum[kWaves];
-    };
-  };
-};
-
-// Device store: the zoom units of the whole layer-step, balanced over the
-// n_wgs zoom workgroups.  Each reads the units of every span task (a few KB,
-// from L2) and forms their prefix; wave W takes the contiguous units
-// [W * per, (W + 1) * per) and writes one partial per unit and query head
-// (empty for heads that do not zoom the span).  Zoom workgroup 0 stores the
-// prefix for the combine kernel.
+// Host-resident bases: workgroups [0, n_zoom_wgs) take the fetched groups;
+// then one workgroup per anchor task.
 template <int D, typename T, int G>
-__device__ void unit_pass(const DecodeArgs& a, int wg, int n_wgs, AttendLds<D, G>& sh) {
-  using Gm = Geo<D, T>;
-  constexpr int EPL = Gm::EPL, LPR = Gm::LPR;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rg = lane / LPR, tg = lane % LPR;
-  const int n = a.n_span_tasks;  // <= kMaxSpanTasks
-  constexpr int PER_T = (kMaxSpanTasks + kThreads) / kThreads;  // covers indices 0..n
-  {
-    // each thread sums a contiguous run of tasks; scan of the runs
-    const int t0 = threadIdx.x * PER_T;
-    int v[PER_T];
-    int run = 0;
-#pragma unroll
-    for (int j = 0; j < PER_T; ++j) {
-      v[j] = (t0 + j < n) ? a.zunits[t0 + j] : 0;
-      run += v[j];
-    }
-    int incl = run;
-#pragma unroll
-    for (int sft = 1; sft < 64; sft <<= 1) {
-      const int y = __shfl_up(incl, sft, 64);
-      if (lane >= sft) incl += y;
-    }
-    if (lane == 63) sh.wsum[wave] = incl;
-    __syncthreads();
-    int before = incl - run;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (w < wave) before += sh.wsum[w];
-#pragma unroll
-    for (int j = 0; j < PER_T; ++j) {
-      if (t0 + j <= n) sh.pre[t0 + j] = before;
-      before += v[j];
-    }
-    __syncthreads();
-    if (wg == 0)
-      for (int t = threadIdx.x; t <= n; t += kThreads) a.upre[t] = sh.pre[t];
-  }
-  const int units = sh.pre[n];
-  const int nw = n_wgs * kWaves;
-  const int per = (units + nw - 1) / nw;
-  const int u0 = (wg * kWaves + wave) * per;
-  const int u1 = min(units, u0 + per);
-  if (u0 >= u1) return;
-  // task of the first unit: last t with pre[t] <= u0
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (sh.pre[mid] <= u0) lo = mid;
-    else hi = mid - 1;
-  }
-  int t = lo;
-  const float c2 = kLog2e * rsqrtf((float)D);
-  const T* src = reinterpret_cast<const T*>(a.bases);
-  // the entries (and tasks) of the first units in one round
-  constexpr int PF = 4;
-  int4 pe[PF];
-  int pbg[PF];
-  {
-    int tt = t;
-#pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int u = min(u0 + x, u1 - 1);
-      while (sh.pre[tt + 1] <= u) ++tt;
-      pe[x] = a.uent[a.uoff[tt] + (u - sh.pre[tt])];
-      pbg[x] = a.tasks[tt].x;
-    }
-  }
-  for (int u = u0; u < u1; ++u) {
-    while (sh.pre[t + 1] <= u) ++t;
-    int4 e;
-    int bg;
-    if (u - u0 < PF) {
-      e = pe[0];
-      bg = pbg[0];
-#pragma unroll
-      for (int x = 1; x < PF; ++x)
-        if (u - u0 == x) {
-          e = pe[x];
-          bg = pbg[x];
-        }
-    } else {
-      e = a.uent[a.uoff[t] + (u - sh.pre[t])];
-      bg = a.tasks[t].x;
-    }
-    const int b = bg / a.Hkv, g = bg % a.Hkv;
-    float qr[G][EPL];
-    load_q<D, G, T>(a, b, g, tg, qr);
-    const uint32_t hb = (uint32_t)e.x;
-    const int r = e.z & 0xff, cnt = (int)((uint32_t)e.z >> 8);
-    float sm[G], sl[G], o[G][EPL];
-    zoom_unit<D, T, G>(src + ((int64_t)(uint32_t)e.y << 3), cnt, r, e.w, qr, sh.zw[wave], c2, rg, tg, sm, sl, o);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bool z = (hb >> h) & 1u;
-      const size_t slot = (size_t)u * G + h;
-      if (rg == 0) {
-        float ov[EPL];
-#pragma unroll
-        for (int x = 0; x < EPL; ++x) ov[x] = z ? o[h][x] : 0.f;
-#pragma unroll
-        for (int x = 0; x < EPL; x += 4) Elem<float>::store16(a.upart_acc + slot * D + tg * EPL + x, ov + x);
-      }
-      if (lane == 0) reinterpret_cast<float2*>(a.upart_ml)[slot] = z ? make_float2(sm[h], sl[h]) : make_float2(kNegInf, 0.f);
-    }
-  }
-}
-
-// Workgroups [0, n_zoom_wgs): zoom (STAGED: one per fetched group; else the
-// unit pass); then one workgroup per anchor task.
-template <int D, typename T, int G, bool STAGED>
 __global__ __launch_bounds__(kThreads) void k_attend(DecodeArgs a) {
-  __shared__ typename std::conditional<STAGED, Smem<D, G>, AttendLds<D, G>>::type sh;
+  __shared__ Smem<D, G> sh;
   const int i = (int)blockIdx.x - a.n_zoom_wgs;
   if (i >= 0) {
     anchor_task<D, T, G>(a, a.tasks[a.n_span_tasks + i], sh.ml);
     return;
   }
-  if constexpr (STAGED) staged_group<D, T, G>(a, blockIdx.x, sh);
-  else unit_pass<D, T, G>(a, blockIdx.x, a.n_zoom_wgs, sh);
+  staged_group<D, T, G>(a, blockIdx.x, sh);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of its slots in
@@ -1002,37 +872,6 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
       }
     }
   }
-  if (a.upart_ml) {
-    // zoom units of the (sequence, kv head)'s span tasks: one contiguous range
-    const int2 bt = a.bg_tasks[(size_t)b * a.Hkv + g];
-    const int v0 = a.upre[bt.x], v1 = a.upre[bt.x + bt.y];
-    const int h = hq % a.G;
-    const float2* uml = reinterpret_cast<const float2*>(a.upart_ml);
-    for (int p0 = v0 + pg; p0 < v1; p0 += UN * PG) {
-      float2 ml[UN];
-      float4 v[UN];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const size_t sl = (size_t)min(p0 + u * PG, v1 - 1) * a.G + h;
-        ml[u] = uml[sl];
-        v[u] = reinterpret_cast<const float4*>(a.upart_acc + sl * D)[c4];
-      }
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        if (p0 + u * PG < v1) {
-          const float mn = fmaxf(M, ml[u].x);
-          const float ms = (mn == kNegInf) ? 0.f : mn;
-          const float x = fast_exp2(M - ms), y = fast_exp2(ml[u].x - ms);
-          L = L * x + ml[u].y * y;
-          A.x = A.x * x + v[u].x * y;
-          A.y = A.y * x + v[u].y * y;
-          A.z = A.z * x + v[u].z * y;
-          A.w = A.w * x + v[u].w * y;
-          M = mn;
-        }
-      }
-    }
-  }
   if (c4 == 0) {
     gm_s[pg] = M;
     gl_s[pg] = L;
@@ -1070,8 +909,7 @@ void launch_t(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s)
     else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1>), gd, bd, 0, s, a);
     else hipLaunchKernelGGL((k_route<D, T, G, 2>), gd, bd, 0, s, a);
   } else {
-    if (mode) hipLaunchKernelGGL((k_attend<D, T, G, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_attend<D, T, G, false>), gd, bd, 0, s, a);
+    hipLaunchKernelGGL((k_attend<D, T, G>), gd, bd, 0, s, a);
   }
 }
 
@@ -1098,9 +936,9 @@ void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArg
   else launch_d<64>(0, kv_bf16, mode, grid, a, s);
 }
 
-void launch_decode_attend(bool staged, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
-  if (d == 128) launch_d<128>(1, kv_bf16, staged ? 1 : 0, grid, a, s);
-  else launch_d<64>(1, kv_bf16, staged ? 1 : 0, grid, a, s);
+void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
+  if (d == 128) launch_d<128>(1, kv_bf16, 0, grid, a, s);
+  else launch_d<64>(1, kv_bf16, 0, grid, a, s);
 }
 
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s) {

@@ -47,15 +47,9 @@ struct LayerSched {
   std::vector<int32_t> parts_n;   // [B*Hkv]
   std::vector<int32_t> chunk;     // [B*Hkv] span rows per task
   std::vector<int32_t> first_span_task;  // [B*Hkv]
-  std::vector<int32_t> uoff;             // [span tasks] first unit entry (device store)
-  std::vector<int2> bg_tasks;            // [B*Hkv] (first span task, span tasks)
-  int64_t n_units_cap = 0;               // unit entries the span tasks can write
-  int unit_wgs = 64;                     // grid of the unit pass
   int max_parts = 0;
   int4* tasks_d = nullptr;
   int32_t* parts_d = nullptr;
-  int32_t* uoff_d = nullptr;      // [tasks_cap]
-  int2* bg_tasks_d = nullptr;     // [B*Hkv]
   size_t tasks_cap = 0;
   int4* tasks_pin = nullptr;      // pinned staging of the uploads
   int32_t* parts_pin = nullptr;
@@ -129,14 +123,6 @@ struct sekv_ctx {
   size_t parts_cap = 0;  // partial slots
 
   uint8_t* mask_d = nullptr;    // [B*Hq*m_max] used when the caller passes no mask
-  // device-store unit pass (sized for the largest schedule so far)
-  int4* uent_d = nullptr;
-  float* upart_ml = nullptr;
-  float* upart_acc = nullptr;
-  size_t units_cap = 0;
-  int32_t* zunits_d = nullptr;
-  int32_t* upre_d = nullptr;
-  size_t ztasks_cap = 0;
   size_t zcap = 0;              // spans capacity B*Hkv*m_max of the buffers above
 
   // HOST-home fetch path: flat list, staged items, groups per span task
@@ -247,8 +233,6 @@ void free_layer(LayerState& L) {
   dfree(L.bases_d);
   hfree(L.bases_h);
   dfree(L.sched.tasks_d);
-  dfree(L.sched.uoff_d);
-  dfree(L.sched.bg_tasks_d);
   dfree(L.sched.parts_d);
   dfree(L.sched.zstat_d);
   hfree(L.sched.tasks_pin);
@@ -514,24 +498,14 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
 
 // Task table of a layer from the per-row zoom estimates.
 void plan_tasks(sekv_ctx* c, LayerSched& S) {
-  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv, d = c->cfg.d_head;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
   const bool dev = c->cfg.basis_home == SEKV_BASES_DEVICE;
-  int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
+  const int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
   const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
   const double zpw = env_int("SEKV_ZOOM_PER_TASK", 4, 1, 256);
-  // device store: the unit pass balances the zoom work, one slot per span task;
-  // host store: a span task's zoomed spans go to its second slot, and zoom-heavy
-  // rows get smaller chunks
+  // device store: a span task folds its zoomed spans into its one slot; host
+  // store: they go to its second slot (written by the attend kernel)
   const int per_span = dev ? 1 : 2;
-  {
-    int64_t ntask = 0;
-    for (int bg = 0; bg < BH; ++bg) ntask += (c->m_b[bg / Hkv] + base - 1) / base;
-    while (dev && ntask > kMaxSpanTasks && base < kMaxSpanChunk) {
-      base = std::min(kMaxSpanChunk, base * 2);
-      ntask = 0;
-      for (int bg = 0; bg < BH; ++bg) ntask += (c->m_b[bg / Hkv] + base - 1) / base;
-    }
-  }
   S.chunk.assign(BH, base);
   S.parts_n.assign(BH, 0);
   S.first_span_task.assign(BH, 0);
@@ -558,23 +532,13 @@ void plan_tasks(sekv_ctx* c, LayerSched& S) {
   }
   std::stable_sort(order.begin(), order.end());
   S.tasks.clear();
-  S.uoff.clear();
-  S.bg_tasks.assign(BH, make_int2(0, 0));
   S.max_parts = 1;
   for (int bg = 0; bg < BH; ++bg) S.max_parts = std::max(S.max_parts, S.parts_n[bg]);
-  int64_t ucap = 0;
   for (auto& o : order) {  // span chunks, the most zoom-heavy rows first
-    const int bg = o.second, b = bg / Hkv;
+    const int bg = o.second;
     S.first_span_task[bg] = (int)S.tasks.size();
-    S.bg_tasks[bg] = make_int2((int)S.tasks.size(), nspan[bg]);
-    for (int j = 0; j < nspan[bg]; ++j) {
-      const int k0 = j * S.chunk[bg], k1 = std::min(c->m_b[b], k0 + S.chunk[bg]);
-      S.tasks.push_back(make_int4(bg, k0, S.chunk[bg], per_span * j));
-      S.uoff.push_back((int32_t)ucap);
-      for (int k = k0; k < k1; ++k) ucap += (c->mcount[b][k] + d - 1) / d;  // token tiles of d tokens
-    }
+    for (int j = 0; j < nspan[bg]; ++j) S.tasks.push_back(make_int4(bg, j * S.chunk[bg], S.chunk[bg], per_span * j));
   }
-  S.n_units_cap = ucap;
   S.n_span_tasks = (int)S.tasks.size();
   int amax = 0;
   for (int bg = 0; bg < BH; ++bg) amax = std::max(amax, nanch[bg]);
@@ -582,12 +546,6 @@ void plan_tasks(sekv_ctx* c, LayerSched& S) {
     for (int bg = 0; bg < BH; ++bg)
       if (j < nanch[bg])
         S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg], anch[bg], per_span * nspan[bg] + j));
-  // unit-pass grid: about one unit per wave at the measured zoom load
-  double est_units = 0.0;
-  for (int bg = 0; bg < BH; ++bg) est_units += S.est[bg];
-  const double upw = env_int("SEKV_UNITS_PER_WAVE", 1, 1, 64);
-  S.unit_wgs = std::max(64, std::min(env_int("SEKV_UNIT_WGS_MAX", 2048, 1, 65536),
-                                     (int)std::ceil(est_units / (upw * kWaves))));
 }
 
 // Refresh a layer's schedule before a launch on `stream`.  `pending` means a
@@ -629,36 +587,11 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
     return SEKV_OK;
   if (S.tasks.size() > S.tasks_cap) {
     dfree(S.tasks_d);
-    dfree(S.uoff_d);
     hfree(S.tasks_pin);
     S.tasks_cap = 0;
     TRY(dalloc(c, &S.tasks_d, S.tasks.size() * sizeof(int4)));
-    TRY(dalloc(c, &S.uoff_d, S.tasks.size() * sizeof(int32_t)));
     TRY(halloc(c, &S.tasks_pin, S.tasks.size() * sizeof(int4)));
     S.tasks_cap = S.tasks.size();
-  }
-  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
-    if (S.n_span_tasks > kMaxSpanTasks) return fail(c, SEKV_ERR_INVALID, "too many span tasks for the zoom unit pass");
-    if ((size_t)S.n_span_tasks + 1 > c->ztasks_cap) {
-      dfree(c->zunits_d);
-      dfree(c->upre_d);
-      c->ztasks_cap = 0;
-      TRY(dalloc(c, &c->zunits_d, ((size_t)S.n_span_tasks + 1) * 4));
-      TRY(dalloc(c, &c->upre_d, ((size_t)S.n_span_tasks + 1) * 4));
-      c->ztasks_cap = (size_t)S.n_span_tasks + 1;
-    }
-    if ((size_t)S.n_units_cap > c->units_cap || !c->uent_d) {
-      dfree(c->uent_d);
-      dfree(c->upart_ml);
-      dfree(c->upart_acc);
-      c->units_cap = 0;
-      const size_t cap = (size_t)S.n_units_cap;
-      TRY(dalloc(c, &c->uent_d, cap * sizeof(int4)));
-      TRY(dalloc(c, &c->upart_ml, cap * c->G * 2 * sizeof(float)));
-      TRY(dalloc(c, &c->upart_acc, cap * c->G * c->cfg.d_head * sizeof(float)));
-      c->units_cap = cap;
-    }
-    if (!S.bg_tasks_d) TRY(dalloc(c, &S.bg_tasks_d, (size_t)BH * sizeof(int2)));
   }
   if (!S.parts_d) {
     TRY(dalloc(c, &S.parts_d, (size_t)BH * 4));
@@ -667,11 +600,6 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   std::memcpy(S.tasks_pin, S.tasks.data(), S.tasks.size() * sizeof(int4));
   std::memcpy(S.parts_pin, S.parts_n.data(), (size_t)BH * 4);
   HIPCHK(c, hipMemcpyAsync(S.tasks_d, S.tasks_pin, S.tasks.size() * sizeof(int4), hipMemcpyHostToDevice, stream));
-  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
-    // small static tables: synchronous copies (no pinned staging kept for them)
-    if (!S.uoff.empty()) HIPCHK(c, hipMemcpy(S.uoff_d, S.uoff.data(), S.uoff.size() * 4, hipMemcpyHostToDevice));
-    HIPCHK(c, hipMemcpy(S.bg_tasks_d, S.bg_tasks.data(), (size_t)BH * sizeof(int2), hipMemcpyHostToDevice));
-  }
   HIPCHK(c, hipMemcpyAsync(S.parts_d, S.parts_pin, (size_t)BH * 4, hipMemcpyHostToDevice, stream));
   S.valid = true;
   return SEKV_OK;
@@ -726,11 +654,6 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.zstat = L.sched.zstat_d;
   a.zlist = c->zlist_d;
   a.zcounter = c->zcounter_d;
-  a.uoff = L.sched.uoff_d;
-  a.uent = c->uent_d;
-  a.zunits = c->zunits_d;
-  a.upre = c->upre_d;
-  a.bg_tasks = L.sched.bg_tasks_d;
 }
 
 sekv_status thetas(sekv_ctx* c, const float* tau, DecodeArgs& a) {
@@ -831,11 +754,6 @@ void sekv_destroy(sekv_ctx* c) {
   dfree(c->zlist_d);
   dfree(c->zcounter_d);
   dfree(c->mask_d);
-  dfree(c->uent_d);
-  dfree(c->upart_ml);
-  dfree(c->upart_acc);
-  dfree(c->zunits_d);
-  dfree(c->upre_d);
   dfree(c->zitems_d);
   dfree(c->zgroups_d);
   hfree(c->zlist_h);
@@ -1093,7 +1011,7 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
     a.zgroups = c->zgroups_d;
     a.staging = c->staging;
     a.n_zoom_wgs = ng;
-    launch_decode_attend(true, ng + (a.n_tasks - a.n_span_tasks), d, c->bf16, a, stream);
+    launch_decode_attend(ng + (a.n_tasks - a.n_span_tasks), d, c->bf16, a, stream);
     HIPCHK(c, hipGetLastError());
   }
   launch_decode_combine(d, a, stream);

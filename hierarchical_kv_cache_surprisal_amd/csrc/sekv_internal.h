@@ -14,7 +14,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxParts = 512;  // split-K partial slots per (sequence, query head)
 constexpr int kCombineThreads = 512;
 constexpr int kMaxSpanChunk = 256;  // span rows per span task
-constexpr int kMaxSpanTasks = 8192; // span tasks per layer (device-store zoom units)
 
 // Every packed basis block starts on a multiple of 8 elements (16 bytes for
 // bf16), so wide loads stay aligned.
@@ -48,15 +47,7 @@ struct DecodeArgs {
   int32_t* zstat;         // [B*Hkv] cumulative zoomed spans of this layer (scheduling statistics)
   float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
   float* part_acc;        // [B][Hq][max_parts][d]
-  // device store: zoom units (one token tile of a zoomed span each)
-  const int32_t* uoff;     // [n_span_tasks] first entry of each span task in uent
-  int4* uent;              // unit entries (head bits, basis offset / 8, rank | count << 8, first token)
-  int32_t* zunits;         // [n_span_tasks] units of each span task
-  int32_t* upre;           // [n_span_tasks + 1] units before each span task (from the units kernel)
-  float* upart_ml;         // [units][G][2] partial of each unit and head (NULL: no unit pass)
-  float* upart_acc;        // [units][G][d]
-  const int2* bg_tasks;    // [B*Hkv] (first span task, span tasks) of each (sequence, kv head)
-  int n_zoom_wgs;          // zoom workgroups at the front of the attend grid
+  int n_zoom_wgs;          // host store: fetched groups at the front of the attend grid
   // host fetch path: flat list (bg | head bits << 24, span, basis offset / 8, rank | count << 8)
   int4* zlist;
   int32_t* zcounter;      // its length (reset by the combine kernel)
@@ -66,13 +57,14 @@ struct DecodeArgs {
   double theta[kMaxHq];   // logit(tau) per query head
 };
 
-// span tasks, grid = span tasks.  mode 0: zoom units to the task table
-// (DEVICE bases); 1: zoomed spans to the flat list (HOST bases); 2: routing
-// scores only
+// mode 0 (DEVICE bases): span tasks with their zoomed spans in place, and the
+// anchor tasks, grid = tasks.  mode 1 (HOST bases): span tasks, zoomed spans
+// to the flat list, grid = span tasks.  mode 2: routing scores of the span
+// tasks only, grid = span tasks
 void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
-// n_zoom_wgs zoom workgroups (staged: one per fetched group; else the unit
-// pass, n_zoom_wgs >= 1), then the anchor tasks; grid = n_zoom_wgs + anchor tasks
-void launch_decode_attend(bool staged, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// HOST bases: n_zoom_wgs workgroups for the fetched groups, then the anchor
+// tasks; grid = n_zoom_wgs + anchor tasks
+void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
 // log-sum-exp merge of every (sequence, query head) into out; resets the counters
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s);
 
