@@ -65,15 +65,17 @@ typedef enum sekv_dtype { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
  *           the zoomed spans' bases into a device staging buffer on a side
  *           stream before the zoomed segment runs (one host sync per step).
  * DEVICE -- device memory (the whole store fits in HBM on MI355X at 128K
- *           context): the decode step is fully device-side, one kernel. */
+ *           context): the decode step is fully device-side and asynchronous,
+ *           two kernels (attention with in-place zoom, then the combine), and
+ *           can be captured into a HIP graph. */
 typedef enum sekv_basis_home { SEKV_BASES_HOST = 0, SEKV_BASES_DEVICE = 1 } sekv_basis_home;
 
 typedef struct sekv_config {
   int32_t n_layers;     /* L >= 1 */
   int32_t batch;        /* B >= 1 independent sequences */
-  int32_t n_ctx;        /* n >= 1 tokens per sequence */
-  int32_t n_q_heads;    /* H_q, a multiple of n_kv_heads, H_q/H_kv <= 8 */
-  int32_t n_kv_heads;   /* H_kv >= 1 */
+  int32_t n_ctx;        /* 1 <= n < 2^24 tokens per sequence */
+  int32_t n_q_heads;    /* H_q <= 64, a multiple of n_kv_heads, H_q/H_kv in {1, 2, 4, 8} */
+  int32_t n_kv_heads;   /* H_kv >= 1, batch * H_kv <= 512 */
   int32_t d_head;       /* 64 or 128 */
   int32_t kv_dtype;     /* sekv_dtype */
   int32_t local_window; /* w >= 0: the last w positions are anchors */
@@ -150,12 +152,15 @@ sekv_status sekv_get_bases_layout(const sekv_ctx* ctx, int32_t layer, int32_t b,
  *   out       dev float32 [B][H_q][d]: attention output
  *   zoom_mask dev uint8 [B][H_q][m_max] or NULL: 1 where the head zoomed the
  *             span; entries at or beyond the sequence's m are left untouched.
- * DEVICE bases: fully asynchronous on `stream` (one kernel).
+ * DEVICE bases: fully asynchronous on `stream` (two kernels); capturable into
+ * a HIP graph once the layer has been decoded eagerly (the first calls size
+ * the work schedule from the zoom counts they measure).
  * HOST bases: route kernel, then the zoomed spans' bases are copied from the
  * pinned store to device staging on the context's side stream (see
- * sekv_zoom_fetch), then the zoomed-segment kernel; synchronises `stream`
- * once, after routing.
- * Errors: STATE (layer not built), INVALID, HIP. */
+ * sekv_zoom_fetch), then the zoomed-segment and anchor kernel and the
+ * combine; synchronises `stream` once, after routing.
+ * Errors: STATE (layer not built, or a graph capture before the first eager
+ * call), INVALID, HIP. */
 sekv_status sekv_decode_attn(sekv_ctx* ctx, int32_t layer, const float* q, const float* tau,
                              float* out, uint8_t* zoom_mask, hipStream_t stream);
 
