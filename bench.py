@@ -14,7 +14,8 @@ layer-step (anchors, summaries, zoomed spans' bases, q/out/mask), timed with
 HIP events around a graph replay of every step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --home host ...          # bases in pinned host memory: PCIe-inclusive rate
+    python bench.py --home host ...          # bases in pinned host memory, read in place: PCIe-inclusive rate
+    python bench.py --home host_staged ...   # bases in pinned host memory, zoomed spans copied to staging per step
     python bench.py --copy-calibration ...   # also runs a 1 GiB device copy (counter scaling)
     python bench.py --traffic-from FETCH_DIR WRITE_DIR   # rocprofv3 --pmc runs -> profiles/decode_traffic.json
 """
@@ -51,7 +52,7 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=4, help="kv heads in the CPU-baseline sample")
     p.add_argument("--cpu-steps", type=int, default=160, help="decode steps in the CPU-baseline sample")
     p.add_argument("--calib-steps", type=int, default=8)
-    p.add_argument("--home", choices=("device", "host"), default="device")
+    p.add_argument("--home", choices=("device", "host", "host_staged"), default="device")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args()
@@ -269,7 +270,7 @@ def main():
 
     # ------------------------------------------------------------------ timed region
     graph = None
-    if not args.no_graph and args.home == "device":  # host-resident bases sync each call: no graph
+    if not args.no_graph and args.home != "host_staged":  # staged bases sync each call: no graph
         try:
             g = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()

@@ -73,7 +73,8 @@ struct LayerState {
   int64_t* boff_d = nullptr;
   int2* smeta_d = nullptr;  // [B*Hkv*m_max] {boff / 8, rank | count << 8} for the decode kernels
   void* bases_d = nullptr;  // DEVICE home (and build scratch for HOST home)
-  void* bases_h = nullptr;  // HOST home: pinned store
+  void* bases_h = nullptr;  // host homes: pinned store
+  void* bases_hd = nullptr; // its device-side address (the kernels read it in place)
   int64_t basis_elems = 0;
   std::vector<int32_t> rank_h;     // [B*Hkv*m_max]
   std::vector<int64_t> boff_h;     // [B*Hkv*m_max], relative to the layer store
@@ -145,6 +146,13 @@ struct sekv_ctx {
 };
 
 namespace {
+
+// The basis store lives in pinned host memory (read in place by the decode
+// kernels, or copied to staging per step).
+bool host_store(const sekv_ctx* c) {
+  return c->cfg.basis_home == SEKV_BASES_HOST || c->cfg.basis_home == SEKV_BASES_HOST_STAGED;
+}
+bool staged(const sekv_ctx* c) { return c->cfg.basis_home == SEKV_BASES_HOST_STAGED; }
 
 sekv_status fail(sekv_ctx* c, sekv_status s, const std::string& msg) {
   if (c) c->err = msg;
@@ -370,7 +378,10 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
     HIPCHK(c, hipMemcpy(L.smeta_d, meta.data(), rows_m * sizeof(int2), hipMemcpyHostToDevice));
   }
   TRY(dalloc(c, &L.bases_d, (size_t)off * c->esz));
-  if (c->cfg.basis_home == SEKV_BASES_HOST) TRY(halloc(c, &L.bases_h, (size_t)off * c->esz));
+  if (host_store(c)) {
+    TRY(halloc(c, &L.bases_h, (size_t)off * c->esz));
+    HIPCHK(c, hipHostGetDevicePointer(&L.bases_hd, L.bases_h, 0));
+  }
   L.allocated = true;
   return SEKV_OK;
 }
@@ -398,7 +409,7 @@ sekv_status ensure_zoom_buffers(sekv_ctx* c) {
   hfree(c->zgroups_h);
   c->zcap = 0;
   TRY(dalloc(c, &c->mask_d, spans * c->G));
-  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+  if (host_store(c)) {  // sekv_zoom_fetch works for both host homes
     TRY(dalloc(c, &c->zlist_d, spans * sizeof(int4)));
     TRY(dalloc(c, &c->zitems_d, spans * sizeof(int4)));
     TRY(dalloc(c, &c->zgroups_d, spans * sizeof(int4)));
@@ -499,13 +510,12 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
 // Task table of a layer from the per-row zoom estimates.
 void plan_tasks(sekv_ctx* c, LayerSched& S) {
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
-  const bool dev = c->cfg.basis_home == SEKV_BASES_DEVICE;
   const int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
   const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
   const double zpw = env_int("SEKV_ZOOM_PER_TASK", 4, 1, 256);
-  // device store: a span task folds its zoomed spans into its one slot; host
-  // store: they go to its second slot (written by the attend kernel)
-  const int per_span = dev ? 1 : 2;
+  // a span task folds its zoomed spans into its one slot; with staged bases
+  // they go to its second slot (written by the attend kernel)
+  const int per_span = staged(c) ? 2 : 1;
   S.chunk.assign(BH, base);
   S.parts_n.assign(BH, 0);
   S.first_span_task.assign(BH, 0);
@@ -695,7 +705,7 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   if (k.d_head != 64 && k.d_head != 128) return fail(nullptr, SEKV_ERR_INVALID, "d_head must be 64 or 128");
   if (k.kv_dtype != SEKV_F32 && k.kv_dtype != SEKV_BF16) return fail(nullptr, SEKV_ERR_INVALID, "bad kv_dtype");
   if (k.local_window < 0) return fail(nullptr, SEKV_ERR_INVALID, "local_window must be >= 0");
-  if (k.basis_home != SEKV_BASES_HOST && k.basis_home != SEKV_BASES_DEVICE)
+  if (k.basis_home != SEKV_BASES_HOST && k.basis_home != SEKV_BASES_DEVICE && k.basis_home != SEKV_BASES_HOST_STAGED)
     return fail(nullptr, SEKV_ERR_INVALID, "bad basis_home");
   if (k.n_ctx >= (1 << 24)) return fail(nullptr, SEKV_ERR_INVALID, "n_ctx must be < 2^24");
   int ndev = 0;
@@ -889,12 +899,12 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
     HIPCHK(c, hipGetLastError());
   }
   // 5. HOST home: move the store to pinned memory
-  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+  if (host_store(c)) {
     HIPCHK(c, hipMemcpyAsync(L.bases_h, L.bases_d, (size_t)L.basis_elems * c->esz, hipMemcpyDeviceToHost,
                              stream));
   }
   HIPCHK(c, hipStreamSynchronize(stream));
-  if (c->cfg.basis_home == SEKV_BASES_HOST) dfree(L.bases_d);
+  if (host_store(c)) dfree(L.bases_d);
   std::fill(L.head_set.begin(), L.head_set.end(), 1);
   L.ready = true;
   return SEKV_OK;
@@ -940,7 +950,7 @@ sekv_status sekv_zoom_fetch(sekv_ctx* c, int32_t layer, const int32_t* entries, 
   if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
   DevGuard dg(c->cfg.device);
   TRY(check_layer(c, layer));
-  if (c->cfg.basis_home != SEKV_BASES_HOST) return fail(c, SEKV_ERR_STATE, "bases are device-resident");
+  if (!host_store(c)) return fail(c, SEKV_ERR_STATE, "bases are device-resident");
   if (!entries || !counts) return fail(c, SEKV_ERR_INVALID, "NULL entries or counts");
   TRY(ensure_zoom_buffers(c));
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, mm = c->m_max;
@@ -984,8 +994,10 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   a.part_acc = c->part_acc;
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
-  if (c->cfg.basis_home == SEKV_BASES_DEVICE) {
-    // span tasks with their zoomed spans in place, and the anchor tasks
+  if (!staged(c)) {
+    // span tasks with their zoomed spans in place (bases in HBM, or read from
+    // the pinned host store over the link), and the anchor tasks
+    if (host_store(c)) a.bases = L.bases_hd;
     launch_decode_route(0, a.n_tasks, d, c->bf16, a, stream);
     HIPCHK(c, hipGetLastError());
   } else {
@@ -1092,7 +1104,7 @@ sekv_status sekv_import_layout(sekv_ctx* c, int32_t layer, const int32_t* rank) 
         rk[i] = rank[i];
       }
   TRY(alloc_layer(c, layer, rk));
-  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+  if (host_store(c)) {
     LayerState& L = c->layers[layer];
     std::memset(L.bases_h, 0, (size_t)L.basis_elems * c->esz);
     dfree(L.bases_d);
@@ -1133,7 +1145,7 @@ sekv_status sekv_import_head(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, c
     HIPCHK(c, hipMemcpy((char*)L.KA + bg * c->na_max * d * es, KA, (size_t)na * d * es, hipMemcpyHostToDevice));
     HIPCHK(c, hipMemcpy((char*)L.VA + bg * c->na_max * d * es, VA, (size_t)na * d * es, hipMemcpyHostToDevice));
   }
-  if (c->cfg.basis_home == SEKV_BASES_HOST) {
+  if (host_store(c)) {
     std::memcpy((char*)L.bases_h + L.head_base[bg] * es, bases, (size_t)he * es);
   } else {
     HIPCHK(c, hipMemcpy((char*)L.bases_d + L.head_base[bg] * es, bases, (size_t)he * es, hipMemcpyHostToDevice));
@@ -1163,7 +1175,7 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
   if (rank) std::memcpy(rank, L.rank_h.data() + bg * mm, (size_t)m * 4);
   if (bases) {
     const int64_t he = L.head_base[bg + 1] - L.head_base[bg];
-    if (c->cfg.basis_home == SEKV_BASES_HOST)
+    if (host_store(c))
       std::memcpy(bases, (char*)L.bases_h + L.head_base[bg] * es, (size_t)he * es);
     else
       HIPCHK(c, hipMemcpy(bases, (char*)L.bases_d + L.head_base[bg] * es, (size_t)he * es, hipMemcpyDeviceToHost));

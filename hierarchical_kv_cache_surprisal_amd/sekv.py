@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libsekv.so")
 
 SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_OOM, SEKV_ERR_HIP, SEKV_ERR_STATE = range(5)
 SEKV_F32, SEKV_BF16 = 0, 1
-SEKV_BASES_HOST, SEKV_BASES_DEVICE = 0, 1
+SEKV_BASES_HOST, SEKV_BASES_DEVICE, SEKV_BASES_HOST_STAGED = 0, 1, 2
 _STATUS = {0: "OK", 1: "INVALID", 2: "OOM", 3: "HIP", 4: "STATE"}
 
 EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sekv_get_spans",
@@ -230,7 +230,8 @@ class Context:
         self.d = d_head
         self.B, self.Hq, self.Hkv, self.L, self.n = batch, n_q_heads, n_kv_heads, n_layers, n_ctx
         dt = {"f32": SEKV_F32, "bf16": SEKV_BF16}[kv_dtype]
-        home = {"host": SEKV_BASES_HOST, "device": SEKV_BASES_DEVICE}[basis_home]
+        home = {"host": SEKV_BASES_HOST, "device": SEKV_BASES_DEVICE,
+                "host_staged": SEKV_BASES_HOST_STAGED}[basis_home]
         self.ptr = sekv_create(n_layers, batch, n_ctx, n_q_heads, n_kv_heads, d_head, dt, local_window,
                                home, device)
 

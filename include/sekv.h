@@ -61,14 +61,23 @@ typedef enum sekv_status {
 typedef enum sekv_dtype { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
 
 /* Where the per-span SVD bases live between decode steps.
- * HOST   -- pinned host memory (the pages' CPU tier): every decode step copies
- *           the zoomed spans' bases into a device staging buffer on a side
- *           stream before the zoomed segment runs (one host sync per step).
- * DEVICE -- device memory (the whole store fits in HBM on MI355X at 128K
- *           context): the decode step is fully device-side and asynchronous,
- *           two kernels (attention with in-place zoom, then the combine), and
- *           can be captured into a HIP graph. */
-typedef enum sekv_basis_home { SEKV_BASES_HOST = 0, SEKV_BASES_DEVICE = 1 } sekv_basis_home;
+ * HOST        -- pinned host memory (the pages' CPU tier), read in place by the
+ *                decode kernel: only the zoomed spans' bytes cross the host
+ *                link, and the step stays asynchronous (two kernels) and
+ *                capturable into a HIP graph.
+ * DEVICE      -- device memory (the whole store fits in HBM on MI355X at 128K
+ *                context): the decode step is fully device-side and
+ *                asynchronous, two kernels (attention with in-place zoom, then
+ *                the combine), and capturable into a HIP graph.
+ * HOST_STAGED -- pinned host memory; every decode step learns the zoom list
+ *                (one host sync), copies the zoomed spans' bases into a device
+ *                staging buffer on a side stream (sekv_zoom_fetch), then runs
+ *                the zoomed segment from staging. */
+typedef enum sekv_basis_home {
+  SEKV_BASES_HOST = 0,
+  SEKV_BASES_DEVICE = 1,
+  SEKV_BASES_HOST_STAGED = 2
+} sekv_basis_home;
 
 typedef struct sekv_config {
   int32_t n_layers;     /* L >= 1 */
@@ -152,11 +161,11 @@ sekv_status sekv_get_bases_layout(const sekv_ctx* ctx, int32_t layer, int32_t b,
  *   out       dev float32 [B][H_q][d]: attention output
  *   zoom_mask dev uint8 [B][H_q][m_max] or NULL: 1 where the head zoomed the
  *             span; entries at or beyond the sequence's m are left untouched.
- * DEVICE bases: fully asynchronous on `stream` (two kernels); capturable into
- * a HIP graph once the layer has been decoded eagerly (the first calls size
- * the work schedule from the zoom counts they measure).
- * HOST bases: route kernel, then the zoomed spans' bases are copied from the
- * pinned store to device staging on the context's side stream (see
+ * DEVICE and HOST bases: fully asynchronous on `stream` (two kernels);
+ * capturable into a HIP graph once the layer has been decoded eagerly (the
+ * first calls size the work schedule from the zoom counts they measure).
+ * HOST_STAGED bases: route kernel, then the zoomed spans' bases are copied
+ * from the pinned store to device staging on the context's side stream (see
  * sekv_zoom_fetch), then the zoomed-segment and anchor kernel and the
  * combine; synchronises `stream` once, after routing.
  * Errors: STATE (layer not built, or a graph capture before the first eager

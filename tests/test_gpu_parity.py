@@ -136,7 +136,7 @@ def _check_build(s, ctx, segs, arts, layer, H, K, V, heads=None, span_sample=Non
 
 # ============================================================================ tiny
 
-@pytest.mark.parametrize("home", ["device", "host"])
+@pytest.mark.parametrize("home", ["device", "host", "host_staged"])
 def test_tiny_fp32_all_zoom(home):
     s = synth.spec("tiny")
     H, K, V = _inputs(s)
@@ -183,7 +183,7 @@ def _small_bf16():
     return synth.spec("single_layer_32k").replace(n=4096, Hq=8, Hkv=8, steps=6)
 
 
-@pytest.mark.parametrize("home", ["device", "host"])
+@pytest.mark.parametrize("home", ["device", "host", "host_staged"])
 def test_small_bf16_decode_on_oracle_artefacts(home):
     s = _small_bf16()
     H, K, V = _inputs(s)
@@ -196,9 +196,11 @@ def test_small_bf16_decode_on_oracle_artefacts(home):
     T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
     worst, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
     assert nz > 0
-    if home == "host":
-        st = ctx.stats()
-        assert st["spans_fetched"] > 0 and st["bytes_fetched"] > 0 and st["host_basis_bytes"] > 0
+    st = ctx.stats()
+    if home == "host_staged":
+        assert st["spans_fetched"] > 0 and st["bytes_fetched"] > 0
+    if home != "device":
+        assert st["host_basis_bytes"] > 0
 
 
 def test_small_bf16_no_zoom_and_all_zoom():
@@ -227,7 +229,7 @@ def _gqa_small():
     return synth.spec("gqa_batch8_128k").replace(B=3, Hq=8, Hkv=2, n=6000, steps=3)
 
 
-@pytest.mark.parametrize("home", ["device", "host"])
+@pytest.mark.parametrize("home", ["device", "host", "host_staged"])
 def test_gqa_ragged_batch_decode_and_build(home):
     s = _gqa_small()
     H, K, V = _inputs(s)
