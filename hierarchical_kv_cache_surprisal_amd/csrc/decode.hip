@@ -97,9 +97,17 @@ struct Geo {
 // Sum over the row slots of a wave (lanes with the same position in their slot).
 template <int LPR>
 __device__ __forceinline__ float slots_sum(float x) {
-#pragma unroll
-  for (int s = LPR; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
+  if constexpr (LPR <= 8) x += __shfl_xor(x, 8, 64);
+  if constexpr (LPR <= 16) x = xor16_sum(x);
+  if constexpr (LPR <= 32) x = xor32_sum(x);
   return x;
+}
+
+// x of the lane `off` apart (off = 8, 16 or 32).
+__device__ __forceinline__ float lane_xor(float x, int off) {
+  if (off == 16) return xor16_get(x);
+  if (off == 32) return xor32_get(x);
+  return __shfl_xor(x, off, 64);
 }
 
 template <int G>
@@ -337,12 +345,13 @@ __device__ void slots_to_lds(SoftState<G>& st, float (&acc)[G][EPL], MergeLds<D,
                              int wave, int slot, int sub) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+#pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
-      const float mo = __shfl_xor(st.m[h], off, 64);
-      const float lo = __shfl_xor(st.l[h], off, 64);
+      const float mo = lane_xor(st.m[h], off);
+      const float lo = lane_xor(st.l[h], off);
       float ao[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ao[e] = __shfl_xor(acc[h][e], off, 64);
+      for (int e = 0; e < EPL; ++e) ao[e] = lane_xor(acc[h][e], off);
       lse_merge<EPL>(st.m[h], st.l[h], acc[h], mo, lo, ao);
     }
   }

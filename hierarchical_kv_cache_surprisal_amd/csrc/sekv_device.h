@@ -70,6 +70,38 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
 
+// Exchanges with the lane 16 or 32 apart through the gfx950 lane-swap
+// instructions (VALU, no LDS round trip).  v_permlane16_swap swaps the odd
+// 16-lane rows of its first operand with the even rows of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; with both operands = x, the two results hold x and x of the partner
+// lane, in an order that depends on the lane's side.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// x of the lane 16 (32) apart.
+__device__ __forceinline__ float xor16_get(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32_get(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1..64, power of two);
 // every lane of a group ends with the group's sum.  After the two quad steps
 // all lanes of a quad hold the same value, so a mirror inside 8 (16) lanes
@@ -80,8 +112,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 
@@ -91,8 +123,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp_f<kDppXor2>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp_f<kDppMirror>(x));
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
 
