@@ -771,9 +771,9 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
   if (MODE == 0) {
     // zoomed spans in place: token-tile units over the waves, folded into the
     // wave records, then the task's one partial
+    if (threadIdx.x == 0) a.zcnt[t] = zc;  // scheduling statistics (read back by the host)
     if (zc) {
       if (hb) sh.zit[pos] = make_int3((int)hb, sh.zmeta[i].x, sh.zmeta[i].y);
-      if (threadIdx.x == 0) atomicAdd(&a.zstat[bg], zc);
       __syncthreads();
       auto item = [&](int j) -> int3 { return sh.zit[j]; };
       zoom_group<D, T, G, true>(a, bg, task.w, zc, item, reinterpret_cast<const T*>(a.bases), sh);
@@ -783,7 +783,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     return;
   }
   if (zc == 0) store_empty<D, G>(a, b, g, task.w + 1);  // the zoom slot, when nothing fills it
-  if (threadIdx.x == 0 && zc) atomicAdd(&a.zstat[bg], zc);
+  if (threadIdx.x == 0) a.zcnt[t] = zc;
   // MODE 1: list for the host fetch
   if (zc) {
     if (threadIdx.x == 0) sh.s_int[0] = atomicAdd(a.zcounter, zc);

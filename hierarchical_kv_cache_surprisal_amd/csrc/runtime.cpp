@@ -38,7 +38,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 // Work schedule of one layer's attend kernel: one task per workgroup.
 // Zoom-heavy (sequence, kv head) rows get smaller span chunks, so that a span
 // task holds about one zoomed span per wave, and go first; the zoom load of
-// each row is measured by the kernels (cumulative counters) and read back
+// each row comes from the per-task zoom counts the kernels store, read back
 // without a sync.
 struct LayerSched {
   bool valid = false;
@@ -53,12 +53,12 @@ struct LayerSched {
   size_t tasks_cap = 0;
   int4* tasks_pin = nullptr;      // pinned staging of the uploads
   int32_t* parts_pin = nullptr;
-  int32_t* zstat_d = nullptr;     // [B*Hkv] cumulative zoomed spans (device)
-  int32_t* stat_pin = nullptr;    // pinned copy
+  int32_t* zcnt_d = nullptr;      // [tasks_cap] zoomed spans of each span task in the last call
+  int32_t* stat_pin = nullptr;    // pinned copy [tasks_cap]
+  std::vector<int4> stat_tasks;   // the task table the copy in flight belongs to
   hipEvent_t ev = nullptr;        // recorded after the last statistics copy
   bool pending = false;
-  uint64_t calls = 0, calls_at_copy = 0, calls_at_read = 0;
-  std::vector<int32_t> prev;      // cumulative counts at the last read
+  uint64_t calls = 0, reads = 0;
   std::vector<double> est;        // zoomed spans per call, per row
 };
 
@@ -242,7 +242,7 @@ void free_layer(LayerState& L) {
   hfree(L.bases_h);
   dfree(L.sched.tasks_d);
   dfree(L.sched.parts_d);
-  dfree(L.sched.zstat_d);
+  dfree(L.sched.zcnt_d);
   hfree(L.sched.tasks_pin);
   hfree(L.sched.parts_pin);
   hfree(L.sched.stat_pin);
@@ -355,11 +355,8 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   TRY(dalloc(c, &L.rank_d, rows_m * 4));
   TRY(dalloc(c, &L.boff_d, rows_m * 8));
   TRY(dalloc(c, &L.smeta_d, rows_m * sizeof(int2)));
-  TRY(dalloc(c, &L.sched.zstat_d, (size_t)B * Hkv * 4));
-  HIPCHK(c, hipMemset(L.sched.zstat_d, 0, (size_t)B * Hkv * 4));
-  TRY(halloc(c, &L.sched.stat_pin, (size_t)B * Hkv * 4));
+
   HIPCHK(c, hipEventCreateWithFlags(&L.sched.ev, hipEventDisableTiming));
-  L.sched.prev.assign((size_t)B * Hkv, 0);
   L.sched.est.assign((size_t)B * Hkv, 0.0);
   HIPCHK(c, hipMemset(L.kbar, 0, rows_m * d * c->esz));
   HIPCHK(c, hipMemset(L.vbar, 0, rows_m * d * c->esz));
@@ -576,17 +573,14 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   }
   bool replan = !S.valid;
   if (S.pending && hipEventQuery(S.ev) == hipSuccess) {
+    // zoomed spans per (sequence, kv head) in the call the copy followed
     S.pending = false;
-    const uint64_t dc = S.calls_at_copy - S.calls_at_read;
-    if (dc > 0) {
-      for (int bg = 0; bg < BH; ++bg) {
-        const double per = (double)(S.stat_pin[bg] - S.prev[bg]) / (double)dc;
-        S.est[bg] = S.calls_at_read == 0 ? per : 0.5 * S.est[bg] + 0.5 * per;
-        S.prev[bg] = S.stat_pin[bg];
-      }
-      S.calls_at_read = S.calls_at_copy;
-      replan = true;
-    }
+    std::vector<double> per(BH, 0.0);
+    for (size_t t = 0; t < S.stat_tasks.size(); ++t)
+      if (S.stat_tasks[t].x >= 0) per[S.stat_tasks[t].x] += S.stat_pin[t];
+    for (int bg = 0; bg < BH; ++bg) S.est[bg] = S.reads == 0 ? per[bg] : 0.5 * S.est[bg] + 0.5 * per[bg];
+    S.reads++;
+    replan = true;
   }
   if (!replan || S.pending) return SEKV_OK;
   const std::vector<int4> old_tasks = S.tasks;
@@ -597,10 +591,14 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
     return SEKV_OK;
   if (S.tasks.size() > S.tasks_cap) {
     dfree(S.tasks_d);
+    dfree(S.zcnt_d);
     hfree(S.tasks_pin);
+    hfree(S.stat_pin);
     S.tasks_cap = 0;
     TRY(dalloc(c, &S.tasks_d, S.tasks.size() * sizeof(int4)));
+    TRY(dalloc(c, &S.zcnt_d, S.tasks.size() * sizeof(int32_t)));
     TRY(halloc(c, &S.tasks_pin, S.tasks.size() * sizeof(int4)));
+    TRY(halloc(c, &S.stat_pin, S.tasks.size() * sizeof(int32_t)));
     S.tasks_cap = S.tasks.size();
   }
   if (!S.parts_d) {
@@ -620,12 +618,11 @@ sekv_status finish_sched(sekv_ctx* c, int layer, hipStream_t stream, bool captur
   LayerSched& S = c->layers[layer].sched;
   if (capturing) return SEKV_OK;
   S.calls++;
-  if (S.pending) return SEKV_OK;
-  const int BH = c->cfg.batch * c->cfg.n_kv_heads;
-  HIPCHK(c, hipMemcpyAsync(S.stat_pin, S.zstat_d, (size_t)BH * 4, hipMemcpyDeviceToHost, stream));
+  if (S.pending || S.n_span_tasks == 0) return SEKV_OK;
+  HIPCHK(c, hipMemcpyAsync(S.stat_pin, S.zcnt_d, (size_t)S.n_span_tasks * 4, hipMemcpyDeviceToHost, stream));
   HIPCHK(c, hipEventRecord(S.ev, stream));
+  S.stat_tasks.assign(S.tasks.begin(), S.tasks.begin() + S.n_span_tasks);
   S.pending = true;
-  S.calls_at_copy = S.calls;
   return SEKV_OK;
 }
 
@@ -661,7 +658,7 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.n_span_tasks = L.sched.n_span_tasks;
   a.parts_n = L.sched.parts_d;
   a.max_parts = L.sched.max_parts;
-  a.zstat = L.sched.zstat_d;
+  a.zcnt = L.sched.zcnt_d;
   a.zlist = c->zlist_d;
   a.zcounter = c->zcounter_d;
 }

@@ -44,7 +44,7 @@ struct DecodeArgs {
   int n_tasks, n_span_tasks;
   const int32_t* parts_n; // [B*Hkv] partial slots used by each (sequence, kv head)
   int max_parts;          // partial slots per (sequence, query head) in the buffers below
-  int32_t* zstat;         // [B*Hkv] cumulative zoomed spans of this layer (scheduling statistics)
+  int32_t* zcnt;          // [n_span_tasks] zoomed spans of each span task in the last call (statistics)
   float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
   float* part_acc;        // [B][Hq][max_parts][d]
   int n_zoom_wgs;          // host store: fetched groups at the front of the attend grid
