@@ -9,7 +9,7 @@ code, table or helper with it.
 Sources (cited by page title, section and equation):
   [Summary] "SeKV：面向长上下文推理的分辨率自适应 KV Cache 与层级语义记忆"
             (long-form summary page), sections 2.1-2.3, eqs. (1), (2), (3),
-            (5), (6), (9), Figure 2.
+            (5), (6), (9), the budget rule after eq. (9), Figure 2.
   [Review]  "SeKV：支持分层语义记忆的分辨率自适应KV缓存，用于长上下文大语言模型推理"
             (review page), workflow paragraph: weighted-mean summaries with a
             log|S| pre-softmax correction sharing one softmax with the
@@ -30,6 +30,8 @@ design notes):
     a splitmix64 hash from a list of choices; r_eff = min(r_S, |S|, d).
   * a zoomed span contributes only its reconstructed tokens; a non-zoomed
     span contributes one summary entry with logit q.kbar/sqrt(d) + ln|S|.
+  * budget cap: a budget counts zoomed spans per (sequence, query head);
+    equal scores are ranked by span index, lower first.
   * stored artefacts (summaries, SVD factors) are rounded to the KV dtype
     with round-to-nearest-even; everything else is fp64.
 
@@ -286,6 +288,26 @@ def zoom_decisions(scores, theta: float) -> np.ndarray:
     return np.asarray(scores) > theta
 
 
+def capped_decisions(scores, theta: float, budget: Optional[int]) -> np.ndarray:
+    """Zoom decisions under a budget of at most `budget` spans  [Summary 2.3, after eq. (9)].
+
+    The spans that pass the threshold are ranked by their gate sigma(s_S),
+    highest first; if there are more of them than the budget, only the first
+    `budget` are zoomed.  sigma is increasing, so ranking by s_S is the same
+    order.  Reading: equal scores are ranked by span index, lower first; a
+    budget of None or below 0 means no cap.
+    """
+    z = zoom_decisions(scores, theta)
+    if budget is None or budget < 0 or int(z.sum()) <= budget:
+        return z
+    s = np.asarray(scores, dtype=np.float64)
+    cand = [k for k in range(s.size) if z[k]]
+    ranked = sorted(cand, key=lambda k: (-s[k], k))
+    out = np.zeros(s.size, dtype=bool)
+    out[ranked[:budget]] = True
+    return out
+
+
 # ----------------------------------------------------------------------------
 # decode: stage 2 mixed-resolution attention in one softmax   [Review; Summary Fig. 2, eq. (6)]
 # ----------------------------------------------------------------------------
@@ -315,11 +337,13 @@ def softmax_attend(logits, values) -> np.ndarray:
     return (p @ np.asarray(values, dtype=np.float64)) / p.sum()
 
 
-def decode_head(q, tau: float, art: HeadArtifacts) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """One decode step of one query head: (output [d], zoom mask [m], scores [m])."""
+def decode_head(q, tau: float, art: HeadArtifacts, budget: Optional[int] = None
+                ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One decode step of one query head: (output [d], zoom mask [m], scores [m]).
+    `budget` caps the zoomed spans (capped_decisions); None: no cap."""
     theta = logit_threshold(tau)
     s = route_scores(q, art.kbar, art.mcount)
-    z = zoom_decisions(s, theta)
+    z = capped_decisions(s, theta, budget)
     logits, values = mixed_entries(q, art, z)
     return softmax_attend(logits, values), z, s
 
@@ -352,8 +376,8 @@ def build_layer(H, K, V, alpha: float, w: int, layer: int, choices: Sequence[int
 
 
 def decode_layer(q, tau, arts: Dict[Tuple[int, int], HeadArtifacts], G: int,
-                 heads: Optional[Sequence[int]] = None):
-    """q [B][Hq][d], tau [Hq]; query head h reads kv head h // G.
+                 heads: Optional[Sequence[int]] = None, budget=None):
+    """q [B][Hq][d], tau [Hq], budget None or [Hq]; query head h reads kv head h // G.
     Returns dicts keyed by (b, h): output, zoom mask, scores."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, _ = q.shape
@@ -365,5 +389,6 @@ def decode_layer(q, tau, arts: Dict[Tuple[int, int], HeadArtifacts], G: int,
             key = (b, h // G)
             if key not in arts:
                 continue
-            out[(b, h)], zm[(b, h)], sc[(b, h)] = decode_head(q[b, h], float(tau[h]), arts[key])
+            cap = None if budget is None else int(budget[h])
+            out[(b, h)], zm[(b, h)], sc[(b, h)] = decode_head(q[b, h], float(tau[h]), arts[key], cap)
     return out, zm, sc

@@ -364,3 +364,62 @@ def test_zoomed_span_uses_reconstruction_not_original_tokens():
     ref = O.dense_attention(q, np.concatenate(rows_k), np.concatenate(rows_v))
     assert np.allclose(out, ref, atol=1e-12)
     assert not np.allclose(out, O.dense_attention(q, K, V), atol=1e-3)
+
+
+# ----------------------------------------------------------------------------- budget cap
+
+@pytest.mark.parametrize("case", _load("budget_hand.json")["cases"], ids=lambda c: c["name"])
+def test_budget_cap_hand_worked(case):
+    z = O.capped_decisions(np.array(case["scores"], dtype=np.float64), case["theta"], case["budget"])
+    assert sorted(np.flatnonzero(z).tolist()) == case["zoom"]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_budget_cap_is_the_top_of_the_candidates(seed):
+    """Brute-force characterisation: the kept set has min(k, c) candidates, and every
+    kept span outranks every dropped candidate (higher score, or equal score and a
+    lower index); the kept sets grow with k."""
+    rng = np.random.default_rng(seed)
+    m = int(rng.integers(1, 40))
+    # few distinct values, so that ties are common
+    s = rng.integers(-4, 5, size=m).astype(np.float64) / 2.0
+    theta = float(rng.choice([-np.inf, -1.0, 0.0, 0.75]))
+    cand = s > theta
+    prev = np.zeros(m, dtype=bool)
+    for k in range(0, m + 2):
+        z = O.capped_decisions(s, theta, k)
+        assert int(z.sum()) == min(k, int(cand.sum()))
+        assert not np.any(z & ~cand)
+        for i in np.flatnonzero(z):
+            for j in np.flatnonzero(cand & ~z):
+                assert s[i] > s[j] or (s[i] == s[j] and i < j)
+        assert np.all(z[prev]), "kept sets must be nested in k"
+        prev = z
+    assert np.array_equal(O.capped_decisions(s, theta, None), cand)
+
+
+def test_budget_cap_through_decode_head():
+    """decode_head with a budget zooms the capped set and assembles the softmax from it;
+    a budget at or above the candidate count changes nothing."""
+    rng = np.random.default_rng(5)
+    n, d, w = 300, 16, 8
+    H = rng.lognormal(0.0, 0.8, n)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    seg = O.segment(H, 0.5, w)
+    art = O.build_head(H, K, V, seg, 0, 0, [4], 3, "f64")
+    q = rng.standard_normal(d)
+    s = O.route_scores(q, art.kbar, art.mcount)
+    tau = 0.5
+    th = O.logit_threshold(tau)
+    c = int(np.sum(s > th))
+    assert c >= 3
+    o_full, z_full, _ = O.decode_head(q, tau, art)
+    o_same, z_same, _ = O.decode_head(q, tau, art, c)
+    assert np.array_equal(z_full, z_same) and np.array_equal(o_full, o_same)
+    k = c // 2
+    o_cap, z_cap, _ = O.decode_head(q, tau, art, k)
+    assert int(z_cap.sum()) == k and np.all(z_full[z_cap])
+    lg, vals = O.mixed_entries(q, art, z_cap)
+    assert np.allclose(o_cap, O.softmax_attend(lg, vals), rtol=0, atol=1e-14)
+    assert not np.allclose(o_cap, o_full)
