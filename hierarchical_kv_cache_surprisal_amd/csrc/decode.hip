@@ -540,7 +540,8 @@ template <typename T, int U>
 struct Stage {
   Raw<T> k[U], v[U];
   float ls[U];
-  int2 meta[U];  // span rows: {basis offset / 8, rank | count << 8}
+  int2 meta[U];      // span rows: {basis offset / 8, rank | count << 8}
+  uint32_t zsel[U];  // span rows under the budget cap: zoom bit of each head
 };
 
 template <int D, typename T, int G>
@@ -669,6 +670,13 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
       if (!SCORES) sg.v[u].load(Vb + (size_t)kk * D);
       sg.ls[u] = lS[kk];
       if (!SCORES) sg.meta[u] = sub == 0 ? a.smeta[(size_t)bg * a.m_max + kk] : make_int2(0, 0);
+      if (!SCORES && a.capped) {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          bits |= (a.mask[((size_t)b * a.Hq + g * G + h) * a.m_max + kk] != 0 ? 1u : 0u) << h;
+        sg.zsel[u] = bits;
+      }
     }
   };
   float qr[G][EPL];
@@ -696,11 +704,12 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
         const float score = (nrm[u] > 0.f ? dp * rsqrtf(nrm[u]) * inv_sqrt_d : 0.f) + sg.ls[u];
         const int k = bs + u * RPW + slot;
         const bool ok = k < k1;
-        const bool zoom = (double)score > a.theta[g * G + h];
+        const bool zoom = (!SCORES && a.capped) ? ((sg.zsel[u] >> h) & 1u) != 0u
+                                                : (double)score > a.theta[g * G + h];
         if (ok && sub == 0) {
           const size_t mi = ((size_t)b * a.Hq + g * G + h) * a.m_max + k;
           if (SCORES) a.scores[mi] = score;
-          else a.mask[mi] = zoom ? 1 : 0;
+          else if (!a.capped) a.mask[mi] = zoom ? 1 : 0;
         }
         if (zoom) zbits[u] |= 1u << h;
         lg[u] = (ok && !zoom) ? dp * c2 + sg.ls[u] * kLog2e : kNegInf;
@@ -909,6 +918,148 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   if (bh == 0 && threadIdx.x == 0 && a.zcounter) *a.zcounter = 0;
 }
 
+// ------------------------------------------------------------------ budget cap
+
+// Summary page, section 2.3 (after eq. (9)): when more spans pass a head's
+// threshold than its budget k allows, the k with the highest relevance are
+// kept.  The gate is monotone in the routing score, so the order is the score
+// order; equal scores go to the lower span index.  One workgroup per
+// (sequence, query head) takes the decisions from the scores of the routing
+// pass and writes them to the zoom mask, which the route kernel then follows:
+//   1. c = #{score > theta}; if c <= k every candidate is kept;
+//   2. otherwise a radix select (four 8-bit digits of an order-preserving key,
+//      histograms in LDS) finds the k-th largest candidate key u* and how many
+//      candidates with key u* are kept (need);
+//   3. a scan in span order finds the index of the need-th candidate with key
+//      u*; the kept set is {key > u*} plus {key = u*, index <= that index}.
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
+
+// Order-preserving map of a non-NaN float to uint32 (-0 taken as +0).
+__device__ __forceinline__ uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s == 0.f ? 0.f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup (every thread passes x); *total gets the sum.
+__device__ int block_excl_scan(int x, int* red, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int y = __shfl_up(incl, sft, 64);
+    if (lane >= sft) incl += y;
+  }
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  int before = incl - x, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelectWaves; ++w) {
+    if (w < wave) before += red[w];
+    tot += red[w];
+  }
+  __syncthreads();  // red is reused by the next scan
+  *total = tot;
+  return before;
+}
+
+__global__ __launch_bounds__(kSelectThreads) void k_select(DecodeArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ int red[kSelectWaves];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need, s_cut;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int m = a.m_b[b];
+  const int k = a.budget[h];
+  const double th = a.theta[h];
+  const float* sc = a.scores + (size_t)bh * a.m_max;
+  uint8_t* mk = a.mask + (size_t)bh * a.m_max;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  int c = 0;
+  for (int i = tid; i < m; i += kSelectThreads) c += (double)sc[i] > th ? 1 : 0;
+  int cand = 0;
+  (void)block_excl_scan(c, red, &cand);
+  if (k < 0 || cand <= k || k == 0) {
+    for (int i = tid; i < m; i += kSelectThreads) mk[i] = (k != 0 && (double)sc[i] > th) ? 1 : 0;
+    return;
+  }
+  // 2. radix select of the k-th largest candidate key, most significant digit first
+  uint32_t prefix = 0u, pmask = 0u;
+  int need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < m; i += kSelectThreads) {
+      const float s = sc[i];
+      if ((double)s > th) {
+        const uint32_t u = order_key(s);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 4l .. 4l+3; `above` counts the candidates with a larger digit
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+      const uint32_t tot = c0 + c1 + c2 + c3;
+      uint32_t suf = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += y;
+      }
+      const uint32_t above = suf - tot;
+      const uint32_t nd0 = (uint32_t)need;
+      if (above < nd0 && nd0 <= above + tot) {
+        uint32_t nd = nd0 - above;
+        int dg;
+        if (nd <= c3) dg = 3;
+        else if ((nd -= c3) <= c2) dg = 2;
+        else if ((nd -= c2) <= c1) dg = 1;
+        else { nd -= c1; dg = 0; }
+        s_prefix = prefix | ((uint32_t)(4 * lane + dg) << shift);
+        s_need = (int)nd;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    pmask |= 0xFFu << shift;
+  }
+  // 3. the need-th candidate with key u* = prefix in span order
+  const int per = (m + kSelectThreads - 1) / kSelectThreads;
+  const int i0 = min(m, tid * per), i1 = min(m, i0 + per);
+  int eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const float s = sc[i];
+    eq += ((double)s > th && order_key(s) == prefix) ? 1 : 0;
+  }
+  int total = 0;
+  const int before = block_excl_scan(eq, red, &total);
+  if (before < need && need <= before + eq) {
+    int left = need - before;
+    for (int i = i0; i < i1; ++i) {
+      const float s = sc[i];
+      if ((double)s > th && order_key(s) == prefix && --left == 0) {
+        s_cut = i;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int cut = s_cut;
+  for (int i = tid; i < m; i += kSelectThreads) {
+    const float s = sc[i];
+    bool z = false;
+    if ((double)s > th) {
+      const uint32_t u = order_key(s);
+      z = u > prefix || (u == prefix && i <= cut);
+    }
+    mk[i] = z ? 1 : 0;
+  }
+}
+
 template <int D, typename T, int G>
 void launch_t(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
   if (grid <= 0) return;
@@ -948,6 +1099,10 @@ void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArg
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
   if (d == 128) launch_d<128>(1, kv_bf16, 0, grid, a, s);
   else launch_d<64>(1, kv_bf16, 0, grid, a, s);
+}
+
+void launch_decode_select(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_select, dim3(a.B * a.Hq), dim3(kSelectThreads), 0, s, a);
 }
 
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s) {

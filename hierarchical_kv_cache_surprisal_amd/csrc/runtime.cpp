@@ -124,6 +124,7 @@ struct sekv_ctx {
   size_t parts_cap = 0;  // partial slots
 
   uint8_t* mask_d = nullptr;    // [B*Hq*m_max] used when the caller passes no mask
+  float* scores_d = nullptr;    // [B*Hq*m_max] routing scores for the budget cap
   size_t zcap = 0;              // spans capacity B*Hkv*m_max of the buffers above
 
   // HOST-home fetch path: flat list, staged items, groups per span task
@@ -405,7 +406,9 @@ sekv_status ensure_zoom_buffers(sekv_ctx* c) {
   hfree(c->zitems_h);
   hfree(c->zgroups_h);
   c->zcap = 0;
+  dfree(c->scores_d);
   TRY(dalloc(c, &c->mask_d, spans * c->G));
+  TRY(dalloc(c, &c->scores_d, spans * c->G * sizeof(float)));
   if (host_store(c)) {  // sekv_zoom_fetch works for both host homes
     TRY(dalloc(c, &c->zlist_d, spans * sizeof(int4)));
     TRY(dalloc(c, &c->zitems_d, spans * sizeof(int4)));
@@ -761,6 +764,7 @@ void sekv_destroy(sekv_ctx* c) {
   dfree(c->zlist_d);
   dfree(c->zcounter_d);
   dfree(c->mask_d);
+  dfree(c->scores_d);
   dfree(c->zitems_d);
   dfree(c->zgroups_d);
   hfree(c->zlist_h);
@@ -963,8 +967,12 @@ sekv_status sekv_zoom_fetch(sekv_ctx* c, int32_t layer, const int32_t* entries, 
   return fetch_items(c, layer, c->zitems_h, n, side, done, nullptr);
 }
 
-sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
-                             uint8_t* zoom_mask, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float* tau, const int32_t* budget,
+                        float* out, uint8_t* zoom_mask, hipStream_t stream) {
   if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
   DevGuard dg(c->cfg.device);
   TRY(check_layer(c, layer));
@@ -973,13 +981,23 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   TRY(ensure_zoom_buffers(c));
   DecodeArgs a;
   TRY(thetas(c, tau, a));  // validates tau before anything is queued
+  bool capped = false;
+  for (int h = 0; h < kMaxHq; ++h) a.budget[h] = -1;
+  if (budget)
+    for (int h = 0; h < c->cfg.n_q_heads; ++h) {
+      a.budget[h] = budget[h] < 0 ? -1 : budget[h];
+      capped |= budget[h] >= 0;
+    }
   bool capturing = false;
   TRY(prepare_sched(c, layer, stream, &capturing));
   {
     double th[kMaxHq];
+    int32_t bu[kMaxHq];
     std::memcpy(th, a.theta, sizeof(th));
+    std::memcpy(bu, a.budget, sizeof(bu));
     fill_decode_geometry(c, L, a);
     std::memcpy(a.theta, th, sizeof(th));
+    std::memcpy(a.budget, bu, sizeof(bu));
   }
   a.q = q;
   a.out = out;
@@ -991,6 +1009,16 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   a.part_acc = c->part_acc;
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
+  if (capped) {
+    // budget cap: routing scores, then the capped decisions into the mask,
+    // which the route kernel below follows
+    a.scores = c->scores_d;
+    launch_decode_route(2, a.n_span_tasks, d, c->bf16, a, stream);
+    HIPCHK(c, hipGetLastError());
+    launch_decode_select(a, stream);
+    HIPCHK(c, hipGetLastError());
+    a.capped = 1;
+  }
   if (!staged(c)) {
     // span tasks with their zoomed spans in place (bases in HBM, or read from
     // the pinned host store over the link), and the anchor tasks
@@ -1026,6 +1054,21 @@ sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const f
   launch_decode_combine(d, a, stream);
   HIPCHK(c, hipGetLastError());
   return finish_sched(c, layer, stream, capturing);
+}
+
+}  // namespace
+
+extern "C" {
+
+sekv_status sekv_decode_attn(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
+                             uint8_t* zoom_mask, hipStream_t stream) {
+  return decode_step(c, layer, q, tau, nullptr, out, zoom_mask, stream);
+}
+
+sekv_status sekv_decode_attn_budget(sekv_ctx* c, int32_t layer, const float* q, const float* tau,
+                                    const int32_t* budget, float* out, uint8_t* zoom_mask, hipStream_t stream) {
+  if (c && !budget) return fail(c, SEKV_ERR_INVALID, "budget is NULL");
+  return decode_step(c, layer, q, tau, budget, out, zoom_mask, stream);
 }
 
 sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float* scores, hipStream_t stream) {

@@ -36,7 +36,8 @@ struct DecodeArgs {
   const float* q;         // [B][Hq][d]
   float* out;             // [B][Hq][d]
   uint8_t* mask;          // [B][Hq][m_max] zoom decisions (always written)
-  float* scores;          // [B][Hq][m_max] (routing-scores mode)
+  float* scores;          // [B][Hq][m_max] (routing-scores mode; input of the budget cap)
+  int capped;             // 1: the decisions were taken by the budget cap and are read from mask
   // tasks: span (bg, first span, spans, partial slot; with host-resident bases
   // the next slot holds its zoomed spans) then anchor (bg | 1 << 31, first
   // anchor, anchors, slot)
@@ -55,6 +56,7 @@ struct DecodeArgs {
   const int4* zgroups;    // (span task, first item, items)
   const void* staging;
   double theta[kMaxHq];   // logit(tau) per query head
+  int32_t budget[kMaxHq]; // most zoomed spans per (sequence, query head); < 0: no cap
 };
 
 // mode 0 (DEVICE bases): span tasks with their zoomed spans in place, and the
@@ -67,6 +69,9 @@ void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArg
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
 // log-sum-exp merge of every (sequence, query head) into out; resets the counters
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s);
+// budget cap: zoom decisions of every (sequence, query head) from the routing
+// scores (mode 2) into mask, one workgroup each, grid = B * Hq
+void launch_decode_select(const DecodeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- build
 

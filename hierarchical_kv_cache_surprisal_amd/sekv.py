@@ -26,7 +26,8 @@ SEKV_BASES_HOST, SEKV_BASES_DEVICE, SEKV_BASES_HOST_STAGED = 0, 1, 2
 _STATUS = {0: "OK", 1: "INVALID", 2: "OOM", 3: "HIP", 4: "STATE"}
 
 EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sekv_get_spans",
-            "sekv_get_bases_layout", "sekv_decode_attn", "sekv_route_scores", "sekv_zoom_fetch",
+            "sekv_get_bases_layout", "sekv_decode_attn", "sekv_decode_attn_budget",
+            "sekv_route_scores", "sekv_zoom_fetch",
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
             "sekv_get_stats"]
 
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH):
         "sekv_get_spans": (I32, [P, I32, pI32, pI32, pI32, pI32, pI32, pI32]),
         "sekv_get_bases_layout": (I32, [P, I32, I32, I32, pI32, pI64, pI64]),
         "sekv_decode_attn": (I32, [P, I32, P, C.POINTER(C.c_float), P, P, P]),
+        "sekv_decode_attn_budget": (I32, [P, I32, P, C.POINTER(C.c_float), pI32, P, P, P]),
         "sekv_route_scores": (I32, [P, I32, P, P, P]),
         "sekv_zoom_fetch": (I32, [P, I32, pI32, pI32, P, P]),
         "sekv_import_spans": (I32, [P, I32, I32, pI32, pI32, I32, pI32]),
@@ -170,6 +172,13 @@ def sekv_decode_attn(ctx, layer: int, q, tau, out, zoom_mask=None, stream=None):
                                            _dptr(out), _dptr(zoom_mask), _stream(stream)), ctx)
 
 
+def sekv_decode_attn_budget(ctx, layer: int, q, tau, budget, out, zoom_mask=None, stream=None):
+    t = np.ascontiguousarray(tau, dtype=np.float32)
+    k = np.ascontiguousarray(budget, dtype=np.int32)
+    _check(load_library().sekv_decode_attn_budget(ctx, layer, _dptr(q), t.ctypes.data_as(C.POINTER(C.c_float)),
+                                                  _i32(k), _dptr(out), _dptr(zoom_mask), _stream(stream)), ctx)
+
+
 def sekv_route_scores(ctx, layer: int, q, scores, stream=None):
     _check(load_library().sekv_route_scores(ctx, layer, _dptr(q), _dptr(scores), _stream(stream)), ctx)
 
@@ -259,8 +268,11 @@ class Context:
     def m_max(self):
         return sekv_get_spans(self.ptr, 0)[3]
 
-    def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None):
-        sekv_decode_attn(self.ptr, layer, q, tau, out, zoom_mask, stream)
+    def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None, budget=None):
+        if budget is None:
+            sekv_decode_attn(self.ptr, layer, q, tau, out, zoom_mask, stream)
+        else:
+            sekv_decode_attn_budget(self.ptr, layer, q, tau, budget, out, zoom_mask, stream)
 
     def route_scores(self, layer, q, scores, stream=None):
         sekv_route_scores(self.ptr, layer, q, scores, stream)

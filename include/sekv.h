@@ -173,6 +173,22 @@ sekv_status sekv_get_bases_layout(const sekv_ctx* ctx, int32_t layer, int32_t b,
 sekv_status sekv_decode_attn(sekv_ctx* ctx, int32_t layer, const float* q, const float* tau,
                              float* out, uint8_t* zoom_mask, hipStream_t stream);
 
+/* sekv_decode_attn with a zoom budget per query head [summary page, section
+ * 2.3, the budget rule after eq. (9)]: when more than budget[h] spans of a
+ * sequence pass head h's threshold, only the budget[h] with the highest
+ * routing score are zoomed (the sigmoid gate is monotone in the score), equal
+ * scores going to the lower span index; the others contribute their summary
+ * entry as non-zoomed spans do.
+ *   budget host int32 [H_q]: most zoomed spans per (sequence, query head);
+ *          a negative entry leaves that head uncapped.  NULL -> INVALID.
+ * Adds two kernels before the route kernel (the routing scores, then one
+ * radix-select workgroup per (sequence, query head) writing the capped
+ * decisions to the zoom mask, or to an internal mask when zoom_mask is NULL).
+ * Other arguments, asynchrony, capture and errors as sekv_decode_attn. */
+sekv_status sekv_decode_attn_budget(sekv_ctx* ctx, int32_t layer, const float* q, const float* tau,
+                                    const int32_t* budget, float* out, uint8_t* zoom_mask,
+                                    hipStream_t stream);
+
 /* Stage-1 routing scores only [eq. (5) with the identity projection]:
  *   scores dev float32 [B][H_q][m_max] = q.kbar/(|kbar| sqrt(d)) + ln|S|
  * (ln|S| alone when kbar = 0).  Entries beyond a sequence's m are untouched.

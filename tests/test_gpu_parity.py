@@ -314,3 +314,150 @@ def test_error_paths_return_status():
         ctx2.build(1, H2, K, K, 1.0, (8,), 1)
     assert ei.value.status == sekv.SEKV_ERR_STATE
     ctx2.build(1, H, K, K, 1.0, (8,), 1)
+
+
+# ============================================================================ budget cap
+
+def _ranked(sc, th):
+    cand = np.flatnonzero(sc > th)
+    return sorted(cand.tolist(), key=lambda k: (-sc[k], k))
+
+
+def _cut_ok(sc, band, order, k, pairs):
+    """The top k of `order` is the same set under fp32 scores: the k-th and
+    (k+1)-th candidates are further apart than their tie bands, or they are a
+    constructed pair with bit-identical inputs whose neighbours are."""
+    def sep(x, y):
+        return sc[x] - sc[y] > band[x] + band[y]
+    a, b = order[k - 1], order[k]
+    if sep(a, b):
+        return True
+    if (min(a, b), max(a, b)) in pairs and sc[a] == sc[b]:
+        return (k < 2 or sep(order[k - 2], a)) and (k + 1 >= len(order) or sep(b, order[k + 1]))
+    return False
+
+
+def _pick_budget(sc, band, th, kind, pairs, rng):
+    order = _ranked(sc, th)
+    c = len(order)
+    if kind == "none":
+        return -1
+    if kind == "zero":
+        return 0
+    if kind == "loose":
+        return c + int(rng.integers(0, 3))
+    if kind == "tie":
+        for k in range(1, c):
+            a, b = order[k - 1], order[k]
+            if (min(a, b), max(a, b)) in pairs and _cut_ok(sc, band, order, k, pairs):
+                return k
+    # a binding cut near the requested fraction of the candidates
+    frac = {"half": 0.5, "quarter": 0.25, "tie": 0.5}[kind]
+    ks = [k for k in range(1, c) if _cut_ok(sc, band, order, k, pairs)]
+    assert ks, "no robust cut"
+    return min(ks, key=lambda k: abs(k - frac * c))
+
+
+@pytest.mark.parametrize("home", ["device", "host", "host_staged"])
+def test_budget_cap_decode_on_oracle_artefacts(home):
+    s = _small_bf16().replace(steps=3)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    # exact ties for query head 0: span j takes the summary of span a < j with
+    # the same member count, so both sides compute bit-identical scores for them
+    a0 = arts[(0, 0)]
+    cnt = a0.mcount
+    pairs = set()
+    big = np.argsort(-cnt, kind="stable")
+    for a in big[: max(8, a0.m // 20)]:
+        js = [j for j in np.flatnonzero(cnt == cnt[a]) if j > a and all(j not in p and a not in p for p in pairs)]
+        if js:
+            j = int(js[-1])
+            a0.kbar[j] = a0.kbar[a]
+            pairs.add((int(a), j))
+        if len(pairs) >= 4:
+            break
+    assert pairs
+    qs = _q_steps(s, 0, s.steps)
+    rates = np.array([0.3, 0.3, 0.6, 0.15, 1.0, 0.3, 0.3, 0.05])
+    taus = T.thresholds_for(qs, arts, s.G, rates, s.B)
+    kinds = ["tie", "half", "quarter", "none", "half", "zero", "loose", "quarter"]
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    m_max = ctx.m_max()
+    rng = np.random.default_rng(11)
+    tie_cuts = 0
+    for t in range(s.steps):
+        q = qs[t]
+        budgets = np.full(s.Hq, -1, np.int32)
+        for h in range(s.Hq):
+            a = arts[(0, h // s.G)]
+            th = O.logit_threshold(float(taus[h]))
+            sc = O.route_scores(q[0, h], a.kbar, a.mcount)
+            band = T.route_band(q[0, h], a.kbar, a.mcount)
+            budgets[h] = _pick_budget(sc, band, th, kinds[h], pairs if h == 0 else set(), rng)
+            if h == 0:
+                order = _ranked(sc, th)
+                k = int(budgets[h])
+                tie_cuts += int(0 < k < len(order) and sc[order[k - 1]] == sc[order[k]])
+        out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+        mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
+        ctx.decode_attn(0, torch.from_numpy(q.astype(np.float32)).to(DEV), taus, out, mask, budget=budgets)
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy().astype(np.float64)
+        mask_h = mask.cpu().numpy()
+        for h in range(s.Hq):
+            a = arts[(0, h // s.G)]
+            T.assert_no_ties(q[0, h], float(taus[h]), a)
+            o_ref, z_ref, _ = O.decode_head(q[0, h], float(taus[h]), a, int(budgets[h]))
+            assert np.array_equal(mask_h[0, h, :a.m].astype(bool), z_ref), \
+                f"capped zoom mask differs at step {t} h {h} budget {budgets[h]}"
+            assert np.all(mask_h[0, h, a.m:] == 7)
+            if budgets[h] >= 0:
+                assert int(z_ref.sum()) <= budgets[h]
+            e = T.rel_err(out_h[0, h], o_ref)
+            assert e <= 1e-4, f"step {t} h {h}: rel err {e}"
+    assert tie_cuts > 0, "no step put an exact tie at the cut"
+
+
+def test_budget_cap_all_zoom_batch_gqa():
+    """Budget with tau = 0 (every span a candidate) on a ragged GQA batch, and
+    the same call without a mask pointer."""
+    s = _gqa_small().replace(steps=1)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    q = _q_steps(s, 0, 1)[0]
+    taus = np.zeros(s.Hq, np.float32)
+    wanted = [1, 5, 40, 0, -1, 2, 17, 1000]
+    budgets = np.zeros(s.Hq, np.int32)
+    for h in range(s.Hq):
+        def robust(k):
+            for b in range(s.B):
+                a = arts[(b, h // s.G)]
+                sc = O.route_scores(q[b, h], a.kbar, a.mcount)
+                order = _ranked(sc, -math.inf)
+                if 0 < k < len(order) and not _cut_ok(sc, T.route_band(q[b, h], a.kbar, a.mcount), order, k, set()):
+                    return False
+            return True
+        # the wanted budget, or the nearest one whose cut is robust for every sequence
+        budgets[h] = min((k for k in range(-1, 2 * max(wanted)) if robust(k)), key=lambda k: abs(k - wanted[h]))
+    ctx = _ctx(s, "device")
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    m_max = ctx.m_max()
+    out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+    mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(q.astype(np.float32)).to(DEV)
+    ctx.decode_attn(0, qd, taus, out, mask, budget=budgets)
+    out2 = torch.zeros_like(out)
+    ctx.decode_attn(0, qd, taus, out2, None, budget=budgets)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    out_h = out.cpu().numpy().astype(np.float64)
+    mask_h = mask.cpu().numpy()
+    for b in range(s.B):
+        for h in range(s.Hq):
+            a = arts[(b, h // s.G)]
+            o_ref, z_ref, _ = O.decode_head(q[b, h], 0.0, a, int(budgets[h]))
+            assert np.array_equal(mask_h[b, h, :a.m].astype(bool), z_ref), f"b {b} h {h}"
+            assert np.all(mask_h[b, h, a.m:] == 7)
+            assert T.rel_err(out_h[b, h], o_ref) <= 1e-4
