@@ -23,7 +23,12 @@ design notes):
   * the members of a span are its positions minus anchors; empty spans are
     dropped; |S| is the member count; log is the natural log.
   * the routing projection W is the identity (no trained weights), so the
-    routing summary of eq. (3) is kbar / ||kbar|| and sqrt(d') = sqrt(d).
+    routing summary of eq. (3) is kbar / ||kbar|| and sqrt(d') = sqrt(d);
+    when a projection is given it is one d' x d matrix per (layer, kv head),
+    applied to the keys (eq. 3) and to every query head reading that kv head
+    (eq. 5).
+  * soft rank gates (eq. 6) are given per stored component and scale the
+    stored factor A = U_r Sigma_r, rounded once to the storage type.
   * the zoom rule sigmoid(s) > tau is evaluated as s > logit(tau); tau <= 0
     zooms everything, tau >= 1 nothing.
   * the trained rank gate of eq. (6) is replaced by a hard rank r_S drawn by
@@ -168,6 +173,23 @@ def weighted_mean(H, X, members: np.ndarray) -> np.ndarray:
     return (wt[:, None] * np.asarray(X, dtype=np.float64)[members]).sum(axis=0) / wt.sum()
 
 
+def routing_summary(H, K, members: np.ndarray, W) -> np.ndarray:
+    """Kbar_S = sum_t w_t W K_t / || sum_t w_t W K_t ||_2   [Summary 2.2, eq. (3)].
+
+    W is the (layer, head) routing projection, d' x d; every member key is
+    projected, the projections are averaged with the surprisal weights of
+    eq. (2) and the result is scaled to unit length (left at zero when the
+    sum is the zero vector).
+    """
+    wt = span_weights(H, members)
+    W = np.asarray(W, dtype=np.float64)
+    acc = np.zeros(W.shape[0])
+    for t, w in zip(members, wt):
+        acc += w * (W @ np.asarray(K[t], dtype=np.float64))
+    nrm = math.sqrt(float(acc @ acc))
+    return acc / nrm if nrm > 0.0 else acc
+
+
 # ----------------------------------------------------------------------------
 # build, step 3: per-span rank and truncated SVD   [Summary 2.2, eq. (6)]
 # ----------------------------------------------------------------------------
@@ -188,6 +210,16 @@ def span_rank(seed: int, layer: int, g: int, k: int, choices: Sequence[int]) -> 
     """Hard rank of span k in (layer, kv head g), standing in for the trained gate of eq. (6)."""
     key = (seed ^ (layer << 40) ^ (g << 32) ^ k) & _M64
     return int(choices[splitmix64(key) % len(choices)])
+
+
+def apply_rank_gates(A, gates, kv_dtype: str) -> np.ndarray:
+    """Soft rank gate of eq. (6) on a stored factor A = U_r Sigma_r (|S| x r):
+    component i is scaled by its gate m_i, so that A' Bt = sum_i m_i sigma_i u_i v_i^T.
+    The exact product of the stored value and the gate is rounded once to the
+    storage type (round to nearest, ties to even)."""
+    A = np.asarray(A, dtype=np.float64)
+    m = np.asarray(gates, dtype=np.float64)[:A.shape[1]]
+    return round_to(A * m[None, :], kv_dtype)
 
 
 def truncated_svd(X, r: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -217,6 +249,8 @@ class HeadArtifacts:
     BKt: List[np.ndarray]  # per span [r, d]
     AV: List[np.ndarray]
     BVt: List[np.ndarray]
+    W: Optional[np.ndarray] = None   # routing projection [d', d] (None: identity)
+    Kr: Optional[np.ndarray] = None  # routing summaries [m, d'] (stored values), with W
 
     @property
     def m(self) -> int:
@@ -228,8 +262,9 @@ class HeadArtifacts:
 
 
 def build_head(H, K, V, seg: Segmentation, layer: int, g: int, choices: Sequence[int],
-               seed: int, kv_dtype: str, with_bases: bool = True) -> HeadArtifacts:
-    """Everything the decode step of one (sequence, layer, kv head) reads."""
+               seed: int, kv_dtype: str, with_bases: bool = True, W=None) -> HeadArtifacts:
+    """Everything the decode step of one (sequence, layer, kv head) reads.
+    W: the head's routing projection [d', d], or None for the identity."""
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     d = K.shape[1]
@@ -249,10 +284,17 @@ def build_head(H, K, V, seg: Segmentation, layer: int, g: int, choices: Sequence
             a, bt = truncated_svd(V[mem], r)
             AV.append(round_to(a, kv_dtype))
             BVt.append(round_to(bt, kv_dtype))
+    Kr = None
+    if W is not None:
+        W = np.asarray(W, dtype=np.float64)
+        Kr = np.zeros((seg.m, W.shape[0]))
+        for k, mem in enumerate(seg.members):
+            Kr[k] = routing_summary(H, K, mem, W)
+        Kr = round_to(Kr, kv_dtype)
     return HeadArtifacts(kv_dtype=kv_dtype, mstart=seg.mstart.copy(), mcount=seg.mcount.copy(),
                          anchors=seg.anchors.copy(), kbar=round_to(kbar, kv_dtype),
                          vbar=round_to(vbar, kv_dtype), KA=K[seg.anchors].copy(),
-                         VA=V[seg.anchors].copy(), rank=rank, AK=AK, BKt=BKt, AV=AV, BVt=BVt)
+                         VA=V[seg.anchors].copy(), rank=rank, AK=AK, BKt=BKt, AV=AV, BVt=BVt, W=W, Kr=Kr)
 
 
 # ----------------------------------------------------------------------------
@@ -269,6 +311,24 @@ def logit_threshold(tau: float) -> float:
     if tau >= 1.0:
         return math.inf
     return math.log(tau) - math.log1p(-tau)
+
+
+def route_scores_projected(q, W, Kr, mcount) -> np.ndarray:
+    """s_S = (W q) . Kbar_S / sqrt(d') + ln|S|   [Summary 2.3, eq. (5)]: the query
+    is projected into the routing space by the same W as the keys of eq. (3)."""
+    qp = np.asarray(W, dtype=np.float64) @ np.asarray(q, dtype=np.float64)
+    dr = qp.size
+    out = np.empty(len(mcount))
+    for k in range(len(mcount)):
+        out[k] = float(qp @ np.asarray(Kr[k], dtype=np.float64)) / math.sqrt(dr) + math.log(int(mcount[k]))
+    return out
+
+
+def head_route_scores(q, art: "HeadArtifacts") -> np.ndarray:
+    """The routing scores of one head: with its projection W if it has one, else eq. (5) with W = I."""
+    if art.W is not None:
+        return route_scores_projected(q, art.W, art.Kr, art.mcount)
+    return route_scores(q, art.kbar, art.mcount)
 
 
 def route_scores(q, kbar, mcount) -> np.ndarray:
@@ -342,7 +402,7 @@ def decode_head(q, tau: float, art: HeadArtifacts, budget: Optional[int] = None
     """One decode step of one query head: (output [d], zoom mask [m], scores [m]).
     `budget` caps the zoomed spans (capped_decisions); None: no cap."""
     theta = logit_threshold(tau)
-    s = route_scores(q, art.kbar, art.mcount)
+    s = head_route_scores(q, art)
     z = capped_decisions(s, theta, budget)
     logits, values = mixed_entries(q, art, z)
     return softmax_attend(logits, values), z, s
@@ -359,10 +419,11 @@ def dense_attention(q, K, V) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def build_layer(H, K, V, alpha: float, w: int, layer: int, choices: Sequence[int], seed: int,
-                kv_dtype: str, heads: Optional[Sequence[int]] = None, with_bases: bool = True
-                ) -> Tuple[List[Segmentation], Dict[Tuple[int, int], HeadArtifacts]]:
-    """H [B][n]; K, V [B][Hkv'][n][d] (Hkv' = len(heads)); returns segmentations per
-    sequence and artefacts keyed by (b, kv head)."""
+                kv_dtype: str, heads: Optional[Sequence[int]] = None, with_bases: bool = True,
+                W=None) -> Tuple[List[Segmentation], Dict[Tuple[int, int], HeadArtifacts]]:
+    """H [B][n]; K, V [B][Hkv'][n][d] (Hkv' = len(heads)); W None or [Hkv][d'][d]
+    (indexed by kv head); returns segmentations per sequence and artefacts keyed
+    by (b, kv head)."""
     H = np.asarray(H, dtype=np.float64)
     B = H.shape[0]
     heads = list(range(np.asarray(K).shape[1])) if heads is None else list(heads)
@@ -371,7 +432,8 @@ def build_layer(H, K, V, alpha: float, w: int, layer: int, choices: Sequence[int
     for b in range(B):
         for i, g in enumerate(heads):
             arts[(b, g)] = build_head(H[b], K[b][i], V[b][i], segs[b], layer, g, choices, seed,
-                                      kv_dtype, with_bases=with_bases)
+                                      kv_dtype, with_bases=with_bases,
+                                      W=None if W is None else W[g])
     return segs, arts
 
 

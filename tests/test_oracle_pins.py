@@ -423,3 +423,96 @@ def test_budget_cap_through_decode_head():
     lg, vals = O.mixed_entries(q, art, z_cap)
     assert np.allclose(o_cap, O.softmax_attend(lg, vals), rtol=0, atol=1e-14)
     assert not np.allclose(o_cap, o_full)
+
+
+# ----------------------------------------------------------------------------- routing projection, soft gates
+
+_RP = _load("routing_projection_hand.json")
+
+
+@pytest.mark.parametrize("case", _RP["cases"], ids=lambda c: c["name"])
+def test_routing_projection_hand_worked(case):
+    H = np.array(case["H"])
+    K = np.array(case["K"])
+    W = np.array(case["W"])
+    mem = np.arange(H.size)
+    kr = O.routing_summary(H, K, mem, W)
+    assert np.allclose(kr, case["Kr"], rtol=0, atol=1e-12)
+    s = O.route_scores_projected(np.array(case["q"]), W, kr[None, :], [H.size])
+    assert abs(s[0] - case["score"]) < 1e-12
+
+
+def _proj_case(seed, n=200, d=16, dr=6, w=4):
+    rng = np.random.default_rng(seed)
+    H = rng.lognormal(0.0, 0.8, n)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    W = rng.standard_normal((dr, d))
+    seg = O.segment(H, 0.5, w)
+    return rng, H, K, V, W, seg
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_routing_projection_identity_reduces_to_cosine_score(seed):
+    """W = I (d' = d): eq. (3)/(5) reduce to q.kbar/(|kbar| sqrt(d)) + ln|S|."""
+    rng, H, K, V, _, seg = _proj_case(seed)
+    d = K.shape[1]
+    art = O.build_head(H, K, V, seg, 0, 0, [4], 1, "f64", with_bases=False, W=np.eye(d))
+    q = rng.standard_normal(d)
+    assert np.allclose(O.head_route_scores(q, art), O.route_scores(q, art.kbar, art.mcount), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_routing_projection_orthogonal_change_of_basis(seed):
+    """Rotating keys and query by Q^T and the projection by Q (W' = W Q) leaves the
+    routing summaries and scores unchanged; a transposed W or a projection of the
+    mean applied on the wrong side breaks this."""
+    rng, H, K, V, W, seg = _proj_case(seed)
+    d = K.shape[1]
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    q = rng.standard_normal(d)
+    a1 = O.build_head(H, K, V, seg, 0, 0, [4], 1, "f64", with_bases=False, W=W)
+    a2 = O.build_head(H, K @ Q, V, seg, 0, 0, [4], 1, "f64", with_bases=False, W=W @ Q)
+    assert np.allclose(a1.Kr, a2.Kr, rtol=0, atol=1e-12)
+    assert np.allclose(O.head_route_scores(q, a1), O.head_route_scores(Q.T @ q, a2), rtol=0, atol=1e-11)
+    assert np.allclose(np.linalg.norm(a1.Kr, axis=1), 1.0)
+
+
+def test_routing_projection_scale_and_linearity():
+    """Kbar is the unit vector of W kbar (eq. 3 is linear in the keys and sum w = 1),
+    does not change when W is scaled by c > 0, and the first score term scales by c."""
+    rng, H, K, V, W, seg = _proj_case(7)
+    q = rng.standard_normal(K.shape[1])
+    a1 = O.build_head(H, K, V, seg, 0, 0, [4], 1, "f64", with_bases=False, W=W)
+    a2 = O.build_head(H, K, V, seg, 0, 0, [4], 1, "f64", with_bases=False, W=2.5 * W)
+    for k in range(a1.m):
+        y = W @ a1.kbar[k]
+        assert np.allclose(a1.Kr[k], y / np.linalg.norm(y), rtol=0, atol=1e-12)
+    assert np.allclose(a1.Kr, a2.Kr, rtol=0, atol=1e-13)
+    ln = np.log(a1.mcount)
+    assert np.allclose(O.head_route_scores(q, a2) - ln, 2.5 * (O.head_route_scores(q, a1) - ln), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", _RP["gates"]["cases"], ids=lambda c: f"{c['A']}x{c['gate']}")
+def test_rank_gate_rounding_hand_worked(case):
+    out = O.apply_rank_gates(np.array([[case["A"]]]), [case["gate"]], "bf16")
+    assert out[0, 0] == case["out"]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_rank_gates_are_eq6_component_weights(seed):
+    """With exact storage, A' B^T equals the explicit sum of m_i sigma_i u_i v_i^T from a
+    LAPACK SVD; gates of one change nothing; 0/1 gates give the shorter truncation."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((30, 12))
+    r = 8
+    A, Bt = O.truncated_svd(X, r)
+    U, sv, Vt = np.linalg.svd(X)
+    m = rng.uniform(0.0, 1.0, r)
+    Ag = O.apply_rank_gates(A, m, "f64")
+    ref = sum(m[i] * sv[i] * np.outer(U[:, i], Vt[i]) for i in range(r))
+    assert np.allclose(Ag @ Bt, ref, rtol=0, atol=1e-10)
+    assert np.array_equal(O.apply_rank_gates(O.round_bf16(A), np.ones(r), "bf16"), O.round_bf16(A))
+    j = 3
+    cut = O.apply_rank_gates(A, np.r_[np.ones(j), np.zeros(r - j)], "f64")
+    assert math.isclose(float(np.linalg.norm(X - cut @ Bt)), math.sqrt(float(np.sum(sv[j:] ** 2))), rel_tol=1e-10)
