@@ -21,7 +21,11 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libsekv.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["runtime.cpp", "decode.hip", "build.hip", "svd.hip"]
+# (source, object name, extra defines): decode.hip builds once per route/attend
+# kernel variant and once for the rest, so the variants compile in parallel
+SOURCES = [("runtime.cpp", "runtime", []), ("decode.hip", "decode", []), ("build.hip", "build", []),
+           ("svd.hip", "svd", [])] + \
+          [("decode.hip", f"decode_v{i}", [f"-DSEKV_DECODE_VARIANT={i}"]) for i in range(4)]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SEKV_ARCH", "gfx950")
@@ -33,10 +37,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}"
           "-munsafe-fp-atomics"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(job) -> str:
+    src, name, defs = job
+    obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -10,6 +10,12 @@
 //
 // Summaries (section 2.2, eq. (2); review page): kbar_S = sum_t H_t K_t / sum_t H_t
 // over the members (uniform weights when that sum is 0), likewise vbar_S.
+// With a routing projection W (d' x d per kv head), the routing summary of
+// eq. (3), sum_t w_t W K_t / |sum_t w_t W K_t|, is W kbar_S / |W kbar_S| (the
+// sum is linear and the weights sum to one), computed from the unrounded mean.
+//
+// Soft rank gates (eq. (6)): component i of a span's stored factor A = U Sigma
+// is scaled by its gate m_i, the exact product rounded once to the storage type.
 #include "sekv_device.h"
 
 namespace sekv {
@@ -225,6 +231,65 @@ __global__ __launch_bounds__(kThreads) void k_summaries(SummaryArgs a) {
       const size_t dst = ((size_t)bg * a.m_max + k) * D + sub * EPL;
       Elem<T>::store16(reinterpret_cast<T*>(a.kbar) + dst, ok);
       Elem<T>::store16(reinterpret_cast<T*>(a.vbar) + dst, ov);
+      if (a.dr > 0) {
+        // routing summary: y = W kbar (lane sub keeps outputs sub*EPL ..), then unit length
+        const float* Wg = a.Wr + (size_t)(bg % a.Hkv) * a.dr * D + sub * EPL;
+        float y[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) y[e] = 0.f;
+        for (int j = 0; j < a.dr; ++j) {
+          float wv[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4) Elem<float>::load16(Wg + (size_t)j * D + e, wv + e);
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p += wv[e] * ok[e];
+          p = group_sum<LPR>(p);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            if (j == sub * EPL + e) y[e] = p;
+        }
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s2 += y[e] * y[e];
+        s2 = group_sum<LPR>(s2);
+        const float inv = s2 > 0.f ? 1.f / sqrtf(s2) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) y[e] *= inv;
+        if (sub * EPL < a.dr)
+          Elem<T>::store16(reinterpret_cast<T*>(a.Kr) + ((size_t)bg * a.m_max + k) * a.dr + sub * EPL, y);
+      }
+    }
+  }
+}
+
+// bfloat16 nearest (ties to even) of a double: round to float with the last
+// bit made sticky (round to odd: truncate, then set bit 0 if anything was
+// dropped), which keeps the information the second rounding needs.
+__device__ __forceinline__ bf16_t bf16_from_f64(double x) {
+  float f = __double2float_rz(x);
+  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f32_to_bf16(f);
+}
+
+// One workgroup per span: rows i < rank of A_K^T (and A_V^T) times gate i.
+// The product of a stored value and a float32 gate is exact in double.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_rank_gates(GateArgs a) {
+  const int k = blockIdx.x;
+  const int r = a.rank[k], c = a.mcount[k];
+  const int c8 = (int)pad8(c);
+  T* AKt = reinterpret_cast<T*>(a.bases) + a.boff[k];
+  T* AVt = AKt + (size_t)r * (c8 + a.d);
+  for (int w = 0; w < 2; ++w) {
+    const float* gt = w == 0 ? a.gk : a.gv;
+    if (!gt) continue;
+    T* At = w == 0 ? AKt : AVt;
+    for (int idx = threadIdx.x; idx < r * c; idx += kThreads) {
+      const int i = idx / c, t = idx % c;
+      const double x = (double)Elem<T>::to_f(At[(size_t)i * c8 + t]) * (double)gt[(size_t)k * a.d + i];
+      if constexpr (sizeof(T) == 2) At[(size_t)i * c8 + t] = bf16_from_f64(x);
+      else At[(size_t)i * c8 + t] = (float)x;
     }
   }
 }
@@ -239,6 +304,12 @@ void launch_summ_t(const SummaryArgs& a, hipStream_t s) {
 
 void launch_segment(const SegmentArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_segment, dim3(a.B), dim3(kSegThreads), 0, s, a);
+}
+
+void launch_rank_gates(int kv_bf16, const GateArgs& a, hipStream_t s) {
+  if (a.m <= 0) return;
+  if (kv_bf16) hipLaunchKernelGGL(k_rank_gates<bf16_t>, dim3(a.m), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_rank_gates<float>, dim3(a.m), dim3(kThreads), 0, s, a);
 }
 
 void launch_summaries(int d, int kv_bf16, const SummaryArgs& a, hipStream_t s) {

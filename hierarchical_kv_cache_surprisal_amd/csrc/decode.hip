@@ -2,7 +2,9 @@
 //
 // One decode step of one layer scores the query of every head against the
 // span summaries (routing score q.kbar/(|kbar| sqrt(d)) + ln|S|, eq. (5) of the
-// long-form summary page with the identity projection), zooms the spans whose
+// long-form summary page with the identity projection; with a routing
+// projection W, (W q).Kbar/sqrt(d') + ln|S| on the routing summaries of
+// eq. (3), the projected queries coming from a small kernel), zooms the spans whose
 // score exceeds logit(tau) (eq. (9)), and runs ONE softmax over three kinds of
 // entries (review page, workflow paragraph; summary page Figure 2):
 //   anchors          q.k_a / sqrt(d), value v_a
@@ -542,6 +544,7 @@ struct Stage {
   float ls[U];
   int2 meta[U];      // span rows: {basis offset / 8, rank | count << 8}
   uint32_t zsel[U];  // span rows under the budget cap: zoom bit of each head
+  Raw<T> kr[U];      // span rows with a routing projection: piece of the routing summary
 };
 
 template <int D, typename T, int G>
@@ -633,7 +636,7 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
 // MODE 0: zoomed spans listed in the chunk's rows of the dense table.
 // MODE 1: zoomed spans appended to the flat list for the host fetch.
 // MODE 2: routing scores only.
-template <int D, typename T, int G, int MODE>
+template <int D, typename T, int G, int MODE, bool ROUTED>
 __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh) {
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
@@ -670,6 +673,10 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
       if (!SCORES) sg.v[u].load(Vb + (size_t)kk * D);
       sg.ls[u] = lS[kk];
       if (!SCORES) sg.meta[u] = sub == 0 ? a.smeta[(size_t)bg * a.m_max + kk] : make_int2(0, 0);
+      if (ROUTED) {
+        const int sp = sub * EPL < a.dr ? sub : 0;  // lanes beyond d' load piece 0 (unused)
+        sg.kr[u].load(reinterpret_cast<const T*>(a.Kr) + ((size_t)bg * a.m_max + kk) * a.dr + sp * EPL);
+      }
       if (!SCORES && a.capped) {
         uint32_t bits = 0u;
 #pragma unroll
@@ -680,14 +687,20 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     }
   };
   float qr[G][EPL];
+  float qpr[ROUTED ? G : 1][EPL];  // projected query piece (routing projection), zero beyond d'
+  constexpr bool routed = ROUTED;
+  const float inv_sqrt_dr = routed ? rsqrtf((float)a.dr) : 0.f;
   auto consume = [&](const Stage<T, U>& sg, int bs) {
     float nrm[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float s2 = 0.f;
+      if (!routed) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s2 += sg.k[u].get(e) * sg.k[u].get(e);
-      nrm[u] = group_sum<LPR>(s2);
+        for (int e = 0; e < EPL; ++e) s2 += sg.k[u].get(e) * sg.k[u].get(e);
+        s2 = group_sum<LPR>(s2);
+      }
+      nrm[u] = s2;
     }
     uint32_t zbits[U];
 #pragma unroll
@@ -701,7 +714,15 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dp += qr[h][e] * sg.k[u].get(e);
         dp = group_sum<LPR>(dp);
-        const float score = (nrm[u] > 0.f ? dp * rsqrtf(nrm[u]) * inv_sqrt_d : 0.f) + sg.ls[u];
+        float score;
+        if (routed) {
+          float dq = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dq += qpr[ROUTED ? h : 0][e] * sg.kr[u].get(e);
+          score = group_sum<LPR>(dq) * inv_sqrt_dr + sg.ls[u];
+        } else {
+          score = (nrm[u] > 0.f ? dp * rsqrtf(nrm[u]) * inv_sqrt_d : 0.f) + sg.ls[u];
+        }
         const int k = bs + u * RPW + slot;
         const bool ok = k < k1;
         const bool zoom = (!SCORES && a.capped) ? ((sg.zsel[u] >> h) & 1u) != 0u
@@ -750,6 +771,17 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     Stage<T, U> A, B;
     load(A, bs);
     load_q<D, G, T>(a, b, g, sub, qr);
+    if constexpr (ROUTED) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bool in = sub * EPL < a.dr;
+        const float* src = a.qp + ((size_t)b * a.Hq + g * G + h) * a.dr + (in ? sub * EPL : 0);
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) Elem<float>::load16(src + e, qpr[h] + e);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qpr[h][e] = in ? qpr[h][e] : 0.f;
+      }
+    }
     for (; bs < k1; bs += 2 * STEP) {
       load(B, bs + STEP);
       consume(A, bs);
@@ -806,7 +838,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
 
 // ------------------------------------------------------------------ kernels
 
-template <int D, typename T, int G, int MODE>
+template <int D, typename T, int G, int MODE, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
   const int4 task = a.tasks[blockIdx.x];
@@ -814,7 +846,7 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
     if (MODE == 0) anchor_task<D, T, G>(a, task, sh.ml);
     return;
   }
-  span_task<D, T, G, MODE>(a, (int)blockIdx.x, task, sh);
+  span_task<D, T, G, MODE, ROUTED>(a, (int)blockIdx.x, task, sh);
 }
 
 // Staged bases: zoom workgroup i takes group i (span task, first item, items)
@@ -916,6 +948,27 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
         make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
   }
   if (bh == 0 && threadIdx.x == 0 && a.zcounter) *a.zcounter = 0;
+}
+
+// ------------------------------------------------------------------ routing projection
+
+// qp[b][h] = W_g q[b][h] (eq. (5): the query is projected into the routing
+// space of eq. (3) by its kv head's projection).  One workgroup per (sequence,
+// query head); wave w computes outputs w, w + 4, ... as wave-wide dot products.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_qproj(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int g = (bh % a.Hq) / a.G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* q = a.q + (size_t)bh * D;
+  const float* Wg = a.Wr + (size_t)g * a.dr * D;
+  for (int j = wave; j < a.dr; j += kWaves) {
+    float x = 0.f;
+#pragma unroll
+    for (int i = lane; i < D; i += 64) x += Wg[(size_t)j * D + i] * q[i];
+    x = wave_sum(x);
+    if (lane == 0) a.qp[(size_t)bh * a.dr + j] = x;
+  }
 }
 
 // ------------------------------------------------------------------ budget cap
@@ -1064,10 +1117,14 @@ template <int D, typename T, int G>
 void launch_t(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
   if (grid <= 0) return;
   const dim3 gd(grid), bd(kThreads);
-  if (which == 0) {
-    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0>), gd, bd, 0, s, a);
-    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_route<D, T, G, 2>), gd, bd, 0, s, a);
+  if (which == 0 && a.dr > 0) {
+    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0, true>), gd, bd, 0, s, a);
+    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_route<D, T, G, 2, true>), gd, bd, 0, s, a);
+  } else if (which == 0) {
+    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0, false>), gd, bd, 0, s, a);
+    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, false>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_route<D, T, G, 2, false>), gd, bd, 0, s, a);
   } else {
     hipLaunchKernelGGL((k_attend<D, T, G>), gd, bd, 0, s, a);
   }
@@ -1083,22 +1140,54 @@ void launch_g(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s)
   }
 }
 
-template <int D>
-void launch_d(int which, int kv_bf16, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
-  if (kv_bf16) launch_g<D, bf16_t>(which, mode, grid, a, s);
-  else launch_g<D, float>(which, mode, grid, a, s);
-}
+}  // namespace
 
+// This file is compiled once per (head dim, KV dtype) variant of the route and
+// attend kernels (SEKV_DECODE_VARIANT 0..3) and once for everything else (no
+// SEKV_DECODE_VARIANT), so that the variants build in parallel.
+#if defined(SEKV_DECODE_VARIANT)
+#if SEKV_DECODE_VARIANT == 0
+void decode_variant_d128_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  launch_g<128, bf16_t>(which, mode, grid, a, s);
+}
+#elif SEKV_DECODE_VARIANT == 1
+void decode_variant_d128_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  launch_g<128, float>(which, mode, grid, a, s);
+}
+#elif SEKV_DECODE_VARIANT == 2
+void decode_variant_d64_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  launch_g<64, bf16_t>(which, mode, grid, a, s);
+}
+#else
+void decode_variant_d64_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  launch_g<64, float>(which, mode, grid, a, s);
+}
+#endif
+#else
+
+namespace {
+void launch_variant(int which, int d, int kv_bf16, int mode, int grid, const DecodeArgs& a, hipStream_t s) {
+  if (d == 128) {
+    if (kv_bf16) decode_variant_d128_bf16(which, mode, grid, a, s);
+    else decode_variant_d128_f32(which, mode, grid, a, s);
+  } else {
+    if (kv_bf16) decode_variant_d64_bf16(which, mode, grid, a, s);
+    else decode_variant_d64_f32(which, mode, grid, a, s);
+  }
+}
 }  // namespace
 
 void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
-  if (d == 128) launch_d<128>(0, kv_bf16, mode, grid, a, s);
-  else launch_d<64>(0, kv_bf16, mode, grid, a, s);
+  launch_variant(0, d, kv_bf16, mode, grid, a, s);
 }
 
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
-  if (d == 128) launch_d<128>(1, kv_bf16, 0, grid, a, s);
-  else launch_d<64>(1, kv_bf16, 0, grid, a, s);
+  launch_variant(1, d, kv_bf16, 0, grid, a, s);
+}
+
+void launch_decode_qproj(int d, const DecodeArgs& a, hipStream_t s) {
+  if (d == 128) hipLaunchKernelGGL(k_qproj<128>, dim3(a.B * a.Hq), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_qproj<64>, dim3(a.B * a.Hq), dim3(kThreads), 0, s, a);
 }
 
 void launch_decode_select(const DecodeArgs& a, hipStream_t s) {
@@ -1109,5 +1198,7 @@ void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s) {
   if (d == 128) hipLaunchKernelGGL((k_combine<128>), dim3(a.B * a.Hq), dim3(kCombineThreads), 0, s, a);
   else hipLaunchKernelGGL((k_combine<64>), dim3(a.B * a.Hq), dim3(kCombineThreads), 0, s, a);
 }
+
+#endif  // SEKV_DECODE_VARIANT
 
 }  // namespace sekv

@@ -80,7 +80,15 @@ struct LayerState {
   std::vector<int64_t> boff_h;     // [B*Hkv*m_max], relative to the layer store
   std::vector<int64_t> head_base;  // [B*Hkv + 1]
   std::vector<uint8_t> head_set;   // [B*Hkv]
+  void* Kr = nullptr;              // [B*Hkv*m_max][dr] routing summaries (with a routing projection)
+  std::vector<uint8_t> route_set;  // [B*Hkv] routing summaries present
   LayerSched sched;
+};
+
+// Routing projection of one layer (set before the layer's layout exists).
+struct RouteProj {
+  int dr = 0;            // 0: identity projection
+  float* W_d = nullptr;  // [Hkv][dr][d]
 };
 
 }  // namespace
@@ -117,6 +125,8 @@ struct sekv_ctx {
   float* H_d_tmp = nullptr;
 
   std::vector<LayerState> layers;
+  std::vector<RouteProj> route;  // per layer
+  float* qp_d = nullptr;         // [B*Hq*d] projected queries
 
   // decode scratch
   float* part_ml = nullptr;
@@ -241,6 +251,7 @@ void free_layer(LayerState& L) {
   dfree(L.smeta_d);
   dfree(L.bases_d);
   hfree(L.bases_h);
+  dfree(L.Kr);
   dfree(L.sched.tasks_d);
   dfree(L.sched.parts_d);
   dfree(L.sched.zcnt_d);
@@ -380,8 +391,22 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
     TRY(halloc(c, &L.bases_h, (size_t)off * c->esz));
     HIPCHK(c, hipHostGetDevicePointer(&L.bases_hd, L.bases_h, 0));
   }
+  const int dr = c->route[layer].dr;
+  L.route_set.assign((size_t)B * Hkv, dr > 0 ? 0 : 1);
+  if (dr > 0) {
+    TRY(dalloc(c, &L.Kr, rows_m * dr * c->esz));
+    HIPCHK(c, hipMemset(L.Kr, 0, rows_m * dr * c->esz));
+  }
   L.allocated = true;
   return SEKV_OK;
+}
+
+// A layer decodes once every (b, g) has its artefacts (and routing summaries).
+void update_ready(LayerState& L) {
+  auto all = [](const std::vector<uint8_t>& v) {
+    return std::all_of(v.begin(), v.end(), [](uint8_t x) { return x != 0; });
+  };
+  L.ready = L.allocated && all(L.head_set) && all(L.route_set);
 }
 
 sekv_status ensure_parts(sekv_ctx* c, size_t slots) {
@@ -664,6 +689,11 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.zcnt = L.sched.zcnt_d;
   a.zlist = c->zlist_d;
   a.zcounter = c->zcounter_d;
+  const int layer = (int)(&L - c->layers.data());
+  a.dr = c->route[layer].dr;
+  a.Kr = L.Kr;
+  a.Wr = c->route[layer].W_d;
+  a.qp = c->qp_d;
 }
 
 sekv_status thetas(sekv_ctx* c, const float* tau, DecodeArgs& a) {
@@ -720,6 +750,7 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->bf16 = k.kv_dtype == SEKV_BF16;
   c->esz = c->bf16 ? 2 : 4;
   c->layers.resize(k.n_layers);
+  c->route.resize(k.n_layers);
   c->pend.assign(k.batch, 0);
   c->mstart.assign(k.batch, {});
   c->mcount.assign(k.batch, {});
@@ -727,6 +758,7 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
   c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
   sekv_status s = dalloc(c, &c->zcounter_d, 4);
+  if (s == SEKV_OK) s = dalloc(c, &c->qp_d, (size_t)k.batch * k.n_q_heads * k.d_head * sizeof(float));
   if (s == SEKV_OK) s = halloc(c, &c->zcount_h, 4);
   if (s == SEKV_OK && hipMemset(c->zcounter_d, 0, 4) != hipSuccess) s = fail(c, SEKV_ERR_HIP, "hipMemset");
   if (s == SEKV_OK && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess)
@@ -749,6 +781,8 @@ void sekv_destroy(sekv_ctx* c) {
   DevGuard dg(c->cfg.device);
   if (c->side) (void)hipStreamSynchronize(c->side);
   for (auto& L : c->layers) free_layer(L);
+  for (auto& r : c->route) dfree(r.W_d);
+  dfree(c->qp_d);
   dfree(c->m_b_d);
   dfree(c->na_b_d);
   dfree(c->mstart_d);
@@ -877,6 +911,9 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
   su.n_span_chunks = (mm + su.span_chunk - 1) / su.span_chunk;
   su.anchor_chunk = 256;
   su.n_anchor_chunks = (c->na_max + su.anchor_chunk - 1) / su.anchor_chunk;
+  su.dr = c->route[layer].dr;
+  su.Wr = c->route[layer].W_d;
+  su.Kr = L.Kr;
   launch_summaries(d, c->bf16, su, stream);
   HIPCHK(c, hipGetLastError());
 
@@ -907,7 +944,8 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
   HIPCHK(c, hipStreamSynchronize(stream));
   if (host_store(c)) dfree(L.bases_d);
   std::fill(L.head_set.begin(), L.head_set.end(), 1);
-  L.ready = true;
+  std::fill(L.route_set.begin(), L.route_set.end(), 1);
+  update_ready(L);
   return SEKV_OK;
 }
 
@@ -1009,6 +1047,10 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
   a.part_acc = c->part_acc;
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
+  if (a.dr > 0) {
+    launch_decode_qproj(d, a, stream);
+    HIPCHK(c, hipGetLastError());
+  }
   if (capped) {
     // budget cap: routing scores, then the capped decisions into the mask,
     // which the route kernel below follows
@@ -1084,6 +1126,10 @@ sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float*
   for (int h = 0; h < kMaxHq; ++h) a.theta[h] = INFINITY;
   a.q = q;
   a.scores = scores;
+  if (a.dr > 0) {
+    launch_decode_qproj(c->cfg.d_head, a, stream);
+    HIPCHK(c, hipGetLastError());
+  }
   launch_decode_route(2, a.n_span_tasks, c->cfg.d_head, c->bf16, a, stream);
   HIPCHK(c, hipGetLastError());
   return SEKV_OK;
@@ -1191,7 +1237,7 @@ sekv_status sekv_import_head(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, c
     HIPCHK(c, hipMemcpy((char*)L.bases_d + L.head_base[bg] * es, bases, (size_t)he * es, hipMemcpyHostToDevice));
   }
   L.head_set[bg] = 1;
-  L.ready = std::all_of(L.head_set.begin(), L.head_set.end(), [](uint8_t x) { return x != 0; });
+  update_ready(L);
   return SEKV_OK;
 }
 
@@ -1223,15 +1269,135 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
   return SEKV_OK;
 }
 
+// ---------------------------------------------------------------------------- routing projection, rank gates
+
+sekv_status sekv_set_routing(sekv_ctx* c, int32_t layer, int32_t d_route, const float* W) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SEKV_ERR_INVALID, "layer out of range");
+  if (c->layers[layer].allocated)
+    return fail(c, SEKV_ERR_STATE, "the layer already has a layout: set its routing projection first");
+  if (d_route != 0 && (d_route < 8 || d_route > d || d_route % 8 != 0))
+    return fail(c, SEKV_ERR_INVALID, "d_route must be 0 or a multiple of 8 in [8, d_head]");
+  RouteProj& R = c->route[layer];
+  if (d_route == 0) {
+    dfree(R.W_d);
+    R.dr = 0;
+    return SEKV_OK;
+  }
+  if (!W) return fail(c, SEKV_ERR_INVALID, "NULL W");
+  const size_t nw = (size_t)Hkv * d_route * d;
+  for (size_t i = 0; i < nw; ++i)
+    if (!std::isfinite(W[i])) return fail(c, SEKV_ERR_INVALID, "W is not finite");
+  dfree(R.W_d);
+  R.dr = 0;
+  TRY(dalloc(c, &R.W_d, nw * sizeof(float)));
+  HIPCHK(c, hipMemcpy(R.W_d, W, nw * sizeof(float), hipMemcpyHostToDevice));
+  R.dr = d_route;
+  return SEKV_OK;
+}
+
+sekv_status sekv_import_route_summary(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, const void* Kr) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads;
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= B || g < 0 || g >= Hkv)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  LayerState& L = c->layers[layer];
+  const int dr = c->route[layer].dr;
+  if (!L.allocated) return fail(c, SEKV_ERR_STATE, "layer has no layout (sekv_import_layout)");
+  if (dr == 0 || !L.Kr) return fail(c, SEKV_ERR_STATE, "the layer has no routing projection");
+  const int m = c->m_b[b];
+  if (m && !Kr) return fail(c, SEKV_ERR_INVALID, "NULL Kr");
+  const size_t bg = (size_t)b * Hkv + g;
+  if (m)
+    HIPCHK(c, hipMemcpy((char*)L.Kr + bg * c->m_max * dr * c->esz, Kr, (size_t)m * dr * c->esz,
+                        hipMemcpyHostToDevice));
+  L.route_set[bg] = 1;
+  update_ready(L);
+  return SEKV_OK;
+}
+
+sekv_status sekv_export_route_summary(const sekv_ctx* cc, int32_t layer, int32_t b, int32_t g, void* Kr) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads;
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= B || g < 0 || g >= Hkv)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  LayerState& L = c->layers[layer];
+  const int dr = c->route[layer].dr;
+  const size_t bg = (size_t)b * Hkv + g;
+  if (!L.allocated || dr == 0 || !L.Kr || !L.route_set[bg])
+    return fail(c, SEKV_ERR_STATE, "no routing summaries for this head");
+  const int m = c->m_b[b];
+  if (m && Kr)
+    HIPCHK(c, hipMemcpy(Kr, (char*)L.Kr + bg * c->m_max * dr * c->esz, (size_t)m * dr * c->esz,
+                        hipMemcpyDeviceToHost));
+  return SEKV_OK;
+}
+
+sekv_status sekv_apply_rank_gates(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, const float* gate_k,
+                                  const float* gate_v, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= B || g < 0 || g >= Hkv)
+    return fail(c, SEKV_ERR_INVALID, "index out of range");
+  LayerState& L = c->layers[layer];
+  const size_t bg = (size_t)b * Hkv + g;
+  if (!L.allocated || !L.head_set[bg]) return fail(c, SEKV_ERR_STATE, "head has no artefacts");
+  const int m = c->m_b[b], mm = c->m_max;
+  if (m == 0 || (!gate_k && !gate_v)) return SEKV_OK;
+  for (int w = 0; w < 2; ++w) {
+    const float* gt = w == 0 ? gate_k : gate_v;
+    if (!gt) continue;
+    for (int k = 0; k < m; ++k) {
+      const int r = L.rank_h[bg * mm + k];
+      for (int i = 0; i < r; ++i) {
+        const float x = gt[(size_t)k * d + i];
+        if (!(x >= 0.f && x <= 1.f))
+          return fail(c, SEKV_ERR_INVALID, "gate outside [0, 1] at span " + std::to_string(k));
+      }
+    }
+  }
+  float* g_d = nullptr;
+  const size_t ng = (size_t)m * d;
+  TRY(dalloc(c, &g_d, 2 * ng * sizeof(float)));
+  GateArgs ga;
+  ga.bases = host_store(c) ? L.bases_hd : L.bases_d;
+  ga.boff = L.boff_d + bg * mm;
+  ga.rank = L.rank_d + bg * mm;
+  ga.mcount = c->mcount_d + (size_t)b * mm;
+  ga.gk = gate_k ? g_d : nullptr;
+  ga.gv = gate_v ? g_d + ng : nullptr;
+  ga.m = m;
+  ga.d = d;
+  hipError_t e = hipSuccess;
+  if (gate_k) e = hipMemcpyAsync(g_d, gate_k, ng * sizeof(float), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess && gate_v) e = hipMemcpyAsync(g_d + ng, gate_v, ng * sizeof(float), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) {
+    launch_rank_gates(c->bf16, ga, stream);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  dfree(g_d);
+  if (e != hipSuccess) return fail(c, SEKV_ERR_HIP, std::string("rank gates: ") + hipGetErrorString(e));
+  return SEKV_OK;
+}
+
 sekv_status sekv_get_stats(const sekv_ctx* cc, sekv_stats* out) {
   sekv_ctx* c = const_cast<sekv_ctx*>(cc);
   if (!c || !out) return fail(c, SEKV_ERR_INVALID, "NULL argument");
   sekv_stats s = c->stats;
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
   int64_t dev = 0, host = 0;
-  for (auto& L : c->layers) {
+  for (size_t li = 0; li < c->layers.size(); ++li) {
+    const LayerState& L = c->layers[li];
     if (!L.allocated) continue;
     dev += (int64_t)2 * B * Hkv * (c->m_max + c->na_max) * d * c->esz;  // summaries + anchors
+    dev += (int64_t)B * Hkv * c->m_max * c->route[li].dr * c->esz;       // routing summaries
     dev += (int64_t)B * Hkv * c->m_max * 12;                              // rank + offset tables
     if (c->cfg.basis_home == SEKV_BASES_DEVICE) dev += L.basis_elems * c->esz;
     else host += L.basis_elems * c->esz;

@@ -55,6 +55,11 @@ struct DecodeArgs {
   const int4* zitems;     // staged items: (bg | head bits << 24, span, staging offset / 8, rank | count << 8)
   const int4* zgroups;    // (span task, first item, items)
   const void* staging;
+  // learned-style routing projection (dr > 0): score = (W q).Kr / sqrt(dr) + ln|S|
+  int dr;                 // routing dimension d' (0: identity projection, cosine score on kbar)
+  const void* Kr;         // [B][Hkv][m_max][dr] routing summaries, KV dtype
+  const float* Wr;        // [Hkv][dr][d] routing projection
+  float* qp;              // [B][Hq][dr] projected queries (written by the projection kernel)
   double theta[kMaxHq];   // logit(tau) per query head
   int32_t budget[kMaxHq]; // most zoomed spans per (sequence, query head); < 0: no cap
 };
@@ -64,11 +69,18 @@ struct DecodeArgs {
 // to the flat list, grid = span tasks.  mode 2: routing scores of the span
 // tasks only, grid = span tasks
 void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
+// the route (which = 0) and attend (which = 1) kernels of one (head dim, KV dtype)
+void decode_variant_d128_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
+void decode_variant_d128_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
+void decode_variant_d64_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
+void decode_variant_d64_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
 // HOST bases: n_zoom_wgs workgroups for the fetched groups, then the anchor
 // tasks; grid = n_zoom_wgs + anchor tasks
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
 // log-sum-exp merge of every (sequence, query head) into out; resets the counters
 void launch_decode_combine(int d, const DecodeArgs& a, hipStream_t s);
+// routing projection: qp = W_g q for every (sequence, query head), grid = B * Hq
+void launch_decode_qproj(int d, const DecodeArgs& a, hipStream_t s);
 // budget cap: zoom decisions of every (sequence, query head) from the routing
 // scores (mode 2) into mask, one workgroup each, grid = B * Hq
 void launch_decode_select(const DecodeArgs& a, hipStream_t s);
@@ -103,8 +115,23 @@ struct SummaryArgs {
   void* KA;                // [B][Hkv][na_max][d]
   void* VA;
   int span_chunk, n_span_chunks, anchor_chunk, n_anchor_chunks;
+  int dr;                  // routing dimension (0: no routing summaries)
+  const float* Wr;         // [Hkv][dr][d]
+  void* Kr;                // [B][Hkv][m_max][dr]
 };
 void launch_summaries(int d, int kv_bf16, const SummaryArgs& a, hipStream_t s);
+
+// Soft rank gates on the stored A factors of the spans of one (sequence, kv head).
+struct GateArgs {
+  void* bases;             // the layer's packed store (device memory or mapped pinned memory)
+  const int64_t* boff;     // [m] element offsets of the spans (of this (b, g))
+  const int32_t* rank;     // [m]
+  const int32_t* mcount;   // [m]
+  const float* gk;         // [m][d] gates of the key components (NULL: keys untouched)
+  const float* gv;         // [m][d] gates of the value components (NULL: values untouched)
+  int m, d;
+};
+void launch_rank_gates(int kv_bf16, const GateArgs& a, hipStream_t s);
 
 struct SvdArgs {
   const void* K;           // [B][Hkv][n][d]

@@ -29,7 +29,8 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_get_bases_layout", "sekv_decode_attn", "sekv_decode_attn_budget",
             "sekv_route_scores", "sekv_zoom_fetch",
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
-            "sekv_get_stats"]
+            "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
+            "sekv_export_route_summary", "sekv_apply_rank_gates"]
 
 
 class SekvError(RuntimeError):
@@ -82,6 +83,10 @@ def load_library(path: str = LIB_PATH):
         "sekv_import_head": (I32, [P, I32, I32, I32, P, P, P, P, pI32, P, I64]),
         "sekv_export_head": (I32, [P, I32, I32, I32, P, P, P, P, pI32, P]),
         "sekv_get_stats": (I32, [P, C.POINTER(sekv_stats)]),
+        "sekv_set_routing": (I32, [P, I32, I32, C.POINTER(C.c_float)]),
+        "sekv_import_route_summary": (I32, [P, I32, I32, I32, P]),
+        "sekv_export_route_summary": (I32, [P, I32, I32, I32, P]),
+        "sekv_apply_rank_gates": (I32, [P, I32, I32, I32, C.POINTER(C.c_float), C.POINTER(C.c_float), P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -228,6 +233,36 @@ def sekv_get_stats(ctx) -> dict:
     return {f: getattr(s, f) for f, _ in sekv_stats._fields_}
 
 
+def sekv_set_routing(ctx, layer: int, d_route: int, W=None):
+    """W: host float32 [H_kv][d_route][d] (None with d_route = 0)."""
+    if d_route == 0:
+        _check(load_library().sekv_set_routing(ctx, layer, 0, None), ctx)
+        return
+    w = np.ascontiguousarray(W, dtype=np.float32)
+    _check(load_library().sekv_set_routing(ctx, layer, d_route, w.ctypes.data_as(C.POINTER(C.c_float))), ctx)
+
+
+def sekv_import_route_summary(ctx, layer: int, b: int, g: int, Kr):
+    k = np.ascontiguousarray(Kr)
+    _check(load_library().sekv_import_route_summary(ctx, layer, b, g, _hbuf(k)), ctx)
+
+
+def sekv_export_route_summary(ctx, layer: int, b: int, g: int, m: int, d_route: int, storage_dtype):
+    k = np.zeros((m, d_route), storage_dtype)
+    _check(load_library().sekv_export_route_summary(ctx, layer, b, g, _hbuf(k)), ctx)
+    return k
+
+
+def sekv_apply_rank_gates(ctx, layer: int, b: int, g: int, gate_k=None, gate_v=None, stream=None):
+    """gate_k, gate_v: host float32 [m][d] or None."""
+    gk = None if gate_k is None else np.ascontiguousarray(gate_k, dtype=np.float32)
+    gv = None if gate_v is None else np.ascontiguousarray(gate_v, dtype=np.float32)
+    fp = C.POINTER(C.c_float)
+    _check(load_library().sekv_apply_rank_gates(ctx, layer, b, g, None if gk is None else gk.ctypes.data_as(fp),
+                                                None if gv is None else gv.ctypes.data_as(fp), _stream(stream)),
+           ctx)
+
+
 # ----------------------------------------------------------------------------- convenience object
 
 class Context:
@@ -297,3 +332,16 @@ class Context:
 
     def stats(self):
         return sekv_get_stats(self.ptr)
+
+    def set_routing(self, layer, d_route, W=None):
+        sekv_set_routing(self.ptr, layer, d_route, W)
+
+    def import_route_summary(self, layer, b, g, Kr):
+        sekv_import_route_summary(self.ptr, layer, b, g, Kr)
+
+    def export_route_summary(self, layer, b, g, d_route):
+        m = len(self.spans(b)[0])
+        return sekv_export_route_summary(self.ptr, layer, b, g, m, d_route, self.storage_dtype)
+
+    def apply_rank_gates(self, layer, b, g, gate_k=None, gate_v=None, stream=None):
+        sekv_apply_rank_gates(self.ptr, layer, b, g, gate_k, gate_v, stream)

@@ -253,6 +253,46 @@ sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g,
 sekv_status sekv_export_head(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* kbar,
                              void* vbar, void* KA, void* VA, int32_t* rank, void* bases);
 
+/* ------------------------------------------- routing projection, rank gates */
+
+/* Routing projection of one layer [summary page, section 2.2, eq. (3); section
+ * 2.3, eq. (5)].  W^(l,g) maps keys of kv head g into a d_route-dimensional
+ * routing space; the builder then stores, per span, the routing summary
+ *     Kbar_S = sum_t w_t W K_t / |sum_t w_t W K_t|      (zero if the sum is zero)
+ * (computed as W kbar_S / |W kbar_S| from the unrounded weighted mean, which is
+ * the same vector since sum_t w_t = 1), and decode scores query head h of kv
+ * head g with (W^(l,g) q_h).Kbar_S / sqrt(d_route) + ln|S|.  The summary-entry
+ * logit of a non-zoomed span keeps q.kbar_S/sqrt(d) + ln|S| in key space.
+ *   W       host float32 [H_kv][d_route][d], finite; copied.
+ *   d_route 0 (back to the identity projection and the cosine score) or a
+ *           multiple of 8 in [8, d].
+ * Must precede the layer's sekv_build / sekv_import_layout (STATE otherwise).
+ * A routed layer decodes with one more small kernel per step (the query
+ * projection).  Errors: INVALID, STATE, OOM, HIP. */
+sekv_status sekv_set_routing(sekv_ctx* ctx, int32_t layer, int32_t d_route, const float* W);
+
+/* Install (test hook) or read the routing summaries of one (layer, b, kv head g)
+ * of a routed layer: host KV dtype [m][d_route].  An imported routed layer is
+ * decodable once every head has both sekv_import_head and this.  Synchronous.
+ * Errors: STATE (no layout, no routing projection, export of a head without
+ * summaries), INVALID, HIP. */
+sekv_status sekv_import_route_summary(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, const void* Kr);
+sekv_status sekv_export_route_summary(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* Kr);
+
+/* Soft rank gates of eq. (6) [summary page, section 2.2]: multiply component i
+ * of span k's stored key factor A_K = U_r Sigma_r by gate_k[k][i] (and of the
+ * value factor by gate_v[k][i]), so that the rebuilt matrix becomes
+ * sum_i m_i sigma_i u_i v_i^T.  Each exact product of a stored value and a gate
+ * is rounded once to the KV dtype (nearest, ties to even).  The factors are
+ * changed in place: applying gates twice multiplies them.
+ *   gate_k, gate_v host float32 [m][d] (entries i >= rank[k] ignored), each in
+ *   [0, 1]; either may be NULL (that factor is left alone).
+ * Works on device and host basis stores; synchronises `stream` before it
+ * returns.  Errors: STATE (head has no artefacts), INVALID (gate outside
+ * [0, 1] or NaN), OOM, HIP. */
+sekv_status sekv_apply_rank_gates(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, const float* gate_k,
+                                  const float* gate_v, hipStream_t stream);
+
 /* ------------------------------------------------------------- diagnostics */
 
 typedef struct sekv_stats {
@@ -261,7 +301,7 @@ typedef struct sekv_stats {
   uint64_t spans_fetched;         /* (b, g, span) bases copied to staging */
   uint64_t bytes_fetched;         /* bytes copied host -> staging */
   uint64_t memcpy_calls;          /* hipMemcpyAsync calls issued by fetches */
-  int64_t device_resident_bytes;  /* anchors + summaries + tables (+ bases if DEVICE) */
+  int64_t device_resident_bytes;  /* anchors + summaries (+ routing summaries) + tables (+ bases if DEVICE) */
   int64_t host_basis_bytes;       /* pinned store (HOST) */
   int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
 } sekv_stats;

@@ -83,6 +83,8 @@ def import_oracle_layer(ctx, layer: int, segs: Sequence[O.Segmentation],
         ctx.import_head(layer, b, g, storage(a.kbar, kv_dtype), storage(a.vbar, kv_dtype),
                         storage(a.KA, kv_dtype), storage(a.VA, kv_dtype), a.rank.astype(np.int32),
                         pack_bases(a, kv_dtype, d))
+        if a.Kr is not None:  # routed layer (the context's routing projection is already set)
+            ctx.import_route_summary(layer, b, g, storage(a.Kr, kv_dtype))
 
 
 # ----------------------------------------------------------------------------- thresholds
@@ -100,6 +102,28 @@ def route_band(q: np.ndarray, kbar: np.ndarray, mcount: np.ndarray) -> np.ndarra
     mag = np.abs(kbar) @ np.abs(q)
     cos_mag = np.where(nrm > 0, mag / np.maximum(nrm, 1e-300) / math.sqrt(d), 0.0)
     return 4 * gam * (cos_mag + np.log(mcount)) + 16 * u * (cos_mag + np.log(mcount) + 1)
+
+
+def route_band_projected(q: np.ndarray, W: np.ndarray, Kr: np.ndarray, mcount: np.ndarray) -> np.ndarray:
+    """Tie band of the projected routing score (W q).Kr/sqrt(d') + ln|S| in fp32:
+    the error of each q'_j = W_j.q (d terms) carried through the dot with Kr,
+    plus the dot over d' terms, with the same gamma bound as route_band."""
+    d = q.size
+    dr = W.shape[0]
+    u = 2.0 ** -24
+    gd = d * u / (1 - d * u)
+    gr = dr * u / (1 - dr * u)
+    qp = W @ q
+    qerr = gd * (np.abs(W) @ np.abs(q))
+    mag = np.abs(Kr) @ np.abs(qp)
+    term = (gr * mag + np.abs(Kr) @ qerr) / math.sqrt(dr)
+    return 4 * term + 16 * u * (mag / math.sqrt(dr) + np.log(mcount) + 1)
+
+
+def head_band(q: np.ndarray, a: O.HeadArtifacts) -> np.ndarray:
+    if a.W is not None:
+        return route_band_projected(q, a.W, a.Kr, a.mcount)
+    return route_band(q, a.kbar, a.mcount)
 
 
 def place_theta(scores: np.ndarray, rate: float, band_max: float) -> float:
@@ -138,8 +162,8 @@ def thresholds_for(q_steps: np.ndarray, arts, G: int, rates: np.ndarray, B: int)
         for b in range(B):
             a = arts[(b, h // G)]
             for t in range(steps):
-                sc.append(O.route_scores(q_steps[t, b, h], a.kbar, a.mcount))
-                bands.append(route_band(q_steps[t, b, h], a.kbar, a.mcount))
+                sc.append(O.head_route_scores(q_steps[t, b, h], a))
+                bands.append(head_band(q_steps[t, b, h], a))
         sc = np.concatenate(sc)
         bm = float(np.concatenate(bands).max())
         taus[h] = tau_from_theta(place_theta(sc, rates[h], bm))
@@ -150,8 +174,8 @@ def assert_no_ties(q: np.ndarray, tau: float, a: O.HeadArtifacts):
     th = O.logit_threshold(tau)
     if not math.isfinite(th):
         return
-    s = O.route_scores(q, a.kbar, a.mcount)
-    bd = route_band(q, a.kbar, a.mcount)
+    s = O.head_route_scores(q, a)
+    bd = head_band(q, a)
     close = np.abs(s - th) <= bd
     assert not close.any(), f"{close.sum()} routing decisions inside the fp32 tie band"
 

@@ -461,3 +461,99 @@ def test_budget_cap_all_zoom_batch_gqa():
             assert np.array_equal(mask_h[b, h, :a.m].astype(bool), z_ref), f"b {b} h {h}"
             assert np.all(mask_h[b, h, a.m:] == 7)
             assert T.rel_err(out_h[b, h], o_ref) <= 1e-4
+
+
+# ============================================================================ routing projection, soft rank gates
+
+def _route_W(s, dr, seed=3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((s.Hkv, dr, s.d)) / math.sqrt(s.d)).astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("home,which", [("device", "mha"), ("host", "mha"), ("host_staged", "gqa"),
+                                        ("device", "gqa")])
+def test_routing_projection_decode_on_oracle_artefacts(home, which):
+    s = _small_bf16() if which == "mha" else _gqa_small()
+    s = s.replace(steps=3)
+    dr = 32
+    W = _route_W(s, dr)
+    H, K, V = _inputs(s)
+    segs, arts = O.build_layer(H, _to_np64(K), _to_np64(V), s.alpha, s.w, 0, s.rank_choices, s.rank_seed,
+                               s.kv_dtype, W=W)
+    qs = _q_steps(s, 0, s.steps)
+    rates = np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1])
+    taus = T.thresholds_for(qs, arts, s.G, rates, s.B)
+    ctx = _ctx(s, home)
+    ctx.set_routing(0, dr, W)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    worst, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert nz > 0
+    # stage-1 scores alone, against the oracle within the fp32 band
+    m_max = ctx.m_max()
+    q = synth.queries(s, 0, 0)
+    sc = torch.full((s.B, s.Hq, m_max), 2.0 ** 100, device=DEV)
+    ctx.route_scores(0, q.to(DEV), sc)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy().astype(np.float64)
+    qn = q.numpy().astype(np.float64)
+    for b in range(s.B):
+        for h in range(s.Hq):
+            a = arts[(b, h // s.G)]
+            ref = O.head_route_scores(qn[b, h], a)
+            assert np.all(np.abs(sc[b, h, :a.m] - ref) <= T.head_band(qn[b, h], a)), (b, h)
+            assert np.all(sc[b, h, a.m:] == 2.0 ** 100)
+
+
+def test_routing_projection_builder_parity():
+    """GPU-built routing summaries against eq. (3) of the oracle, within one bf16 ulp."""
+    s = _gqa_small()
+    dr = 16
+    W = _route_W(s, dr, seed=9)
+    H, K, V = _inputs(s)
+    segs, arts = O.build_layer(H, _to_np64(K), _to_np64(V), s.alpha, s.w, 0, s.rank_choices, s.rank_seed,
+                               s.kv_dtype, W=W, with_bases=False)
+    ctx = _ctx(s, "device")
+    ctx.set_routing(0, dr, W)
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    for (b, g), a in arts.items():
+        kr = T.from_storage(ctx.export_route_summary(0, b, g, dr), s.kv_dtype)
+        assert kr.shape == a.Kr.shape
+        tol = 2.0 ** -7 * np.max(np.abs(a.Kr), axis=1, keepdims=True) + 1e-30
+        assert np.all(np.abs(kr - a.Kr) <= tol), (b, g, float(np.max(np.abs(kr - a.Kr) / tol)))
+    # the identity projection can be restored only before a layout exists
+    sekv = _lib()
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.set_routing(0, 0)
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+
+
+@pytest.mark.parametrize("home", ["device", "host"])
+def test_rank_gates_bit_exact_then_decode(home):
+    s = _small_bf16().replace(Hq=4, Hkv=4, steps=2)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    rng = np.random.default_rng(21)
+    for g in range(s.Hkv):
+        a = arts[(0, g)]
+        gk = rng.uniform(0.0, 1.0, (a.m, s.d)).astype(np.float32)
+        gv = rng.uniform(0.0, 1.0, (a.m, s.d)).astype(np.float32)
+        gk[:, 1::3] = 1.0      # open gates keep the stored value
+        gv[:, 2::5] = 0.0      # closed gates remove the component
+        ctx.apply_rank_gates(0, 0, g, gk if g != 1 else None, gv if g != 2 else None)
+        if g != 1:
+            a.AK = [O.apply_rank_gates(a.AK[k], gk[k].astype(np.float64), s.kv_dtype) for k in range(a.m)]
+        if g != 2:
+            a.AV = [O.apply_rank_gates(a.AV[k], gv[k].astype(np.float64), s.kv_dtype) for k in range(a.m)]
+        *_, bases = ctx.export_head(0, 0, g)
+        assert np.array_equal(bases, T.pack_bases(a, s.kv_dtype, s.d)), f"gated factors differ (g {g})"
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.1, 0.3, 1.0, 0.05]), s.B)
+    _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    sekv = _lib()
+    bad = np.full((arts[(0, 0)].m, s.d), 1.5, np.float32)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.apply_rank_gates(0, 0, 0, bad, None)
+    assert ei.value.status == sekv.SEKV_ERR_INVALID
