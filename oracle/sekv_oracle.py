@@ -37,6 +37,8 @@ design notes):
     span contributes one summary entry with logit q.kbar/sqrt(d) + ln|S|.
   * budget cap: a budget counts zoomed spans per (sequence, query head);
     equal scores are ranked by span index, lower first.
+  * decode-time append: appended tokens stay in the full-resolution window
+    and are not re-segmented into spans.
   * stored artefacts (summaries, SVD factors) are rounded to the KV dtype
     with round-to-nearest-even; everything else is fp64.
 
@@ -412,6 +414,19 @@ def dense_attention(q, K, V) -> np.ndarray:
     """softmax(K q / sqrt(d)) V over every token: the full-KV reference."""
     q = np.asarray(q, dtype=np.float64)
     return softmax_attend(np.asarray(K, dtype=np.float64) @ q / math.sqrt(q.size), V)
+
+
+# ----------------------------------------------------------------------------
+# decode-time append   [Summary Figure 2, eq. (17): the recent tokens stay at full resolution]
+# ----------------------------------------------------------------------------
+
+def append_tokens(art: HeadArtifacts, K_new, V_new) -> HeadArtifacts:
+    """New tokens join the full-resolution local window: later decode steps see
+    them as exact entries of the shared softmax, like the anchors.  Reading:
+    they are not re-segmented into spans (no summary, no basis)."""
+    K_new = np.asarray(K_new, dtype=np.float64).reshape(-1, art.KA.shape[1])
+    V_new = np.asarray(V_new, dtype=np.float64).reshape(-1, art.VA.shape[1])
+    return dataclasses.replace(art, KA=np.concatenate([art.KA, K_new]), VA=np.concatenate([art.VA, V_new]))
 
 
 # ----------------------------------------------------------------------------

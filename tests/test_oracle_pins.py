@@ -516,3 +516,39 @@ def test_rank_gates_are_eq6_component_weights(seed):
     j = 3
     cut = O.apply_rank_gates(A, np.r_[np.ones(j), np.zeros(r - j)], "f64")
     assert math.isclose(float(np.linalg.norm(X - cut @ Bt)), math.sqrt(float(np.sum(sv[j:] ** 2))), rel_tol=1e-10)
+
+
+# ----------------------------------------------------------------------------- decode-time append
+
+@pytest.mark.parametrize("seed", range(3))
+def test_append_then_all_zoom_equals_dense_attention_over_the_longer_context(seed):
+    """P1 with a grown window: tau = 0, full ranks, exact storage, and tokens appended
+    after the prefill: the output is dense attention over all n + n_new tokens."""
+    rng = np.random.default_rng(100 + seed)
+    n, d, w, n_new = 150, 8, 6, 5
+    H = rng.lognormal(0.0, 0.8, n)
+    K = rng.standard_normal((n + n_new, d))
+    V = rng.standard_normal((n + n_new, d))
+    seg = O.segment(H, 0.5, w)
+    art = O.build_head(H, K[:n], V[:n], seg, 0, 0, [d], 1, "f64")
+    art2 = O.append_tokens(art, K[n:], V[n:])
+    q = rng.standard_normal(d)
+    o, _, _ = O.decode_head(q, 0.0, art2)
+    assert np.allclose(o, O.dense_attention(q, K, V), rtol=0, atol=1e-11)
+    # nothing appended: unchanged
+    o0, _, _ = O.decode_head(q, 0.3, O.append_tokens(art, K[:0], V[:0]))
+    assert np.array_equal(o0, O.decode_head(q, 0.3, art)[0])
+
+
+def test_appended_dominant_token_takes_the_output():
+    """An appended key aligned with q and scaled up takes (almost) all the softmax mass."""
+    rng = np.random.default_rng(3)
+    n, d = 120, 8
+    H = rng.lognormal(0.0, 0.8, n)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    art = O.build_head(H, K, V, O.segment(H, 1.0, 4), 0, 0, [4], 1, "f64")
+    q = rng.standard_normal(d)
+    v_new = rng.standard_normal(d)
+    o, _, _ = O.decode_head(q, 0.5, O.append_tokens(art, 400.0 * q / np.linalg.norm(q), v_new))
+    assert np.allclose(o, v_new, rtol=0, atol=1e-9)
