@@ -18,6 +18,8 @@
 // is scaled by its gate m_i, the exact product rounded once to the storage type.
 #include "sekv_device.h"
 
+#include <algorithm>
+
 namespace sekv {
 
 namespace {
@@ -172,8 +174,8 @@ __global__ __launch_bounds__(kThreads) void k_summaries(SummaryArgs a) {
     const int r0 = c * a.anchor_chunk, r1 = min(na, r0 + a.anchor_chunk);
     const T* K = reinterpret_cast<const T*>(a.K) + (size_t)bg * a.n * D;
     const T* V = reinterpret_cast<const T*>(a.V) + (size_t)bg * a.n * D;
-    T* KA = reinterpret_cast<T*>(a.KA) + (size_t)bg * a.na_max * D;
-    T* VA = reinterpret_cast<T*>(a.VA) + (size_t)bg * a.na_max * D;
+    T* KA = reinterpret_cast<T*>(a.KA) + (size_t)bg * a.na_cap * D;
+    T* VA = reinterpret_cast<T*>(a.VA) + (size_t)bg * a.na_cap * D;
     const int32_t* anc = a.anchors + (size_t)b * a.na_max;
     for (int r = r0 + (threadIdx.x / LPR); r < r1; r += kThreads / LPR) {
       const size_t src = (size_t)anc[r] * D + sub * EPL, dst = (size_t)r * D + sub * EPL;
@@ -263,6 +265,29 @@ __global__ __launch_bounds__(kThreads) void k_summaries(SummaryArgs a) {
   }
 }
 
+// Decode-time append: block (bg, row chunk) copies rows of the new keys and
+// values behind the current anchors of sequence b; 16-byte pieces.
+__global__ __launch_bounds__(kThreads) void k_append(AppendArgs a, int row_bytes) {
+  const int bg = blockIdx.x, b = bg / a.Hkv;
+  const int base = a.na[b];
+  const int p16 = row_bytes / 16;
+  const size_t n16 = (size_t)a.n_new * p16;
+  const uint4* ks = reinterpret_cast<const uint4*>(a.K_new) + (size_t)bg * n16;
+  const uint4* vs = reinterpret_cast<const uint4*>(a.V_new) + (size_t)bg * n16;
+  uint4* kd = reinterpret_cast<uint4*>(a.KA) + ((size_t)bg * a.na_cap + base) * p16;
+  uint4* vd = reinterpret_cast<uint4*>(a.VA) + ((size_t)bg * a.na_cap + base) * p16;
+  for (size_t i = (size_t)blockIdx.y * kThreads + threadIdx.x; i < n16; i += (size_t)gridDim.y * kThreads) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+// The counts follow in their own launch, after every copy has read them.
+__global__ void k_append_count(int32_t* na, int B, int n_new) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) na[b] += n_new;
+}
+
 // bfloat16 nearest (ties to even) of a double: round to float with the last
 // bit made sticky (round to odd: truncate, then set bit 0 if anything was
 // dropped), which keeps the information the second rounding needs.
@@ -304,6 +329,13 @@ void launch_summ_t(const SummaryArgs& a, hipStream_t s) {
 
 void launch_segment(const SegmentArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_segment, dim3(a.B), dim3(kSegThreads), 0, s, a);
+}
+
+void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s) {
+  const int row_bytes = d * (kv_bf16 ? 2 : 4);
+  const int chunks = std::max(1, std::min(64, (a.n_new * row_bytes / 16 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_append, dim3(B * a.Hkv, chunks), dim3(kThreads), 0, s, a, row_bytes);
+  hipLaunchKernelGGL(k_append_count, dim3((B + 255) / 256), dim3(256), 0, s, a.na, B, a.n_new);
 }
 
 void launch_rank_gates(int kv_bf16, const GateArgs& a, hipStream_t s) {

@@ -42,6 +42,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 // without a sync.
 struct LayerSched {
   bool valid = false;
+  bool anchors_changed = false;  // tokens were appended: replan before the next launch
   std::vector<int4> tasks;        // (bg | anchor << 31, first row, rows, partial slot)
   int n_span_tasks = 0;           // span tasks come first
   std::vector<int32_t> parts_n;   // [B*Hkv]
@@ -81,6 +82,9 @@ struct LayerState {
   std::vector<int64_t> head_base;  // [B*Hkv + 1]
   std::vector<uint8_t> head_set;   // [B*Hkv]
   void* Kr = nullptr;              // [B*Hkv*m_max][dr] routing summaries (with a routing projection)
+  int na_cap = 0;                  // anchor rows per (b, g) in KA / VA (prefill anchors + appended tokens)
+  std::vector<int32_t> na_l;       // [B] anchors of this layer per sequence (grows with appends)
+  int32_t* na_l_d = nullptr;       // device copy
   std::vector<uint8_t> route_set;  // [B*Hkv] routing summaries present
   LayerSched sched;
 };
@@ -252,6 +256,7 @@ void free_layer(LayerState& L) {
   dfree(L.bases_d);
   hfree(L.bases_h);
   dfree(L.Kr);
+  dfree(L.na_l_d);
   dfree(L.sched.tasks_d);
   dfree(L.sched.parts_d);
   dfree(L.sched.zcnt_d);
@@ -359,6 +364,8 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   L.basis_elems = off;
   if ((off >> 3) >= ((int64_t)1 << 32))
     return fail(c, SEKV_ERR_INVALID, "basis store of one layer exceeds 2^35 elements");
+  L.na_cap = nm;
+  L.na_l = c->na_b;
   const size_t rows_m = (size_t)B * Hkv * mm, rows_a = (size_t)B * Hkv * nm;
   TRY(dalloc(c, &L.kbar, rows_m * d * c->esz));
   TRY(dalloc(c, &L.vbar, rows_m * d * c->esz));
@@ -367,6 +374,8 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   TRY(dalloc(c, &L.rank_d, rows_m * 4));
   TRY(dalloc(c, &L.boff_d, rows_m * 8));
   TRY(dalloc(c, &L.smeta_d, rows_m * sizeof(int2)));
+  TRY(dalloc(c, &L.na_l_d, (size_t)B * sizeof(int32_t)));
+  HIPCHK(c, hipMemcpy(L.na_l_d, L.na_l.data(), (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice));
 
   HIPCHK(c, hipEventCreateWithFlags(&L.sched.ev, hipEventDisableTiming));
   L.sched.est.assign((size_t)B * Hkv, 0.0);
@@ -533,7 +542,8 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
 }
 
 // Task table of a layer from the per-row zoom estimates.
-void plan_tasks(sekv_ctx* c, LayerSched& S) {
+void plan_tasks(sekv_ctx* c, LayerState& L) {
+  LayerSched& S = L.sched;
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
   const int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
   const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
@@ -547,7 +557,7 @@ void plan_tasks(sekv_ctx* c, LayerSched& S) {
   std::vector<int> nspan(BH), nanch(BH), anch(BH, ach);
   std::vector<std::pair<double, int>> order;
   for (int bg = 0; bg < BH; ++bg) {
-    const int m = c->m_b[bg / Hkv], na = c->na_b[bg / Hkv];
+    const int m = c->m_b[bg / Hkv], na = L.na_l[bg / Hkv];
     int n = (m + base - 1) / base;
     n = std::max(n, (int)std::ceil(S.est[bg] / zpw));
     n = std::max(1, std::min(n, std::max(1, (m + 15) / 16)));
@@ -610,9 +620,18 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
     S.reads++;
     replan = true;
   }
+  if (S.anchors_changed) {
+    // appended tokens: the anchor tasks must cover them from this launch on
+    if (S.pending) {
+      HIPCHK(c, hipEventSynchronize(S.ev));
+      S.pending = false;  // those counts are dropped; the next call measures again
+    }
+    S.anchors_changed = false;
+    replan = true;
+  }
   if (!replan || S.pending) return SEKV_OK;
   const std::vector<int4> old_tasks = S.tasks;
-  plan_tasks(c, S);
+  plan_tasks(c, c->layers[layer]);
   // the slot counts follow from the tasks: both tables change together
   if (S.valid && old_tasks.size() == S.tasks.size() &&
       std::memcmp(old_tasks.data(), S.tasks.data(), S.tasks.size() * sizeof(int4)) == 0)
@@ -670,9 +689,9 @@ void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   a.Hkv = c->cfg.n_kv_heads;
   a.G = c->G;
   a.m_max = c->m_max;
-  a.na_max = c->na_max;
+  a.na_max = L.na_cap;
   a.m_b = c->m_b_d;
-  a.na_b = c->na_b_d;
+  a.na_b = L.na_l_d;
   a.logS = c->logS_d;
   a.kbar = L.kbar;
   a.vbar = L.vbar;
@@ -898,6 +917,7 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
   su.n = n;
   su.m_max = mm;
   su.na_max = c->na_max;
+  su.na_cap = L.na_cap;
   su.m_b = c->m_b_d;
   su.mstart = c->mstart_d;
   su.mcount = c->mcount_d;
@@ -1228,8 +1248,8 @@ sekv_status sekv_import_head(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, c
     HIPCHK(c, hipMemcpy((char*)L.vbar + bg * mm * d * es, vbar, (size_t)m * d * es, hipMemcpyHostToDevice));
   }
   if (na) {
-    HIPCHK(c, hipMemcpy((char*)L.KA + bg * c->na_max * d * es, KA, (size_t)na * d * es, hipMemcpyHostToDevice));
-    HIPCHK(c, hipMemcpy((char*)L.VA + bg * c->na_max * d * es, VA, (size_t)na * d * es, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy((char*)L.KA + bg * L.na_cap * d * es, KA, (size_t)na * d * es, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy((char*)L.VA + bg * L.na_cap * d * es, VA, (size_t)na * d * es, hipMemcpyHostToDevice));
   }
   if (host_store(c)) {
     std::memcpy((char*)L.bases_h + L.head_base[bg] * es, bases, (size_t)he * es);
@@ -1256,8 +1276,8 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
   const size_t es = c->esz;
   if (kbar && m) HIPCHK(c, hipMemcpy(kbar, (char*)L.kbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
   if (vbar && m) HIPCHK(c, hipMemcpy(vbar, (char*)L.vbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
-  if (KA && na) HIPCHK(c, hipMemcpy(KA, (char*)L.KA + bg * c->na_max * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
-  if (VA && na) HIPCHK(c, hipMemcpy(VA, (char*)L.VA + bg * c->na_max * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
+  if (KA && na) HIPCHK(c, hipMemcpy(KA, (char*)L.KA + bg * L.na_cap * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
+  if (VA && na) HIPCHK(c, hipMemcpy(VA, (char*)L.VA + bg * L.na_cap * d * es, (size_t)na * d * es, hipMemcpyDeviceToHost));
   if (rank) std::memcpy(rank, L.rank_h.data() + bg * mm, (size_t)m * 4);
   if (bases) {
     const int64_t he = L.head_base[bg + 1] - L.head_base[bg];
@@ -1266,6 +1286,85 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
     else
       HIPCHK(c, hipMemcpy(bases, (char*)L.bases_d + L.head_base[bg] * es, (size_t)he * es, hipMemcpyDeviceToHost));
   }
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------------------- decode-time append
+
+sekv_status sekv_append_tokens(sekv_ctx* c, int32_t layer, const void* K_new, const void* V_new, int32_t n_new,
+                               hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  TRY(check_layer(c, layer));
+  if (n_new < 0) return fail(c, SEKV_ERR_INVALID, "n_new < 0");
+  if (n_new == 0) return SEKV_OK;
+  if (!K_new || !V_new) return fail(c, SEKV_ERR_INVALID, "NULL K_new or V_new");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIPCHK(c, hipStreamIsCapturing(stream, &cs));
+  if (cs != hipStreamCaptureStatusNone) return fail(c, SEKV_ERR_STATE, "append is not capturable");
+  LayerState& L = c->layers[layer];
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head;
+  int need = 0;
+  for (int b = 0; b < B; ++b) need = std::max(need, L.na_l[b] + n_new);
+  if ((int64_t)need >= ((int64_t)1 << 30)) return fail(c, SEKV_ERR_INVALID, "window too large");
+  if (need > L.na_cap) {
+    // grow the anchor rows of every (b, g) by half at least, keeping the rows in place
+    const int cap = std::max(need, L.na_cap + L.na_cap / 2 + 64);
+    const size_t es = c->esz, rows = (size_t)B * Hkv * cap;
+    void* nk = nullptr;
+    void* nv = nullptr;
+    TRY(dalloc(c, &nk, rows * d * es));
+    sekv_status st = dalloc(c, &nv, rows * d * es);
+    if (st != SEKV_OK) {
+      dfree(nk);
+      return st;
+    }
+    hipError_t e = hipSuccess;
+    if (L.na_cap > 0) {
+      const size_t src_pitch = (size_t)L.na_cap * d * es, dst_pitch = (size_t)cap * d * es;
+      e = hipMemcpy2DAsync(nk, dst_pitch, L.KA, src_pitch, src_pitch, (size_t)B * Hkv, hipMemcpyDeviceToDevice,
+                           stream);
+      if (e == hipSuccess)
+        e = hipMemcpy2DAsync(nv, dst_pitch, L.VA, src_pitch, src_pitch, (size_t)B * Hkv, hipMemcpyDeviceToDevice,
+                             stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+      dfree(nk);
+      dfree(nv);
+      return fail(c, SEKV_ERR_HIP, std::string("growing the window: ") + hipGetErrorString(e));
+    }
+    dfree(L.KA);
+    dfree(L.VA);
+    L.KA = nk;
+    L.VA = nv;
+    L.na_cap = cap;
+  }
+  AppendArgs ap;
+  ap.K_new = K_new;
+  ap.V_new = V_new;
+  ap.KA = L.KA;
+  ap.VA = L.VA;
+  ap.na = L.na_l_d;
+  ap.Hkv = Hkv;
+  ap.n_new = n_new;
+  ap.na_cap = L.na_cap;
+  launch_append(d, c->bf16, B, ap, stream);
+  HIPCHK(c, hipGetLastError());
+  for (int b = 0; b < B; ++b) L.na_l[b] += n_new;
+  L.sched.anchors_changed = true;
+  c->stats.tokens_appended += (uint64_t)n_new * B;
+  return SEKV_OK;
+}
+
+sekv_status sekv_get_window(const sekv_ctx* cc, int32_t layer, int32_t b, int32_t* n_anchors) {
+  sekv_ctx* c = const_cast<sekv_ctx*>(cc);
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  if (layer < 0 || layer >= c->cfg.n_layers || b < 0 || b >= c->cfg.batch || !n_anchors)
+    return fail(c, SEKV_ERR_INVALID, "bad argument");
+  const LayerState& L = c->layers[layer];
+  if (!L.allocated) return fail(c, SEKV_ERR_STATE, "layer has no layout");
+  *n_anchors = L.na_l[b];
   return SEKV_OK;
 }
 
@@ -1396,7 +1495,7 @@ sekv_status sekv_get_stats(const sekv_ctx* cc, sekv_stats* out) {
   for (size_t li = 0; li < c->layers.size(); ++li) {
     const LayerState& L = c->layers[li];
     if (!L.allocated) continue;
-    dev += (int64_t)2 * B * Hkv * (c->m_max + c->na_max) * d * c->esz;  // summaries + anchors
+    dev += (int64_t)2 * B * Hkv * (c->m_max + L.na_cap) * d * c->esz;   // summaries + anchors
     dev += (int64_t)B * Hkv * c->m_max * c->route[li].dr * c->esz;       // routing summaries
     dev += (int64_t)B * Hkv * c->m_max * 12;                              // rank + offset tables
     if (c->cfg.basis_home == SEKV_BASES_DEVICE) dev += L.basis_elems * c->esz;

@@ -118,8 +118,21 @@ struct SummaryArgs {
   int dr;                  // routing dimension (0: no routing summaries)
   const float* Wr;         // [Hkv][dr][d]
   void* Kr;                // [B][Hkv][m_max][dr]
+  int na_cap;              // anchor rows per (b, g) in KA / VA
 };
 void launch_summaries(int d, int kv_bf16, const SummaryArgs& a, hipStream_t s);
+
+// Decode-time append: n_new rows per (b, g) copied to KA / VA after the
+// sequence's current anchors, then the counts na[b] += n_new (two kernels).
+struct AppendArgs {
+  const void* K_new;       // [B][Hkv][n_new][d]
+  const void* V_new;
+  void* KA;                // [B][Hkv][na_cap][d]
+  void* VA;
+  int32_t* na;             // [B] anchors before the append (device)
+  int Hkv, n_new, na_cap;
+};
+void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s);
 
 // Soft rank gates on the stored A factors of the spans of one (sequence, kv head).
 struct GateArgs {

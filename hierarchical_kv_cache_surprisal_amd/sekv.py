@@ -30,7 +30,7 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_route_scores", "sekv_zoom_fetch",
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
             "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
-            "sekv_export_route_summary", "sekv_apply_rank_gates"]
+            "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window"]
 
 
 class SekvError(RuntimeError):
@@ -50,7 +50,8 @@ class sekv_stats(C.Structure):
     _fields_ = [("decode_calls", C.c_uint64), ("fetch_calls", C.c_uint64),
                 ("spans_fetched", C.c_uint64), ("bytes_fetched", C.c_uint64),
                 ("memcpy_calls", C.c_uint64), ("device_resident_bytes", C.c_int64),
-                ("host_basis_bytes", C.c_int64), ("full_kv_bytes", C.c_int64)]
+                ("host_basis_bytes", C.c_int64), ("full_kv_bytes", C.c_int64),
+                ("tokens_appended", C.c_uint64)]
 
 
 _lib = None
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH):
         "sekv_export_head": (I32, [P, I32, I32, I32, P, P, P, P, pI32, P]),
         "sekv_get_stats": (I32, [P, C.POINTER(sekv_stats)]),
         "sekv_set_routing": (I32, [P, I32, I32, C.POINTER(C.c_float)]),
+        "sekv_append_tokens": (I32, [P, I32, P, P, I32, P]),
+        "sekv_get_window": (I32, [P, I32, I32, pI32]),
         "sekv_import_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_export_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_apply_rank_gates": (I32, [P, I32, I32, I32, C.POINTER(C.c_float), C.POINTER(C.c_float), P]),
@@ -233,6 +236,18 @@ def sekv_get_stats(ctx) -> dict:
     return {f: getattr(s, f) for f, _ in sekv_stats._fields_}
 
 
+def sekv_append_tokens(ctx, layer: int, K_new, V_new, stream=None):
+    """K_new, V_new: device tensors [B][H_kv][n_new][d] in the KV dtype."""
+    n_new = int(K_new.shape[2])
+    _check(load_library().sekv_append_tokens(ctx, layer, _dptr(K_new), _dptr(V_new), n_new, _stream(stream)), ctx)
+
+
+def sekv_get_window(ctx, layer: int, b: int) -> int:
+    n = np.zeros(1, np.int32)
+    _check(load_library().sekv_get_window(ctx, layer, b, _i32(n)), ctx)
+    return int(n[0])
+
+
 def sekv_set_routing(ctx, layer: int, d_route: int, W=None):
     """W: host float32 [H_kv][d_route][d] (None with d_route = 0)."""
     if d_route == 0:
@@ -332,6 +347,12 @@ class Context:
 
     def stats(self):
         return sekv_get_stats(self.ptr)
+
+    def append_tokens(self, layer, K_new, V_new, stream=None):
+        sekv_append_tokens(self.ptr, layer, K_new, V_new, stream)
+
+    def window(self, layer, b):
+        return sekv_get_window(self.ptr, layer, b)
 
     def set_routing(self, layer, d_route, W=None):
         sekv_set_routing(self.ptr, layer, d_route, W)

@@ -253,6 +253,28 @@ sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g,
 sekv_status sekv_export_head(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* kbar,
                              void* vbar, void* KA, void* VA, int32_t* rank, void* bases);
 
+/* ---------------------------------------------------------- decode-time append */
+
+/* Append n_new decoded tokens per sequence to layer `layer`'s local window
+ * [summary page, Figure 2 and eq. (17): the recent tokens stay at full
+ * resolution on the GPU].  They become full-resolution entries of the shared
+ * softmax (like the anchors) for every later decode step of this layer.
+ *   K_new, V_new dev KV dtype [B][H_kv][n_new][d]; n_new >= 0.
+ * The tokens that pass beyond the last w positions stay at full resolution:
+ * they are not re-segmented into spans (no summaries or bases are built for
+ * them).  Asynchronous on `stream`, except when the window storage must grow
+ * (geometrically): then the call copies the rows and synchronises `stream`.
+ * Not capturable; a decode graph captured before an append does not see the
+ * new tokens (capture again after appending).  Each layer appends on its own
+ * (in a model, layer l appends its token before it decodes).
+ * Errors: STATE (layer not built, capture), INVALID, OOM, HIP. */
+sekv_status sekv_append_tokens(sekv_ctx* ctx, int32_t layer, const void* K_new, const void* V_new, int32_t n_new,
+                               hipStream_t stream);
+
+/* Full-resolution entries (anchors + appended tokens) of sequence b in layer
+ * `layer`.  Errors: STATE (no layout), INVALID. */
+sekv_status sekv_get_window(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t* n_anchors);
+
 /* ------------------------------------------- routing projection, rank gates */
 
 /* Routing projection of one layer [summary page, section 2.2, eq. (3); section
@@ -304,6 +326,7 @@ typedef struct sekv_stats {
   int64_t device_resident_bytes;  /* anchors + summaries (+ routing summaries) + tables (+ bases if DEVICE) */
   int64_t host_basis_bytes;       /* pinned store (HOST) */
   int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
+  uint64_t tokens_appended;       /* (b, layer) rows added by sekv_append_tokens */
 } sekv_stats;
 
 sekv_status sekv_get_stats(const sekv_ctx* ctx, sekv_stats* out);

@@ -557,3 +557,35 @@ def test_rank_gates_bit_exact_then_decode(home):
     with pytest.raises(sekv.SekvError) as ei:
         ctx.apply_rank_gates(0, 0, 0, bad, None)
     assert ei.value.status == sekv.SEKV_ERR_INVALID
+
+
+# ============================================================================ decode-time append
+
+@pytest.mark.parametrize("home,which", [("device", "gqa"), ("host", "mha"), ("host_staged", "gqa")])
+def test_append_tokens_then_decode(home, which):
+    """Tokens appended to the window after the prefill (one at a time, then a block
+    that makes the window storage grow) enter every later decode step as exact entries."""
+    s = (_small_bf16().replace(Hq=4, Hkv=4) if which == "mha" else _gqa_small()).replace(steps=2)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1])[:s.Hq], s.B)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    _decode_compare(s, ctx, arts, 0, 1, taus)
+    gen = torch.Generator().manual_seed(5)
+    dt = torch.bfloat16 if s.kv_dtype == "bf16" else torch.float32
+    for n_new in (1, 1, 3, 700, 1):
+        Kn = torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(dt)
+        Vn = torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(dt)
+        ctx.append_tokens(0, Kn.to(DEV).contiguous(), Vn.to(DEV).contiguous())
+        for (b, g) in list(arts):
+            arts[(b, g)] = O.append_tokens(arts[(b, g)], _to_np64(Kn[b, g]), _to_np64(Vn[b, g]))
+        worst, _ = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    for b in range(s.B):
+        assert ctx.window(0, b) == arts[(b, 0)].KA.shape[0]
+    assert ctx.stats()["tokens_appended"] == s.B * 706
+    sekv = _lib()
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.append_tokens(1 if s.L > 1 else 7, Kn.to(DEV), Vn.to(DEV))
+    assert ei.value.status in (sekv.SEKV_ERR_INVALID, sekv.SEKV_ERR_STATE)
