@@ -112,6 +112,9 @@ __device__ __forceinline__ float lane_xor(float x, int off) {
   return __shfl_xor(x, off, 64);
 }
 
+// Item flag: the span's bases are read from the device cache (bits 0..7 are head bits).
+constexpr uint32_t kCachedBit = 0x100u;
+
 template <int G>
 struct ZoomLds {
   float P[G][128];  // p = B_K^T q, pre-scaled by log2(e)/sqrt(d); zero beyond r
@@ -477,10 +480,11 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
     for (int u = wave; u < units; u += kWaves) {
       while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
       const int3 it = sh.zit[j];
-      const uint32_t hb = (uint32_t)it.x;
+      const uint32_t hb = (uint32_t)it.x;  // head bits; bit kCachedBit: the bases are in the device cache
       const int r = it.z & 0xff, cnt = (int)((uint32_t)it.z >> 8);
       float sm[G], sl[G], o[G][EPL];
-      zoom_unit<D, T, G>(src + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, qr, sh.zw[wave], c2,
+      const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
+      zoom_unit<D, T, G>(from + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, qr, sh.zw[wave], c2,
                          rg, tg, sm, sl, o);
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -814,7 +818,18 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     // wave records, then the task's one partial
     if (threadIdx.x == 0) a.zcnt[t] = zc;  // scheduling statistics (read back by the host)
     if (zc) {
-      if (hb) sh.zit[pos] = make_int3((int)hb, sh.zmeta[i].x, sh.zmeta[i].y);
+      if (hb) {
+        int off8 = sh.zmeta[i].x;
+        uint32_t bits = hb;
+        if (a.cslot) {  // host-resident bases with a device cache: use the cached copy if any
+          const int cs = a.cslot[(size_t)bg * a.m_max + k0 + i];
+          if (cs >= 0) {
+            off8 = cs;
+            bits |= kCachedBit;
+          }
+        }
+        sh.zit[pos] = make_int3((int)bits, off8, sh.zmeta[i].y);
+      }
       __syncthreads();
       auto item = [&](int j) -> int3 { return sh.zit[j]; };
       zoom_group<D, T, G, true>(a, bg, task.w, zc, item, reinterpret_cast<const T*>(a.bases), sh);

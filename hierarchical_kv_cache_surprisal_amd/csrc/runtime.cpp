@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <string>
 #include <vector>
 
@@ -63,6 +64,28 @@ struct LayerSched {
   std::vector<double> est;        // zoomed spans per call, per row
 };
 
+// Device cache of one layer's host-resident bases: a ring region of the
+// context's cache; entries are placed in order and evicted oldest first.
+struct CacheEntry {
+  int64_t idx;   // (b * Hkv + g) * m_max + k
+  int64_t off;   // region-relative element offset
+  int64_t len;   // elements
+};
+struct LayerCache {
+  bool init = false;
+  int64_t base = 0, size = 0;      // region [base, base + size) elements of the cache
+  int64_t head = 0;                // next free position (region-relative)
+  std::deque<CacheEntry> fifo;     // resident entries, oldest first
+  std::vector<int32_t> slot_h;     // [B*Hkv*m_max] (base + off) / 8, or -1
+  int32_t* slot_d = nullptr;       // device copy read by the decode kernel
+  int32_t* slot_pin = nullptr;     // pinned staging of its uploads
+  uint8_t* zm_pin = nullptr;       // [B*Hq*m_max] zoom mask of the last decode, copied back
+  hipEvent_t ev_zm = nullptr;      // after that copy
+  hipEvent_t ev_pref = nullptr;    // after the last prefetch (copies + table upload)
+  hipEvent_t ev_done = nullptr;    // after the last decode of the layer
+  bool zm_valid = false, pref_pending = false, done_valid = false;
+};
+
 struct LayerState {
   bool ready = false;      // every head has artefacts
   bool allocated = false;  // layout fixed, buffers allocated
@@ -86,6 +109,7 @@ struct LayerState {
   std::vector<int32_t> na_l;       // [B] anchors of this layer per sequence (grows with appends)
   int32_t* na_l_d = nullptr;       // device copy
   std::vector<uint8_t> route_set;  // [B*Hkv] routing summaries present
+  LayerCache lc;                   // device cache of its host-resident bases
   LayerSched sched;
 };
 
@@ -131,6 +155,10 @@ struct sekv_ctx {
   std::vector<LayerState> layers;
   std::vector<RouteProj> route;  // per layer
   float* qp_d = nullptr;         // [B*Hq*d] projected queries
+
+  // device cache of host-resident bases (HOST home), split evenly over the layers
+  void* cache_d = nullptr;
+  int64_t cache_elems = 0;
 
   // decode scratch
   float* part_ml = nullptr;
@@ -245,7 +273,18 @@ void hfree(P*& p) {
   p = nullptr;
 }
 
+void free_layer_cache(LayerCache& C) {
+  dfree(C.slot_d);
+  hfree(C.slot_pin);
+  hfree(C.zm_pin);
+  if (C.ev_zm) (void)hipEventDestroy(C.ev_zm);
+  if (C.ev_pref) (void)hipEventDestroy(C.ev_pref);
+  if (C.ev_done) (void)hipEventDestroy(C.ev_done);
+  C = LayerCache();
+}
+
 void free_layer(LayerState& L) {
+  free_layer_cache(L.lc);
   dfree(L.kbar);
   dfree(L.vbar);
   dfree(L.KA);
@@ -682,6 +721,119 @@ sekv_status check_layer(sekv_ctx* c, int layer) {
   return SEKV_OK;
 }
 
+// ---------------------------------------------------------------------------- basis cache
+
+sekv_status ensure_layer_cache(sekv_ctx* c, int layer) {
+  LayerState& L = c->layers[layer];
+  LayerCache& C = L.lc;
+  if (C.init) return SEKV_OK;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads, L_ = c->cfg.n_layers;
+  const size_t rows = (size_t)B * Hkv * c->m_max;
+  C.size = (c->cache_elems / L_) & ~int64_t(7);
+  C.base = C.size * layer;
+  C.head = 0;
+  C.slot_h.assign(rows, -1);
+  TRY(dalloc(c, &C.slot_d, rows * 4));
+  TRY(halloc(c, &C.slot_pin, rows * 4));
+  TRY(halloc(c, &C.zm_pin, (size_t)B * Hq * c->m_max));
+  HIPCHK(c, hipMemset(C.slot_d, 0xff, rows * 4));
+  HIPCHK(c, hipEventCreateWithFlags(&C.ev_zm, hipEventDisableTiming));
+  HIPCHK(c, hipEventCreateWithFlags(&C.ev_pref, hipEventDisableTiming));
+  HIPCHK(c, hipEventCreateWithFlags(&C.ev_done, hipEventDisableTiming));
+  C.init = true;
+  return SEKV_OK;
+}
+
+// Place `len` elements in the ring, evicting the oldest entries it overlaps.
+bool cache_place(LayerCache& C, int64_t len, int64_t* off) {
+  if (len > C.size) return false;
+  auto evict = [&](int64_t lo, int64_t hi) {
+    while (!C.fifo.empty()) {
+      const CacheEntry& f = C.fifo.front();
+      if (!(f.off < hi && f.off + f.len > lo)) break;
+      C.slot_h[f.idx] = -1;
+      C.fifo.pop_front();
+    }
+  };
+  if (C.head + len > C.size) {
+    evict(C.head, C.size);
+    C.head = 0;
+  }
+  evict(C.head, C.head + len);
+  *off = C.head;
+  C.head += len;
+  return true;
+}
+
+// Predictive prefetch for `layer` (called while an earlier layer is being
+// decoded): the spans its last decode zoomed (any head of the group) are
+// expected again at its next decode; those not cached are copied from the
+// pinned store into its region on the side stream, then the slot table is
+// uploaded.  Its next decode waits for ev_pref.  Entries are evicted only after
+// the layer's previous decode has finished (ev_done).
+sekv_status cache_prefetch(sekv_ctx* c, int layer) {
+  LayerState& L = c->layers[layer];
+  LayerCache& C = L.lc;
+  if (!C.init || !L.ready || !C.zm_valid || C.size == 0) return SEKV_OK;
+  if (hipEventQuery(C.ev_zm) != hipSuccess) return SEKV_OK;  // that mask is not back yet: no prediction
+  C.zm_valid = false;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads, G = c->G, mm = c->m_max;
+  const int d = c->cfg.d_head;
+  std::vector<int64_t> need;
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      const size_t bg = (size_t)b * Hkv + g;
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        bool z = false;
+        for (int h = 0; h < G && !z; ++h) z = C.zm_pin[((size_t)b * Hq + g * G + h) * mm + k] != 0;
+        if (!z) continue;
+        c->stats.cache_zoomed++;
+        if (C.slot_h[bg * mm + k] >= 0) c->stats.cache_hits++;
+        else need.push_back((int64_t)bg * mm + k);
+      }
+    }
+  if (need.empty()) return SEKV_OK;
+  if (hipEventQuery(C.ev_pref) != hipSuccess) HIPCHK(c, hipEventSynchronize(C.ev_pref));  // slot_pin is free
+  if (C.done_valid) HIPCHK(c, hipStreamWaitEvent(c->side, C.ev_done, 0));
+  const size_t es = c->esz;
+  int64_t run_src = -1, run_dst = -1, run_len = 0;
+  auto flush = [&]() -> sekv_status {
+    if (run_len > 0) {
+      HIPCHK(c, hipMemcpyAsync((char*)c->cache_d + (size_t)run_dst * es, (const char*)L.bases_h + (size_t)run_src * es,
+                               (size_t)run_len * es, hipMemcpyHostToDevice, c->side));
+      c->stats.memcpy_calls++;
+    }
+    run_len = 0;
+    return SEKV_OK;
+  };
+  for (int64_t idx : need) {
+    const int b = (int)(idx / mm / Hkv), k = (int)(idx % mm);
+    const int64_t len = span_elems(c->mcount[b][k], L.rank_h[idx], d);
+    int64_t off = 0;
+    if (!cache_place(C, len, &off)) continue;
+    const int64_t dst = C.base + off, src = L.boff_h[idx];
+    C.slot_h[idx] = (int32_t)(dst >> 3);
+    C.fifo.push_back({idx, off, len});
+    c->stats.cache_spans_fetched++;
+    c->stats.cache_bytes_fetched += (uint64_t)len * es;
+    if (run_len > 0 && run_src + run_len == src && run_dst + run_len == dst) {
+      run_len += len;
+    } else {
+      TRY(flush());
+      run_src = src;
+      run_dst = dst;
+      run_len = len;
+    }
+  }
+  TRY(flush());
+  const size_t rows = C.slot_h.size();
+  std::memcpy(C.slot_pin, C.slot_h.data(), rows * 4);
+  HIPCHK(c, hipMemcpyAsync(C.slot_d, C.slot_pin, rows * 4, hipMemcpyHostToDevice, c->side));
+  HIPCHK(c, hipEventRecord(C.ev_pref, c->side));
+  C.pref_pending = true;
+  return SEKV_OK;
+}
+
 void fill_decode_geometry(sekv_ctx* c, LayerState& L, DecodeArgs& a) {
   std::memset(&a, 0, sizeof(a));
   a.B = c->cfg.batch;
@@ -802,6 +954,7 @@ void sekv_destroy(sekv_ctx* c) {
   for (auto& L : c->layers) free_layer(L);
   for (auto& r : c->route) dfree(r.W_d);
   dfree(c->qp_d);
+  dfree(c->cache_d);
   dfree(c->m_b_d);
   dfree(c->na_b_d);
   dfree(c->mstart_d);
@@ -1081,9 +1234,20 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
     HIPCHK(c, hipGetLastError());
     a.capped = 1;
   }
+  const bool cached = c->cache_d && c->cfg.basis_home == SEKV_BASES_HOST;
+  if (cached) {
+    if (capturing) return fail(c, SEKV_ERR_STATE, "decode with a basis cache is not capturable");
+    TRY(ensure_layer_cache(c, layer));
+    TRY(cache_prefetch(c, layer));  // if the previous mask is back and no earlier call used it
+    if (L.lc.pref_pending) HIPCHK(c, hipStreamWaitEvent(stream, L.lc.ev_pref, 0));
+    L.lc.pref_pending = false;
+    a.cslot = L.lc.slot_d;
+    a.cache = c->cache_d;
+  }
   if (!staged(c)) {
     // span tasks with their zoomed spans in place (bases in HBM, or read from
-    // the pinned host store over the link), and the anchor tasks
+    // the pinned host store over the link, or from its device cache), and the
+    // anchor tasks
     if (host_store(c)) a.bases = L.bases_hd;
     launch_decode_route(0, a.n_tasks, d, c->bf16, a, stream);
     HIPCHK(c, hipGetLastError());
@@ -1115,6 +1279,21 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
   }
   launch_decode_combine(d, a, stream);
   HIPCHK(c, hipGetLastError());
+  if (cached) {
+    // this step's zoom mask comes back for the prediction of the next one
+    LayerCache& C = L.lc;
+    HIPCHK(c, hipEventRecord(C.ev_done, stream));
+    C.done_valid = true;
+    HIPCHK(c, hipMemcpyAsync(C.zm_pin, a.mask, (size_t)a.B * a.Hq * a.m_max, hipMemcpyDeviceToHost, stream));
+    HIPCHK(c, hipEventRecord(C.ev_zm, stream));
+    C.zm_valid = true;
+    // the next layer's prefetch runs on the side stream while this one decodes
+    const int nxt = (layer + 1) % c->cfg.n_layers;
+    if (nxt != layer && c->layers[nxt].ready) {
+      TRY(ensure_layer_cache(c, nxt));
+      TRY(cache_prefetch(c, nxt));
+    }
+  }
   return finish_sched(c, layer, stream, capturing);
 }
 
@@ -1285,6 +1464,27 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
       std::memcpy(bases, (char*)L.bases_h + L.head_base[bg] * es, (size_t)he * es);
     else
       HIPCHK(c, hipMemcpy(bases, (char*)L.bases_d + L.head_base[bg] * es, (size_t)he * es, hipMemcpyDeviceToHost));
+  }
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------------------- basis cache
+
+sekv_status sekv_set_basis_cache(sekv_ctx* c, int64_t bytes) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  if (c->cfg.basis_home != SEKV_BASES_HOST)
+    return fail(c, SEKV_ERR_INVALID, "the basis cache serves SEKV_BASES_HOST contexts only");
+  if (bytes < 0) return fail(c, SEKV_ERR_INVALID, "bytes < 0");
+  const int64_t elems = bytes / (int64_t)c->esz;
+  if ((elems >> 3) >= ((int64_t)1 << 31)) return fail(c, SEKV_ERR_INVALID, "cache larger than 2^34 elements");
+  HIPCHK(c, hipDeviceSynchronize());
+  for (auto& L : c->layers) free_layer_cache(L.lc);
+  dfree(c->cache_d);
+  c->cache_elems = 0;
+  if (elems >= 8 * c->cfg.n_layers) {
+    TRY(dalloc(c, &c->cache_d, (size_t)elems * c->esz));
+    c->cache_elems = elems;
   }
   return SEKV_OK;
 }

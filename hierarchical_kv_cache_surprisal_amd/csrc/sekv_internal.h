@@ -31,7 +31,9 @@ struct DecodeArgs {
   const void* KA;         // [B][Hkv][na_max][d]
   const void* VA;
   const int2* smeta;      // [B][Hkv][m_max] {basis offset / 8, rank | member count << 8}
-  const void* bases;      // device basis store of the layer (DEVICE home)
+  const void* bases;      // device basis store of the layer (DEVICE home), or the mapped pinned store
+  const int32_t* cslot;   // [B][Hkv][m_max] device-cache offset / 8 of each span's bases, -1: not cached (or NULL)
+  const void* cache;      // the device basis cache
   int64_t basis_elems;    // its size in elements
   const float* q;         // [B][Hq][d]
   float* out;             // [B][Hq][d]

@@ -30,7 +30,8 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_route_scores", "sekv_zoom_fetch",
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
             "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
-            "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window"]
+            "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window",
+            "sekv_set_basis_cache"]
 
 
 class SekvError(RuntimeError):
@@ -51,7 +52,9 @@ class sekv_stats(C.Structure):
                 ("spans_fetched", C.c_uint64), ("bytes_fetched", C.c_uint64),
                 ("memcpy_calls", C.c_uint64), ("device_resident_bytes", C.c_int64),
                 ("host_basis_bytes", C.c_int64), ("full_kv_bytes", C.c_int64),
-                ("tokens_appended", C.c_uint64)]
+                ("tokens_appended", C.c_uint64), ("cache_zoomed", C.c_uint64),
+                ("cache_hits", C.c_uint64), ("cache_spans_fetched", C.c_uint64),
+                ("cache_bytes_fetched", C.c_uint64)]
 
 
 _lib = None
@@ -86,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         "sekv_get_stats": (I32, [P, C.POINTER(sekv_stats)]),
         "sekv_set_routing": (I32, [P, I32, I32, C.POINTER(C.c_float)]),
         "sekv_append_tokens": (I32, [P, I32, P, P, I32, P]),
+        "sekv_set_basis_cache": (I32, [P, I64]),
         "sekv_get_window": (I32, [P, I32, I32, pI32]),
         "sekv_import_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_export_route_summary": (I32, [P, I32, I32, I32, P]),
@@ -242,6 +246,10 @@ def sekv_append_tokens(ctx, layer: int, K_new, V_new, stream=None):
     _check(load_library().sekv_append_tokens(ctx, layer, _dptr(K_new), _dptr(V_new), n_new, _stream(stream)), ctx)
 
 
+def sekv_set_basis_cache(ctx, nbytes: int):
+    _check(load_library().sekv_set_basis_cache(ctx, int(nbytes)), ctx)
+
+
 def sekv_get_window(ctx, layer: int, b: int) -> int:
     n = np.zeros(1, np.int32)
     _check(load_library().sekv_get_window(ctx, layer, b, _i32(n)), ctx)
@@ -350,6 +358,9 @@ class Context:
 
     def append_tokens(self, layer, K_new, V_new, stream=None):
         sekv_append_tokens(self.ptr, layer, K_new, V_new, stream)
+
+    def set_basis_cache(self, nbytes):
+        sekv_set_basis_cache(self.ptr, nbytes)
 
     def window(self, layer, b):
         return sekv_get_window(self.ptr, layer, b)

@@ -253,6 +253,25 @@ sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g,
 sekv_status sekv_export_head(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* kbar,
                              void* vbar, void* KA, void* VA, int32_t* rank, void* bases);
 
+/* ------------------------------------------------------------ basis cache */
+
+/* Device cache of host-resident bases with predictive prefetch, for
+ * SEKV_BASES_HOST contexts [summary page, Figure 2: the zoomed spans' bases are
+ * fetched asynchronously from the CPU; the pages point to prefetching the
+ * spans likely needed next].  `bytes` of device memory are split evenly over
+ * the layers, each share a ring whose oldest entries are evicted first.  After
+ * each decode of layer l the zoom mask comes back to pinned memory; while a
+ * layer decodes, the spans that the next layer zoomed at its previous step
+ * (any head of the group) and that are not cached are copied into that
+ * layer's ring on the context's side stream, and the next layer's decode
+ * waits for that copy.  The decode kernel reads a zoomed span from the cache
+ * when it is there and in place from the pinned store otherwise, so results do
+ * not depend on the prediction.  bytes = 0 frees the cache.  Synchronises the
+ * device.  With a cache, sekv_decode_attn is not capturable (it plans on the
+ * host).  Statistics: sekv_stats.cache_*.
+ * Errors: INVALID (other homes, bytes < 0), OOM, HIP. */
+sekv_status sekv_set_basis_cache(sekv_ctx* ctx, int64_t bytes);
+
 /* ---------------------------------------------------------- decode-time append */
 
 /* Append n_new decoded tokens per sequence to layer `layer`'s local window
@@ -327,6 +346,10 @@ typedef struct sekv_stats {
   int64_t host_basis_bytes;       /* pinned store (HOST) */
   int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
   uint64_t tokens_appended;       /* (b, layer) rows added by sekv_append_tokens */
+  uint64_t cache_zoomed;          /* (layer-step, b, g, span) zoomed, counted by the cache's predictor */
+  uint64_t cache_hits;            /* ... of which the bases were in the device cache */
+  uint64_t cache_spans_fetched;   /* spans copied into the device cache by prefetch */
+  uint64_t cache_bytes_fetched;   /* their bytes */
 } sekv_stats;
 
 sekv_status sekv_get_stats(const sekv_ctx* ctx, sekv_stats* out);

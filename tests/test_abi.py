@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     from hierarchical_kv_cache_surprisal_amd import sekv
     assert ctypes.sizeof(sekv.sekv_config) == 10 * 4
-    assert ctypes.sizeof(sekv.sekv_stats) == 9 * 8
+    assert ctypes.sizeof(sekv.sekv_stats) == 13 * 8
 
 
 def test_create_rejects_bad_configs_without_touching_a_device():

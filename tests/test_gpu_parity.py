@@ -589,3 +589,35 @@ def test_append_tokens_then_decode(home, which):
     with pytest.raises(sekv.SekvError) as ei:
         ctx.append_tokens(1 if s.L > 1 else 7, Kn.to(DEV), Vn.to(DEV))
     assert ei.value.status in (sekv.SEKV_ERR_INVALID, sekv.SEKV_ERR_STATE)
+
+
+# ============================================================================ device basis cache
+
+@pytest.mark.parametrize("cache_kb,L", [(4096, 2), (48, 1)])
+def test_basis_cache_prefetch_decode(cache_kb, L):
+    """Host-resident bases with a device cache: outputs match the oracle at every
+    step whatever is cached; spans zoomed again are found in the cache; a cache
+    too small for the working set keeps evicting and stays correct."""
+    s = _small_bf16().replace(Hq=4, Hkv=4, steps=4)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.1, 0.3, 0.6, 0.05]), s.B)
+    ctx = _ctx(s, "host", L=L)
+    for layer in range(L):
+        T.import_oracle_layer(ctx, layer, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype, set_spans=layer == 0)
+    ctx.set_basis_cache(cache_kb * 1024)
+    for rep in range(3):
+        for layer in range(L):
+            _decode_compare(s, ctx, arts, layer, s.steps, taus)
+    st = ctx.stats()
+    assert st["cache_zoomed"] > 0 and st["cache_spans_fetched"] > 0
+    if cache_kb >= 4096:
+        assert st["cache_hits"] > 0.5 * st["cache_zoomed"], st
+    sekv = _lib()
+    ctx_dev = _ctx(s, "device")
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx_dev.set_basis_cache(1 << 20)
+    assert ei.value.status == sekv.SEKV_ERR_INVALID
+    ctx.set_basis_cache(0)
+    _decode_compare(s, ctx, arts, 0, 1, taus)
