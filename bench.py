@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=160, help="decode steps in the CPU-baseline sample")
     p.add_argument("--calib-steps", type=int, default=8)
     p.add_argument("--home", choices=("device", "host", "host_staged"), default="device")
+    p.add_argument("--cache-gb", type=float, default=0.0,
+                   help="device cache of host-resident bases (--home host), GiB over all layers")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args()
@@ -222,6 +224,10 @@ def main():
     out = torch.empty(B, Hq, d, device=dev)
     mask = torch.zeros(L, B, Hq, m_max, dtype=torch.uint8, device=dev)
 
+    if args.cache_gb > 0:
+        ctx.set_basis_cache(int(args.cache_gb * (1 << 30)))
+        log(f"device basis cache: {args.cache_gb} GiB over {L} layers (eager launches: the cache plans on the host)")
+
     def step(t):
         for l in range(L):
             ctx.decode_attn(l, qs[l, t], taus[l], out, mask[l], stream)
@@ -270,7 +276,8 @@ def main():
 
     # ------------------------------------------------------------------ timed region
     graph = None
-    if not args.no_graph and args.home != "host_staged":  # staged bases sync each call: no graph
+    # staged bases sync each call, the basis cache plans on the host: no graph for either
+    if not args.no_graph and args.home != "host_staged" and args.cache_gb <= 0:
         try:
             g = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()
@@ -325,6 +332,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s, ctx, H, taus, args.cpu_heads, args.cpu_steps)
 
+    st2 = ctx.stats()
     traffic = load_traffic(s.name)
     res = {
         "metric": METRIC,
@@ -343,7 +351,8 @@ def main():
                                f"{s.kv_dtype} KV, batch {B}, {args.steps} decode steps, zoom 0.5-20% per head, "
                                f"bases {args.home}-resident",
                    "layers": L, "q_heads": Hq, "kv_heads": Hkv, "d_head": d, "ctx": n, "batch": B,
-                   "spans": m_tot, "anchors": n_a, "graph": graph is not None, "bases": args.home},
+                   "spans": m_tot, "anchors": n_a, "graph": graph is not None, "bases": args.home,
+                   **({"basis_cache_gib": args.cache_gb} if args.cache_gb > 0 else {})},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS,
                      "traffic": traffic if args.home == "device" else None,
@@ -356,6 +365,8 @@ def main():
         "builder": {"layers": L, "seconds": t_build, "tokens_per_s": L * B * n / t_build,
                     "kv_head_rows_per_s": L * B * Hkv * n / t_build, "gen_seconds": t_gen},
         "memory": {"device_resident_bytes": st["device_resident_bytes"], "full_kv_bytes": st["full_kv_bytes"]},
+        **({"basis_cache": {k: st2[k] for k in ("cache_zoomed", "cache_hits", "cache_spans_fetched",
+                                                 "cache_bytes_fetched")}} if args.cache_gb > 0 else {}),
     }
     print(json.dumps(res), flush=True)
 

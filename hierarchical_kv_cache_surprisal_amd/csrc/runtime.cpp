@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <deque>
@@ -84,6 +85,7 @@ struct LayerCache {
   hipEvent_t ev_pref = nullptr;    // after the last prefetch (copies + table upload)
   hipEvent_t ev_done = nullptr;    // after the last decode of the layer
   bool zm_valid = false, pref_pending = false, done_valid = false;
+  int64_t dirty_lo = INT64_MAX, dirty_hi = 0;  // slot entries changed since the last upload
 };
 
 struct LayerState {
@@ -735,7 +737,7 @@ sekv_status ensure_layer_cache(sekv_ctx* c, int layer) {
   C.slot_h.assign(rows, -1);
   TRY(dalloc(c, &C.slot_d, rows * 4));
   TRY(halloc(c, &C.slot_pin, rows * 4));
-  TRY(halloc(c, &C.zm_pin, (size_t)B * Hq * c->m_max));
+  TRY(halloc(c, &C.zm_pin, (size_t)B * Hq * c->m_max + 8));  // + 8: the scan reads whole words
   HIPCHK(c, hipMemset(C.slot_d, 0xff, rows * 4));
   HIPCHK(c, hipEventCreateWithFlags(&C.ev_zm, hipEventDisableTiming));
   HIPCHK(c, hipEventCreateWithFlags(&C.ev_pref, hipEventDisableTiming));
@@ -752,6 +754,8 @@ bool cache_place(LayerCache& C, int64_t len, int64_t* off) {
       const CacheEntry& f = C.fifo.front();
       if (!(f.off < hi && f.off + f.len > lo)) break;
       C.slot_h[f.idx] = -1;
+      C.dirty_lo = std::min(C.dirty_lo, f.idx);
+      C.dirty_hi = std::max(C.dirty_hi, f.idx + 1);
       C.fifo.pop_front();
     }
   };
@@ -780,16 +784,34 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads, G = c->G, mm = c->m_max;
   const int d = c->cfg.d_head;
   std::vector<int64_t> need;
+  std::vector<uint64_t> un((mm + 7) / 8);
   for (int b = 0; b < B; ++b)
     for (int g = 0; g < Hkv; ++g) {
       const size_t bg = (size_t)b * Hkv + g;
-      for (int k = 0; k < c->m_b[b]; ++k) {
-        bool z = false;
-        for (int h = 0; h < G && !z; ++h) z = C.zm_pin[((size_t)b * Hq + g * G + h) * mm + k] != 0;
-        if (!z) continue;
-        c->stats.cache_zoomed++;
-        if (C.slot_h[bg * mm + k] >= 0) c->stats.cache_hits++;
-        else need.push_back((int64_t)bg * mm + k);
+      const int m = c->m_b[b];
+      const int nw = (m + 7) / 8;
+      // union of the group's mask rows, eight spans per word (bytes beyond m are masked off)
+      for (int w = 0; w < nw; ++w) {
+        uint64_t x = 0;
+        for (int h = 0; h < G; ++h) {
+          uint64_t y;
+          std::memcpy(&y, C.zm_pin + ((size_t)b * Hq + g * G + h) * mm + (size_t)w * 8, 8);
+          x |= y;
+        }
+        const int left = m - w * 8;
+        if (left < 8) x &= (uint64_t(1) << (8 * left)) - 1;
+        un[w] = x;
+      }
+      for (int w = 0; w < nw; ++w) {
+        uint64_t x = un[w];
+        while (x) {
+          const int byte = __builtin_ctzll(x) >> 3;
+          x &= ~(uint64_t(0xff) << (8 * byte));
+          const int k = w * 8 + byte;
+          c->stats.cache_zoomed++;
+          if (C.slot_h[bg * mm + k] >= 0) c->stats.cache_hits++;
+          else need.push_back((int64_t)bg * mm + k);
+        }
       }
     }
   if (need.empty()) return SEKV_OK;
@@ -813,6 +835,8 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     if (!cache_place(C, len, &off)) continue;
     const int64_t dst = C.base + off, src = L.boff_h[idx];
     C.slot_h[idx] = (int32_t)(dst >> 3);
+    C.dirty_lo = std::min(C.dirty_lo, idx);
+    C.dirty_hi = std::max(C.dirty_hi, idx + 1);
     C.fifo.push_back({idx, off, len});
     c->stats.cache_spans_fetched++;
     c->stats.cache_bytes_fetched += (uint64_t)len * es;
@@ -826,9 +850,13 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     }
   }
   TRY(flush());
-  const size_t rows = C.slot_h.size();
-  std::memcpy(C.slot_pin, C.slot_h.data(), rows * 4);
-  HIPCHK(c, hipMemcpyAsync(C.slot_d, C.slot_pin, rows * 4, hipMemcpyHostToDevice, c->side));
+  if (C.dirty_lo < C.dirty_hi) {  // upload the changed range of the slot table
+    const size_t lo = (size_t)C.dirty_lo, n = (size_t)(C.dirty_hi - C.dirty_lo);
+    std::memcpy(C.slot_pin + lo, C.slot_h.data() + lo, n * 4);
+    HIPCHK(c, hipMemcpyAsync(C.slot_d + lo, C.slot_pin + lo, n * 4, hipMemcpyHostToDevice, c->side));
+    C.dirty_lo = INT64_MAX;
+    C.dirty_hi = 0;
+  }
   HIPCHK(c, hipEventRecord(C.ev_pref, c->side));
   C.pref_pending = true;
   return SEKV_OK;
