@@ -84,6 +84,17 @@ struct Raw<float> {
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 };
 
+// Marks the raw words as changed (an empty asm statement, no instruction):
+// the unpacking of a loaded piece then stays next to its use instead of being
+// hoisted out of a loop over the query heads, where it would need G times the
+// registers.
+__device__ __forceinline__ void keep_packed(Raw<bf16_t>& r) {
+  asm volatile("" : "+v"(r.v.x), "+v"(r.v.y), "+v"(r.v.z), "+v"(r.v.w));
+}
+__device__ __forceinline__ void keep_packed(Raw<float>& r) {
+  asm volatile("" : "+v"(r.v.x), "+v"(r.v.y), "+v"(r.v.z), "+v"(r.v.w));
+}
+
 // Lane geometry for head dimension D and element type T.
 template <int D, typename T>
 struct Geo {
@@ -121,6 +132,36 @@ struct ZoomLds {
   float W[G][128];  // w = sum_t e_t A_V[t]; zero beyond r
 };
 
+template <int D, int G>
+struct MergeLds {
+  float m[kWaves][G];
+  float l[kWaves][G];
+  float acc[kWaves][G][D];
+};
+
+// Fold one softmax piece of head h (max sm in log2 units, sum sl, output
+// slice o of columns tg*EPL ..) into the wave's running record in LDS.  Every
+// row slot holds the same values; row slot 0 writes the slice.
+template <int D, int G, int EPL>
+__device__ __forceinline__ void fold_record(MergeLds<D, G>& ml, int wave, int h, int lane, int rg, int tg, float sm,
+                                            float sl, const float (&o)[EPL]) {
+  float mr = ml.m[wave][h], lr = ml.l[wave][h];
+  float ar[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ar[e] = ml.acc[wave][h][tg * EPL + e];
+  lse_merge<EPL>(mr, lr, ar, sm, sl, o);
+  wave_lds_sync();  // every lane has read the record before it is rewritten
+  if (lane == 0) {
+    ml.m[wave][h] = mr;
+    ml.l[wave][h] = lr;
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ml.acc[wave][h][tg * EPL + e] = ar[e];
+  }
+  wave_lds_sync();
+}
+
 // ------------------------------------------------------------------ zoomed span tile, one wave
 
 // One unit of a zoomed span (c tokens, rank r <= D) of one kv head: the
@@ -134,14 +175,14 @@ struct ZoomLds {
 // that hold row j of A_K^T, and w_j in those holding row j of B_V^T, so no
 // data moves between the four products.  Addresses are clamped to valid rows
 // and tokens (no load sits behind a branch).  With r <= RBATCH every load of
-// the unit is issued in one round; larger ranks go in rank batches with p and
-// w in LDS.
-// Out, per head: softmax max sm (log2 units), sum sl, and the output slice
-// o[e] of column tg*EPL + e (the same in every row slot).
-template <int D, typename T, int G>
-__device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, const float (&qr)[G][Elem<T>::kPer16],
-                          ZoomLds<G>& z, float c2, int rg, int tg, float (&sm)[G], float (&sl)[G],
-                          float (&o)[G][Elem<T>::kPer16]) {
+// the unit is issued in one round and the query heads of the group (those in
+// hb) are taken one after the other on the loaded bases; larger ranks go in
+// rank batches with p and w in LDS.  qget(h, e) is element e of the lane's
+// query slice of head h; each head's piece (softmax max in log2 units, sum,
+// output slice of columns tg*EPL ..) goes to sink(h, max, sum, slice).
+template <int D, typename T, int G, class QGet, class Sink>
+__device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, uint32_t hb, QGet qget,
+                                          Sink sink, ZoomLds<G>& z, float c2, int rg, int tg) {
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr int RB = Gm::RB, RBATCH = Gm::RBATCH;
@@ -165,61 +206,68 @@ __device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, cons
       av[u].load(AVt + (size_t)j * c8 + tokc);
       bv[u].load(BVt + (size_t)j * D + tg * EPL);
     }
-    float lg[G][EPL];
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {  // one head at a time on the loaded bases
+      if (!((hb >> h) & 1u)) continue;  // the same for the whole wave
+      if (G > 1) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+        for (int u = 0; u < RB; ++u) {
+          keep_packed(bk[u]);
+          keep_packed(ak[u]);
+          keep_packed(av[u]);
+          keep_packed(bv[u]);
+        }
+      }
+      float q[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = qget(h, e);
       float p[RB];
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * bk[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += q[e] * bk[u].get(e);
         dp = group_sum<LPR>(dp);
         p[u] = (rg + RPW * u < r) ? dp * c2 : 0.f;
       }
+      float lg[EPL];
+      float mx = kNegInf;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         float x = 0.f;
 #pragma unroll
         for (int u = 0; u < RB; ++u) x += p[u] * ak[u].get(e);
-        lg[h][e] = x;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = slots_sum<LPR>(lg[h][e]);
+        x = slots_sum<LPR>(x);
         x = (tok + e < c) ? x : kNegInf;
-        lg[h][e] = x;
+        lg[e] = x;
         mx = fmaxf(mx, x);
       }
       mx = group_max<LPR>(mx);  // finite: token t0 is valid
-      float s = 0.f;
+      float sl = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        lg[h][e] = fast_exp2(lg[h][e] - mx);
-        s += lg[h][e];
+        lg[e] = fast_exp2(lg[e] - mx);
+        sl += lg[e];
       }
-      sm[h] = mx;
-      sl[h] = group_sum<LPR>(s);
+      sl = group_sum<LPR>(sl);
       float w[RB];
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         float x = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x += lg[h][e] * av[u].get(e);
+        for (int e = 0; e < EPL; ++e) x += lg[e] * av[u].get(e);
         x = group_sum<LPR>(x);
         w[u] = (rg + RPW * u < r) ? x : 0.f;
       }
+      float o[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         float x = 0.f;
 #pragma unroll
         for (int u = 0; u < RB; ++u) x += w[u] * bv[u].get(e);
-        o[h][e] = slots_sum<LPR>(x);
+        o[e] = slots_sum<LPR>(x);
       }
+      sink(h, mx, sl, o);
     }
     return;
   }
@@ -231,16 +279,18 @@ __device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, cons
 #pragma unroll
     for (int u = 0; u < RB; ++u) bk[u].load(BKt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      if (!((hb >> h) & 1u)) continue;
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * bk[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qget(h, e) * bk[u].get(e);
         dp = group_sum<LPR>(dp);
         const int j = j0 + rg + RPW * u;
         if (tg == 0) z.P[h][j] = j < r ? dp * c2 : 0.f;
       }
+    }
   }
   wave_lds_sync();
   float lg[G][EPL];
@@ -253,14 +303,17 @@ __device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, cons
 #pragma unroll
     for (int u = 0; u < RB; ++u) ak[u].load(AKt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      if (!((hb >> h) & 1u)) continue;
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         const float pv = z.P[h][j0 + rg + RPW * u];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) lg[h][e] += pv * ak[u].get(e);
       }
+    }
   }
+  float sm[G], sl[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float mx = kNegInf;
@@ -272,21 +325,22 @@ __device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, cons
       mx = fmaxf(mx, x);
     }
     mx = group_max<LPR>(mx);
-    float s = 0.f;
+    float s1 = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       lg[h][e] = fast_exp2(lg[h][e] - mx);
-      s += lg[h][e];
+      s1 += lg[h][e];
     }
     sm[h] = mx;
-    sl[h] = group_sum<LPR>(s);
+    sl[h] = group_sum<LPR>(s1);
   }
   for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
     Raw<T> av[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) av[u].load(AVt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      if (!((hb >> h) & 1u)) continue;
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         float x = 0.f;
@@ -296,46 +350,41 @@ __device__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, cons
         const int j = j0 + rg + RPW * u;
         if (tg == 0) z.W[h][j] = j < r ? x : 0.f;
       }
+    }
   }
   wave_lds_sync();
-  float acc[G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    if (!((hb >> h) & 1u)) continue;
+    float acc[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
-    Raw<T> bv[RB];
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
+      Raw<T> bv[RB];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) bv[u].load(BVt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int u = 0; u < RB; ++u) bv[u].load(BVt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         const float wv = z.W[h][j0 + rg + RPW * u];  // zero beyond r
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] += wv * bv[u].get(e);
+        for (int e = 0; e < EPL; ++e) acc[e] += wv * bv[u].get(e);
       }
+    }
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = slots_sum<LPR>(acc[e]);
+    sink(h, sm[h], sl[h], o);
   }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = slots_sum<LPR>(acc[h][e]);
   wave_lds_sync();  // P and W are rewritten by the next unit
 }
 
 // ------------------------------------------------------------------ workgroup state and merges
 
 template <int D, int G>
-struct MergeLds {
-  float m[kWaves][G];
-  float l[kWaves][G];
-  float acc[kWaves][G][D];
-};
-
-template <int D, int G>
 struct Smem {
   MergeLds<D, G> ml;
   ZoomLds<G> zw[kWaves];
+  float q[G][D];                 // the group's queries (zoom units)
   uint8_t zb[kMaxSpanChunk];     // zoom head bits of each row of a span chunk
   int2 zmeta[kMaxSpanChunk];     // their basis metadata (rows with zoom bits only)
   int3 zit[kMaxSpanChunk];       // a span task's zoomed spans
@@ -436,6 +485,17 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
   const int rg = lane / LPR, tg = lane % LPR;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const float c2 = kLog2e * rsqrtf((float)D);
+  // (G > 1) the group's queries into LDS; without a merge, empty records to fold into
+  if (G > 1)
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+      sh.q[idx / D][idx % D] = a.q[((size_t)b * a.Hq + g * G) * D + idx];
+  if (!MERGE) {
+    for (int idx = lane; idx < G * D; idx += 64) sh.ml.acc[wave][idx / D][idx % D] = 0.f;
+    if (lane < G) {
+      sh.ml.m[wave][lane] = kNegInf;
+      sh.ml.l[wave][lane] = 0.f;
+    }
+  }
   // unit table: tiles of span j start at ustart[j] (exclusive scan over the threads)
   {
     const int i = threadIdx.x;
@@ -464,70 +524,42 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
     __syncthreads();
   }
   const int units = sh.ustart[zc];
-  SoftState<G> st;
-  float acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = kNegInf;
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-  if (wave < units) {
-    float qr[G][EPL];
-    load_q<D, G, T>(a, b, g, tg, qr);
+  auto for_units = [&](auto qget, auto sink) {
     int j = 0;
+#pragma unroll 1
     for (int u = wave; u < units; u += kWaves) {
       while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
       const int3 it = sh.zit[j];
       const uint32_t hb = (uint32_t)it.x;  // head bits; bit kCachedBit: the bases are in the device cache
       const int r = it.z & 0xff, cnt = (int)((uint32_t)it.z >> 8);
-      float sm[G], sl[G], o[G][EPL];
       const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
-      zoom_unit<D, T, G>(from + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, qr, sh.zw[wave], c2,
-                         rg, tg, sm, sl, o);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (hb & (1u << h)) lse_merge<EPL>(st.m[h], st.l[h], acc[h], sm[h], sl[h], o[h]);
+      zoom_unit<D, T, G>(from + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, hb & 0xffu, qget,
+                         sink, sh.zw[wave], c2, rg, tg);
     }
-  }
-  // every row slot holds the same state: slot 0 writes the wave's record, or
-  // (MERGE) folds it into the record the wave already holds
-  if (MERGE) {
+  };
+  if constexpr (G == 1) {
+    // one head: the query slice and the running softmax stay in registers,
+    // folded into the wave's record once
     if (wave < units) {
+      float qr[EPL];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mr = sh.ml.m[wave][h], lr = sh.ml.l[wave][h];
-        float ar[EPL];
+      for (int e = 0; e < EPL; e += 4)
+        Elem<float>::load16(a.q + ((size_t)b * a.Hq + g) * D + tg * EPL + e, qr + e);
+      float m = kNegInf, l = 0.f, acc[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ar[e] = sh.ml.acc[wave][h][tg * EPL + e];
-        lse_merge<EPL>(mr, lr, ar, st.m[h], st.l[h], acc[h]);
-        wave_lds_sync();  // every lane has read the record before it is rewritten
-        if (lane == 0) {
-          sh.ml.m[wave][h] = mr;
-          sh.ml.l[wave][h] = lr;
-        }
-        if (rg == 0) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) sh.ml.acc[wave][h][tg * EPL + e] = ar[e];
-        }
-      }
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      for_units([&](int, int e) { return qr[e]; },
+                [&](int, float sm, float sl, const float (&o)[EPL]) { lse_merge<EPL>(m, l, acc, sm, sl, o); });
+      fold_record<D, G, EPL>(sh.ml, wave, 0, lane, rg, tg, m, l, acc);
     }
-    return;
+  } else {
+    // several heads: queries from LDS, each head's pieces folded into the wave's records
+    for_units([&](int h, int e) { return sh.q[h][tg * EPL + e]; },
+              [&](int h, float sm, float sl, const float (&o)[EPL]) {
+                fold_record<D, G, EPL>(sh.ml, wave, h, lane, rg, tg, sm, sl, o);
+              });
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sh.ml.m[wave][h] = st.m[h];
-      sh.ml.l[wave][h] = st.l[h];
-    }
-  }
-  if (rg == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sh.ml.acc[wave][h][tg * EPL + e] = acc[h][e];
-  }
+  if (MERGE) return;  // the records of the caller's partial now hold the zoomed entries too
   __syncthreads();
   store_partial<D, G>(sh.ml, a, b, g, part);
 }
@@ -555,7 +587,7 @@ template <int D, typename T, int G>
 __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) {
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
-  constexpr int U = kAnchorStageRows;
+  constexpr int U = G >= 4 ? kSpanStageRows : kAnchorStageRows;  // wide groups: registers for the heads
   constexpr int STEP = kWaves * RPW * U;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPR, sub = lane % LPR;
@@ -589,12 +621,22 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
   auto consume = [&](const Stage<T, U>& sg, int bs) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      Raw<T> kx[U], vx[U];  // per head, so that their unpacking is not hoisted out of the loop
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kx[u] = sg.k[u];
+        vx[u] = sg.v[u];
+        if (G > 1) {
+          keep_packed(kx[u]);
+          keep_packed(vx[u]);
+        }
+      }
       float lg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * sg.k[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * kx[u].get(e);
         dp = group_sum<LPR>(dp);
         lg[u] = (bs + u * RPW + slot < r1) ? dp * c2 : kNegInf;
       }
@@ -611,7 +653,7 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
         const float p = fast_exp2(lg[u] - ms);
         ls += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] += p * sg.v[u].get(e);
+        for (int e = 0; e < EPL; ++e) acc[h][e] += p * vx[u].get(e);
       }
       st.l[h] = ls;
       st.m[h] = mx;
@@ -711,12 +753,22 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     for (int u = 0; u < U; ++u) zbits[u] = 0u;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      Raw<T> kx[U], vx[U];  // per head, so that their unpacking is not hoisted out of the loop
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kx[u] = sg.k[u];
+        vx[u] = sg.v[u];
+        if (G > 1) {
+          keep_packed(kx[u]);
+          keep_packed(vx[u]);
+        }
+      }
       float lg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * sg.k[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * kx[u].get(e);
         dp = group_sum<LPR>(dp);
         float score;
         if (routed) {
@@ -753,7 +805,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
           const float p = fast_exp2(lg[u] - ms);
           ls += p;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] += p * sg.v[u].get(e);
+          for (int e = 0; e < EPL; ++e) acc[h][e] += p * vx[u].get(e);
         }
         st.l[h] = ls;
         st.m[h] = mx;
