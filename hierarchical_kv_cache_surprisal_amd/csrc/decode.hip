@@ -126,12 +126,6 @@ __device__ __forceinline__ float lane_xor(float x, int off) {
 // Item flag: the span's bases are read from the device cache (bits 0..7 are head bits).
 constexpr uint32_t kCachedBit = 0x100u;
 
-template <int G>
-struct ZoomLds {
-  float P[G][128];  // p = B_K^T q, pre-scaled by log2(e)/sqrt(d); zero beyond r
-  float W[G][128];  // w = sum_t e_t A_V[t]; zero beyond r
-};
-
 template <int D, int G>
 struct MergeLds {
   float m[kWaves][G];
@@ -174,15 +168,17 @@ __device__ __forceinline__ void fold_record(MergeLds<D, G>& ml, int wave, int h,
 // p_j lands, after the reduction inside the row slot, exactly in the lanes
 // that hold row j of A_K^T, and w_j in those holding row j of B_V^T, so no
 // data moves between the four products.  Addresses are clamped to valid rows
-// and tokens (no load sits behind a branch).  With r <= RBATCH every load of
-// the unit is issued in one round and the query heads of the group (those in
-// hb) are taken one after the other on the loaded bases; larger ranks go in
-// rank batches with p and w in LDS.  qget(h, e) is element e of the lane's
+// and tokens (no load sits behind a branch).  A one-head group with
+// r <= RBATCH issues every load of the unit in one round.  Otherwise the ranks
+// go in batches of RBATCH rows: the key batches (B_K^T, A_K^T) accumulate the
+// logits of every head in hb, then the value batches (A_V^T, B_V^T) the
+// outputs, two rounds per batch; the heads are taken one after the other on
+// each loaded batch.  qget(h, e) is element e of the lane's
 // query slice of head h; each head's piece (softmax max in log2 units, sum,
 // output slice of columns tg*EPL ..) goes to sink(h, max, sum, slice).
 template <int D, typename T, int G, class QGet, class Sink>
 __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int r, int t0, uint32_t hb, QGet qget,
-                                          Sink sink, ZoomLds<G>& z, float c2, int rg, int tg) {
+                                          Sink sink, float c2, int rg, int tg) {
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
   constexpr int RB = Gm::RB, RBATCH = Gm::RBATCH;
@@ -195,8 +191,8 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
   const int tok = t0 + tg * EPL;
   const int tokc = tok < c8 ? tok : t0;  // t0 < c: a valid piece
 
-  if (r <= RBATCH) {
-    // ---------------- one rank batch: everything in registers, one round
+  if (G == 1 && r <= RBATCH) {
+    // ---------------- one head, one rank batch: everything in registers, one round
     Raw<T> bk[RB], ak[RB], av[RB], bv[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
@@ -272,44 +268,44 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
     return;
   }
 
-  // ---------------- larger ranks: rank batches, p and w in LDS
-  const int rpad = (r + RBATCH - 1) / RBATCH * RBATCH;
-  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
-    Raw<T> bk[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) bk[u].load(BKt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!((hb >> h) & 1u)) continue;
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        float dp = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qget(h, e) * bk[u].get(e);
-        dp = group_sum<LPR>(dp);
-        const int j = j0 + rg + RPW * u;
-        if (tg == 0) z.P[h][j] = j < r ? dp * c2 : 0.f;
-      }
-    }
-  }
-  wave_lds_sync();
+  // ---------------- rank batches: the key batches accumulate the logits of
+  // every head in hb, then the value batches accumulate the outputs
   float lg[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) lg[h][e] = 0.f;
-  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
-    Raw<T> ak[RB];
+#pragma unroll 1
+  for (int j0 = 0; j0 < r; j0 += RBATCH) {
+    Raw<T> bk[RB], ak[RB];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) ak[u].load(AKt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
+    for (int u = 0; u < RB; ++u) {
+      const int j = min(j0 + rg + RPW * u, rl);
+      bk[u].load(BKt + (size_t)j * D + tg * EPL);
+      ak[u].load(AKt + (size_t)j * c8 + tokc);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (!((hb >> h) & 1u)) continue;
+      if (G > 1) {
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          keep_packed(bk[u]);
+          keep_packed(ak[u]);
+        }
+      }
+      float q[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = qget(h, e);
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        const float pv = z.P[h][j0 + rg + RPW * u];
+        float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) lg[h][e] += pv * ak[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += q[e] * bk[u].get(e);
+        dp = group_sum<LPR>(dp);
+        const float pv = (j0 + rg + RPW * u < r) ? dp * c2 : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) lg[h][e] += pv * ak[u].get(e);  // this row slot's ranks
       }
     }
   }
@@ -334,48 +330,50 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
     sm[h] = mx;
     sl[h] = group_sum<LPR>(s1);
   }
-  for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
-    Raw<T> av[RB];
+  float acc[G][EPL];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) av[u].load(AVt + (size_t)min(j0 + rg + RPW * u, rl) * c8 + tokc);
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+#pragma unroll 1
+  for (int j0 = 0; j0 < r; j0 += RBATCH) {
+    Raw<T> av[RB], bv[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int j = min(j0 + rg + RPW * u, rl);
+      av[u].load(AVt + (size_t)j * c8 + tokc);
+      bv[u].load(BVt + (size_t)j * D + tg * EPL);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (!((hb >> h) & 1u)) continue;
+      if (G > 1) {
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          keep_packed(av[u]);
+          keep_packed(bv[u]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         float x = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) x += lg[h][e] * av[u].get(e);
         x = group_sum<LPR>(x);
-        const int j = j0 + rg + RPW * u;
-        if (tg == 0) z.W[h][j] = j < r ? x : 0.f;
+        const float wv = (j0 + rg + RPW * u < r) ? x : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] += wv * bv[u].get(e);
       }
     }
   }
-  wave_lds_sync();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hb >> h) & 1u)) continue;
-    float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < rpad; j0 += RBATCH) {
-      Raw<T> bv[RB];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) bv[u].load(BVt + (size_t)min(j0 + rg + RPW * u, rl) * D + tg * EPL);
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        const float wv = z.W[h][j0 + rg + RPW * u];  // zero beyond r
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += wv * bv[u].get(e);
-      }
-    }
     float o[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = slots_sum<LPR>(acc[e]);
+    for (int e = 0; e < EPL; ++e) o[e] = slots_sum<LPR>(acc[h][e]);
     sink(h, sm[h], sl[h], o);
   }
-  wave_lds_sync();  // P and W are rewritten by the next unit
 }
 
 // ------------------------------------------------------------------ workgroup state and merges
@@ -383,7 +381,6 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
 template <int D, int G>
 struct Smem {
   MergeLds<D, G> ml;
-  ZoomLds<G> zw[kWaves];
   float q[G][D];                 // the group's queries (zoom units)
   uint8_t zb[kMaxSpanChunk];     // zoom head bits of each row of a span chunk
   int2 zmeta[kMaxSpanChunk];     // their basis metadata (rows with zoom bits only)
@@ -529,12 +526,16 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
 #pragma unroll 1
     for (int u = wave; u < units; u += kWaves) {
       while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
+      // the item is the same for the whole wave: scalar registers (loads then
+      // take a scalar base and a 32-bit lane offset)
       const int3 it = sh.zit[j];
-      const uint32_t hb = (uint32_t)it.x;  // head bits; bit kCachedBit: the bases are in the device cache
-      const int r = it.z & 0xff, cnt = (int)((uint32_t)it.z >> 8);
+      const uint32_t hb = (uint32_t)__builtin_amdgcn_readfirstlane(it.x);  // head bits; kCachedBit: device cache
+      const uint32_t iz = (uint32_t)__builtin_amdgcn_readfirstlane(it.z);
+      const int r = (int)(iz & 0xffu), cnt = (int)(iz >> 8);
+      const int t0 = __builtin_amdgcn_readfirstlane((u - sh.ustart[j]) * TILE);
       const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
-      zoom_unit<D, T, G>(from + ((int64_t)(uint32_t)it.y << 3), cnt, r, (u - sh.ustart[j]) * TILE, hb & 0xffu, qget,
-                         sink, sh.zw[wave], c2, rg, tg);
+      const uint32_t off8 = (uint32_t)__builtin_amdgcn_readfirstlane(it.y);
+      zoom_unit<D, T, G>(from + ((int64_t)off8 << 3), cnt, r, t0, hb & 0xffu, qget, sink, c2, rg, tg);
     }
   };
   if constexpr (G == 1) {
