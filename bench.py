@@ -88,10 +88,11 @@ COPY_BYTES = 1 << 30
 
 def decode_kernel(name: str):
     """The decode kernels of a device-resident layer-step: the route kernel in
-    its decode mode (last template argument 0; mode 2 is the routing-scores
-    pass used to calibrate thresholds) and the combine kernel."""
+    its decode mode (mode template argument 0, before the routing-projection
+    flag; mode 2 is the routing-scores pass used to calibrate thresholds) and
+    the combine kernel."""
     import re
-    if re.search(r"k_route<[^>]*,\s*0>", name):
+    if re.search(r"k_route<[^>]*,\s*0,\s*(false|true)>", name):
         return "k_route"
     if "k_combine<" in name:
         return "k_combine"
