@@ -281,3 +281,75 @@ def test_largest_group_and_head_count():
     graph_decode(ctx, 0, q_dev, taus, outs, masks)
     worst, nz = compare_sampled(s, q_np, taus, arts, outs, masks)
     assert nz > 0
+
+
+def test_single_layer_32k_routing_projection_budget_append():
+    """The routing projection (d' = 32), a zoom budget per head and decode-time
+    appends at full size: 32 heads, n = 32768.  The GPU builds the layer with the
+    projection; every head's artefacts (routing summaries included) are exported
+    and decoded by the oracle with the same budgets and appended tokens."""
+    from tests.test_gpu_parity import _cut_ok, _ranked
+    s = synth.spec("single_layer_32k")
+    dr = 32
+    rng = np.random.default_rng(17)
+    W = (rng.standard_normal((s.Hkv, dr, s.d)) / math.sqrt(s.d)).astype(np.float32).astype(np.float64)
+    ctx = _ctx(s, "device", L=1)
+    ctx.set_routing(0, dr, W)
+    H = synth.surprisal_batch(s)
+    K, V = synth.kv_layer(s, 0, device=DEV)
+    ctx.build(0, torch.from_numpy(H).to(DEV), K, V, s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    seg = gpu_segmentation(ctx, 0)
+    arts = {}
+    for g in range(s.Hkv):
+        a = gpu_artefacts(ctx, s, 0, 0, g, seg)
+        a.W = W[g]
+        a.Kr = T.from_storage(ctx.export_route_summary(0, 0, g, dr), s.kv_dtype)
+        arts[(0, g)] = a
+    # the routing summaries against eq. (3) on the GPU's own unrounded inputs, two heads
+    segs_o = O.segment(H[0], s.alpha, s.w)
+    for g in (0, s.Hkv - 1):
+        a = arts[(0, g)]
+        Kg = K[0, g].float().cpu().numpy().astype(np.float64)
+        for k in range(0, a.m, max(1, a.m // 40)):
+            ref = O.routing_summary(H[0], Kg, segs_o.members[k], W[g])
+            assert np.all(np.abs(a.Kr[k] - ref) <= 2.0 ** -7 * np.max(np.abs(ref)) + 1e-30), (g, k)
+    steps = 3
+    q_np = np.stack([synth.queries(s, 0, t).numpy().astype(np.float64) for t in range(steps)])
+    taus = T.thresholds_for(q_np, arts, s.G, np.full(s.Hq, 0.08), s.B)
+    m_max = ctx.m_max()
+    gen = torch.Generator().manual_seed(9)
+    for t in range(steps):
+        q = q_np[t]
+        budgets = np.full(s.Hq, -1, np.int32)
+        for h in range(s.Hq):
+            a = arts[(0, h)]
+            sc = O.head_route_scores(q[0, h], a)
+            band = T.head_band(q[0, h], a)
+            order = _ranked(sc, O.logit_threshold(float(taus[h])))
+            ks = [k for k in range(1, len(order)) if _cut_ok(sc, band, order, k, set())]
+            if h % 4 != 3 and ks:
+                budgets[h] = min(ks, key=lambda k: abs(k - len(order) // 2))
+        out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+        mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
+        ctx.decode_attn(0, torch.from_numpy(q.astype(np.float32)).to(DEV), taus, out, mask, budget=budgets)
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy().astype(np.float64)
+        mask_h = mask.cpu().numpy()
+        capped = 0
+        for h in range(s.Hq):
+            a = arts[(0, h)]
+            T.assert_no_ties(q[0, h], float(taus[h]), a)
+            bud = int(budgets[h])
+            o_ref, z_ref, _ = O.decode_head(q[0, h], float(taus[h]), a, bud)
+            assert np.array_equal(mask_h[0, h, :a.m].astype(bool), z_ref), f"mask differs: step {t} h {h}"
+            assert T.rel_err(out_h[0, h], o_ref) <= 1e-4, f"step {t} h {h}"
+            capped += int(bud >= 0)
+        assert capped > s.Hq // 2
+        # a few decoded tokens join the window before the next step
+        Kn = torch.randn(s.B, s.Hkv, 3, s.d, generator=gen).to(torch.bfloat16)
+        Vn = torch.randn(s.B, s.Hkv, 3, s.d, generator=gen).to(torch.bfloat16)
+        ctx.append_tokens(0, Kn.to(DEV).contiguous(), Vn.to(DEV).contiguous())
+        for g in range(s.Hkv):
+            arts[(0, g)] = O.append_tokens(arts[(0, g)], Kn[0, g].float().numpy().astype(np.float64),
+                                           Vn[0, g].float().numpy().astype(np.float64))
