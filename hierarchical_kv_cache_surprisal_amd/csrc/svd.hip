@@ -7,28 +7,32 @@
 // every rank gate on).
 //
 // Short spans (c <= 128): one-sided Jacobi (Hestenes) on the c rows of X held
-// in LDS: plane rotations of row pairs until all pairs are orthogonal, with the
-// rotations accumulated in J (c x c), so X = J X' with orthogonal rows x'_i.
-// Then U = J, sigma_i = |x'_i|, V_i = x'_i / sigma_i.
+// in LDS: plane rotations of row pairs until all pairs are orthogonal,
+// X = J X' with orthogonal rows x'_i.  Then sigma_i = |x'_i|,
+// V_i = x'_i / sigma_i, and A = U_r Sigma_r = X V_r is formed from the original
+// rows (streamed again from X), so J is never stored.
 //
-// Tall spans (c > 128): the d x d Gram matrix X^T X is accumulated in fp64,
-// factored by Cholesky (R^T R, semidefinite pivots dropped) and one-sided
-// Jacobi orthogonalises the columns of R (R J = N); then V = J,
-// sigma_i = |N_i| and A = X V_r is streamed from X.  fp64 for the Gram and the
-// factorisation keeps the squared condition number away from fp32 rounding.
+// Tall spans (c > 128): the d x d Gram matrix X^T X is accumulated in fp64
+// (upper triangle, packed), factored by Cholesky (R^T R, semidefinite pivots
+// dropped) and one-sided Jacobi orthogonalises the rows of R (R = J N with
+// orthogonal rows n_i, so R^T R = N^T N and the right singular vectors of X
+// are the normalised n_i); sigma_i = |n_i| and A = X V_r is streamed from X.
+// fp64 for the Gram and the factorisation keeps the squared condition number
+// away from fp32 rounding.
 //
 // Rotations are applied to disjoint pairs in parallel (round-robin tournament
-// ordering), one group of 512/PMAX threads per pair.
+// ordering), one group of 512/PMAX threads per pair.  Neither path keeps the
+// rotations, so a workgroup needs about 70 KB of LDS and two fit on a CU.
 #include "sekv_device.h"
 
 namespace sekv {
 
 namespace {
 
-// One-sided Jacobi on p vectors (length D, stride XS) with the rotations applied
-// to p companion vectors (length p, stride JS).  All threads of the workgroup.
+// One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
+// of the workgroup.
 template <int D, int PMAX>
-__device__ void jacobi_sweeps(float* Xv, int XS, float* Jv, int JS, int p, int* s_rot) {
+__device__ void jacobi_sweeps(float* Xv, int XS, int p, int* s_rot) {
   constexpr int TPP = 512 / PMAX;
   const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
   const int pe = p + (p & 1);
@@ -76,13 +80,6 @@ __device__ void jacobi_sweeps(float* Xv, int XS, float* Jv, int JS, int p, int* 
           const float u = xi[e], v = xj[e];
           xi[e] = cs * u - sn * v;
           xj[e] = sn * u + cs * v;
-        }
-        float* ji = Jv + i * JS;
-        float* jj = Jv + j * JS;
-        for (int e = li; e < p; e += TPP) {
-          const float u = ji[e], v = jj[e];
-          ji[e] = cs * u - sn * v;
-          jj[e] = sn * u + cs * v;
         }
         if (li == 0) *s_rot = 1;
       }
@@ -141,12 +138,48 @@ __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt
 
 // ---------------------------------------------------------------- short spans
 
+// A^T [r][c8] = (X V_r)^T from the original rows of X (streamed ROWS at a time
+// through Xr), with V_i = Vt[order[kk]] / sig[order[kk]]; zero beyond c.
+template <int D, typename T, int ROWS>
+__device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src, float* Xr, const float* Vt,
+                                  int VS, const float* sig, const int* order) {
+  constexpr int XS = D + 1;
+  T* At = block_ptr<T, D>(a, p, false);
+  const int c8 = (int)pad8(p.c);
+  const int r = p.r;
+  for (int t0 = 0; t0 < p.c; t0 += ROWS) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
+      const int t = idx / D, e = idx % D;
+      Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROWS * r; idx += kThreads) {
+      const int t = idx % ROWS, kk = idx / ROWS;
+      if (t0 + t >= p.c) continue;
+      const int i = order[kk];
+      const float si = sig[i];
+      float s = 0.f;
+      if (si > 0.f) {
+        for (int e = 0; e < D; ++e) s += Xr[t * XS + e] * Vt[i * VS + e];
+        s /= si;
+      }
+      At[(size_t)kk * c8 + t0 + t] = Elem<T>::from_f(s);
+    }
+  }
+  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kThreads) {
+    const int kk = idx / (c8 - p.c), t = p.c + idx % (c8 - p.c);
+    At[(size_t)kk * c8 + t] = Elem<T>::from_f(0.f);
+  }
+}
+
 template <int D, typename T, int PMAX>
 __global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
   extern __shared__ float smem[];
-  constexpr int XS = D + 1, JS = PMAX + 1;
-  float* X = smem;                 // [PMAX][XS]
-  float* Jv = smem + PMAX * XS;    // [PMAX][JS]
+  constexpr int XS = D + 1;
+  constexpr int ROWS = 16;
+  float* X = smem;                 // [PMAX][XS]: rows of X, orthogonalised in place
+  float* Xr = smem + PMAX * XS;    // [ROWS][XS]: original rows, for A
   __shared__ float sig[PMAX];
   __shared__ int order[PMAX];
   __shared__ int s_rot;
@@ -157,23 +190,12 @@ __global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
     const int t = idx / D, e = idx % D;
     X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
   }
-  for (int idx = threadIdx.x; idx < p.c * p.c; idx += kThreads) {
-    const int i = idx / p.c, t = idx % p.c;
-    Jv[i * JS + t] = (i == t) ? 1.f : 0.f;
-  }
   __syncthreads();
-  jacobi_sweeps<D, PMAX>(X, XS, Jv, JS, p.c, &s_rot);
+  jacobi_sweeps<D, PMAX>(X, XS, p.c, &s_rot);
   __syncthreads();
   rank_by_norm(X, XS, D, p.c, p.r, sig, order);
 
-  // A^T [r][c8]: row kk = sigma_i * (column i of J), zero beyond c
-  T* At = block_ptr<T, D>(a, p, false);
-  const int c8 = (int)pad8(p.c);
-  for (int idx = threadIdx.x; idx < p.r * c8; idx += kThreads) {
-    const int kk = idx / c8, t = idx % c8;
-    const int i = order[kk];
-    At[idx] = Elem<T>::from_f(t < p.c ? Jv[i * JS + t] * sig[i] : 0.f);
-  }
+  // B^T rows: the chosen orthogonal rows, normalised
   T* Bt = block_ptr<T, D>(a, p, true);
   for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
     const int kk = idx / D, e = idx % D;
@@ -181,19 +203,26 @@ __global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
     const float s = sig[i];
     Bt[idx] = Elem<T>::from_f(s > 0.f ? X[i * XS + e] / s : 0.f);
   }
+  store_a_from_rows<D, T, ROWS>(a, p, src, Xr, X, XS, sig, order);
 }
 
 // ---------------------------------------------------------------- tall spans
 
+// Packed upper triangle of a D x D symmetric matrix: (i, j), j >= i.
+template <int D>
+__device__ __forceinline__ int upk(int i, int j) {
+  return i * D - (i * (i - 1)) / 2 + (j - i);
+}
+
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
   extern __shared__ double smd[];
-  constexpr int GS = D + 1;       // Gram row stride (doubles)
   constexpr int XS = D + 1;       // float vector stride
-  constexpr int ROWS = 32;        // X rows staged per step
+  constexpr int ROWS = 16;        // X rows staged per step
   constexpr int NB = D / 8;       // 8x8 Gram blocks per dimension
-  double* Gm = smd;                                       // [D][GS]
-  float* Xs = reinterpret_cast<float*>(smd + D * GS);     // [ROWS][D]
+  constexpr int NP = D * (D + 1) / 2;
+  double* Gp = smd;                                       // [NP] packed upper Gram, then R
+  float* Xs = reinterpret_cast<float*>(smd + NP);         // [ROWS][D]
   __shared__ float sig[D];
   __shared__ int order[D];
   __shared__ int s_rot;
@@ -202,9 +231,9 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
 
-  // 1. Gram matrix in fp64
+  // 1. Gram matrix in fp64 (8 x 8 blocks on and above the diagonal)
   const int bi = threadIdx.x / NB, bj = threadIdx.x % NB;
-  const bool gact = threadIdx.x < NB * NB;
+  const bool gact = threadIdx.x < NB * NB && bj >= bi;
   double gacc[8][8];
 #pragma unroll
   for (int u = 0; u < 8; ++u)
@@ -236,97 +265,78 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int v = 0; v < 8; ++v) Gm[(bi * 8 + u) * GS + bj * 8 + v] = gacc[u][v];
+      for (int v = 0; v < 8; ++v) {
+        const int gi = bi * 8 + u, gj = bj * 8 + v;
+        if (gj >= gi) Gp[upk<D>(gi, gj)] = gacc[u][v];
+      }
   }
   __syncthreads();
 
   // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped
   if (threadIdx.x == 0) {
     double mx = 0.0;
-    for (int i = 0; i < D; ++i) mx = fmax(mx, Gm[i * GS + i]);
+    for (int i = 0; i < D; ++i) mx = fmax(mx, Gp[upk<D>(i, i)]);
     s_tol = mx * (double)D * 4.440892098500626e-16;
   }
   __syncthreads();
   const double tolc = s_tol;
   for (int kc = 0; kc < D; ++kc) {
     if (threadIdx.x == 0) {
-      const double piv = Gm[kc * GS + kc];
+      const double piv = Gp[upk<D>(kc, kc)];
       s_rkk = piv > tolc ? sqrt(piv) : 0.0;
     }
     __syncthreads();
     const double rkk = s_rkk;
-    for (int j = kc + threadIdx.x; j < D; j += kThreads)
-      Gm[kc * GS + j] = rkk > 0.0 ? (j == kc ? rkk : Gm[kc * GS + j] / rkk) : 0.0;
+    for (int j = kc + threadIdx.x; j < D; j += kThreads) {
+      const int q = upk<D>(kc, j);
+      Gp[q] = rkk > 0.0 ? (j == kc ? rkk : Gp[q] / rkk) : 0.0;
+    }
     __syncthreads();
     const int w = D - kc - 1;
     for (int idx = threadIdx.x; idx < w * w; idx += kThreads) {
       const int i = kc + 1 + idx / w, j = kc + 1 + idx % w;
-      if (j >= i) Gm[i * GS + j] -= Gm[kc * GS + i] * Gm[kc * GS + j];
+      if (j >= i) Gp[upk<D>(i, j)] -= Gp[upk<D>(kc, i)] * Gp[upk<D>(kc, j)];
     }
     __syncthreads();
   }
 
-  // 3. columns of R (fp32) and J = I
+  // 3. rows of R in fp32 (through registers: they overwrite the packed factor)
   constexpr int PER = D * D / kThreads;
   float rv[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = threadIdx.x + u * kThreads;
-    const int col = idx / D, row = idx % D;
-    rv[u] = row <= col ? (float)Gm[row * GS + col] : 0.f;
+    const int row = idx / D, col = idx % D;
+    rv[u] = col >= row ? (float)Gp[upk<D>(row, col)] : 0.f;
   }
   __syncthreads();
-  float* Rc = reinterpret_cast<float*>(smd);  // [D][XS]: vector col = column col of R
-  float* Jv = Rc + D * XS;                    // [D][XS]
+  float* Rr = reinterpret_cast<float*>(smd);  // [D][XS]: vector row = row `row` of R
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = threadIdx.x + u * kThreads;
-    const int col = idx / D, row = idx % D;
-    Rc[col * XS + row] = rv[u];
-    Jv[col * XS + row] = (row == col) ? 1.f : 0.f;
+    const int row = idx / D, col = idx % D;
+    Rr[row * XS + col] = rv[u];
   }
   __syncthreads();
-  jacobi_sweeps<D, D>(Rc, XS, Jv, XS, D, &s_rot);
+  jacobi_sweeps<D, D>(Rr, XS, D, &s_rot);
   __syncthreads();
-  const int r = p.r;
-  rank_by_norm(Rc, XS, D, D, r, sig, order);
+  rank_by_norm(Rr, XS, D, D, p.r, sig, order);
 
-  // 4. B^T rows = chosen columns of V = J
+  // 4. B^T rows = the chosen orthogonal rows of R, normalised
   T* Bt = block_ptr<T, D>(a, p, true);
-  for (int idx = threadIdx.x; idx < r * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
     const int kk = idx / D, e = idx % D;
-    Bt[idx] = Elem<T>::from_f(sig[order[kk]] > 0.f ? Jv[order[kk] * XS + e] : 0.f);
+    const int i = order[kk];
+    Bt[idx] = Elem<T>::from_f(sig[i] > 0.f ? Rr[i * XS + e] / sig[i] : 0.f);
   }
-  // 5. A = X V_r, streamed (R no longer needed: reuse its LDS for X rows), stored as A^T [r][c8]
-  T* At = block_ptr<T, D>(a, p, false);
-  const int c8 = (int)pad8(p.c);
-  float* Xr = Rc;  // [ROWS][XS]
-  for (int t0 = 0; t0 < p.c; t0 += ROWS) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
-      const int t = idx / D, e = idx % D;
-      Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * r; idx += kThreads) {
-      const int t = idx / r, kk = idx % r;
-      if (t0 + t >= p.c) continue;
-      const int i = order[kk];
-      float s = 0.f;
-      if (sig[i] > 0.f)
-        for (int e = 0; e < D; ++e) s += Xr[t * XS + e] * Jv[i * XS + e];
-      At[(size_t)kk * c8 + t0 + t] = Elem<T>::from_f(s);
-    }
-  }
-  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kThreads) {
-    const int kk = idx / (c8 - p.c), t = p.c + idx % (c8 - p.c);
-    At[(size_t)kk * c8 + t] = Elem<T>::from_f(0.f);
-  }
+  // 5. A = X V_r, streamed from X through the staging rows
+  float* Xr = Rr + D * XS;  // [ROWS][XS], after the rows of R
+  store_a_from_rows<D, T, ROWS>(a, p, src, Xr, Rr, XS, sig, order);
 }
 
 template <int D, typename T, int PMAX>
 void launch_rows(const SvdArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(float) * (PMAX * (D + 1) + PMAX * (PMAX + 1));
+  const size_t lds = sizeof(float) * (PMAX + 16) * (D + 1);
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
@@ -338,7 +348,10 @@ void launch_rows(const SvdArgs& a, hipStream_t s) {
 
 template <int D, typename T>
 void launch_tall(const SvdArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(double) * D * (D + 1) + sizeof(float) * 32 * D;
+  // max(packed fp64 Gram + 16 staged rows, fp32 rows of R + 16 staged rows)
+  const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * D;
+  const size_t rows = sizeof(float) * (D + 16) * (D + 1);
+  const size_t lds = gram > rows ? gram : rows;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
