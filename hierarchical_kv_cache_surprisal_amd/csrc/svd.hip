@@ -29,14 +29,24 @@ namespace sekv {
 
 namespace {
 
+constexpr int kSvdThreads = 512;  // 8 waves per workgroup
+
+// Rotation threshold: a pair is rotated while |x_i . x_j| > tol |x_i| |x_j|.
+// fp32 storage: p ulps of fp32; bf16 storage: 1e-4, far below the storage
+// rounding of the factors (2^-9).
+template <typename T>
+__device__ __forceinline__ float jacobi_tol(int p) {
+  return sizeof(T) == 2 ? 1e-4f : (float)(p + (p & 1)) * 1.1920929e-7f;
+}
+
 // One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
-// of the workgroup.
+// of the workgroup; each disjoint pair of a round gets 2 * kSvdThreads / PMAX
+// threads.
 template <int D, int PMAX>
-__device__ void jacobi_sweeps(float* Xv, int XS, int p, int* s_rot) {
-  constexpr int TPP = 512 / PMAX;
+__device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
+  constexpr int TPP = 2 * kSvdThreads / PMAX;
   const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
   const int pe = p + (p & 1);
-  const float tol = (float)pe * 1.1920929e-7f;
   if (p < 2) return;
   for (int sweep = 0; sweep < 40; ++sweep) {
     if (threadIdx.x == 0) *s_rot = 0;
@@ -93,13 +103,13 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, int* s_rot) {
 
 // sigma_i = |v_i| for p vectors, and order[kk] = index of the kk-th largest (kk < r).
 __device__ void rank_by_norm(const float* Xv, int XS, int len, int p, int r, float* sig, int* order) {
-  for (int i = threadIdx.x; i < p; i += kThreads) {
+  for (int i = threadIdx.x; i < p; i += kSvdThreads) {
     float s = 0.f;
     for (int e = 0; e < len; ++e) s += Xv[i * XS + e] * Xv[i * XS + e];
     sig[i] = sqrtf(s);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < p; i += kThreads) {
+  for (int i = threadIdx.x; i < p; i += kSvdThreads) {
     const float si = sig[i];
     int rk = 0;
     for (int j = 0; j < p; ++j) rk += (sig[j] > si || (sig[j] == si && j < i)) ? 1 : 0;
@@ -149,12 +159,12 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
   const int r = p.r;
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += kSvdThreads) {
       const int t = idx / D, e = idx % D;
       Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * r; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < ROWS * r; idx += kSvdThreads) {
       const int t = idx % ROWS, kk = idx / ROWS;
       if (t0 + t >= p.c) continue;
       const int i = order[kk];
@@ -167,14 +177,14 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
       At[(size_t)kk * c8 + t0 + t] = Elem<T>::from_f(s);
     }
   }
-  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kThreads) {
+  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kSvdThreads) {
     const int kk = idx / (c8 - p.c), t = p.c + idx % (c8 - p.c);
     At[(size_t)kk * c8 + t] = Elem<T>::from_f(0.f);
   }
 }
 
 template <int D, typename T, int PMAX>
-__global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
+__global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
   extern __shared__ float smem[];
   constexpr int XS = D + 1;
   constexpr int ROWS = 16;
@@ -186,18 +196,18 @@ __global__ __launch_bounds__(kThreads) void k_svd_rows(SvdArgs a) {
 
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
-  for (int idx = threadIdx.x; idx < p.c * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < p.c * D; idx += kSvdThreads) {
     const int t = idx / D, e = idx % D;
     X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
   }
   __syncthreads();
-  jacobi_sweeps<D, PMAX>(X, XS, p.c, &s_rot);
+  jacobi_sweeps<D, PMAX>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot);
   __syncthreads();
   rank_by_norm(X, XS, D, p.c, p.r, sig, order);
 
   // B^T rows: the chosen orthogonal rows, normalised
   T* Bt = block_ptr<T, D>(a, p, true);
-  for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < p.r * D; idx += kSvdThreads) {
     const int kk = idx / D, e = idx % D;
     const int i = order[kk];
     const float s = sig[i];
@@ -215,7 +225,7 @@ __device__ __forceinline__ int upk(int i, int j) {
 }
 
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
+__global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   extern __shared__ double smd[];
   constexpr int XS = D + 1;       // float vector stride
   constexpr int ROWS = 16;        // X rows staged per step
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) gacc[u][v] = 0.0;
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
-    for (int idx = threadIdx.x; idx < ROWS * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += kSvdThreads) {
       const int t = idx / D, e = idx % D;
       Xs[idx] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
@@ -287,13 +297,13 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
     }
     __syncthreads();
     const double rkk = s_rkk;
-    for (int j = kc + threadIdx.x; j < D; j += kThreads) {
+    for (int j = kc + threadIdx.x; j < D; j += kSvdThreads) {
       const int q = upk<D>(kc, j);
       Gp[q] = rkk > 0.0 ? (j == kc ? rkk : Gp[q] / rkk) : 0.0;
     }
     __syncthreads();
     const int w = D - kc - 1;
-    for (int idx = threadIdx.x; idx < w * w; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < w * w; idx += kSvdThreads) {
       const int i = kc + 1 + idx / w, j = kc + 1 + idx % w;
       if (j >= i) Gp[upk<D>(i, j)] -= Gp[upk<D>(kc, i)] * Gp[upk<D>(kc, j)];
     }
@@ -301,11 +311,11 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
   }
 
   // 3. rows of R in fp32 (through registers: they overwrite the packed factor)
-  constexpr int PER = D * D / kThreads;
+  constexpr int PER = D * D / kSvdThreads;
   float rv[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int idx = threadIdx.x + u * kThreads;
+    const int idx = threadIdx.x + u * kSvdThreads;
     const int row = idx / D, col = idx % D;
     rv[u] = col >= row ? (float)Gp[upk<D>(row, col)] : 0.f;
   }
@@ -313,18 +323,18 @@ __global__ __launch_bounds__(kThreads) void k_svd_tall(SvdArgs a) {
   float* Rr = reinterpret_cast<float*>(smd);  // [D][XS]: vector row = row `row` of R
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int idx = threadIdx.x + u * kThreads;
+    const int idx = threadIdx.x + u * kSvdThreads;
     const int row = idx / D, col = idx % D;
     Rr[row * XS + col] = rv[u];
   }
   __syncthreads();
-  jacobi_sweeps<D, D>(Rr, XS, D, &s_rot);
+  jacobi_sweeps<D, D>(Rr, XS, D, jacobi_tol<T>(D), &s_rot);
   __syncthreads();
   rank_by_norm(Rr, XS, D, D, p.r, sig, order);
 
   // 4. B^T rows = the chosen orthogonal rows of R, normalised
   T* Bt = block_ptr<T, D>(a, p, true);
-  for (int idx = threadIdx.x; idx < p.r * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < p.r * D; idx += kSvdThreads) {
     const int kk = idx / D, e = idx % D;
     const int i = order[kk];
     Bt[idx] = Elem<T>::from_f(sig[i] > 0.f ? Rr[i * XS + e] / sig[i] : 0.f);
@@ -343,7 +353,7 @@ void launch_rows(const SvdArgs& a, hipStream_t s) {
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(kSvdThreads), lds, s, a);
 }
 
 template <int D, typename T>
@@ -358,7 +368,7 @@ void launch_tall(const SvdArgs& a, hipStream_t s) {
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((k_svd_tall<D, T>), dim3(a.n_problems), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((k_svd_tall<D, T>), dim3(a.n_problems), dim3(kSvdThreads), lds, s, a);
 }
 
 template <int D, typename T>
