@@ -37,8 +37,9 @@ design notes):
     span contributes one summary entry with logit q.kbar/sqrt(d) + ln|S|.
   * budget cap: a budget counts zoomed spans per (sequence, query head);
     equal scores are ranked by span index, lower first.
-  * decode-time append: appended tokens stay in the full-resolution window
-    and are not re-segmented into spans.
+  * decode-time append: appended tokens join the full-resolution window;
+    re-segmentation (resegment_window) moves rows older than the last w
+    positions out of it, with the prefill's threshold.
   * stored artefacts (summaries, SVD factors) are rounded to the KV dtype
     with round-to-nearest-even; everything else is fp64.
 
@@ -427,6 +428,73 @@ def append_tokens(art: HeadArtifacts, K_new, V_new) -> HeadArtifacts:
     K_new = np.asarray(K_new, dtype=np.float64).reshape(-1, art.KA.shape[1])
     V_new = np.asarray(V_new, dtype=np.float64).reshape(-1, art.VA.shape[1])
     return dataclasses.replace(art, KA=np.concatenate([art.KA, K_new]), VA=np.concatenate([art.VA, V_new]))
+
+
+def resegment_window(art: HeadArtifacts, positions, H_all, theta: float, w: int, n_total: int,
+                     layer: int, g: int, choices: Sequence[int], seed: int) -> HeadArtifacts:
+    """Streaming re-segmentation of the full-resolution window  [Summary 2.1 and Figure 2,
+    applied to decoded tokens].
+
+    positions: the context position of every row of art.KA / art.VA.  H_all: the
+    surprisal of every position so far (prefill and decoded tokens); theta: the
+    prefill's mu + alpha * sigma; n_total: positions so far.  The window keeps the
+    last w positions; an older row leaves it when it is not itself a boundary
+    (H_t <= theta: a row above theta stays a full-resolution anchor).  Readings:
+      * the threshold stays the prefill's (earlier cuts never move);
+      * every maximal run of consecutive leaving positions becomes a new span; a
+        run next to the last span before the window starts a span of its own,
+        since that span's members are no longer held at full resolution;
+      * new spans follow the existing ones (span index m_old, m_old + 1, ...), with
+        summaries, routing summaries, hard ranks and truncated SVD bases built as
+        in the prefill from the stored rows.
+    Returns the new artefacts; the positions of the remaining rows are
+    [p for p in positions if p is not leaving], in their order.
+    """
+    H_all = np.asarray(H_all, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    leave = (positions < n_total - w) & (H_all[positions] <= theta)
+    order = np.argsort(positions[leave], kind="stable")
+    rows = np.flatnonzero(leave)[order]
+    runs: List[np.ndarray] = []
+    for r in rows:
+        if runs and positions[r] == positions[runs[-1][-1]] + 1:
+            runs[-1] = np.append(runs[-1], r)
+        else:
+            runs.append(np.array([r]))
+    KA = np.asarray(art.KA, dtype=np.float64)
+    VA = np.asarray(art.VA, dtype=np.float64)
+    d = KA.shape[1]
+    mstart, mcount = list(art.mstart), list(art.mcount)
+    kbar, vbar, rank = list(art.kbar), list(art.vbar), list(art.rank)
+    AK, BKt, AV, BVt = list(art.AK), list(art.BKt), list(art.AV), list(art.BVt)
+    Kr = None if art.Kr is None else list(art.Kr)
+    m_old = art.m
+    for j, run in enumerate(runs):
+        k = m_old + j
+        mem = np.arange(run.size)                    # members, in the gathered rows
+        Hm = H_all[positions[run]]
+        Kmem, Vmem = KA[run], VA[run]
+        mstart.append(int(positions[run[0]]))
+        mcount.append(int(run.size))
+        kbar.append(round_to(weighted_mean(Hm, Kmem, mem), art.kv_dtype))
+        vbar.append(round_to(weighted_mean(Hm, Vmem, mem), art.kv_dtype))
+        if Kr is not None:
+            Kr.append(round_to(routing_summary(Hm, Kmem, mem, art.W), art.kv_dtype))
+        r = min(span_rank(seed, layer, g, k, choices), run.size, d)
+        rank.append(r)
+        a, bt = truncated_svd(Kmem, r)
+        AK.append(round_to(a, art.kv_dtype))
+        BKt.append(round_to(bt, art.kv_dtype))
+        a, bt = truncated_svd(Vmem, r)
+        AV.append(round_to(a, art.kv_dtype))
+        BVt.append(round_to(bt, art.kv_dtype))
+    keep = ~leave
+    dm = lambda lst: np.asarray(lst, dtype=np.float64).reshape(-1, d) if lst else np.zeros((0, d))
+    return dataclasses.replace(
+        art, mstart=np.asarray(mstart, dtype=np.int64), mcount=np.asarray(mcount, dtype=np.int64),
+        anchors=positions[keep].copy(), kbar=dm(kbar), vbar=dm(vbar), KA=KA[keep].copy(), VA=VA[keep].copy(),
+        rank=np.asarray(rank, dtype=np.int64), AK=AK, BKt=BKt, AV=AV, BVt=BVt,
+        Kr=None if Kr is None else np.asarray(Kr, dtype=np.float64).reshape(len(Kr), -1))
 
 
 # ----------------------------------------------------------------------------

@@ -552,3 +552,61 @@ def test_appended_dominant_token_takes_the_output():
     v_new = rng.standard_normal(d)
     o, _, _ = O.decode_head(q, 0.5, O.append_tokens(art, 400.0 * q / np.linalg.norm(q), v_new))
     assert np.allclose(o, v_new, rtol=0, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- window re-segmentation
+
+_RS = _load("resegment_hand.json")
+
+
+def _prefill_then_append(H_pre, H_new, alpha, w, d=6, seed=0, kv="f64", choices=(4,)):
+    rng = np.random.default_rng(seed)
+    n, a = len(H_pre), len(H_new)
+    K = rng.standard_normal((n + a, d))
+    V = rng.standard_normal((n + a, d))
+    seg = O.segment(np.asarray(H_pre, dtype=np.float64), alpha, w)
+    art = O.build_head(np.asarray(H_pre, dtype=np.float64), K[:n], V[:n], seg, 0, 0, list(choices), 3, kv)
+    art = O.append_tokens(art, K[n:], V[n:])
+    positions = np.concatenate([seg.anchors, np.arange(n, n + a)])
+    H_all = np.concatenate([np.asarray(H_pre, dtype=np.float64), np.asarray(H_new, dtype=np.float64)])
+    return seg, art, positions, H_all, K, V
+
+
+@pytest.mark.parametrize("case", _RS["cases"], ids=lambda c: c["name"])
+def test_resegment_hand_worked(case):
+    pre = _RS["prefill"]
+    seg, art, positions, H_all, _, _ = _prefill_then_append(pre["H"], case["H_new"], pre["alpha"], pre["w"])
+    assert abs(seg.theta - pre["theta"]) < 1e-6
+    assert seg.anchors.tolist() == pre["anchors"]
+    new = O.resegment_window(art, positions, H_all, seg.theta, pre["w"], H_all.size, 0, 0, [4], 3)
+    assert new.mstart.tolist() == case["mstart"]
+    assert new.mcount.tolist() == case["mcount"]
+    assert new.anchors.tolist() == case["anchors"]
+    assert new.KA.shape[0] == len(case["anchors"])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_resegment_keeps_a_partition_and_dense_equivalence(seed):
+    """After appends and re-segmentation every position is a member of exactly one
+    span or an anchor row, and with tau = 0, full ranks and exact storage the
+    mixed softmax is dense attention over every position so far."""
+    rng = np.random.default_rng(200 + seed)
+    n, a, w, d = 120, int(rng.integers(5, 60)), int(rng.integers(0, 20)), 8
+    H_pre = rng.lognormal(0.0, 0.8, n)
+    H_new = rng.lognormal(0.0, 0.8, a)
+    seg, art, positions, H_all, K, V = _prefill_then_append(H_pre, H_new, 0.5, w, d=d, seed=seed, choices=(d,))
+    new = O.resegment_window(art, positions, H_all, seg.theta, w, n + a, 0, 0, [d], 3)
+    covered = np.zeros(n + a, dtype=int)
+    for k in range(new.m):
+        if k < seg.m:
+            covered[seg.members[k]] += 1
+        else:
+            covered[new.mstart[k]:new.mstart[k] + new.mcount[k]] += 1
+    covered[new.anchors] += 1
+    assert np.all(covered == 1)
+    q = rng.standard_normal(d)
+    o, _, _ = O.decode_head(q, 0.0, new)
+    assert np.allclose(o, O.dense_attention(q, K, V), rtol=0, atol=1e-10)
+    # a second pass with nothing new to move changes nothing
+    again = O.resegment_window(new, new.anchors, H_all, seg.theta, w, n + a, 0, 0, [d], 3)
+    assert again.m == new.m and np.array_equal(again.anchors, new.anchors)
