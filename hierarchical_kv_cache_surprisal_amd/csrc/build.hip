@@ -282,6 +282,20 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendArgs a, int row_bytes
   }
 }
 
+// Block (bg, chunk) gathers rows of one (sequence, kv head) in 16-byte pieces.
+__global__ __launch_bounds__(kThreads) void k_gather_rows(GatherArgs a) {
+  const int bg = blockIdx.x, b = bg / a.Hkv;
+  const int n = a.cnt[b];
+  const int p16 = a.row_bytes / 16;
+  const uint4* in = reinterpret_cast<const uint4*>(a.in) + (size_t)bg * a.in_rows * p16;
+  uint4* out = reinterpret_cast<uint4*>(a.out) + (size_t)bg * a.out_rows * p16;
+  const int32_t* idx = a.idx + (size_t)b * a.idx_stride;
+  for (int i = blockIdx.y * kThreads + threadIdx.x; i < n * p16; i += gridDim.y * kThreads) {
+    const int row = i / p16, piece = i % p16;
+    out[(size_t)row * p16 + piece] = in[(size_t)idx[row] * p16 + piece];
+  }
+}
+
 // The counts follow in their own launch, after every copy has read them.
 __global__ void k_append_count(int32_t* na, int B, int n_new) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -336,6 +350,12 @@ void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s
   const int chunks = std::max(1, std::min(64, (a.n_new * row_bytes / 16 + kThreads - 1) / kThreads));
   hipLaunchKernelGGL(k_append, dim3(B * a.Hkv, chunks), dim3(kThreads), 0, s, a, row_bytes);
   hipLaunchKernelGGL(k_append_count, dim3((B + 255) / 256), dim3(256), 0, s, a.na, B, a.n_new);
+}
+
+void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s) {
+  if (a.max_cnt <= 0) return;
+  const int chunks = std::max(1, std::min(64, (a.max_cnt * (a.row_bytes / 16) + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_gather_rows, dim3(B * a.Hkv, chunks), dim3(kThreads), 0, s, a);
 }
 
 void launch_rank_gates(int kv_bf16, const GateArgs& a, hipStream_t s) {

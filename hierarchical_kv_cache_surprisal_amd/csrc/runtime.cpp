@@ -111,6 +111,8 @@ struct LayerState {
   std::vector<int32_t> na_l;       // [B] anchors of this layer per sequence (grows with appends)
   int32_t* na_l_d = nullptr;       // device copy
   std::vector<uint8_t> route_set;  // [B*Hkv] routing summaries present
+  std::vector<int32_t> choices;    // rank choices and seed of its build (re-segmentation ranks)
+  uint64_t seed = 0;
   LayerCache lc;                   // device cache of its host-resident bases
   LayerSched sched;
 };
@@ -134,7 +136,13 @@ struct sekv_ctx {
   bool spans_ready = false;
   bool spans_built = false;
   double alpha = 0.0;
-  std::vector<float> H_first;
+  // window re-segmentation (contexts whose span table came from sekv_build)
+  int m_reserve = 0;                            // spare span rows per sequence
+  std::vector<std::vector<float>> H_seq;        // [B] surprisal of every position so far
+  std::vector<double> theta_b;                  // [B] the prefill's mu + alpha sigma
+  std::vector<std::vector<int32_t>> row_pos;    // [B] positions of the anchor rows every layer holds
+  std::vector<int32_t> next_pos;                // [B] position of the next appended row
+  bool resegmented = false;
   int m_max = 0, na_max = 0;
   std::vector<int32_t> m_b, na_b;
   std::vector<std::vector<int32_t>> mstart, mcount, anchors;
@@ -326,7 +334,8 @@ sekv_status install_spans(sekv_ctx* c) {
     mm = std::max(mm, c->m_b[b]);
     nm = std::max(nm, c->na_b[b]);
   }
-  c->m_max = mm;
+  c->m_max = mm + c->m_reserve;  // the row stride of every per-span array
+  mm = c->m_max;
   c->na_max = nm;
   dfree(c->m_b_d);
   dfree(c->na_b_d);
@@ -1022,6 +1031,7 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SEKV_ERR_INVALID, "layer out of range");
   if (!H || !K || !V) return fail(c, SEKV_ERR_INVALID, "NULL H, K or V");
   if (!std::isfinite(alpha)) return fail(c, SEKV_ERR_INVALID, "alpha must be finite");
+  if (c->resegmented) return fail(c, SEKV_ERR_STATE, "the window was re-segmented: build every layer first");
   if (!rank_choices || n_choices < 1) return fail(c, SEKV_ERR_INVALID, "rank choices missing");
   for (int i = 0; i < n_choices; ++i)
     if (rank_choices[i] < 1) return fail(c, SEKV_ERR_INVALID, "rank choice < 1");
@@ -1072,6 +1082,16 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
     TRY(install_spans(c));
     c->spans_built = true;
     c->alpha = alpha;
+    // what re-segmenting the window needs later: surprisal, thresholds, row positions
+    c->H_seq.assign(B, std::vector<float>(n));
+    for (int b = 0; b < B; ++b)
+      HIPCHK(c, hipMemcpy(c->H_seq[b].data(), H + (size_t)b * n, (size_t)n * 4, hipMemcpyDeviceToHost));
+    std::vector<double> st(3 * (size_t)B);
+    HIPCHK(c, hipMemcpy(st.data(), c->seg_stats, st.size() * 8, hipMemcpyDeviceToHost));
+    c->theta_b.assign(B, 0.0);
+    for (int b = 0; b < B; ++b) c->theta_b[b] = st[3 * b + 2];
+    c->row_pos = an;
+    c->next_pos.assign(B, n);
   }
 
   // 2. ranks and layout
@@ -1087,6 +1107,8 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
       }
   TRY(alloc_layer(c, layer, rank));
   LayerState& L = c->layers[layer];
+  L.choices.assign(rank_choices, rank_choices + n_choices);
+  L.seed = rank_seed;
 
   // 3. summaries and anchors
   SummaryArgs su;
@@ -1479,7 +1501,7 @@ sekv_status sekv_export_head(const sekv_ctx* cc, int32_t layer, int32_t b, int32
   LayerState& L = c->layers[layer];
   const size_t bg = (size_t)b * Hkv + g;
   if (!L.allocated || !L.head_set[bg]) return fail(c, SEKV_ERR_STATE, "head has no artefacts");
-  const int m = c->m_b[b], na = c->na_b[b], mm = c->m_max;
+  const int m = c->m_b[b], na = L.na_l[b], mm = c->m_max;
   const size_t es = c->esz;
   if (kbar && m) HIPCHK(c, hipMemcpy(kbar, (char*)L.kbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
   if (vbar && m) HIPCHK(c, hipMemcpy(vbar, (char*)L.vbar + bg * mm * d * es, (size_t)m * d * es, hipMemcpyDeviceToHost));
@@ -1514,6 +1536,402 @@ sekv_status sekv_set_basis_cache(sekv_ctx* c, int64_t bytes) {
     TRY(dalloc(c, &c->cache_d, (size_t)elems * c->esz));
     c->cache_elems = elems;
   }
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------------------- window re-segmentation
+
+sekv_status sekv_reserve_spans(sekv_ctx* c, int32_t extra) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  if (extra < 0 || extra > (1 << 22)) return fail(c, SEKV_ERR_INVALID, "extra out of range");
+  if (c->spans_ready) return fail(c, SEKV_ERR_STATE, "the span table exists: reserve before the first build");
+  c->m_reserve = extra;
+  return SEKV_OK;
+}
+
+sekv_status sekv_append_surprisal(sekv_ctx* c, const float* H_new, int32_t n_new) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  if (c->H_seq.empty()) return fail(c, SEKV_ERR_STATE, "no surprisal record: the span table did not come from sekv_build");
+  if (n_new < 0 || (n_new > 0 && !H_new)) return fail(c, SEKV_ERR_INVALID, "bad H_new");
+  const int B = c->cfg.batch;
+  for (size_t i = 0; i < (size_t)B * n_new; ++i)
+    if (!std::isfinite(H_new[i]) || H_new[i] < 0.f) return fail(c, SEKV_ERR_INVALID, "surprisal must be finite and >= 0");
+  for (int b = 0; b < B; ++b) c->H_seq[b].insert(c->H_seq[b].end(), H_new + (size_t)b * n_new, H_new + (size_t)(b + 1) * n_new);
+  return SEKV_OK;
+}
+
+sekv_status sekv_resegment_window(sekv_ctx* c, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  if (c->H_seq.empty()) return fail(c, SEKV_ERR_STATE, "no surprisal record: the span table did not come from sekv_build");
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, NL = c->cfg.n_layers;
+  const int w = c->cfg.local_window, mm = c->m_max;
+  const size_t es = c->esz;
+  for (int l = 0; l < NL; ++l)
+    if (!c->layers[l].ready) return fail(c, SEKV_ERR_STATE, "every layer must be built before re-segmenting");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIPCHK(c, hipStreamIsCapturing(stream, &cs));
+  if (cs != hipStreamCaptureStatusNone) return fail(c, SEKV_ERR_STATE, "re-segmentation is not capturable");
+  // window rows, bases and cache tables are replaced below: nothing may still read them
+  HIPCHK(c, hipDeviceSynchronize());
+
+  // 1. host plan per sequence: row positions, leaving rows, runs
+  std::vector<std::vector<int32_t>> pos(B), keep_rows(B), mem_rows(B);
+  std::vector<std::vector<int32_t>> run_start(B), run_cnt(B), run_off(B);
+  int nm_max = 1, nr_max = 1, any = 0;
+  for (int b = 0; b < B; ++b) {
+    const int R = c->layers[0].na_l[b];
+    for (int l = 1; l < NL; ++l)
+      if (c->layers[l].na_l[b] != R) return fail(c, SEKV_ERR_STATE, "layers hold different window rows: append to every layer");
+    const int known = (int)c->row_pos[b].size();
+    if (R < known) return fail(c, SEKV_ERR_STATE, "window rows fewer than recorded");
+    pos[b] = c->row_pos[b];
+    for (int i = 0; i < R - known; ++i) pos[b].push_back(c->next_pos[b] + i);
+    const int n_tot = c->next_pos[b] + (R - known);
+    if ((int)c->H_seq[b].size() < n_tot)
+      return fail(c, SEKV_ERR_STATE, "surprisal missing for appended tokens (sekv_append_surprisal)");
+    for (int i = 0; i < R; ++i) {
+      const int p = pos[b][i];
+      const bool leaving = p < n_tot - w && !((double)c->H_seq[b][p] > c->theta_b[b]);
+      (leaving ? mem_rows[b] : keep_rows[b]).push_back(i);
+    }
+    // runs of consecutive positions (the rows are in position order)
+    for (size_t j = 0; j < mem_rows[b].size(); ++j) {
+      const int p = pos[b][mem_rows[b][j]];
+      if (j > 0 && p == pos[b][mem_rows[b][j - 1]] + 1) {
+        run_cnt[b].back()++;
+      } else {
+        run_start[b].push_back(p);
+        run_cnt[b].push_back(1);
+        run_off[b].push_back((int)j);
+      }
+    }
+    if (c->m_b[b] + (int)run_start[b].size() > mm)
+      return fail(c, SEKV_ERR_OOM, "no span rows left for the re-segmented window (sekv_reserve_spans)");
+    nm_max = std::max(nm_max, (int)mem_rows[b].size());
+    nr_max = std::max(nr_max, (int)run_start[b].size());
+    any |= !run_start[b].empty();
+  }
+  if (!any) {
+    // nothing leaves: only the positions of the rows appended since are recorded
+    for (int b = 0; b < B; ++b) {
+      const int known = (int)c->row_pos[b].size();
+      if ((int)pos[b].size() > known) c->next_pos[b] = pos[b].back() + 1;
+      c->row_pos[b] = pos[b];
+    }
+    return SEKV_OK;
+  }
+
+  // 2. device inputs shared by the layers: member row indices, their surprisal, the runs
+  std::vector<int32_t> idx_h((size_t)B * nm_max, 0), cnt_h(B), kidx_h, kcnt_h(B);
+  std::vector<float> Hm_h((size_t)B * nm_max, 0.f);
+  std::vector<int32_t> tms_h((size_t)B * nr_max, 0), tmc_h((size_t)B * nr_max, 0), tmb_h(B);
+  int nk_max = 1;
+  for (int b = 0; b < B; ++b) nk_max = std::max(nk_max, (int)keep_rows[b].size());
+  kidx_h.assign((size_t)B * nk_max, 0);
+  for (int b = 0; b < B; ++b) {
+    cnt_h[b] = (int)mem_rows[b].size();
+    for (size_t j = 0; j < mem_rows[b].size(); ++j) {
+      idx_h[(size_t)b * nm_max + j] = mem_rows[b][j];
+      Hm_h[(size_t)b * nm_max + j] = c->H_seq[b][pos[b][mem_rows[b][j]]];
+    }
+    tmb_h[b] = (int)run_start[b].size();
+    for (size_t j = 0; j < run_start[b].size(); ++j) {
+      tms_h[(size_t)b * nr_max + j] = run_off[b][j];
+      tmc_h[(size_t)b * nr_max + j] = run_cnt[b][j];
+    }
+    kcnt_h[b] = (int)keep_rows[b].size();
+    for (size_t j = 0; j < keep_rows[b].size(); ++j) kidx_h[(size_t)b * nk_max + j] = keep_rows[b][j];
+  }
+  struct Tmp {
+    std::vector<void*> p;
+    ~Tmp() { for (void* q : p) if (q) (void)hipFree(q); }
+  } tmp;
+  auto talloc = [&](void** q, size_t bytes) -> sekv_status {
+    TRY(dalloc(c, q, bytes));
+    tmp.p.push_back(*q);
+    return SEKV_OK;
+  };
+  int32_t *idx_d, *cnt_d, *kidx_d, *kcnt_d, *tms_d, *tmc_d, *tmb_d;
+  float* Hm_d;
+  TRY(talloc((void**)&idx_d, idx_h.size() * 4));
+  TRY(talloc((void**)&cnt_d, (size_t)B * 4));
+  TRY(talloc((void**)&kidx_d, kidx_h.size() * 4));
+  TRY(talloc((void**)&kcnt_d, (size_t)B * 4));
+  TRY(talloc((void**)&tms_d, tms_h.size() * 4));
+  TRY(talloc((void**)&tmc_d, tmc_h.size() * 4));
+  TRY(talloc((void**)&tmb_d, (size_t)B * 4));
+  TRY(talloc((void**)&Hm_d, Hm_h.size() * 4));
+  HIPCHK(c, hipMemcpy(idx_d, idx_h.data(), idx_h.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(cnt_d, cnt_h.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(kidx_d, kidx_h.data(), kidx_h.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(kcnt_d, kcnt_h.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(tms_d, tms_h.data(), tms_h.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(tmc_d, tmc_h.data(), tmc_h.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(tmb_d, tmb_h.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(Hm_d, Hm_h.data(), Hm_h.size() * 4, hipMemcpyHostToDevice));
+  const size_t rows_t = (size_t)B * Hkv * nm_max, spans_t = (size_t)B * Hkv * nr_max;
+  void *Kt, *Vt, *kb_t, *vb_t, *Kr_t = nullptr;
+  int32_t *rank_t, *prob_t;
+  int64_t* boff_t;
+  TRY(talloc(&Kt, rows_t * d * es));
+  TRY(talloc(&Vt, rows_t * d * es));
+  TRY(talloc(&kb_t, spans_t * d * es));
+  TRY(talloc(&vb_t, spans_t * d * es));
+  TRY(talloc((void**)&rank_t, spans_t * 4));
+  TRY(talloc((void**)&boff_t, spans_t * 8));
+  TRY(talloc((void**)&prob_t, spans_t * 2 * 3 * 4));
+
+  for (int layer = 0; layer < NL; ++layer) {
+    LayerState& L = c->layers[layer];
+    const int dr = c->route[layer].dr;
+    // 3. the leaving rows of this layer, in run order
+    GatherArgs ga;
+    ga.Hkv = Hkv;
+    ga.in_rows = L.na_cap;
+    ga.out_rows = nm_max;
+    ga.idx = idx_d;
+    ga.idx_stride = nm_max;
+    ga.cnt = cnt_d;
+    ga.row_bytes = (int)(d * es);
+    ga.max_cnt = nm_max;
+    ga.in = L.KA;
+    ga.out = Kt;
+    launch_gather_rows(B, ga, stream);
+    ga.in = L.VA;
+    ga.out = Vt;
+    launch_gather_rows(B, ga, stream);
+    HIPCHK(c, hipGetLastError());
+    // 4. summaries of the new spans (and routing summaries)
+    if (dr > 0 && !Kr_t) TRY(talloc(&Kr_t, spans_t * dr * es));
+    SummaryArgs su;
+    std::memset(&su, 0, sizeof(su));
+    su.H = Hm_d;
+    su.K = Kt;
+    su.V = Vt;
+    su.B = B;
+    su.Hkv = Hkv;
+    su.n = nm_max;
+    su.m_max = nr_max;
+    su.m_b = tmb_d;
+    su.mstart = tms_d;
+    su.mcount = tmc_d;
+    su.kbar = kb_t;
+    su.vbar = vb_t;
+    su.span_chunk = 16;
+    su.n_span_chunks = (nr_max + 15) / 16;
+    su.n_anchor_chunks = 0;
+    su.dr = dr;
+    su.Wr = c->route[layer].W_d;
+    su.Kr = Kr_t;
+    launch_summaries(d, c->bf16, su, stream);
+    HIPCHK(c, hipGetLastError());
+    // 5. ranks, the new layout of the basis store (each head's spans stay contiguous)
+    const int nch = (int)L.choices.size();
+    std::vector<int32_t> rank_th(spans_t, 1);
+    std::vector<int64_t> boff_th(spans_t, 0);
+    std::vector<int64_t> nbase((size_t)B * Hkv + 1, 0), add((size_t)B * Hkv, 0);
+    int64_t new_tot = 0, tmp_tot = 0;
+    std::vector<int32_t> probs[5];
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < Hkv; ++g) {
+        const size_t bg = (size_t)b * Hkv + g;
+        nbase[bg] = new_tot;
+        const int64_t old_len = L.head_base[bg + 1] - L.head_base[bg];
+        int64_t extra = 0;
+        for (int j = 0; j < tmb_h[b]; ++j) {
+          const int cnt = run_cnt[b][j], k = c->m_b[b] + j;
+          const uint64_t key = L.seed ^ ((uint64_t)layer << 40) ^ ((uint64_t)g << 32) ^ (uint64_t)k;
+          int r = L.choices[splitmix64(key) % (uint64_t)nch];
+          r = std::min(r, std::min(cnt, d));
+          rank_th[bg * nr_max + j] = r;
+          boff_th[bg * nr_max + j] = tmp_tot;
+          const int64_t el = span_elems(cnt, r, d);
+          tmp_tot += el;
+          extra += el;
+          const int bk = cnt <= 16 ? 0 : cnt <= 32 ? 1 : cnt <= 64 ? 2 : cnt <= 128 ? 3 : 4;
+          for (int wv = 0; wv < 2; ++wv) {
+            probs[bk].push_back((int)bg);
+            probs[bk].push_back(j);
+            probs[bk].push_back(wv);
+          }
+        }
+        add[bg] = extra;
+        new_tot += old_len + extra;
+      }
+    nbase[(size_t)B * Hkv] = new_tot;
+    if ((new_tot >> 3) >= ((int64_t)1 << 32)) return fail(c, SEKV_ERR_INVALID, "basis store exceeds 2^35 elements");
+    void* newb = nullptr;
+    TRY(talloc(&newb, (size_t)std::max<int64_t>(tmp_tot, 8) * es));
+    HIPCHK(c, hipMemcpy(rank_t, rank_th.data(), spans_t * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(boff_t, boff_th.data(), spans_t * 8, hipMemcpyHostToDevice));
+    // 6. truncated SVD of the new spans into the temporary store
+    SvdArgs sv;
+    sv.K = Kt;
+    sv.V = Vt;
+    sv.Hkv = Hkv;
+    sv.n = nm_max;
+    sv.m_max = nr_max;
+    sv.mstart = tms_d;
+    sv.mcount = tmc_d;
+    sv.rank = rank_t;
+    sv.boff = boff_t;
+    sv.bases = newb;
+    const int cmax[5] = {16, 32, 64, 128, 0};
+    for (int i = 0; i < 5; ++i) {
+      if (probs[i].empty()) continue;
+      HIPCHK(c, hipMemcpy(prob_t, probs[i].data(), probs[i].size() * 4, hipMemcpyHostToDevice));
+      sv.problems = prob_t;
+      sv.n_problems = (int)(probs[i].size() / 3);
+      launch_svd(cmax[i], d, c->bf16, sv, stream);
+      HIPCHK(c, hipGetLastError());
+      HIPCHK(c, hipStreamSynchronize(stream));  // prob_t is reused by the next bucket
+    }
+    // 7. the new store: each head's old spans, then its new ones
+    void* nstore_d = nullptr;
+    void* nstore_h = nullptr;
+    if (host_store(c)) {
+      TRY(halloc(c, &nstore_h, (size_t)std::max<int64_t>(new_tot, 8) * es));
+    } else {
+      TRY(dalloc(c, &nstore_d, (size_t)std::max<int64_t>(new_tot, 8) * es));
+    }
+    for (size_t bg = 0; bg < (size_t)B * Hkv; ++bg) {
+      const int64_t old_len = L.head_base[bg + 1] - L.head_base[bg];
+      if (host_store(c)) {
+        std::memcpy((char*)nstore_h + (size_t)nbase[bg] * es, (char*)L.bases_h + (size_t)L.head_base[bg] * es,
+                    (size_t)old_len * es);
+      } else if (old_len) {
+        HIPCHK(c, hipMemcpyAsync((char*)nstore_d + (size_t)nbase[bg] * es, (char*)L.bases_d + (size_t)L.head_base[bg] * es,
+                                 (size_t)old_len * es, hipMemcpyDeviceToDevice, stream));
+      }
+      const int b = (int)(bg / Hkv);
+      if (add[bg] && tmb_h[b]) {
+        const int64_t src = boff_th[bg * nr_max + 0];
+        HIPCHK(c, hipMemcpyAsync(host_store(c) ? (void*)((char*)nstore_h + (size_t)(nbase[bg] + old_len) * es)
+                                               : (void*)((char*)nstore_d + (size_t)(nbase[bg] + old_len) * es),
+                                 (char*)newb + (size_t)src * es, (size_t)add[bg] * es,
+                                 host_store(c) ? hipMemcpyDeviceToHost : hipMemcpyDeviceToDevice, stream));
+      }
+    }
+    // 8. summaries (and routing summaries) of the new spans into the layer's rows
+    for (int b = 0; b < B; ++b) {
+      if (!tmb_h[b]) continue;
+      for (int g = 0; g < Hkv; ++g) {
+        const size_t bg = (size_t)b * Hkv + g;
+        const size_t dst = bg * mm + c->m_b[b], srcr = bg * nr_max;
+        HIPCHK(c, hipMemcpyAsync((char*)L.kbar + dst * d * es, (char*)kb_t + srcr * d * es, (size_t)tmb_h[b] * d * es,
+                                 hipMemcpyDeviceToDevice, stream));
+        HIPCHK(c, hipMemcpyAsync((char*)L.vbar + dst * d * es, (char*)vb_t + srcr * d * es, (size_t)tmb_h[b] * d * es,
+                                 hipMemcpyDeviceToDevice, stream));
+        if (dr > 0)
+          HIPCHK(c, hipMemcpyAsync((char*)L.Kr + dst * dr * es, (char*)Kr_t + srcr * dr * es,
+                                   (size_t)tmb_h[b] * dr * es, hipMemcpyDeviceToDevice, stream));
+      }
+    }
+    // 9. the window rows that stay, compacted
+    void *nKA, *nVA;
+    TRY(dalloc(c, &nKA, (size_t)B * Hkv * L.na_cap * d * es));
+    sekv_status st2 = dalloc(c, &nVA, (size_t)B * Hkv * L.na_cap * d * es);
+    if (st2 != SEKV_OK) {
+      dfree(nKA);
+      return st2;
+    }
+    GatherArgs gk;
+    gk.Hkv = Hkv;
+    gk.in_rows = L.na_cap;
+    gk.out_rows = L.na_cap;
+    gk.idx = kidx_d;
+    gk.idx_stride = nk_max;
+    gk.cnt = kcnt_d;
+    gk.row_bytes = (int)(d * es);
+    gk.max_cnt = nk_max;
+    gk.in = L.KA;
+    gk.out = nKA;
+    launch_gather_rows(B, gk, stream);
+    gk.in = L.VA;
+    gk.out = nVA;
+    launch_gather_rows(B, gk, stream);
+    HIPCHK(c, hipGetLastError());
+    HIPCHK(c, hipStreamSynchronize(stream));
+    dfree(L.KA);
+    dfree(L.VA);
+    L.KA = nKA;
+    L.VA = nVA;
+    // 10. tables: ranks, offsets, metadata, counts
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < Hkv; ++g) {
+        const size_t bg = (size_t)b * Hkv + g;
+        for (int k = 0; k < c->m_b[b]; ++k) L.boff_h[bg * mm + k] += nbase[bg] - L.head_base[bg];
+        const int64_t old_len = L.head_base[bg + 1] - L.head_base[bg];
+        int64_t o = nbase[bg] + old_len;
+        for (int j = 0; j < tmb_h[b]; ++j) {
+          const size_t i = bg * mm + c->m_b[b] + j;
+          L.rank_h[i] = rank_th[bg * nr_max + j];
+          L.boff_h[i] = o;
+          o += span_elems(run_cnt[b][j], L.rank_h[i], d);
+        }
+      }
+    L.head_base = nbase;
+    L.basis_elems = new_tot;
+    if (host_store(c)) {
+      hfree(L.bases_h);
+      L.bases_h = nstore_h;
+      HIPCHK(c, hipHostGetDevicePointer(&L.bases_hd, L.bases_h, 0));
+    } else {
+      dfree(L.bases_d);
+      L.bases_d = nstore_d;
+    }
+    for (int b = 0; b < B; ++b) L.na_l[b] = kcnt_h[b];
+    HIPCHK(c, hipMemcpy(L.na_l_d, L.na_l.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+    const size_t rows_m = (size_t)B * Hkv * mm;
+    HIPCHK(c, hipMemcpy(L.rank_d, L.rank_h.data(), rows_m * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(L.boff_d, L.boff_h.data(), rows_m * 8, hipMemcpyHostToDevice));
+    {
+      std::vector<int2> meta(rows_m, make_int2(0, 0));
+      for (int b = 0; b < B; ++b)
+        for (int g = 0; g < Hkv; ++g)
+          for (int k = 0; k < c->m_b[b] + tmb_h[b]; ++k) {
+            const size_t i = ((size_t)b * Hkv + g) * mm + k;
+            const int cnt = k < c->m_b[b] ? c->mcount[b][k] : run_cnt[b][k - c->m_b[b]];
+            meta[i] = make_int2((int)(uint32_t)(L.boff_h[i] >> 3), L.rank_h[i] | (cnt << 8));
+          }
+      HIPCHK(c, hipMemcpy(L.smeta_d, meta.data(), rows_m * sizeof(int2), hipMemcpyHostToDevice));
+    }
+    free_layer_cache(L.lc);
+    L.sched.valid = false;
+    L.sched.anchors_changed = true;
+  }
+
+  // 11. the shared span table
+  for (int b = 0; b < B; ++b) {
+    for (size_t j = 0; j < run_start[b].size(); ++j) {
+      c->mstart[b].push_back(run_start[b][j]);
+      c->mcount[b].push_back(run_cnt[b][j]);
+    }
+    c->m_b[b] = (int)c->mstart[b].size();
+    std::vector<int32_t> kept;
+    for (int r : keep_rows[b]) kept.push_back(pos[b][r]);
+    c->next_pos[b] = pos[b].empty() ? c->next_pos[b] : std::max(c->next_pos[b], pos[b].back() + 1);
+    c->row_pos[b] = kept;
+    c->anchors[b] = kept;
+    c->na_b[b] = (int)kept.size();
+  }
+  {
+    std::vector<int32_t> ms((size_t)B * mm, 0), mc((size_t)B * mm, 0);
+    std::vector<float> ls((size_t)B * mm, 0.f);
+    for (int b = 0; b < B; ++b)
+      for (int k = 0; k < c->m_b[b]; ++k) {
+        ms[(size_t)b * mm + k] = c->mstart[b][k];
+        mc[(size_t)b * mm + k] = c->mcount[b][k];
+        ls[(size_t)b * mm + k] = (float)std::log((double)c->mcount[b][k]);
+      }
+    HIPCHK(c, hipMemcpy(c->mstart_d, ms.data(), ms.size() * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(c->mcount_d, mc.data(), mc.size() * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(c->logS_d, ls.data(), ls.size() * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(c->m_b_d, c->m_b.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+    HIPCHK(c, hipMemcpy(c->na_b_d, c->na_b.data(), (size_t)B * 4, hipMemcpyHostToDevice));
+  }
+  c->resegmented = true;
   return SEKV_OK;
 }
 

@@ -136,6 +136,16 @@ struct AppendArgs {
 };
 void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s);
 
+// Row gather per (b, g): out[bg][i] = in[bg][idx[b][i]] for i < cnt[b].
+struct GatherArgs {
+  const void* in;          // [B*Hkv][in_rows][row_bytes]
+  void* out;               // [B*Hkv][out_rows][row_bytes]
+  const int32_t* idx;      // [B][idx_stride]
+  const int32_t* cnt;      // [B]
+  int Hkv, in_rows, out_rows, idx_stride, row_bytes, max_cnt;
+};
+void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s);
+
 // Soft rank gates on the stored A factors of the spans of one (sequence, kv head).
 struct GateArgs {
   void* bases;             // the layer's packed store (device memory or mapped pinned memory)

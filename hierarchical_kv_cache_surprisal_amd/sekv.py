@@ -31,7 +31,7 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
             "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
             "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window",
-            "sekv_set_basis_cache"]
+            "sekv_set_basis_cache", "sekv_reserve_spans", "sekv_append_surprisal", "sekv_resegment_window"]
 
 
 class SekvError(RuntimeError):
@@ -91,6 +91,9 @@ def load_library(path: str = LIB_PATH):
         "sekv_append_tokens": (I32, [P, I32, P, P, I32, P]),
         "sekv_set_basis_cache": (I32, [P, I64]),
         "sekv_get_window": (I32, [P, I32, I32, pI32]),
+        "sekv_reserve_spans": (I32, [P, I32]),
+        "sekv_append_surprisal": (I32, [P, C.POINTER(C.c_float), I32]),
+        "sekv_resegment_window": (I32, [P, P]),
         "sekv_import_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_export_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_apply_rank_gates": (I32, [P, I32, I32, I32, C.POINTER(C.c_float), C.POINTER(C.c_float), P]),
@@ -256,6 +259,21 @@ def sekv_get_window(ctx, layer: int, b: int) -> int:
     return int(n[0])
 
 
+def sekv_reserve_spans(ctx, extra: int):
+    _check(load_library().sekv_reserve_spans(ctx, int(extra)), ctx)
+
+
+def sekv_append_surprisal(ctx, H_new):
+    """H_new: host float32 [B][n_new]."""
+    h = np.ascontiguousarray(H_new, dtype=np.float32)
+    n_new = int(h.shape[1]) if h.ndim == 2 else 0
+    _check(load_library().sekv_append_surprisal(ctx, h.ctypes.data_as(C.POINTER(C.c_float)), n_new), ctx)
+
+
+def sekv_resegment_window(ctx, stream=None):
+    _check(load_library().sekv_resegment_window(ctx, _stream(stream)), ctx)
+
+
 def sekv_set_routing(ctx, layer: int, d_route: int, W=None):
     """W: host float32 [H_kv][d_route][d] (None with d_route = 0)."""
     if d_route == 0:
@@ -340,9 +358,10 @@ class Context:
         return sekv_get_bases_layout(self.ptr, layer, b, g, m)
 
     def export_head(self, layer, b, g):
-        ms, mc, an, _ = self.spans(b)
+        ms, _, _, _ = self.spans(b)
         _, _, tot = self.bases_layout(layer, b, g)
-        return sekv_export_head(self.ptr, layer, b, g, len(ms), len(an), self.d, tot, self.storage_dtype)
+        return sekv_export_head(self.ptr, layer, b, g, len(ms), self.window(layer, b), self.d, tot,
+                                self.storage_dtype)
 
     def import_spans(self, b, mstart, mcount, anchors):
         sekv_import_spans(self.ptr, b, mstart, mcount, anchors)
@@ -364,6 +383,15 @@ class Context:
 
     def window(self, layer, b):
         return sekv_get_window(self.ptr, layer, b)
+
+    def reserve_spans(self, extra):
+        sekv_reserve_spans(self.ptr, extra)
+
+    def append_surprisal(self, H_new):
+        sekv_append_surprisal(self.ptr, H_new)
+
+    def resegment_window(self, stream=None):
+        sekv_resegment_window(self.ptr, stream)
 
     def set_routing(self, layer, d_route, W=None):
         sekv_set_routing(self.ptr, layer, d_route, W)

@@ -130,8 +130,10 @@ sekv_status sekv_build(sekv_ctx* ctx, int32_t layer, const float* H, const void*
 /* Span table of sequence b (shared by every layer and head).
  *   m, n_anchors, m_max (max over sequences) are written when non-NULL.
  *   mstart/mcount host int32 [m]: first member position and member count of
- *   each kept span, in position order.  anchors host int32 [n_anchors],
- *   ascending.  Pass NULL arrays to query sizes only.
+ *   each kept span, in position order (spans added by re-segmentation follow
+ *   the prefill's).  anchors host int32 [n_anchors], ascending: the positions
+ *   of the window rows as of the last build or re-segmentation (tokens
+ *   appended since then are not listed).  Pass NULL arrays to query sizes only.
  * Errors: STATE before the first build/import, INVALID (b out of range). */
 sekv_status sekv_get_spans(const sekv_ctx* ctx, int32_t b, int32_t* m, int32_t* n_anchors,
                            int32_t* m_max, int32_t* mstart, int32_t* mcount, int32_t* anchors);
@@ -248,7 +250,9 @@ sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g,
                              const void* bases, int64_t basis_elems);
 
 /* Copy the artefacts of one (layer, b, g) to host memory (same layouts as
- * sekv_import_head; any pointer may be NULL).  Synchronous.
+ * sekv_import_head; any pointer may be NULL).  KA / VA hold the layer's
+ * window rows: sekv_get_window of them (the anchors plus the tokens appended
+ * since the last build or re-segmentation).  Synchronous.
  * Errors: STATE (layer not built), INVALID, HIP. */
 sekv_status sekv_export_head(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, void* kbar,
                              void* vbar, void* KA, void* VA, int32_t* rank, void* bases);
@@ -279,9 +283,9 @@ sekv_status sekv_set_basis_cache(sekv_ctx* ctx, int64_t bytes);
  * resolution on the GPU].  They become full-resolution entries of the shared
  * softmax (like the anchors) for every later decode step of this layer.
  *   K_new, V_new dev KV dtype [B][H_kv][n_new][d]; n_new >= 0.
- * The tokens that pass beyond the last w positions stay at full resolution:
- * they are not re-segmented into spans (no summaries or bases are built for
- * them).  Asynchronous on `stream`, except when the window storage must grow
+ * The tokens that pass beyond the last w positions stay at full resolution
+ * until sekv_resegment_window turns them into spans.  Asynchronous on
+ * `stream`, except when the window storage must grow
  * (geometrically): then the call copies the rows and synchronises `stream`.
  * Not capturable; a decode graph captured before an append does not see the
  * new tokens (capture again after appending).  Each layer appends on its own
@@ -293,6 +297,43 @@ sekv_status sekv_append_tokens(sekv_ctx* ctx, int32_t layer, const void* K_new, 
 /* Full-resolution entries (anchors + appended tokens) of sequence b in layer
  * `layer`.  Errors: STATE (no layout), INVALID. */
 sekv_status sekv_get_window(const sekv_ctx* ctx, int32_t layer, int32_t b, int32_t* n_anchors);
+
+/* ------------------------------------------------- window re-segmentation */
+
+/* Spare span rows per sequence for spans that re-segmentation adds later.
+ * Call before the first sekv_build (the per-span arrays take their row stride,
+ * the maximum span count plus `extra`, from the first build).  extra in
+ * [0, 2^22].  Errors: STATE (the span table exists), INVALID. */
+sekv_status sekv_reserve_spans(sekv_ctx* ctx, int32_t extra);
+
+/* Surprisal of n_new decoded tokens per sequence, in the order they were (or
+ * will be) appended with sekv_append_tokens.  H_new host fp32 [B][n_new],
+ * finite and >= 0; copied.  Only for contexts whose span table came from
+ * sekv_build (which records the prefill surprisal and threshold).
+ * Errors: STATE (no surprisal record), INVALID. */
+sekv_status sekv_append_surprisal(sekv_ctx* ctx, const float* H_new, int32_t n_new);
+
+/* Streaming re-segmentation of the full-resolution window [summary page,
+ * section 2.1 and Figure 2, applied to decoded tokens], all layers at once.
+ * The window holds the last w positions; an older row (an appended token, or a
+ * prefill anchor once appended tokens push it out) leaves it unless its
+ * surprisal lies strictly above the prefill threshold mu + alpha sigma (such a
+ * row is a boundary and stays a full-resolution anchor).  Every maximal run of
+ * consecutive leaving positions becomes one new span, numbered after the
+ * existing ones, with the weighted-mean summaries, routing summary, hard rank
+ * (the rank choices and seed of the layer's build) and truncated SVD bases of
+ * the prefill builder; the remaining rows stay in position order.  Earlier
+ * spans and cuts never move.  Requires every layer built by sekv_build, the
+ * same number of window rows in every layer (append to every layer first) and
+ * the surprisal of every appended token.  Synchronous on `stream`; changes the
+ * span table (sekv_get_spans), the bases layout and every layer's window, so
+ * decode graphs must be captured again; clears the basis caches.  After it,
+ * sekv_build is refused.  Not capturable.
+ * Errors: STATE (not built by sekv_build, layers differ, surprisal missing,
+ * capture), OOM (no span rows left: sekv_reserve_spans), INVALID, HIP.  These
+ * refusals come before anything changes; an OOM or HIP error while the layers
+ * are rebuilt leaves the context unusable (destroy it). */
+sekv_status sekv_resegment_window(sekv_ctx* ctx, hipStream_t stream);
 
 /* ------------------------------------------- routing projection, rank gates */
 

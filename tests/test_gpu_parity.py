@@ -621,3 +621,188 @@ def test_basis_cache_prefetch_decode(cache_kb, L):
     assert ei.value.status == sekv.SEKV_ERR_INVALID
     ctx.set_basis_cache(0)
     _decode_compare(s, ctx, arts, 0, 1, taus)
+
+
+# ============================================================================ window re-segmentation
+
+def _export_arts(ctx, s, layer, W=None, dr=0):
+    """The GPU's artefacts of every (b, g) of a layer, upcast to float64."""
+    arts = {}
+    for b in range(s.B):
+        ms, mc, an, _ = ctx.spans(b)
+        for g in range(s.Hkv):
+            kb, vb, KA, VA, rank, bases = ctx.export_head(layer, b, g)
+            mc64 = np.asarray(mc, np.int64)
+            AK, BKt, AV, BVt = T.unpack_bases(bases, mc64, rank, s.kv_dtype, s.d)
+            f = lambda x: T.from_storage(x, s.kv_dtype)
+            a = O.HeadArtifacts(kv_dtype=s.kv_dtype, mstart=np.asarray(ms, np.int64), mcount=mc64,
+                                anchors=np.asarray(an, np.int64), kbar=f(kb), vbar=f(vb), KA=f(KA), VA=f(VA),
+                                rank=np.asarray(rank, np.int64), AK=AK, BKt=BKt, AV=AV, BVt=BVt)
+            if W is not None:
+                a.W = W[g]
+                a.Kr = f(ctx.export_route_summary(layer, b, g, dr))
+            arts[(b, g)] = (a, bases)
+    return arts
+
+
+def _new_surprisal(rng, theta, B, n_new):
+    """Decoded-token surprisal: mostly below the threshold, a few spikes above it,
+    none within 5% of it."""
+    H = rng.uniform(0.0, 0.95 * theta, (B, n_new))
+    spike = rng.random((B, n_new)) < 0.04
+    H[spike] = rng.uniform(1.05 * theta, 2.0 * theta, int(spike.sum()))
+    return H.astype(np.float32)
+
+
+@pytest.mark.parametrize("home,route_layer", [("device", None), ("host", 1)])
+def test_resegment_window_then_decode(home, route_layer):
+    """Decoded tokens age out of the local window and become spans: two layers built
+    on the GPU (one with a routing projection), tokens and their surprisal appended,
+    the window re-segmented twice.  The span table and window rows match the oracle
+    bit for bit; earlier spans are untouched; the new spans' summaries within one
+    bf16 ulp and their SVD factors by reconstruction error; then the GPU decodes its
+    own re-segmented artefacts and the oracle decodes the same artefacts."""
+    s = _gqa_small().replace(L=2, steps=2)
+    dr = 16
+    Wr = _route_W(s, dr, seed=11)
+    ctx = _ctx(s, home, L=2)
+    ctx.reserve_spans(96)
+    H = synth.surprisal_batch(s)
+    if route_layer is not None:
+        ctx.set_routing(route_layer, dr, Wr)
+    KV = []
+    for layer in range(s.L):
+        K, V = synth.kv_layer(s, layer, device="cpu")
+        KV.append((K, V))
+        ctx.build(layer, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices,
+                  s.rank_seed)
+    torch.cuda.synchronize()
+    segs = [O.segment(H[b], s.alpha, s.w) for b in range(s.B)]
+    theta = [float(segs[b].theta) for b in range(s.B)]
+    lw = lambda layer: Wr if layer == route_layer else None
+    arts = {layer: {k: v[0] for k, v in _export_arts(ctx, s, layer, lw(layer), dr).items()} for layer in range(s.L)}
+    positions = [list(np.asarray(segs[b].anchors, np.int64)) for b in range(s.B)]
+    H_all = [list(H[b].astype(np.float64)) for b in range(s.B)]
+    n_tot = [s.n] * s.B
+    rng = np.random.default_rng(31)
+    gen = torch.Generator().manual_seed(13)
+    dt = torch.bfloat16 if s.kv_dtype == "bf16" else torch.float32
+    new_total = 0
+    for n_steps in ((1, 200, 3, 500), (2, 350)):
+        for n_new in n_steps:
+            Hn = _new_surprisal(rng, min(theta), s.B, n_new)
+            ctx.append_surprisal(Hn)
+            for layer in range(s.L):
+                Kn = torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(dt)
+                Vn = torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(dt)
+                ctx.append_tokens(layer, Kn.to(DEV).contiguous(), Vn.to(DEV).contiguous())
+                for (b, g) in list(arts[layer]):
+                    arts[layer][(b, g)] = O.append_tokens(arts[layer][(b, g)], _to_np64(Kn[b, g]), _to_np64(Vn[b, g]))
+            for b in range(s.B):
+                positions[b] += list(range(n_tot[b], n_tot[b] + n_new))
+                H_all[b] += list(Hn[b].astype(np.float64))
+                n_tot[b] += n_new
+        before = {layer: _export_arts(ctx, s, layer, lw(layer), dr) for layer in range(s.L)}
+        ctx.resegment_window()
+        torch.cuda.synchronize()
+        for layer in range(s.L):
+            for (b, g), a in list(arts[layer].items()):
+                arts[layer][(b, g)] = O.resegment_window(a, positions[b], H_all[b], theta[b], s.w, n_tot[b], layer,
+                                                         g, s.rank_choices, s.rank_seed)
+        for b in range(s.B):
+            ref = arts[0][(b, 0)]
+            ms, mc, an, _ = ctx.spans(b)
+            assert np.array_equal(ms, ref.mstart) and np.array_equal(mc, ref.mcount), f"span table differs (b {b})"
+            assert np.array_equal(an, ref.anchors), f"window positions differ (b {b})"
+            new_total += int(ref.m - before[0][(b, 0)][0].m)
+            row_of = {p: i for i, p in enumerate(positions[b])}
+            positions[b] = list(ref.anchors)
+            for layer in range(s.L):
+                got = _export_arts(ctx, s, layer, lw(layer), dr)
+                for g in range(s.Hkv):
+                    ga, gbases = got[(b, g)]
+                    pa, pbases = before[layer][(b, g)]
+                    oa = arts[layer][(b, g)]
+                    m0 = pa.m
+                    assert ga.KA.shape[0] == ctx.window(layer, b)
+                    assert np.array_equal(ga.KA, oa.KA) and np.array_equal(ga.VA, oa.VA), (layer, b, g)
+                    assert np.array_equal(ga.rank, oa.rank), (layer, b, g)
+                    assert np.array_equal(gbases[:pbases.size], pbases), "earlier spans' bases moved"
+                    assert np.array_equal(ga.kbar[:m0], pa.kbar) and np.array_equal(ga.vbar[:m0], pa.vbar)
+                    pairs = [(ga.kbar[m0:], oa.kbar[m0:]), (ga.vbar[m0:], oa.vbar[m0:])]
+                    if oa.Kr is not None:
+                        assert np.array_equal(ga.Kr[:m0], pa.Kr)
+                        pairs.append((ga.Kr[m0:], oa.Kr[m0:]))
+                    for x, r in pairs:
+                        tol = 2.0 ** -7 * np.max(np.abs(r), axis=1, keepdims=True) + 1e-30
+                        assert np.all(np.abs(x - r) <= tol), (layer, b, g, float(np.max(np.abs(x - r) / tol)))
+                    # new spans: SVD factors against the Eckart-Young optimum of their member rows
+                    for k in range(m0, ga.m):
+                        rows = [row_of[p] for p in range(int(ga.mstart[k]), int(ga.mstart[k] + ga.mcount[k]))]
+                        for X, A, Bt in ((pa.KA[rows], ga.AK[k], ga.BKt[k]), (pa.VA[rows], ga.AV[k], ga.BVt[k])):
+                            sv = np.linalg.svd(X, compute_uv=False)
+                            r = int(ga.rank[k])
+                            e_opt = math.sqrt(float(np.sum(sv[r:] ** 2)))
+                            nx = float(np.linalg.norm(X))
+                            assert float(np.linalg.norm(X - A @ Bt)) <= e_opt + 2.0 ** -7 * nx, (layer, b, g, k)
+                            assert np.allclose(np.linalg.norm(A, axis=0), sv[:r], atol=2.0 ** -7 * sv[0])
+        # the decode of the re-segmented layers: GPU against the oracle on the same artefacts
+        for layer in range(s.L):
+            ga = {k: v[0] for k, v in _export_arts(ctx, s, layer, lw(layer), dr).items()}
+            qs = _q_steps(s, layer, s.steps)
+            taus = T.thresholds_for(qs, ga, s.G, np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1])[:s.Hq], s.B)
+            _decode_compare(s, ctx, ga, layer, s.steps, taus)
+    assert new_total > 0
+    sekv = _lib()
+    with pytest.raises(sekv.SekvError) as ei:
+        K, V = KV[0]
+        ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+
+
+def test_resegment_window_errors_leave_state():
+    """Refusals happen before anything changes: no surprisal for appended tokens,
+    layers holding different windows, no span rows left; the decode afterwards
+    still matches the oracle on the unchanged artefacts."""
+    s = _gqa_small().replace(L=2, steps=1)
+    sekv = _lib()
+    H = synth.surprisal_batch(s)
+    ctx = _ctx(s, "device", L=2)
+    for layer in range(s.L):
+        K, V = synth.kv_layer(s, layer, device="cpu")
+        ctx.build(layer, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.reserve_spans(8)          # too late: the span table exists
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    ctx.resegment_window()            # nothing appended: nothing leaves
+    gen = torch.Generator().manual_seed(3)
+    n_new = 900
+    kv = [(torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(torch.bfloat16),
+           torch.randn(s.B, s.Hkv, n_new, s.d, generator=gen).to(torch.bfloat16)) for _ in range(s.L)]
+    ctx.append_tokens(0, kv[0][0].to(DEV).contiguous(), kv[0][1].to(DEV).contiguous())
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.resegment_window()        # layer 1 lacks the tokens
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    ctx.append_tokens(1, kv[1][0].to(DEV).contiguous(), kv[1][1].to(DEV).contiguous())
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.resegment_window()        # their surprisal is missing
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    theta = min(float(O.segment(H[b], s.alpha, s.w).theta) for b in range(s.B))
+    Hn = np.full((s.B, n_new), 0.5 * theta, np.float32)
+    Hn[:, ::2] = 2.0 * theta      # every other token stays: 450 single-token runs per sequence
+    ctx.append_surprisal(Hn)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.resegment_window()        # no span rows reserved for them
+    assert ei.value.status == sekv.SEKV_ERR_OOM
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.append_surprisal(np.full((s.B, 1), np.nan, np.float32))
+    assert ei.value.status == sekv.SEKV_ERR_INVALID
+    # unchanged: the exported artefacts (with the appended rows) decode as before
+    for layer in range(s.L):
+        ga = {k: v[0] for k, v in _export_arts(ctx, s, layer).items()}
+        for b in range(s.B):
+            assert ga[(b, 0)].KA.shape[0] == ctx.window(layer, b)
+        qs = _q_steps(s, layer, s.steps)
+        taus = T.thresholds_for(qs, ga, s.G, np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1]), s.B)
+        _decode_compare(s, ctx, ga, layer, s.steps, taus)
