@@ -318,6 +318,8 @@ def main():
     log(f"timed {args.steps} steps x {L} layers: {t_ms:.3f} ms (wall {wall*1e3:.1f} ms), "
         f"t_layer_step {t_ls*1e6:.2f} us, {kps:.3e} KP/s, {gbs:.0f} GB/s = {100*gbs/PEAK_HBM_GBS:.1f}% of peak")
 
+    read_ref = read_reference(dev, stream, [int(bytes_per_ls), 1 << 30])
+
     if args.copy_calibration:
         # a device copy of known size, for scaling the HBM byte counters
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -359,6 +361,7 @@ def main():
                      "traffic": traffic if args.home == "device" else None,
                      "kernel": "one layer-step: k_route (the work) + k_combine"},
         "cpu_baseline": cpu,
+        "read_reference": read_ref,
         "t_layer_step_us": t_ls * 1e6,
         "algorithmic_bytes_per_layer_step": bytes_per_ls,
         "head_positions_per_s": B * Hq * n / t_ls,
@@ -370,6 +373,36 @@ def main():
                                                  "cache_bytes_fetched")}} if args.cache_gb > 0 else {}),
     }
     print(json.dumps(res), flush=True)
+
+
+def read_reference(dev, stream, sizes, reps=40):
+    """What a plain library read achieves on this GPU: torch.sum over a float32
+    tensor of each size (one layer-step's algorithmic bytes, and 1 GiB), launched
+    back to back on the timing stream.  Context for the roofline fraction: the
+    decode step is one short launch, which a streaming read of the same size
+    does not fill at the spec peak either."""
+    import torch
+
+    out = []
+    for nbytes in sizes:
+        x = torch.ones(max(1, nbytes // 4), dtype=torch.float32, device=dev)
+        r = torch.empty((), dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                torch.sum(x, dim=0, out=r)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                torch.sum(x, dim=0, out=r)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        out.append({"bytes": int(x.numel() * 4), "us": t * 1e6, "GB/s": x.numel() * 4 / t / 1e9,
+                    "frac_of_peak": x.numel() * 4 / t / 1e9 / PEAK_HBM_GBS})
+        del x, r
+    log("read reference (torch.sum): " + ", ".join(f"{o['bytes'] / 1e6:.1f} MB {o['GB/s']:.0f} GB/s" for o in out))
+    return {"kernel": "torch.sum over float32, back-to-back launches", "runs": out}
 
 
 def cpu_baseline(s, ctx, H, taus, n_heads, steps):

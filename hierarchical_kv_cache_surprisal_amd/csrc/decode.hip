@@ -966,12 +966,15 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)bh * a.max_parts;
   const float4* pa = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * a.max_parts * D) + c4;
-  for (int p0 = pg; p0 < np; p0 += UN * PG) {
+  // the slot loads are bounded by the buffer (max_parts), not by np, so the
+  // first batch is in flight together with the load of np; slots >= np are
+  // loaded but never merged
+  for (int p0 = pg; p0 < a.max_parts; p0 += UN * PG) {
     float2 ml[UN];
     float4 v[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int p = min(p0 + u * PG, np - 1);
+      const int p = min(p0 + u * PG, a.max_parts - 1);
       ml[u] = pml[p];
       v[u] = pa[(size_t)p * C4];
     }
@@ -989,6 +992,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
         M = mn;
       }
     }
+    if (p0 + UN * PG >= np) break;
   }
   if (c4 == 0) {
     gm_s[pg] = M;
