@@ -1567,8 +1567,11 @@ sekv_status sekv_resegment_window(sekv_ctx* c, hipStream_t stream) {
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, d = c->cfg.d_head, NL = c->cfg.n_layers;
   const int w = c->cfg.local_window, mm = c->m_max;
   const size_t es = c->esz;
-  for (int l = 0; l < NL; ++l)
+  for (int l = 0; l < NL; ++l) {
     if (!c->layers[l].ready) return fail(c, SEKV_ERR_STATE, "every layer must be built before re-segmenting");
+    if (c->layers[l].choices.empty())  // imported artefacts: no rank choices to draw new ranks from
+      return fail(c, SEKV_ERR_STATE, "layer " + std::to_string(l) + " was not built by sekv_build");
+  }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   HIPCHK(c, hipStreamIsCapturing(stream, &cs));
   if (cs != hipStreamCaptureStatusNone) return fail(c, SEKV_ERR_STATE, "re-segmentation is not capturable");

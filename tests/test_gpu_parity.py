@@ -806,3 +806,22 @@ def test_resegment_window_errors_leave_state():
         qs = _q_steps(s, layer, s.steps)
         taus = T.thresholds_for(qs, ga, s.G, np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1]), s.B)
         _decode_compare(s, ctx, ga, layer, s.steps, taus)
+
+
+def test_resegment_window_refuses_imported_layers():
+    """Re-segmentation draws the new spans' ranks from each layer's build: a layer
+    whose artefacts were imported has none, and the call is refused."""
+    s = _gqa_small().replace(L=2, steps=1)
+    sekv = _lib()
+    H = synth.surprisal_batch(s)
+    ctx = _ctx(s, "device", L=2)
+    K, V = synth.kv_layer(s, 0, device="cpu")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    H1, K1, V1 = _inputs(s, layer=1)
+    segs, arts = _oracle_layer(s, H1, K1, V1, layer=1)
+    T.import_oracle_layer(ctx, 1, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype, set_spans=False)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.resegment_window()
+    assert ei.value.status == sekv.SEKV_ERR_STATE
+    assert "not built" in str(ei.value)
