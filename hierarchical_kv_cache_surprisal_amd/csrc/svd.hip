@@ -22,7 +22,7 @@
 //
 // Rotations are applied to disjoint pairs in parallel (round-robin tournament
 // ordering), one group of 512/PMAX threads per pair.  Neither path keeps the
-// rotations, so a workgroup needs about 70 KB of LDS and two fit on a CU.
+// rotations, so a workgroup needs about 78 KB of LDS and two fit on a CU.
 #include "sekv_device.h"
 
 namespace sekv {
@@ -30,6 +30,11 @@ namespace sekv {
 namespace {
 
 constexpr int kSvdThreads = 512;  // 8 waves per workgroup
+// Row stride of the fp32 vectors in LDS: D + 8 floats.  In a Jacobi round on
+// 128 vectors each pair has 8 threads, which read 8 consecutive elements of
+// their row; rows of neighbouring pairs then start 8 banks apart and a
+// half-wave's 32 reads hit 32 different banks (with D + 1, about 11).
+constexpr int kVecPad = 8;
 
 // Rotation threshold: a pair is rotated while |x_i . x_j| > tol |x_i| |x_j|.
 // fp32 storage: p ulps of fp32; bf16 storage: 1e-4, far below the storage
@@ -45,6 +50,8 @@ __device__ __forceinline__ float jacobi_tol(int p) {
 template <int D, int PMAX>
 __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
   constexpr int TPP = 2 * kSvdThreads / PMAX;
+  constexpr int EPT = D / TPP;  // elements of a vector per thread of its pair group
+  static_assert(D % TPP == 0, "pair groups must tile the vector length");
   const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
   const int pe = p + (p & 1);
   if (p < 2) return;
@@ -63,15 +70,19 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
         }
       }
       const bool act = i >= 0 && i < p && j < p;
+      // the pair's elements stay in registers from the dot products to the rotation
+      float u[EPT], v[EPT];
       float al = 0.f, be = 0.f, ga = 0.f;
+      float* xi = Xv + (act ? i : 0) * XS + li;
+      float* xj = Xv + (act ? j : 0) * XS + li;
       if (act) {
-        const float* xi = Xv + i * XS;
-        const float* xj = Xv + j * XS;
-        for (int e = li; e < D; e += TPP) {
-          const float u = xi[e], v = xj[e];
-          al += u * u;
-          be += v * v;
-          ga += u * v;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          u[k] = xi[k * TPP];
+          v[k] = xj[k * TPP];
+          al += u[k] * u[k];
+          be += v[k] * v[k];
+          ga += u[k] * v[k];
         }
       }
       al = group_sum<TPP>(al);
@@ -84,12 +95,10 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
                                      : copysignf(1.f, zeta) / (az + sqrtf(1.f + zeta * zeta));
         const float cs = 1.f / sqrtf(1.f + tt * tt);
         const float sn = cs * tt;
-        float* xi = Xv + i * XS;
-        float* xj = Xv + j * XS;
-        for (int e = li; e < D; e += TPP) {
-          const float u = xi[e], v = xj[e];
-          xi[e] = cs * u - sn * v;
-          xj[e] = sn * u + cs * v;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          xi[k * TPP] = cs * u[k] - sn * v[k];
+          xj[k * TPP] = sn * u[k] + cs * v[k];
         }
         if (li == 0) *s_rot = 1;
       }
@@ -150,10 +159,9 @@ __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt
 
 // A^T [r][c8] = (X V_r)^T from the original rows of X (streamed ROWS at a time
 // through Xr), with V_i = Vt[order[kk]] / sig[order[kk]]; zero beyond c.
-template <int D, typename T, int ROWS>
+template <int D, typename T, int ROWS, int XS>
 __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src, float* Xr, const float* Vt,
                                   int VS, const float* sig, const int* order) {
-  constexpr int XS = D + 1;
   T* At = block_ptr<T, D>(a, p, false);
   const int c8 = (int)pad8(p.c);
   const int r = p.r;
@@ -186,7 +194,7 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
 template <int D, typename T, int PMAX>
 __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
   extern __shared__ float smem[];
-  constexpr int XS = D + 1;
+  constexpr int XS = D + kVecPad;
   constexpr int ROWS = 16;
   float* X = smem;                 // [PMAX][XS]: rows of X, orthogonalised in place
   float* Xr = smem + PMAX * XS;    // [ROWS][XS]: original rows, for A
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
     const float s = sig[i];
     Bt[idx] = Elem<T>::from_f(s > 0.f ? X[i * XS + e] / s : 0.f);
   }
-  store_a_from_rows<D, T, ROWS>(a, p, src, Xr, X, XS, sig, order);
+  store_a_from_rows<D, T, ROWS, XS>(a, p, src, Xr, X, XS, sig, order);
 }
 
 // ---------------------------------------------------------------- tall spans
@@ -227,9 +235,9 @@ __device__ __forceinline__ int upk(int i, int j) {
 template <int D, typename T>
 __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   extern __shared__ double smd[];
-  constexpr int XS = D + 1;       // float vector stride
+  constexpr int XS = D + kVecPad;  // float vector stride
   constexpr int ROWS = 16;        // X rows staged per step
-  constexpr int NB = D / 8;       // 8x8 Gram blocks per dimension
+  constexpr int NB = D / 8;       // 8-column Gram blocks per row of blocks
   constexpr int NP = D * (D + 1) / 2;
   double* Gp = smd;                                       // [NP] packed upper Gram, then R
   float* Xs = reinterpret_cast<float*>(smd + NP);         // [ROWS][D]
@@ -241,12 +249,14 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
 
-  // 1. Gram matrix in fp64 (8 x 8 blocks on and above the diagonal)
+  // 1. Gram matrix in fp64: 4 x 8 blocks (rows 4 bi.., columns 8 bj..) that
+  // reach the upper triangle; 32 fp64 accumulators per thread keep two
+  // workgroups per CU
   const int bi = threadIdx.x / NB, bj = threadIdx.x % NB;
-  const bool gact = threadIdx.x < NB * NB && bj >= bi;
-  double gacc[8][8];
+  const bool gact = bi < 2 * NB && bj * 8 + 7 >= bi * 4;
+  double gacc[4][8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 8; ++v) gacc[u][v] = 0.0;
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
@@ -257,14 +267,13 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
     __syncthreads();
     if (gact) {
       for (int t = 0; t < ROWS; ++t) {
-        double xa[8], xb[8];
+        double xa[4], xb[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          xa[u] = (double)Xs[t * D + bi * 8 + u];
-          xb[u] = (double)Xs[t * D + bj * 8 + u];
-        }
+        for (int u = 0; u < 4; ++u) xa[u] = (double)Xs[t * D + bi * 4 + u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int v = 0; v < 8; ++v) xb[v] = (double)Xs[t * D + bj * 8 + v];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int v = 0; v < 8; ++v) gacc[u][v] = fma(xa[u], xb[v], gacc[u][v]);
       }
@@ -273,10 +282,10 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   }
   if (gact) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        const int gi = bi * 8 + u, gj = bj * 8 + v;
+        const int gi = bi * 4 + u, gj = bj * 8 + v;
         if (gj >= gi) Gp[upk<D>(gi, gj)] = gacc[u][v];
       }
   }
@@ -341,12 +350,12 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   }
   // 5. A = X V_r, streamed from X through the staging rows
   float* Xr = Rr + D * XS;  // [ROWS][XS], after the rows of R
-  store_a_from_rows<D, T, ROWS>(a, p, src, Xr, Rr, XS, sig, order);
+  store_a_from_rows<D, T, ROWS, XS>(a, p, src, Xr, Rr, XS, sig, order);
 }
 
 template <int D, typename T, int PMAX>
 void launch_rows(const SvdArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(float) * (PMAX + 16) * (D + 1);
+  const size_t lds = sizeof(float) * (PMAX + 16) * (D + kVecPad);
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
@@ -360,7 +369,7 @@ template <int D, typename T>
 void launch_tall(const SvdArgs& a, hipStream_t s) {
   // max(packed fp64 Gram + 16 staged rows, fp32 rows of R + 16 staged rows)
   const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * D;
-  const size_t rows = sizeof(float) * (D + 16) * (D + 1);
+  const size_t rows = sizeof(float) * (D + 16) * (D + kVecPad);
   const size_t lds = gram > rows ? gram : rows;
   static bool attr = false;
   if (!attr) {
