@@ -825,3 +825,62 @@ def test_resegment_window_refuses_imported_layers():
         ctx.resegment_window()
     assert ei.value.status == sekv.SEKV_ERR_STATE
     assert "not built" in str(ei.value)
+
+
+def test_resegment_window_tiny_fp32_no_window():
+    """fp32, d = 64, no local window (w = 0): every appended token at or below the
+    threshold leaves at once.  Span table and window rows bit-exact against the
+    oracle; new summaries within fp32 rounding; new SVD factors by the fp32
+    reconstruction bound; decode of the re-segmented artefacts against the oracle
+    with every span zoomed and with none."""
+    s = synth.spec("tiny")
+    ctx = _ctx(s, "device")
+    ctx.reserve_spans(64)
+    H = synth.surprisal_batch(s)
+    K, V = synth.kv_layer(s, 0, device="cpu")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    seg = O.segment(H[0], s.alpha, s.w)
+    theta = float(seg.theta)
+    a = _export_arts(ctx, s, 0)[(0, 0)][0]
+    positions = list(np.asarray(seg.anchors, np.int64))
+    H_all = list(H[0].astype(np.float64))
+    n_tot = s.n
+    rng = np.random.default_rng(5)
+    gen = torch.Generator().manual_seed(8)
+    for n_new in (7, 40, 1):
+        Hn = _new_surprisal(rng, theta, 1, n_new)
+        Kn = torch.randn(1, 1, n_new, s.d, generator=gen)
+        Vn = torch.randn(1, 1, n_new, s.d, generator=gen)
+        ctx.append_surprisal(Hn)
+        ctx.append_tokens(0, Kn.to(DEV).contiguous(), Vn.to(DEV).contiguous())
+        a = O.append_tokens(a, _to_np64(Kn[0, 0]), _to_np64(Vn[0, 0]))
+        positions += list(range(n_tot, n_tot + n_new))
+        H_all += list(Hn[0].astype(np.float64))
+        n_tot += n_new
+        pre = a
+        ctx.resegment_window()
+        torch.cuda.synchronize()
+        a = O.resegment_window(a, positions, H_all, theta, s.w, n_tot, 0, 0, s.rank_choices, s.rank_seed)
+        ms, mc, an, _ = ctx.spans(0)
+        assert np.array_equal(ms, a.mstart) and np.array_equal(mc, a.mcount) and np.array_equal(an, a.anchors)
+        g = _export_arts(ctx, s, 0)[(0, 0)][0]
+        assert np.array_equal(g.KA, a.KA) and np.array_equal(g.VA, a.VA) and np.array_equal(g.rank, a.rank)
+        m0 = pre.m
+        for x, r in ((g.kbar[m0:], a.kbar[m0:]), (g.vbar[m0:], a.vbar[m0:])):
+            assert np.all(np.abs(x - r) <= 1e-5 * np.max(np.abs(r), axis=1, keepdims=True) + 1e-30)
+        row_of = {p: i for i, p in enumerate(positions)}
+        for k in range(m0, g.m):
+            rows = [row_of[p] for p in range(int(g.mstart[k]), int(g.mstart[k] + g.mcount[k]))]
+            for X, A, Bt in ((pre.KA[rows], g.AK[k], g.BKt[k]), (pre.VA[rows], g.AV[k], g.BVt[k])):
+                sv = np.linalg.svd(X, compute_uv=False)
+                r = int(g.rank[k])
+                e_opt = math.sqrt(float(np.sum(sv[r:] ** 2)))
+                nx = float(np.linalg.norm(X))
+                assert float(np.linalg.norm(X - A @ Bt)) <= e_opt * (1 + 1e-3) + 1e-5 * nx, (k, r)
+                assert np.allclose(np.linalg.norm(A, axis=0), sv[:r], atol=1e-4 * sv[0])
+        positions = list(a.anchors)
+        assert g.m > m0 or n_new == 1
+        arts = {(0, 0): g}
+        _decode_compare(s, ctx, arts, 0, 2, np.array([0.0], np.float32))   # every span zoomed
+        _decode_compare(s, ctx, arts, 0, 2, np.array([1.0], np.float32))   # none zoomed
