@@ -63,6 +63,7 @@ struct LayerSched {
   bool pending = false;
   uint64_t calls = 0, reads = 0;
   std::vector<double> est;        // zoomed spans per call, per row
+  std::vector<double> est_plan;   // the estimates the current tables were planned from
 };
 
 // Device cache of one layer's host-resident bases: a ring region of the
@@ -668,7 +669,13 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
       if (S.stat_tasks[t].x >= 0) per[S.stat_tasks[t].x] += S.stat_pin[t];
     for (int bg = 0; bg < BH; ++bg) S.est[bg] = S.reads == 0 ? per[bg] : 0.5 * S.est[bg] + 0.5 * per[bg];
     S.reads++;
-    replan = true;
+    // replan only when some row's zoom load moved by more than a quarter (and
+    // one span): steady zoom rates keep the tables, and with them the order of
+    // the merges, from call to call
+    for (int bg = 0; bg < BH && !replan; ++bg) {
+      const double p0 = bg < (int)S.est_plan.size() ? S.est_plan[bg] : 0.0;
+      replan = std::fabs(S.est[bg] - p0) > 0.25 * p0 + 1.0;
+    }
   }
   if (S.anchors_changed) {
     // appended tokens: the anchor tasks must cover them from this launch on
@@ -682,21 +689,23 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   if (!replan || S.pending) return SEKV_OK;
   const std::vector<int4> old_tasks = S.tasks;
   plan_tasks(c, c->layers[layer]);
+  S.est_plan = S.est;
   // the slot counts follow from the tasks: both tables change together
   if (S.valid && old_tasks.size() == S.tasks.size() &&
       std::memcmp(old_tasks.data(), S.tasks.data(), S.tasks.size() * sizeof(int4)) == 0)
     return SEKV_OK;
-  if (S.tasks.size() > S.tasks_cap) {
+  const size_t nrec = S.tasks.size();
+  if (nrec > S.tasks_cap) {
     dfree(S.tasks_d);
     dfree(S.zcnt_d);
     hfree(S.tasks_pin);
     hfree(S.stat_pin);
     S.tasks_cap = 0;
-    TRY(dalloc(c, &S.tasks_d, S.tasks.size() * sizeof(int4)));
-    TRY(dalloc(c, &S.zcnt_d, S.tasks.size() * sizeof(int32_t)));
-    TRY(halloc(c, &S.tasks_pin, S.tasks.size() * sizeof(int4)));
-    TRY(halloc(c, &S.stat_pin, S.tasks.size() * sizeof(int32_t)));
-    S.tasks_cap = S.tasks.size();
+    TRY(dalloc(c, &S.tasks_d, nrec * sizeof(int4)));
+    TRY(dalloc(c, &S.zcnt_d, nrec * sizeof(int32_t)));
+    TRY(halloc(c, &S.tasks_pin, nrec * sizeof(int4)));
+    TRY(halloc(c, &S.stat_pin, nrec * sizeof(int32_t)));
+    S.tasks_cap = nrec;
   }
   if (!S.parts_d) {
     TRY(dalloc(c, &S.parts_d, (size_t)BH * 4));
@@ -704,7 +713,7 @@ sekv_status prepare_sched(sekv_ctx* c, int layer, hipStream_t stream, bool* capt
   }
   std::memcpy(S.tasks_pin, S.tasks.data(), S.tasks.size() * sizeof(int4));
   std::memcpy(S.parts_pin, S.parts_n.data(), (size_t)BH * 4);
-  HIPCHK(c, hipMemcpyAsync(S.tasks_d, S.tasks_pin, S.tasks.size() * sizeof(int4), hipMemcpyHostToDevice, stream));
+  HIPCHK(c, hipMemcpyAsync(S.tasks_d, S.tasks_pin, nrec * sizeof(int4), hipMemcpyHostToDevice, stream));
   HIPCHK(c, hipMemcpyAsync(S.parts_d, S.parts_pin, (size_t)BH * 4, hipMemcpyHostToDevice, stream));
   S.valid = true;
   return SEKV_OK;

@@ -447,6 +447,11 @@ def test_budget_cap_all_zoom_batch_gqa():
     out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
     mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
     qd = torch.from_numpy(q.astype(np.float32)).to(DEV)
+    # the schedule adapts to the zoom counts of earlier calls, and with it the
+    # order of the split-K merges: settle it before comparing two calls bit for bit
+    for _ in range(3):
+        ctx.decode_attn(0, qd, taus, out, mask, budget=budgets)
+        torch.cuda.synchronize()
     ctx.decode_attn(0, qd, taus, out, mask, budget=budgets)
     out2 = torch.zeros_like(out)
     ctx.decode_attn(0, qd, taus, out2, None, budget=budgets)
