@@ -442,7 +442,10 @@ def cpu_baseline(s, ctx, H, taus, n_heads, steps):
     return {"value": kps, "unit": "key-positions/s", "cores": 1, "kind": "oracle",
             "sample": f"numpy fp64 oracle, 1 thread: decode of {len(heads)} kv heads x {s.G} q-heads of layer 0 "
                       f"for {steps} steps ({t_dec:.1f}s) at the same thresholds, scaled to a {s.Hq}-head layer-step "
-                      f"(oracle artefact build of the sample: {t_build:.1f}s, not timed)"}
+                      f"(oracle artefact build of the sample: {t_build:.1f}s, not timed)",
+            # the oracle's build of the same sample (segmentation, summaries, LAPACK SVD), for
+            # the builder's own comparison; not part of the decode figure above
+            "builder_kv_head_rows_per_s": s.B * len(heads) * s.n / t_build}
 
 
 if __name__ == "__main__":
