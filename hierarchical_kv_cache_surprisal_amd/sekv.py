@@ -367,7 +367,10 @@ class Context:
         sekv_import_spans(self.ptr, b, mstart, mcount, anchors)
 
     def import_layout(self, layer, rank):
-        sekv_import_layout(self.ptr, layer, rank)
+        r = np.ascontiguousarray(rank, dtype=np.int32)
+        if r.size != self.B * self.Hkv * self.m_max():  # the library reads exactly this many
+            raise ValueError(f"rank must hold B * H_kv * m_max = {self.B * self.Hkv * self.m_max()} entries")
+        sekv_import_layout(self.ptr, layer, r)
 
     def import_head(self, layer, b, g, kbar, vbar, KA, VA, rank, bases):
         sekv_import_head(self.ptr, layer, b, g, kbar, vbar, KA, VA, rank, bases)

@@ -228,8 +228,10 @@ sekv_status sekv_import_spans(sekv_ctx* ctx, int32_t b, int32_t m, const int32_t
                               const int32_t* mcount, int32_t n_anchors, const int32_t* anchors);
 
 /* Fix the packed-basis layout of a layer that is not built here (test hook):
- *   rank host int32 [B][H_kv][m_max]: r_eff of every (b, g, span); entries at
- *   or beyond a sequence's m are ignored; 1 <= rank <= min(mcount, d).
+ *   rank host int32 [B][H_kv][m_max], m_max as returned by sekv_get_spans (it
+ *   includes the spare rows of sekv_reserve_spans): r_eff of every (b, g,
+ *   span); entries at or beyond a sequence's m are ignored;
+ *   1 <= rank <= min(mcount, d).
  * Allocates the layer's summaries, anchors and basis store (zero-filled);
  * sekv_import_head then fills them head by head.  A layer produced by
  * sekv_build already has its layout and needs no call.

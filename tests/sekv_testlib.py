@@ -73,7 +73,7 @@ def import_oracle_layer(ctx, layer: int, segs: Sequence[O.Segmentation],
     if set_spans:
         for b in range(B):
             ctx.import_spans(b, segs[b].mstart, segs[b].mcount, segs[b].anchors)
-    m_max = max(1, max(s.m for s in segs))
+    m_max = ctx.m_max()  # the row stride of the context's per-span arrays (spare rows included)
     if set_layout:
         rank = np.ones((B, Hkv, m_max), np.int32)
         for (b, g), a in arts.items():
