@@ -585,10 +585,11 @@ struct Stage {
 };
 
 template <int D, typename T, int G>
-__device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) {
+__device__ void anchor_task(const DecodeArgs& a, int4 task, Smem<D, G>& sh) {
+  MergeLds<D, G>& ml = sh.ml;
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
-  constexpr int U = G >= 4 ? kSpanStageRows : kAnchorStageRows;  // wide groups: registers for the heads
+  constexpr int U = G >= 4 ? 1 : kAnchorStageRows;  // wide groups: registers for the heads
   constexpr int STEP = kWaves * RPW * U;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPR, sub = lane % LPR;
@@ -618,10 +619,20 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
       sg.v[u].load(Vb + (size_t)rr * D);
     }
   };
-  float qr[G][EPL];
+  // wide groups keep the queries in LDS: G x EPL registers less, read once per head and stage
+  constexpr bool QLDS = G >= 4;
+  float qr[QLDS ? 1 : G][EPL];
   auto consume = [&](const Stage<T, U>& sg, int bs) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      float qh[EPL];
+      if constexpr (QLDS) {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) *reinterpret_cast<float4*>(qh + e) = *reinterpret_cast<const float4*>(&sh.q[h][sub * EPL + e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qh[e] = qr[h][e];
+      }
       Raw<T> kx[U], vx[U];  // per head, so that their unpacking is not hoisted out of the loop
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -637,7 +648,7 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
       for (int u = 0; u < U; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * kx[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qh[e] * kx[u].get(e);
         dp = group_sum<LPR>(dp);
         lg[u] = (bs + u * RPW + slot < r1) ? dp * c2 : kNegInf;
       }
@@ -661,10 +672,15 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, MergeLds<D, G>& ml) 
     }
   };
   int bs = r0 + wave * RPW * U;
+  if constexpr (QLDS) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+      sh.q[idx / D][idx % D] = a.q[((size_t)b * a.Hq + g * G) * D + idx];
+    __syncthreads();
+  }
   if (bs < r1) {
     Stage<T, U> A, B;
     load(A, bs);
-    load_q<D, G, T>(a, b, g, sub, qr);
+    if constexpr (!QLDS) load_q<D, G, T>(a, b, g, sub, qr);
     for (; bs < r1; bs += 2 * STEP) {
       load(B, bs + STEP);
       consume(A, bs);
@@ -687,7 +703,7 @@ template <int D, typename T, int G, int MODE, bool ROUTED>
 __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh) {
   using Gm = Geo<D, T>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
-  constexpr int U = kSpanStageRows;
+  constexpr int U = G >= 4 ? 1 : kSpanStageRows;
   constexpr int STEP = kWaves * RPW * U;
   constexpr bool SCORES = MODE == 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -733,7 +749,8 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
       }
     }
   };
-  float qr[G][EPL];
+  constexpr bool QLDS = G >= 4 && !ROUTED;
+  float qr[QLDS ? 1 : G][EPL];
   float qpr[ROUTED ? G : 1][EPL];  // projected query piece (routing projection), zero beyond d'
   constexpr bool routed = ROUTED;
   const float inv_sqrt_dr = routed ? rsqrtf((float)a.dr) : 0.f;
@@ -754,6 +771,14 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     for (int u = 0; u < U; ++u) zbits[u] = 0u;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      float qh[EPL];
+      if constexpr (QLDS) {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) *reinterpret_cast<float4*>(qh + e) = *reinterpret_cast<const float4*>(&sh.q[h][sub * EPL + e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qh[e] = qr[h][e];
+      }
       Raw<T> kx[U], vx[U];  // per head, so that their unpacking is not hoisted out of the loop
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -769,7 +794,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
       for (int u = 0; u < U; ++u) {
         float dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += qr[h][e] * kx[u].get(e);
+        for (int e = 0; e < EPL; ++e) dp += qh[e] * kx[u].get(e);
         dp = group_sum<LPR>(dp);
         float score;
         if (routed) {
@@ -824,10 +849,15 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     }
   };
   int bs = k0 + wave * RPW * U;
+  if constexpr (QLDS) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+      sh.q[idx / D][idx % D] = a.q[((size_t)b * a.Hq + g * G) * D + idx];
+    __syncthreads();
+  }
   if (bs < k1) {
     Stage<T, U> A, B;
     load(A, bs);
-    load_q<D, G, T>(a, b, g, sub, qr);
+    if constexpr (!QLDS) load_q<D, G, T>(a, b, g, sub, qr);
     if constexpr (ROUTED) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -911,7 +941,7 @@ __global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
   const int4 task = a.tasks[blockIdx.x];
   if (task.x < 0) {  // anchor tasks: MODE 0 only (the attend kernel runs them otherwise)
-    if (MODE == 0) anchor_task<D, T, G>(a, task, sh.ml);
+    if (MODE == 0) anchor_task<D, T, G>(a, task, sh);
     return;
   }
   span_task<D, T, G, MODE, ROUTED>(a, (int)blockIdx.x, task, sh);
@@ -939,7 +969,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
   const int i = (int)blockIdx.x - a.n_zoom_wgs;
   if (i >= 0) {
-    anchor_task<D, T, G>(a, a.tasks[a.n_span_tasks + i], sh.ml);
+    anchor_task<D, T, G>(a, a.tasks[a.n_span_tasks + i], sh);
     return;
   }
   staged_group<D, T, G>(a, blockIdx.x, sh);
