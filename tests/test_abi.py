@@ -69,6 +69,20 @@ def test_null_context_calls_fail_cleanly():
     st = sekv.sekv_stats()
     assert lib.sekv_get_stats(None, ctypes.byref(st)) == sekv.SEKV_ERR_INVALID
     lib.sekv_destroy(None)
+    # every other entry point that takes a context refuses a NULL one before any HIP call
+    for name in _declared():
+        f = getattr(lib, name)
+        if name in ("sekv_create", "sekv_destroy", "sekv_last_error") or not f.argtypes:
+            continue
+        args = []
+        for t in f.argtypes:
+            if t in (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64):
+                args.append(0)
+            elif t is ctypes.c_double:
+                args.append(1.0)
+            else:
+                args.append(None)
+        assert f(*args) == sekv.SEKV_ERR_INVALID, name
 
 
 def test_pack_unpack_roundtrip():
