@@ -247,6 +247,21 @@ def test_gqa_ragged_batch_decode_and_build(home):
     _check_build(s, ctx2, segs, arts, 0, H, K, V)
 
 
+@pytest.mark.parametrize("home", ["device", "host"])
+def test_groups_of_two_decode(home):
+    """Groups of two query heads (the route kernel's G = 2 variant), ragged batch,
+    zoom rates from 1% to 50%, ranks up to 64 (two register batches)."""
+    s = _gqa_small().replace(Hq=4, Hkv=2, steps=2)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.01, 0.5, 0.15, 0.05]), s.B)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    _, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert nz > 0
+
+
 # ============================================================================ edge cases
 
 def test_window_covers_everything_no_spans():
