@@ -197,6 +197,7 @@ struct sekv_ctx {
 
   sekv_stats stats{};
   int anchor_chunk = 256, span_chunk = 64;
+  int fill_tasks = 768;           // route workgroups that fill the GPU once (three per CU)
 };
 
 namespace {
@@ -596,8 +597,18 @@ sekv_status fetch_items(sekv_ctx* c, int layer, const int4* items, int count, hi
 void plan_tasks(sekv_ctx* c, LayerState& L) {
   LayerSched& S = L.sched;
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv;
-  const int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
-  const int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
+  int base = std::min(kMaxSpanChunk, env_int("SEKV_SPAN_CHUNK", c->span_chunk, 16, kMaxSpanChunk));
+  int ach = env_int("SEKV_ANCHOR_CHUNK", c->anchor_chunk, 16, 1 << 20);
+  // small layers: halve the chunks (spans down to 32 rows, anchors down to 64)
+  // while the tasks would not fill the GPU once
+  for (;;) {
+    int64_t total = 0;
+    for (int bg = 0; bg < BH; ++bg)
+      total += (c->m_b[bg / Hkv] + base - 1) / base + (L.na_l[bg / Hkv] + ach - 1) / ach;
+    if (total >= c->fill_tasks || (base <= 32 && ach <= 64)) break;
+    if (base > 32) base /= 2;
+    if (ach > 64) ach /= 2;
+  }
   const double zpw = env_int("SEKV_ZOOM_PER_TASK", 4, 1, 256);
   // a span task folds its zoomed spans into its one slot; with staged bases
   // they go to its second slot (written by the attend kernel)
@@ -973,6 +984,11 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->mcount.assign(k.batch, {});
   c->anchors.assign(k.batch, {});
   c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
+  {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->cfg.device) == hipSuccess && cus > 0)
+      c->fill_tasks = 3 * cus;
+  }
   c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
   sekv_status s = dalloc(c, &c->zcounter_d, 4);
   if (s == SEKV_OK) s = dalloc(c, &c->qp_d, (size_t)k.batch * k.n_q_heads * k.d_head * sizeof(float));
