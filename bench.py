@@ -158,7 +158,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              f"(the decode path has no multi-GPU split in this build).", file=sys.stderr)
+              f"(the decode path runs on one GPU; multi-GPU execution is not implemented).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
