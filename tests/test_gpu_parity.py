@@ -904,3 +904,18 @@ def test_resegment_window_tiny_fp32_no_window():
         arts = {(0, 0): g}
         _decode_compare(s, ctx, arts, 0, 2, np.array([0.0], np.float32))   # every span zoomed
         _decode_compare(s, ctx, arts, 0, 2, np.array([1.0], np.float32))   # none zoomed
+
+
+def test_mha_bf16_ranks_above_one_register_batch():
+    """One query head per kv head with bf16 ranks above 32: the zoom units take the
+    rank-batch path (two batches of 32 rows at rank 64) instead of the one-round path."""
+    s = _small_bf16().replace(Hq=4, Hkv=4, steps=2, rank_choices=(24, 40, 64))
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    assert max(int(a.rank.max()) for a in arts.values()) > 32
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.05, 0.3, 1.0, 0.15]), s.B)
+    ctx = _ctx(s, "device")
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    _, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert nz > 0
