@@ -919,3 +919,41 @@ def test_mha_bf16_ranks_above_one_register_batch():
     T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
     _, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus)
     assert nz > 0
+
+
+def test_forced_failures_leave_the_context_usable(monkeypatch):
+    """Failure handling, forced from the host (SEKV_FAULT): a refused pinned
+    allocation fails the host-home build with OOM, and a failed basis fetch fails
+    the staged decode with a HIP error; both leave the context usable, and the
+    next calls match the oracle."""
+    s = _small_bf16().replace(Hq=4, Hkv=4, steps=1)
+    sekv = _lib()
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.1, 0.3, 0.05, 0.6]), s.B)
+    # pinned store refused: the host-home build fails cleanly
+    ctx = _ctx(s, "host")
+    monkeypatch.setenv("SEKV_FAULT", "pinned_oom")
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    assert ei.value.status == sekv.SEKV_ERR_OOM
+    monkeypatch.delenv("SEKV_FAULT")
+    torch.cuda.synchronize()
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    for b in range(s.B):
+        ms, mc, an, _ = ctx.spans(b)
+        assert np.array_equal(ms, segs[b].mstart) and np.array_equal(an, segs[b].anchors)
+    # staged fetch failure: the decode call fails, the next one works
+    ctx2 = _ctx(s, "host_staged")
+    T.import_oracle_layer(ctx2, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    _decode_compare(s, ctx2, arts, 0, 1, taus)
+    monkeypatch.setenv("SEKV_FAULT", "fetch")
+    out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
+    with pytest.raises(sekv.SekvError) as ei:
+        ctx2.decode_attn(0, torch.from_numpy(qs[0].astype(np.float32)).to(DEV), taus, out)
+    assert ei.value.status == sekv.SEKV_ERR_HIP
+    monkeypatch.delenv("SEKV_FAULT")
+    torch.cuda.synchronize()
+    _decode_compare(s, ctx2, arts, 0, 1, taus)
