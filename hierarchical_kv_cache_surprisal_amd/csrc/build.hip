@@ -283,6 +283,14 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendArgs a, int row_bytes
 }
 
 // Block (bg, chunk) gathers rows of one (sequence, kv head) in 16-byte pieces.
+__global__ __launch_bounds__(kThreads) void k_copy_runs(const int4* list, const void* src, void* dst, int esz) {
+  const int4 e = list[blockIdx.x];
+  const int64_t n16 = (int64_t)e.z * 8 * esz / 16;
+  const uint4* in = reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((int64_t)(uint32_t)e.x << 3) * esz);
+  uint4* out = reinterpret_cast<uint4*>(static_cast<char*>(dst) + ((int64_t)(uint32_t)e.y << 3) * esz);
+  for (int64_t i = threadIdx.x; i < n16; i += kThreads) out[i] = in[i];
+}
+
 __global__ __launch_bounds__(kThreads) void k_gather_rows(GatherArgs a) {
   const int bg = blockIdx.x, b = bg / a.Hkv;
   const int n = a.cnt[b];
@@ -350,6 +358,11 @@ void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s
   const int chunks = std::max(1, std::min(64, (a.n_new * row_bytes / 16 + kThreads - 1) / kThreads));
   hipLaunchKernelGGL(k_append, dim3(B * a.Hkv, chunks), dim3(kThreads), 0, s, a, row_bytes);
   hipLaunchKernelGGL(k_append_count, dim3((B + 255) / 256), dim3(256), 0, s, a.na, B, a.n_new);
+}
+
+void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_copy_runs, dim3(n), dim3(kThreads), 0, s, list, src, dst, esz);
 }
 
 void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s) {

@@ -72,6 +72,7 @@ template <>
 struct Raw<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0u, 0u, 0u, 0u); }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
@@ -81,6 +82,7 @@ template <>
 struct Raw<float> {
   float4 v;
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 };
 
@@ -158,6 +160,95 @@ __device__ __forceinline__ void fold_record(MergeLds<D, G>& ml, int wave, int h,
 
 // ------------------------------------------------------------------ zoomed span tile, one wave
 
+// One unit of a one-head group with r <= NU*RPW: lane rank rows j = rg + RPW*u
+// for u < NU, every load of the unit in one round, the products in registers
+// (the layout of zoom_unit below).
+template <int D, typename T, int NU, class QGet, class Sink>
+__device__ __forceinline__ void zoom_unit_one(const T* __restrict__ AKt, const T* __restrict__ BKt,
+                                              const T* __restrict__ AVt, const T* __restrict__ BVt, int c, int c8,
+                                              int r, int tok, int tokc, QGet qget, Sink sink, float c2, int rg,
+                                              int tg) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  const int rl = r - 1;
+  const int nu = (r + RPW - 1) / RPW;  // rank rows per lane that r needs
+  Raw<T> bk[NU], ak[NU], av[NU], bv[NU];
+  // rows [lo, hi) load when nu > lo, else hold zeros: a few wave-uniform branches
+  auto rows = [&](int lo, int hi) {
+    if (nu > lo) {
+#pragma unroll
+      for (int u = lo; u < hi; ++u) {
+        const int j = min(rg + RPW * u, rl);
+        bk[u].load(BKt + (size_t)j * D + tg * EPL);
+        ak[u].load(AKt + (size_t)j * c8 + tokc);
+        av[u].load(AVt + (size_t)j * c8 + tokc);
+        bv[u].load(BVt + (size_t)j * D + tg * EPL);
+      }
+    } else {
+#pragma unroll
+      for (int u = lo; u < hi; ++u) {
+        bk[u].zero();
+        ak[u].zero();
+        av[u].zero();
+        bv[u].zero();
+      }
+    }
+  };
+  rows(0, NU >= 2 ? 2 : 1);
+  if constexpr (NU >= 4) rows(2, 4);
+  if constexpr (NU >= 8) rows(4, 8);
+  float q[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) q[e] = qget(0, e);
+  float p[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    float dp = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dp += q[e] * bk[u].get(e);
+    dp = group_sum<LPR>(dp);
+    p[u] = (rg + RPW * u < r) ? dp * c2 : 0.f;
+  }
+  float lg[EPL];
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) x += p[u] * ak[u].get(e);
+    x = slots_sum<LPR>(x);
+    x = (tok + e < c) ? x : kNegInf;
+    lg[e] = x;
+    mx = fmaxf(mx, x);
+  }
+  mx = group_max<LPR>(mx);  // finite: token t0 is valid
+  float sl = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    lg[e] = fast_exp2(lg[e] - mx);
+    sl += lg[e];
+  }
+  sl = group_sum<LPR>(sl);
+  float w[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x += lg[e] * av[u].get(e);
+    x = group_sum<LPR>(x);
+    w[u] = (rg + RPW * u < r) ? x : 0.f;
+  }
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) x += w[u] * bv[u].get(e);
+    o[e] = slots_sum<LPR>(x);
+  }
+  sink(0, mx, sl, o);
+}
+
 // One unit of a zoomed span (c tokens, rank r <= D) of one kv head: the
 // tokens [t0, min(c, t0 + TILE)), in rank space.  Units of one span are
 // independent entries of the softmax and merge by log-sum-exp.
@@ -168,7 +259,8 @@ __device__ __forceinline__ void fold_record(MergeLds<D, G>& ml, int wave, int h,
 // p_j lands, after the reduction inside the row slot, exactly in the lanes
 // that hold row j of A_K^T, and w_j in those holding row j of B_V^T, so no
 // data moves between the four products.  Addresses are clamped to valid rows
-// and tokens (no load sits behind a branch).  A one-head group with
+// and tokens; the rank rows a lane loads stop at the first one past r (the
+// bound is the same for the whole wave).  A one-head group with
 // r <= RBATCH issues every load of the unit in one round.  Otherwise the ranks
 // go in batches of RBATCH rows: the key batches (B_K^T, A_K^T) accumulate the
 // logits of every head in hb, then the value batches (A_V^T, B_V^T) the
@@ -192,79 +284,9 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
   const int tokc = tok < c8 ? tok : t0;  // t0 < c: a valid piece
 
   if (G == 1 && r <= RBATCH) {
-    // ---------------- one head, one rank batch: everything in registers, one round
-    Raw<T> bk[RB], ak[RB], av[RB], bv[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int j = min(rg + RPW * u, rl);
-      bk[u].load(BKt + (size_t)j * D + tg * EPL);
-      ak[u].load(AKt + (size_t)j * c8 + tokc);
-      av[u].load(AVt + (size_t)j * c8 + tokc);
-      bv[u].load(BVt + (size_t)j * D + tg * EPL);
-    }
-#pragma unroll 1
-    for (int h = 0; h < G; ++h) {  // one head at a time on the loaded bases
-      if (!((hb >> h) & 1u)) continue;  // the same for the whole wave
-      if (G > 1) {
-#pragma unroll
-        for (int u = 0; u < RB; ++u) {
-          keep_packed(bk[u]);
-          keep_packed(ak[u]);
-          keep_packed(av[u]);
-          keep_packed(bv[u]);
-        }
-      }
-      float q[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) q[e] = qget(h, e);
-      float p[RB];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        float dp = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dp += q[e] * bk[u].get(e);
-        dp = group_sum<LPR>(dp);
-        p[u] = (rg + RPW * u < r) ? dp * c2 : 0.f;
-      }
-      float lg[EPL];
-      float mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = 0.f;
-#pragma unroll
-        for (int u = 0; u < RB; ++u) x += p[u] * ak[u].get(e);
-        x = slots_sum<LPR>(x);
-        x = (tok + e < c) ? x : kNegInf;
-        lg[e] = x;
-        mx = fmaxf(mx, x);
-      }
-      mx = group_max<LPR>(mx);  // finite: token t0 is valid
-      float sl = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        lg[e] = fast_exp2(lg[e] - mx);
-        sl += lg[e];
-      }
-      sl = group_sum<LPR>(sl);
-      float w[RB];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        float x = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x += lg[e] * av[u].get(e);
-        x = group_sum<LPR>(x);
-        w[u] = (rg + RPW * u < r) ? x : 0.f;
-      }
-      float o[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = 0.f;
-#pragma unroll
-        for (int u = 0; u < RB; ++u) x += w[u] * bv[u].get(e);
-        o[e] = slots_sum<LPR>(x);
-      }
-      sink(h, mx, sl, o);
-    }
+    // one head, one rank batch: as many rank rows per lane as r needs (r is
+    // the same for the whole wave), so that no load repeats another
+    zoom_unit_one<D, T, RB>(AKt, BKt, AVt, BVt, c, c8, r, tok, tokc, qget, sink, c2, rg, tg);
     return;
   }
 
@@ -277,12 +299,18 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
     for (int e = 0; e < EPL; ++e) lg[h][e] = 0.f;
 #pragma unroll 1
   for (int j0 = 0; j0 < r; j0 += RBATCH) {
+    const int nu = (r - j0 + RPW - 1) / RPW;  // rank rows per lane in this batch (the same for the wave)
     Raw<T> bk[RB], ak[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int j = min(j0 + rg + RPW * u, rl);
-      bk[u].load(BKt + (size_t)j * D + tg * EPL);
-      ak[u].load(AKt + (size_t)j * c8 + tokc);
+      if (u < nu) {
+        const int j = min(j0 + rg + RPW * u, rl);
+        bk[u].load(BKt + (size_t)j * D + tg * EPL);
+        ak[u].load(AKt + (size_t)j * c8 + tokc);
+      } else {
+        bk[u].zero();
+        ak[u].zero();
+      }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -337,12 +365,18 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 #pragma unroll 1
   for (int j0 = 0; j0 < r; j0 += RBATCH) {
+    const int nu = (r - j0 + RPW - 1) / RPW;
     Raw<T> av[RB], bv[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int j = min(j0 + rg + RPW * u, rl);
-      av[u].load(AVt + (size_t)j * c8 + tokc);
-      bv[u].load(BVt + (size_t)j * D + tg * EPL);
+      if (u < nu) {
+        const int j = min(j0 + rg + RPW * u, rl);
+        av[u].load(AVt + (size_t)j * c8 + tokc);
+        bv[u].load(BVt + (size_t)j * D + tg * EPL);
+      } else {
+        av[u].zero();
+        bv[u].zero();
+      }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -937,7 +971,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
 // ------------------------------------------------------------------ kernels
 
 template <int D, typename T, int G, int MODE, bool ROUTED>
-__global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1 && MODE == 0 ? 3 : 1))) void k_route(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
   const int4 task = a.tasks[blockIdx.x];
   if (task.x < 0) {  // anchor tasks: MODE 0 only (the attend kernel runs them otherwise)

@@ -72,16 +72,21 @@ struct CacheEntry {
   int64_t idx;   // (b * Hkv + g) * m_max + k
   int64_t off;   // region-relative element offset
   int64_t len;   // elements
+  uint64_t batch;  // the prefetch that placed it
 };
 struct LayerCache {
   bool init = false;
   int64_t base = 0, size = 0;      // region [base, base + size) elements of the cache
   int64_t head = 0;                // next free position (region-relative)
+  uint64_t batch = 0;              // prefetches so far
   std::deque<CacheEntry> fifo;     // resident entries, oldest first
   std::vector<int32_t> slot_h;     // [B*Hkv*m_max] (base + off) / 8, or -1
   int32_t* slot_d = nullptr;       // device copy read by the decode kernel
   int32_t* slot_pin = nullptr;     // pinned staging of its uploads
   uint8_t* zm_pin = nullptr;       // [B*Hq*m_max] zoom mask of the last decode, copied back
+  int4* runs_pin = nullptr;        // copy runs of the last prefetch (source, destination, length; / 8)
+  int4* runs_d = nullptr;
+  size_t runs_cap = 0;
   hipEvent_t ev_zm = nullptr;      // after that copy
   hipEvent_t ev_pref = nullptr;    // after the last prefetch (copies + table upload)
   hipEvent_t ev_done = nullptr;    // after the last decode of the layer
@@ -287,6 +292,8 @@ void hfree(P*& p) {
 
 void free_layer_cache(LayerCache& C) {
   dfree(C.slot_d);
+  dfree(C.runs_d);
+  hfree(C.runs_pin);
   hfree(C.slot_pin);
   hfree(C.zm_pin);
   if (C.ev_zm) (void)hipEventDestroy(C.ev_zm);
@@ -776,27 +783,36 @@ sekv_status ensure_layer_cache(sekv_ctx* c, int layer) {
 }
 
 // Place `len` elements in the ring, evicting the oldest entries it overlaps.
+// An entry placed by the same prefetch is never evicted: all of a prefetch's
+// copies run at once, so its destinations must not overlap.  Then the span is
+// not placed (and is read from the host store).
 bool cache_place(LayerCache& C, int64_t len, int64_t* off) {
   if (len > C.size) return false;
-  auto evict = [&](int64_t lo, int64_t hi) {
+  auto evict = [&](int64_t lo, int64_t hi) -> bool {
     while (!C.fifo.empty()) {
       const CacheEntry& f = C.fifo.front();
       if (!(f.off < hi && f.off + f.len > lo)) break;
+      if (f.batch == C.batch) return false;
       C.slot_h[f.idx] = -1;
       C.dirty_lo = std::min(C.dirty_lo, f.idx);
       C.dirty_hi = std::max(C.dirty_hi, f.idx + 1);
       C.fifo.pop_front();
     }
+    return true;
   };
-  if (C.head + len > C.size) {
-    evict(C.head, C.size);
-    C.head = 0;
+  int64_t at = C.head;
+  if (at + len > C.size) {
+    if (!evict(at, C.size)) return false;
+    at = 0;
   }
-  evict(C.head, C.head + len);
-  *off = C.head;
-  C.head += len;
+  if (!evict(at, at + len)) return false;
+  *off = at;
+  C.head = at + len;
   return true;
 }
+
+// Elements per piece of a cache fill copy (a multiple of 8).
+constexpr int64_t kCopyPiece = 16384;
 
 // Predictive prefetch for `layer` (called while an earlier layer is being
 // decoded): the spans its last decode zoomed (any head of the group) are
@@ -845,14 +861,19 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     }
   if (need.empty()) return SEKV_OK;
   if (hipEventQuery(C.ev_pref) != hipSuccess) HIPCHK(c, hipEventSynchronize(C.ev_pref));  // slot_pin is free
+  C.batch++;
   if (C.done_valid) HIPCHK(c, hipStreamWaitEvent(c->side, C.ev_done, 0));
   const size_t es = c->esz;
+  // the misses, merged into runs of consecutive store and cache positions, are
+  // copied by one kernel that reads the pinned store in place
+  std::vector<int4> runs;
   int64_t run_src = -1, run_dst = -1, run_len = 0;
   auto flush = [&]() -> sekv_status {
-    if (run_len > 0) {
-      HIPCHK(c, hipMemcpyAsync((char*)c->cache_d + (size_t)run_dst * es, (const char*)L.bases_h + (size_t)run_src * es,
-                               (size_t)run_len * es, hipMemcpyHostToDevice, c->side));
-      c->stats.memcpy_calls++;
+    // pieces of at most kCopyPiece elements: one workgroup each
+    for (int64_t o = 0; o < run_len; o += kCopyPiece) {
+      const int64_t n = std::min<int64_t>(kCopyPiece, run_len - o);
+      runs.push_back(make_int4((int)(uint32_t)((run_src + o) >> 3), (int)(uint32_t)((run_dst + o) >> 3),
+                               (int)(n >> 3), 0));
     }
     run_len = 0;
     return SEKV_OK;
@@ -866,7 +887,7 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     C.slot_h[idx] = (int32_t)(dst >> 3);
     C.dirty_lo = std::min(C.dirty_lo, idx);
     C.dirty_hi = std::max(C.dirty_hi, idx + 1);
-    C.fifo.push_back({idx, off, len});
+    C.fifo.push_back({idx, off, len, C.batch});
     c->stats.cache_spans_fetched++;
     c->stats.cache_bytes_fetched += (uint64_t)len * es;
     if (run_len > 0 && run_src + run_len == src && run_dst + run_len == dst) {
@@ -879,6 +900,22 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     }
   }
   TRY(flush());
+  if (!runs.empty()) {
+    if (runs.size() > C.runs_cap) {  // the previous prefetch's copies are done (ev_pref)
+      const size_t cap = std::max<size_t>(runs.size(), 2 * C.runs_cap + 256);
+      dfree(C.runs_d);
+      hfree(C.runs_pin);
+      C.runs_cap = 0;
+      TRY(dalloc(c, &C.runs_d, cap * sizeof(int4)));
+      TRY(halloc(c, &C.runs_pin, cap * sizeof(int4)));
+      C.runs_cap = cap;
+    }
+    std::memcpy(C.runs_pin, runs.data(), runs.size() * sizeof(int4));
+    HIPCHK(c, hipMemcpyAsync(C.runs_d, C.runs_pin, runs.size() * sizeof(int4), hipMemcpyHostToDevice, c->side));
+    launch_copy_runs(C.runs_d, (int)runs.size(), L.bases_hd, c->cache_d, (int)es, c->side);
+    HIPCHK(c, hipGetLastError());
+    c->stats.memcpy_calls++;
+  }
   if (C.dirty_lo < C.dirty_hi) {  // upload the changed range of the slot table
     const size_t lo = (size_t)C.dirty_lo, n = (size_t)(C.dirty_hi - C.dirty_lo);
     std::memcpy(C.slot_pin + lo, C.slot_h.data() + lo, n * 4);

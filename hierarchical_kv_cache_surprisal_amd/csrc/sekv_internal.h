@@ -146,6 +146,12 @@ struct GatherArgs {
 };
 void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s);
 
+// Copies of element runs, one workgroup per run: list[i] = (source offset / 8,
+// destination offset / 8, elements / 8, unused), offsets in elements of esz
+// bytes (elements / 8 * esz a multiple of 16).  src may be mapped pinned host
+// memory (the device basis cache fills this way in one launch).
+void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, hipStream_t s);
+
 // Soft rank gates on the stored A factors of the spans of one (sequence, kv head).
 struct GateArgs {
   void* bases;             // the layer's packed store (device memory or mapped pinned memory)

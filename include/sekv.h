@@ -384,7 +384,7 @@ typedef struct sekv_stats {
   uint64_t fetch_calls;           /* sekv_zoom_fetch calls */
   uint64_t spans_fetched;         /* (b, g, span) bases copied to staging */
   uint64_t bytes_fetched;         /* bytes copied host -> staging */
-  uint64_t memcpy_calls;          /* hipMemcpyAsync calls issued by fetches */
+  uint64_t memcpy_calls;          /* copy calls issued by fetches (a staged fetch: one per run; a cache prefetch: one kernel) */
   int64_t device_resident_bytes;  /* anchors + summaries (+ routing summaries) + tables (+ bases if DEVICE) */
   int64_t host_basis_bytes;       /* pinned store (HOST) */
   int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
