@@ -22,6 +22,7 @@ HIP events around a graph replay of every step.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -299,6 +300,12 @@ def main():
             graph = None
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # eager launches allocate small Python objects on every call: a full
+    # collection of the calibration leftovers inside the timed region would stall
+    # the launch loop for milliseconds, so collect now and pause the collector
+    pooled = None
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
@@ -310,6 +317,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    gc.enable()
     t_ms = ev0.elapsed_time(ev1)
     launches = args.steps * L
     t_ls = t_ms * 1e-3 / launches

@@ -283,12 +283,20 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendArgs a, int row_bytes
 }
 
 // Block (bg, chunk) gathers rows of one (sequence, kv head) in 16-byte pieces.
-__global__ __launch_bounds__(kThreads) void k_copy_runs(const int4* list, const void* src, void* dst, int esz) {
+// Workgroups [0, n) copy one run each; the workgroups after them copy the
+// 16-byte pieces [0, n16) of a table range, one piece per thread.
+__global__ __launch_bounds__(kThreads) void k_copy_runs(const int4* list, int n, const void* src, void* dst, int esz,
+                                                       const uint4* tsrc, uint4* tdst, int64_t n16) {
+  if ((int)blockIdx.x >= n) {
+    const int64_t i = (int64_t)(blockIdx.x - n) * kThreads + threadIdx.x;
+    if (i < n16) tdst[i] = tsrc[i];
+    return;
+  }
   const int4 e = list[blockIdx.x];
-  const int64_t n16 = (int64_t)e.z * 8 * esz / 16;
+  const int64_t m16 = (int64_t)e.z * 8 * esz / 16;
   const uint4* in = reinterpret_cast<const uint4*>(static_cast<const char*>(src) + ((int64_t)(uint32_t)e.x << 3) * esz);
   uint4* out = reinterpret_cast<uint4*>(static_cast<char*>(dst) + ((int64_t)(uint32_t)e.y << 3) * esz);
-  for (int64_t i = threadIdx.x; i < n16; i += kThreads) out[i] = in[i];
+  for (int64_t i = threadIdx.x; i < m16; i += kThreads) out[i] = in[i];
 }
 
 __global__ __launch_bounds__(kThreads) void k_gather_rows(GatherArgs a) {
@@ -360,9 +368,13 @@ void launch_append(int d, int kv_bf16, int B, const AppendArgs& a, hipStream_t s
   hipLaunchKernelGGL(k_append_count, dim3((B + 255) / 256), dim3(256), 0, s, a.na, B, a.n_new);
 }
 
-void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, hipStream_t s) {
-  if (n <= 0) return;
-  hipLaunchKernelGGL(k_copy_runs, dim3(n), dim3(kThreads), 0, s, list, src, dst, esz);
+void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, const void* tsrc, void* tdst,
+                      int64_t table_bytes, hipStream_t s) {
+  const int64_t n16 = table_bytes / 16;
+  const int64_t blocks = n + (n16 + kThreads - 1) / kThreads;
+  if (blocks <= 0) return;
+  hipLaunchKernelGGL(k_copy_runs, dim3((unsigned)blocks), dim3(kThreads), 0, s, list, n, src, dst, esz,
+                     static_cast<const uint4*>(tsrc), static_cast<uint4*>(tdst), n16);
 }
 
 void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s) {

@@ -1024,6 +1024,20 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, hq = bh % a.Hq;
   const int g = hq / a.G;
+  if (a.mask_h) {
+    // the zoom mask back to host memory (the device basis cache predicts the
+    // next step from it), spread over the grid; 16-byte pieces when aligned
+    const int64_t tid = (int64_t)blockIdx.x * NT + threadIdx.x, nth = (int64_t)gridDim.x * NT;
+    const int64_t n = a.mask_bytes;
+    int64_t i0 = 0;
+    if ((((uintptr_t)a.mask | (uintptr_t)a.mask_h) & 15u) == 0) {
+      const int64_t n16 = n >> 4;
+      for (int64_t i = tid; i < n16; i += nth)
+        reinterpret_cast<uint4*>(a.mask_h)[i] = reinterpret_cast<const uint4*>(a.mask)[i];
+      i0 = n16 << 4;
+    }
+    for (int64_t i = i0 + tid; i < n; i += nth) a.mask_h[i] = a.mask[i];
+  }
   const int np = a.parts_n[(size_t)b * a.Hkv + g];
   const int pg = threadIdx.x / C4, c4 = threadIdx.x % C4;
   float M = kNegInf, L = 0.f;

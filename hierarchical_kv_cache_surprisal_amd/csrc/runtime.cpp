@@ -80,14 +80,15 @@ struct LayerCache {
   int64_t head = 0;                // next free position (region-relative)
   uint64_t batch = 0;              // prefetches so far
   std::deque<CacheEntry> fifo;     // resident entries, oldest first
-  std::vector<int32_t> slot_h;     // [B*Hkv*m_max] (base + off) / 8, or -1
+  std::vector<int32_t> slot_h;     // [B*Hkv*m_max, rounded up to 4] (base + off) / 8, or -1
   int32_t* slot_d = nullptr;       // device copy read by the decode kernel
-  int32_t* slot_pin = nullptr;     // pinned staging of its uploads
-  uint8_t* zm_pin = nullptr;       // [B*Hq*m_max] zoom mask of the last decode, copied back
-  int4* runs_pin = nullptr;        // copy runs of the last prefetch (source, destination, length; / 8)
-  int4* runs_d = nullptr;
+  int32_t* slot_pin = nullptr;     // coherent pinned staging of its updates (read by the copy kernel)
+  int32_t* slot_hd = nullptr;      // its device-side address
+  uint8_t* zm_pin = nullptr;       // [B*Hq*m_max] zoom mask of the last decode, written back by the combine kernel
+  uint8_t* zm_hd = nullptr;        // its device-side address
+  int4* runs_pin = nullptr;        // coherent: copy runs of the last prefetch (source, destination, length; / 8)
+  int4* runs_hd = nullptr;         // its device-side address
   size_t runs_cap = 0;
-  hipEvent_t ev_zm = nullptr;      // after that copy
   hipEvent_t ev_pref = nullptr;    // after the last prefetch (copies + table upload)
   hipEvent_t ev_done = nullptr;    // after the last decode of the layer
   bool zm_valid = false, pref_pending = false, done_valid = false;
@@ -262,15 +263,18 @@ sekv_status dalloc(sekv_ctx* c, P** p, size_t bytes) {
   return SEKV_OK;
 }
 
+// Pinned host memory.  hipHostMallocCoherent where a kernel reads what the host
+// rewrites between launches, or writes what the host reads: such accesses then
+// bypass the GPU caches.
 template <typename P>
-sekv_status halloc(sekv_ctx* c, P** p, size_t bytes) {
+sekv_status halloc(sekv_ctx* c, P** p, size_t bytes, unsigned flags = hipHostMallocDefault) {
   *p = nullptr;
   if (bytes == 0) bytes = 16;
   const char* f = std::getenv("SEKV_FAULT");
   if (f && std::strcmp(f, "pinned_oom") == 0)
     return fail(c, SEKV_ERR_OOM, "pinned host allocation refused (SEKV_FAULT=pinned_oom)");
   void* q = nullptr;
-  hipError_t e = hipHostMalloc(&q, bytes, hipHostMallocDefault);
+  hipError_t e = hipHostMalloc(&q, bytes, flags);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(c, SEKV_ERR_OOM, "hipHostMalloc(" + std::to_string(bytes) + "): " + hipGetErrorString(e));
@@ -292,11 +296,9 @@ void hfree(P*& p) {
 
 void free_layer_cache(LayerCache& C) {
   dfree(C.slot_d);
-  dfree(C.runs_d);
   hfree(C.runs_pin);
   hfree(C.slot_pin);
   hfree(C.zm_pin);
-  if (C.ev_zm) (void)hipEventDestroy(C.ev_zm);
   if (C.ev_pref) (void)hipEventDestroy(C.ev_pref);
   if (C.ev_done) (void)hipEventDestroy(C.ev_done);
   C = LayerCache();
@@ -770,12 +772,14 @@ sekv_status ensure_layer_cache(sekv_ctx* c, int layer) {
   C.size = (c->cache_elems / L_) & ~int64_t(7);
   C.base = C.size * layer;
   C.head = 0;
-  C.slot_h.assign(rows, -1);
-  TRY(dalloc(c, &C.slot_d, rows * 4));
-  TRY(halloc(c, &C.slot_pin, rows * 4));
-  TRY(halloc(c, &C.zm_pin, (size_t)B * Hq * c->m_max + 8));  // + 8: the scan reads whole words
-  HIPCHK(c, hipMemset(C.slot_d, 0xff, rows * 4));
-  HIPCHK(c, hipEventCreateWithFlags(&C.ev_zm, hipEventDisableTiming));
+  const size_t rows4 = (rows + 3) & ~size_t(3);  // the slot table moves in 16-byte pieces
+  C.slot_h.assign(rows4, -1);
+  TRY(dalloc(c, &C.slot_d, rows4 * 4));
+  TRY(halloc(c, &C.slot_pin, rows4 * 4, hipHostMallocCoherent));
+  TRY(halloc(c, &C.zm_pin, (size_t)B * Hq * c->m_max + 8, hipHostMallocCoherent));  // + 8: the scan reads whole words
+  HIPCHK(c, hipHostGetDevicePointer((void**)&C.slot_hd, C.slot_pin, 0));
+  HIPCHK(c, hipHostGetDevicePointer((void**)&C.zm_hd, C.zm_pin, 0));
+  HIPCHK(c, hipMemset(C.slot_d, 0xff, rows4 * 4));
   HIPCHK(c, hipEventCreateWithFlags(&C.ev_pref, hipEventDisableTiming));
   HIPCHK(c, hipEventCreateWithFlags(&C.ev_done, hipEventDisableTiming));
   C.init = true;
@@ -824,7 +828,9 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
   LayerState& L = c->layers[layer];
   LayerCache& C = L.lc;
   if (!C.init || !L.ready || !C.zm_valid || C.size == 0) return SEKV_OK;
-  if (hipEventQuery(C.ev_zm) != hipSuccess) return SEKV_OK;  // that mask is not back yet: no prediction
+  // the layer's last decode is done: its zoom mask is back (no prediction
+  // otherwise), and entries can be evicted
+  if (hipEventQuery(C.ev_done) != hipSuccess) return SEKV_OK;
   C.zm_valid = false;
   const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads, G = c->G, mm = c->m_max;
   const int d = c->cfg.d_head;
@@ -860,9 +866,9 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
       }
     }
   if (need.empty()) return SEKV_OK;
-  if (hipEventQuery(C.ev_pref) != hipSuccess) HIPCHK(c, hipEventSynchronize(C.ev_pref));  // slot_pin is free
+  // the last prefetch's copy kernel has read runs_pin and slot_pin
+  if (hipEventQuery(C.ev_pref) != hipSuccess) HIPCHK(c, hipEventSynchronize(C.ev_pref));
   C.batch++;
-  if (C.done_valid) HIPCHK(c, hipStreamWaitEvent(c->side, C.ev_done, 0));
   const size_t es = c->esz;
   // the misses, merged into runs of consecutive store and cache positions, are
   // copied by one kernel that reads the pinned store in place
@@ -900,29 +906,29 @@ sekv_status cache_prefetch(sekv_ctx* c, int layer) {
     }
   }
   TRY(flush());
-  if (!runs.empty()) {
-    if (runs.size() > C.runs_cap) {  // the previous prefetch's copies are done (ev_pref)
-      const size_t cap = std::max<size_t>(runs.size(), 2 * C.runs_cap + 256);
-      dfree(C.runs_d);
-      hfree(C.runs_pin);
-      C.runs_cap = 0;
-      TRY(dalloc(c, &C.runs_d, cap * sizeof(int4)));
-      TRY(halloc(c, &C.runs_pin, cap * sizeof(int4)));
-      C.runs_cap = cap;
-    }
-    std::memcpy(C.runs_pin, runs.data(), runs.size() * sizeof(int4));
-    HIPCHK(c, hipMemcpyAsync(C.runs_d, C.runs_pin, runs.size() * sizeof(int4), hipMemcpyHostToDevice, c->side));
-    launch_copy_runs(C.runs_d, (int)runs.size(), L.bases_hd, c->cache_d, (int)es, c->side);
-    HIPCHK(c, hipGetLastError());
-    c->stats.memcpy_calls++;
+  if (runs.size() > C.runs_cap) {  // the last prefetch's copy kernel is done (ev_pref)
+    const size_t cap = std::max<size_t>(runs.size(), 2 * C.runs_cap + 256);
+    hfree(C.runs_pin);
+    C.runs_cap = 0;
+    TRY(halloc(c, &C.runs_pin, cap * sizeof(int4), hipHostMallocCoherent));
+    HIPCHK(c, hipHostGetDevicePointer((void**)&C.runs_hd, C.runs_pin, 0));
+    C.runs_cap = cap;
   }
-  if (C.dirty_lo < C.dirty_hi) {  // upload the changed range of the slot table
-    const size_t lo = (size_t)C.dirty_lo, n = (size_t)(C.dirty_hi - C.dirty_lo);
+  if (!runs.empty()) std::memcpy(C.runs_pin, runs.data(), runs.size() * sizeof(int4));
+  // the changed range of the slot table, in whole 16-byte pieces
+  size_t lo = 0, n = 0;
+  if (C.dirty_lo < C.dirty_hi) {
+    lo = (size_t)C.dirty_lo & ~size_t(3);
+    n = (((size_t)C.dirty_hi + 3) & ~size_t(3)) - lo;
     std::memcpy(C.slot_pin + lo, C.slot_h.data() + lo, n * 4);
-    HIPCHK(c, hipMemcpyAsync(C.slot_d + lo, C.slot_pin + lo, n * 4, hipMemcpyHostToDevice, c->side));
     C.dirty_lo = INT64_MAX;
     C.dirty_hi = 0;
   }
+  // one launch: the runs from the mapped store into the region, then the table
+  launch_copy_runs(C.runs_hd, (int)runs.size(), L.bases_hd, c->cache_d, (int)es, C.slot_hd + lo, C.slot_d + lo,
+                   (int64_t)n * 4, c->side);
+  HIPCHK(c, hipGetLastError());
+  c->stats.memcpy_calls++;
   HIPCHK(c, hipEventRecord(C.ev_pref, c->side));
   C.pref_pending = true;
   return SEKV_OK;
@@ -1351,10 +1357,14 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
     if (capturing) return fail(c, SEKV_ERR_STATE, "decode with a basis cache is not capturable");
     TRY(ensure_layer_cache(c, layer));
     TRY(cache_prefetch(c, layer));  // if the previous mask is back and no earlier call used it
-    if (L.lc.pref_pending) HIPCHK(c, hipStreamWaitEvent(stream, L.lc.ev_pref, 0));
+    if (L.lc.pref_pending && hipEventQuery(L.lc.ev_pref) != hipSuccess)
+      HIPCHK(c, hipStreamWaitEvent(stream, L.lc.ev_pref, 0));
     L.lc.pref_pending = false;
     a.cslot = L.lc.slot_d;
     a.cache = c->cache_d;
+    // the combine kernel writes this step's zoom mask back for the prediction of the next one
+    a.mask_h = L.lc.zm_hd;
+    a.mask_bytes = (int64_t)a.B * a.Hq * a.m_max;
   }
   if (!staged(c)) {
     // span tasks with their zoomed spans in place (bases in HBM, or read from
@@ -1392,12 +1402,10 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
   launch_decode_combine(d, a, stream);
   HIPCHK(c, hipGetLastError());
   if (cached) {
-    // this step's zoom mask comes back for the prediction of the next one
+    // the decode is done, and this step's zoom mask is back (the combine kernel wrote it)
     LayerCache& C = L.lc;
     HIPCHK(c, hipEventRecord(C.ev_done, stream));
     C.done_valid = true;
-    HIPCHK(c, hipMemcpyAsync(C.zm_pin, a.mask, (size_t)a.B * a.Hq * a.m_max, hipMemcpyDeviceToHost, stream));
-    HIPCHK(c, hipEventRecord(C.ev_zm, stream));
     C.zm_valid = true;
     // the next layer's prefetch runs on the side stream while this one decodes
     const int nxt = (layer + 1) % c->cfg.n_layers;

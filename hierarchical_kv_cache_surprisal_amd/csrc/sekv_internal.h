@@ -38,6 +38,8 @@ struct DecodeArgs {
   const float* q;         // [B][Hq][d]
   float* out;             // [B][Hq][d]
   uint8_t* mask;          // [B][Hq][m_max] zoom decisions (always written)
+  uint8_t* mask_h;        // or NULL: the combine kernel copies mask (mask_bytes) here (mapped host memory)
+  int64_t mask_bytes;
   float* scores;          // [B][Hq][m_max] (routing-scores mode; input of the budget cap)
   int capped;             // 1: the decisions were taken by the budget cap and are read from mask
   // tasks: span (bg, first span, spans, partial slot; with host-resident bases
@@ -148,9 +150,12 @@ void launch_gather_rows(int B, const GatherArgs& a, hipStream_t s);
 
 // Copies of element runs, one workgroup per run: list[i] = (source offset / 8,
 // destination offset / 8, elements / 8, unused), offsets in elements of esz
-// bytes (elements / 8 * esz a multiple of 16).  src may be mapped pinned host
-// memory (the device basis cache fills this way in one launch).
-void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, hipStream_t s);
+// bytes (elements / 8 * esz a multiple of 16); then table_bytes (a multiple of
+// 16, both pointers 16-byte aligned) from tsrc to tdst.  The list, src and tsrc
+// may be mapped pinned host memory: the device basis cache fills its region and
+// updates its slot table this way in one launch.
+void launch_copy_runs(const int4* list, int n, const void* src, void* dst, int esz, const void* tsrc, void* tdst,
+                      int64_t table_bytes, hipStream_t s);
 
 // Soft rank gates on the stored A factors of the spans of one (sequence, kv head).
 struct GateArgs {
