@@ -57,8 +57,10 @@ def _check_margins(s, H, segs):
         assert np.min(np.abs(H[b].astype(np.float64) - th)) > 1e-12 * max(1.0, abs(th))
 
 
-def _decode_compare(s, ctx, arts, layer, steps, taus, heads=None, tol=1e-4):
-    """Decode `steps` queries on the GPU and compare every (b, h) with the oracle."""
+def _decode_compare(s, ctx, arts, layer, steps, taus, heads=None, tol=1e-4, mask_offset=0):
+    """Decode `steps` queries on the GPU and compare every (b, h) with the oracle.
+    mask_offset > 0 passes the zoom mask as a view that many bytes into a larger
+    buffer (an unaligned address); the bytes before it must stay untouched."""
     m_max = ctx.m_max()
     worst = 0.0
     nz = 0
@@ -66,9 +68,13 @@ def _decode_compare(s, ctx, arts, layer, steps, taus, heads=None, tol=1e-4):
         q = synth.queries(s, layer, t)
         qd = q.to(DEV)
         out = torch.zeros(s.B, s.Hq, s.d, device=DEV)
-        mask = torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV)
+        n_mask = s.B * s.Hq * m_max
+        buf = torch.full((n_mask + mask_offset,), 7, dtype=torch.uint8, device=DEV)
+        mask = buf[mask_offset:].view(s.B, s.Hq, m_max)
         ctx.decode_attn(layer, qd, taus, out, mask)
         torch.cuda.synchronize()
+        if mask_offset:
+            assert torch.all(buf[:mask_offset] == 7).item(), "bytes before the mask view were written"
         out_h = out.cpu().numpy().astype(np.float64)
         mask_h = mask.cpu().numpy()
         qn = q.numpy().astype(np.float64)
@@ -613,11 +619,13 @@ def test_append_tokens_then_decode(home, which):
 
 # ============================================================================ device basis cache
 
-@pytest.mark.parametrize("cache_kb,L", [(4096, 2), (48, 1)])
-def test_basis_cache_prefetch_decode(cache_kb, L):
+@pytest.mark.parametrize("cache_kb,L,mask_offset", [(4096, 2, 0), (48, 1, 0), (4096, 1, 3)])
+def test_basis_cache_prefetch_decode(cache_kb, L, mask_offset):
     """Host-resident bases with a device cache: outputs match the oracle at every
     step whatever is cached; spans zoomed again are found in the cache; a cache
-    too small for the working set keeps evicting and stays correct."""
+    too small for the working set keeps evicting and stays correct.  With an
+    unaligned zoom mask the combine kernel's copy of it back to the host (which
+    drives the prediction) takes its byte path, and the hit rate must hold."""
     s = _small_bf16().replace(Hq=4, Hkv=4, steps=4)
     H, K, V = _inputs(s)
     segs, arts = _oracle_layer(s, H, K, V)
@@ -629,7 +637,7 @@ def test_basis_cache_prefetch_decode(cache_kb, L):
     ctx.set_basis_cache(cache_kb * 1024)
     for rep in range(3):
         for layer in range(L):
-            _decode_compare(s, ctx, arts, layer, s.steps, taus)
+            _decode_compare(s, ctx, arts, layer, s.steps, taus, mask_offset=mask_offset)
     st = ctx.stats()
     assert st["cache_zoomed"] > 0 and st["cache_spans_fetched"] > 0
     if cache_kb >= 4096:
