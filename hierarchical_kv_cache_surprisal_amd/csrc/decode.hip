@@ -639,9 +639,8 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, Smem<D, G>& sh) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  const int na = a.na_b[b];
   const int r0 = task.y;
-  const int r1 = min(na, r0 + task.z);
+  const int r1 = r0 + task.z;  // the planner clamps the chunk to the anchor count
   const T* Kb = reinterpret_cast<const T*>(a.KA) + (size_t)bg * a.na_max * D + sub * EPL;
   const T* Vb = reinterpret_cast<const T*>(a.VA) + (size_t)bg * a.na_max * D + sub * EPL;
   auto load = [&](Stage<T, U>& sg, int bs) {
@@ -755,9 +754,8 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  const int m = a.m_b[b];
   const int k0 = task.y;
-  const int k1 = min(m, k0 + task.z);
+  const int k1 = k0 + task.z;  // the planner clamps the chunk to the span count
   const T* Kb = reinterpret_cast<const T*>(a.kbar) + (size_t)bg * a.m_max * D + sub * EPL;
   const T* Vb = reinterpret_cast<const T*>(a.vbar) + (size_t)bg * a.m_max * D + sub * EPL;
   const float* lS = a.logS + (size_t)b * a.m_max;

@@ -653,7 +653,12 @@ void plan_tasks(sekv_ctx* c, LayerState& L) {
   for (auto& o : order) {  // span chunks, the most zoom-heavy rows first
     const int bg = o.second;
     S.first_span_task[bg] = (int)S.tasks.size();
-    for (int j = 0; j < nspan[bg]; ++j) S.tasks.push_back(make_int4(bg, j * S.chunk[bg], S.chunk[bg], per_span * j));
+    // task lengths are clamped to the row's span count: the kernels read no count
+    const int m = c->m_b[bg / Hkv];
+    for (int j = 0; j < nspan[bg]; ++j) {
+      const int k0 = j * S.chunk[bg];
+      S.tasks.push_back(make_int4(bg, k0, std::min(S.chunk[bg], m - k0), per_span * j));
+    }
   }
   S.n_span_tasks = (int)S.tasks.size();
   int amax = 0;
@@ -661,7 +666,9 @@ void plan_tasks(sekv_ctx* c, LayerState& L) {
   for (int j = 0; j < amax; ++j)  // anchor chunks, interleaved over the rows
     for (int bg = 0; bg < BH; ++bg)
       if (j < nanch[bg])
-        S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg], anch[bg], per_span * nspan[bg] + j));
+        S.tasks.push_back(make_int4(bg | (int)0x80000000u, j * anch[bg],
+                                    std::min(anch[bg], L.na_l[bg / Hkv] - j * anch[bg]),
+                                    per_span * nspan[bg] + j));
 }
 
 // Refresh a layer's schedule before a launch on `stream`.  `pending` means a
