@@ -125,6 +125,9 @@ __device__ __forceinline__ float lane_xor(float x, int off) {
   return __shfl_xor(x, off, 64);
 }
 
+// One-head groups: a wave takes two units of rank <= RBATCH / 2 in one round.
+constexpr bool kPairUnits = true;
+
 // Item flag: the span's bases are read from the device cache (bits 0..7 are head bits).
 constexpr uint32_t kCachedBit = 0x100u;
 
@@ -160,43 +163,60 @@ __device__ __forceinline__ void fold_record(MergeLds<D, G>& ml, int wave, int h,
 
 // ------------------------------------------------------------------ zoomed span tile, one wave
 
-// One unit of a one-head group with r <= NU*RPW: lane rank rows j = rg + RPW*u
-// for u < NU, every load of the unit in one round, the products in registers
-// (the layout of zoom_unit below).
-template <int D, typename T, int NU, class QGet, class Sink>
-__device__ __forceinline__ void zoom_unit_one(const T* __restrict__ AKt, const T* __restrict__ BKt,
-                                              const T* __restrict__ AVt, const T* __restrict__ BVt, int c, int c8,
-                                              int r, int tok, int tokc, QGet qget, Sink sink, float c2, int rg,
-                                              int tg) {
-  using Gm = Geo<D, T>;
-  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
-  const int rl = r - 1;
-  const int nu = (r + RPW - 1) / RPW;  // rank rows per lane that r needs
+// The rank rows of one unit that a lane holds: rows j = rg + RPW*u, u < NU, of
+// B_K^T and B_V^T (the 16-byte piece at column tg*EPL) and of A_K^T and A_V^T
+// (the piece of EPL tokens at tokc).  Rows past the rank hold zeros.
+template <typename T, int NU>
+struct UnitRows {
   Raw<T> bk[NU], ak[NU], av[NU], bv[NU];
-  // rows [lo, hi) load when nu > lo, else hold zeros: a few wave-uniform branches
+};
+
+// Load a unit's rows: the rows that r needs (rows 0..1, 2..3 and 4..7 sit
+// behind wave-uniform branches; r is the same for the whole wave).
+template <int D, typename T, int NU>
+__device__ __forceinline__ void unit_rows_load(UnitRows<T, NU>& x, const T* __restrict__ base, int c8, int r,
+                                               int tokc, int rg, int tg) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, RPW = Gm::RPW;
+  const T* AKt = base;
+  const T* BKt = AKt + (size_t)r * c8;
+  const T* AVt = BKt + (size_t)r * D;
+  const T* BVt = AVt + (size_t)r * c8;
+  const int rl = r - 1;
+  const int nu = (r + RPW - 1) / RPW;
   auto rows = [&](int lo, int hi) {
     if (nu > lo) {
 #pragma unroll
       for (int u = lo; u < hi; ++u) {
         const int j = min(rg + RPW * u, rl);
-        bk[u].load(BKt + (size_t)j * D + tg * EPL);
-        ak[u].load(AKt + (size_t)j * c8 + tokc);
-        av[u].load(AVt + (size_t)j * c8 + tokc);
-        bv[u].load(BVt + (size_t)j * D + tg * EPL);
+        x.bk[u].load(BKt + (size_t)j * D + tg * EPL);
+        x.ak[u].load(AKt + (size_t)j * c8 + tokc);
+        x.av[u].load(AVt + (size_t)j * c8 + tokc);
+        x.bv[u].load(BVt + (size_t)j * D + tg * EPL);
       }
     } else {
 #pragma unroll
       for (int u = lo; u < hi; ++u) {
-        bk[u].zero();
-        ak[u].zero();
-        av[u].zero();
-        bv[u].zero();
+        x.bk[u].zero();
+        x.ak[u].zero();
+        x.av[u].zero();
+        x.bv[u].zero();
       }
     }
   };
   rows(0, NU >= 2 ? 2 : 1);
   if constexpr (NU >= 4) rows(2, 4);
   if constexpr (NU >= 8) rows(4, 8);
+}
+
+// One head's piece of a loaded unit (c tokens, the tile's tokens from tok):
+// p = B_K^T q, logits A_K p, softmax, w = A_V^T e, o = B_V w; goes to
+// sink(0, max, sum, slice).
+template <int D, typename T, int NU, class QGet, class Sink>
+__device__ __forceinline__ void unit_rows_attend(const UnitRows<T, NU>& x, int c, int r, int tok, QGet qget,
+                                                 Sink sink, float c2, int rg) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
   float q[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) q[e] = qget(0, e);
@@ -205,7 +225,7 @@ __device__ __forceinline__ void zoom_unit_one(const T* __restrict__ AKt, const T
   for (int u = 0; u < NU; ++u) {
     float dp = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dp += q[e] * bk[u].get(e);
+    for (int e = 0; e < EPL; ++e) dp += q[e] * x.bk[u].get(e);
     dp = group_sum<LPR>(dp);
     p[u] = (rg + RPW * u < r) ? dp * c2 : 0.f;
   }
@@ -213,15 +233,15 @@ __device__ __forceinline__ void zoom_unit_one(const T* __restrict__ AKt, const T
   float mx = kNegInf;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    float x = 0.f;
+    float y = 0.f;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) x += p[u] * ak[u].get(e);
-    x = slots_sum<LPR>(x);
-    x = (tok + e < c) ? x : kNegInf;
-    lg[e] = x;
-    mx = fmaxf(mx, x);
+    for (int u = 0; u < NU; ++u) y += p[u] * x.ak[u].get(e);
+    y = slots_sum<LPR>(y);
+    y = (tok + e < c) ? y : kNegInf;
+    lg[e] = y;
+    mx = fmaxf(mx, y);
   }
-  mx = group_max<LPR>(mx);  // finite: token t0 is valid
+  mx = group_max<LPR>(mx);  // finite: the tile's first token is valid
   float sl = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
@@ -232,19 +252,19 @@ __device__ __forceinline__ void zoom_unit_one(const T* __restrict__ AKt, const T
   float w[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    float x = 0.f;
+    float y = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) x += lg[e] * av[u].get(e);
-    x = group_sum<LPR>(x);
-    w[u] = (rg + RPW * u < r) ? x : 0.f;
+    for (int e = 0; e < EPL; ++e) y += lg[e] * x.av[u].get(e);
+    y = group_sum<LPR>(y);
+    w[u] = (rg + RPW * u < r) ? y : 0.f;
   }
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    float x = 0.f;
+    float y = 0.f;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) x += w[u] * bv[u].get(e);
-    o[e] = slots_sum<LPR>(x);
+    for (int u = 0; u < NU; ++u) y += w[u] * x.bv[u].get(e);
+    o[e] = slots_sum<LPR>(y);
   }
   sink(0, mx, sl, o);
 }
@@ -286,7 +306,9 @@ __device__ __forceinline__ void zoom_unit(const T* __restrict__ base, int c, int
   if (G == 1 && r <= RBATCH) {
     // one head, one rank batch: as many rank rows per lane as r needs (r is
     // the same for the whole wave), so that no load repeats another
-    zoom_unit_one<D, T, RB>(AKt, BKt, AVt, BVt, c, c8, r, tok, tokc, qget, sink, c2, rg, tg);
+    UnitRows<T, RB> x;
+    unit_rows_load<D, T, RB>(x, base, c8, r, tokc, rg, tg);
+    unit_rows_attend<D, T, RB>(x, c, r, tok, qget, sink, c2, rg);
     return;
   }
 
@@ -555,21 +577,51 @@ __device__ void zoom_group(const DecodeArgs& a, int bg, int part, int zc, Item i
     __syncthreads();
   }
   const int units = sh.ustart[zc];
+  // unit u of item j: the item is the same for the whole wave, in scalar
+  // registers (loads then take a scalar base and a 32-bit lane offset)
+  struct UnitRef {
+    const T* base;
+    uint32_t hb;
+    int r, cnt, t0;
+  };
+  auto unit_ref = [&](int u, int j) -> UnitRef {
+    const int3 it = sh.zit[j];
+    const uint32_t hb = (uint32_t)__builtin_amdgcn_readfirstlane(it.x);  // head bits; kCachedBit: device cache
+    const uint32_t iz = (uint32_t)__builtin_amdgcn_readfirstlane(it.z);
+    const uint32_t off8 = (uint32_t)__builtin_amdgcn_readfirstlane(it.y);
+    const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
+    return {from + ((int64_t)off8 << 3), hb & 0xffu, (int)(iz & 0xffu), (int)(iz >> 8),
+            __builtin_amdgcn_readfirstlane((u - sh.ustart[j]) * TILE)};
+  };
   auto for_units = [&](auto qget, auto sink) {
     int j = 0;
 #pragma unroll 1
     for (int u = wave; u < units; u += kWaves) {
       while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
-      // the item is the same for the whole wave: scalar registers (loads then
-      // take a scalar base and a 32-bit lane offset)
-      const int3 it = sh.zit[j];
-      const uint32_t hb = (uint32_t)__builtin_amdgcn_readfirstlane(it.x);  // head bits; kCachedBit: device cache
-      const uint32_t iz = (uint32_t)__builtin_amdgcn_readfirstlane(it.z);
-      const int r = (int)(iz & 0xffu), cnt = (int)(iz >> 8);
-      const int t0 = __builtin_amdgcn_readfirstlane((u - sh.ustart[j]) * TILE);
-      const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
-      const uint32_t off8 = (uint32_t)__builtin_amdgcn_readfirstlane(it.y);
-      zoom_unit<D, T, G>(from + ((int64_t)off8 << 3), cnt, r, t0, hb & 0xffu, qget, sink, c2, rg, tg);
+      const UnitRef x = unit_ref(u, j);
+      if constexpr (G == 1 && kPairUnits) {
+        // two units of rank <= RBATCH / 2 (this one and the wave's next) fit the
+        // registers of one full-rank unit: load both in one round
+        constexpr int NP = Gm::RB / 2;
+        const int u2 = u + kWaves;
+        if (x.r <= NP * Gm::RPW && u2 < units) {
+          int j2 = j;
+          while (sh.ustart[j2 + 1] <= u2) ++j2;
+          const UnitRef y = unit_ref(u2, j2);
+          if (y.r <= NP * Gm::RPW) {
+            UnitRows<T, NP> X, Y;
+            const int tx = x.t0 + tg * EPL, ty = y.t0 + tg * EPL;
+            unit_rows_load<D, T, NP>(X, x.base, (x.cnt + 7) & ~7, x.r, tx < ((x.cnt + 7) & ~7) ? tx : x.t0, rg, tg);
+            unit_rows_load<D, T, NP>(Y, y.base, (y.cnt + 7) & ~7, y.r, ty < ((y.cnt + 7) & ~7) ? ty : y.t0, rg, tg);
+            unit_rows_attend<D, T, NP>(X, x.cnt, x.r, tx, qget, sink, c2, rg);
+            unit_rows_attend<D, T, NP>(Y, y.cnt, y.r, ty, qget, sink, c2, rg);
+            u = u2;
+            j = j2;
+            continue;
+          }
+        }
+      }
+      zoom_unit<D, T, G>(x.base, x.cnt, x.r, x.t0, x.hb, qget, sink, c2, rg, tg);
     }
   };
   if constexpr (G == 1) {
