@@ -167,6 +167,25 @@ def test_tiny_fp32_all_zoom(home):
     assert T.rel_err(out[0, 0].cpu().double().numpy(), o_ref) < 1e-3
 
 
+@pytest.mark.parametrize("kv_dtype,d,ranks", [("f32", 128, (2, 4, 8, 16)), ("bf16", 64, (4, 8, 16, 32))])
+def test_one_head_small_ranks_unit_pairs(kv_dtype, d, ranks):
+    """One-head groups whose ranks fit half a register batch take their zoom units
+    two per round (fp32 with d = 128 pairs ranks <= 8, bf16 with d = 64 ranks
+    <= 16); mixed ranks interleave pairs and single units.  Every span zoomed,
+    outputs against the oracle on its own artefacts."""
+    s = synth.spec("tiny").replace(d=d, kv_dtype=kv_dtype, n=3000, Hq=2, Hkv=2, w=64, steps=3,
+                                   rank_choices=ranks)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    ctx = _ctx(s, "device")
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    taus = np.zeros(s.Hq, np.float32)   # tau = 0: every span zoomed
+    worst, nz = _decode_compare(s, ctx, arts, 0, s.steps, taus, tol=1e-4 if kv_dtype == "f32" else 2e-2)
+    assert nz == s.steps * s.Hq * segs[0].m
+    ranks_seen = {int(arts[(0, g)].rank[k]) for g in range(s.Hkv) for k in range(segs[0].m)}
+    assert len(ranks_seen) >= 3, ranks_seen
+
+
 def test_dense_equivalence_full_rank_fp32_d128():
     """P1 on the GPU: tau = 0 and ranks >= min(|S|, d) make the mixed softmax
     dense attention over all n tokens (GPU-built SVD, fp32 storage)."""
