@@ -14,23 +14,26 @@
 //                    p = B_K^T q, logit_t = A_K[t].p / sqrt(d),
 //                    w = sum_t e_t A_V[t], contribution w . B_V^T.
 //
-// A layer-step is split over the context into tasks, each writing one partial
-// (running max in log2 units, sum, d-vector accumulator) per query head into
-// a slot of its own:
-//   k_route    one workgroup per task.  Span task: routing scores of a chunk
-//              of spans, the zoom decisions (zoom mask) and the summary
-//              entries of the spans a head does not zoom; then its zoomed
-//              spans, cut into units of one token tile each (independent
-//              entries of the softmax), spread over the waves and folded into
-//              the same partial (device-resident bases), or listed for the
-//              host fetch (host-resident bases).  Anchor task (device-resident
-//              bases): the exact tokens of a chunk of anchors.  The runtime
-//              sizes the span chunks of each (sequence, kv head) from the zoom
-//              counts of earlier steps, so that a chunk holds about one zoomed
-//              span per wave.
-//   k_attend   (host-resident bases) one workgroup per fetched span task, its
-//              zoomed spans from the staged bases into the task's second slot,
-//              then one workgroup per anchor task.
+// A layer-step is split over the context into segments (runs of span rows or
+// of anchor rows of one (sequence, kv head)), each writing one partial
+// (running max in log2 units, sum, d-vector accumulator) per query head into a
+// slot of its own:
+//   k_planned  (device-resident bases, and host-resident bases read in place)
+//              one wave of workgroups, each running a short list of segments
+//              planned on the host from the expected cost of every row (the
+//              zoom frequency of each span over recent calls).  Its span
+//              segments first: routing scores, zoom decisions and the summary
+//              entries of the spans a head does not zoom; then the zoomed spans
+//              of those rows, cut into units of one token tile each
+//              (independent entries of the softmax) spread over the waves; then
+//              its anchor segments (exact tokens).  Rows stream in
+//              double-buffered rounds.
+//   k_route    (pinned bases copied to staging; and the routing-scores pass)
+//              one workgroup per span task: routing scores, decisions, summary
+//              entries, and the zoomed spans listed for the host fetch.
+//   k_attend   (staged bases) one workgroup per fetched span task, its zoomed
+//              spans from the staged bases into the task's second slot, then
+//              one workgroup per anchor task.
 //   k_combine  log-sum-exp merge of every (sequence, query head)'s slots, in
 //              slot order.
 // No workgroup waits for another and no atomic shares an address across the
@@ -781,7 +784,6 @@ __device__ void anchor_task(const DecodeArgs& a, int4 task, Smem<D, G>& sh) {
 
 // ------------------------------------------------------------------ span task
 
-// MODE 0: zoomed spans listed in the chunk's rows of the dense table.
 // MODE 1: zoomed spans appended to the flat list for the host fetch.
 // MODE 2: routing scores only.
 template <int D, typename T, int G, int MODE, bool ROUTED>
@@ -819,7 +821,7 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
       sg.k[u].load(Kb + (size_t)kk * D);
       if (!SCORES) sg.v[u].load(Vb + (size_t)kk * D);
       sg.ls[u] = lS[kk];
-      if (!SCORES) sg.meta[u] = sub == 0 ? a.smeta[(size_t)bg * a.m_max + kk] : make_int2(0, 0);
+      if (!SCORES) sg.meta[u] = a.smeta[(size_t)bg * a.m_max + kk];  // every lane: no load under a lane condition
       if (ROUTED) {
         const int sp = sub * EPL < a.dr ? sub : 0;  // lanes beyond d' load piece 0 (unused)
         sg.kr[u].load(reinterpret_cast<const T*>(a.Kr) + ((size_t)bg * a.m_max + kk) * a.dr + sp * EPL);
@@ -972,38 +974,13 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
   const u64 bal = __ballot(hb != 0);
   int pos = __popcll(bal & ((1ull << lane) - 1ull));
   if (lane == 0) sh.wcount[wave] = __popcll(bal);
-  if (MODE != 0) store_partial<D, G>(sh.ml, a, b, g, task.w);
+  store_partial<D, G>(sh.ml, a, b, g, task.w);
   __syncthreads();
   int zc = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     if (w < wave) pos += sh.wcount[w];
     zc += sh.wcount[w];
-  }
-  if (MODE == 0) {
-    // zoomed spans in place: token-tile units over the waves, folded into the
-    // wave records, then the task's one partial
-    if (threadIdx.x == 0) a.zcnt[t] = zc;  // scheduling statistics (read back by the host)
-    if (zc) {
-      if (hb) {
-        int off8 = sh.zmeta[i].x;
-        uint32_t bits = hb;
-        if (a.cslot) {  // host-resident bases with a device cache: use the cached copy if any
-          const int cs = a.cslot[(size_t)bg * a.m_max + k0 + i];
-          if (cs >= 0) {
-            off8 = cs;
-            bits |= kCachedBit;
-          }
-        }
-        sh.zit[pos] = make_int3((int)bits, off8, sh.zmeta[i].y);
-      }
-      __syncthreads();
-      auto item = [&](int j) -> int3 { return sh.zit[j]; };
-      zoom_group<D, T, G, true>(a, bg, task.w, zc, item, reinterpret_cast<const T*>(a.bases), sh);
-      __syncthreads();
-    }
-    store_partial<D, G>(sh.ml, a, b, g, task.w);
-    return;
   }
   if (zc == 0) store_empty<D, G>(a, b, g, task.w + 1);  // the zoom slot, when nothing fills it
   if (threadIdx.x == 0) a.zcnt[t] = zc;
@@ -1018,16 +995,614 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
   }
 }
 
+// ------------------------------------------------------------------ planned layer-step kernel
+
+// The planned kernel runs one wave of workgroups over the whole layer-step.
+// The runtime cuts the sequence "span rows of (b, g), anchor rows of (b, g),
+// next (b, g) ..." into one contiguous share per workgroup, of equal predicted
+// cost: bytes streamed plus the bases of the spans predicted to be zoomed (the
+// zoom sets of the previous calls).  A share is a short list of segments, each
+// folded into one partial slot of its (sequence, kv head).  A workgroup streams
+// its span segments first (routing scores, zoom decisions, summary entries),
+// then rebuilds its zoomed spans (token-tile units spread over the waves),
+// then streams its anchor segments, and stores one partial per segment.  The
+// rows of a segment are interleaved over the waves by pipeline stage; each
+// wave keeps its own running record per segment in LDS, merged at the end.
+template <int D, int G, int NS>
+struct PlanSmem {
+  int4 seg[NS];                    // the workgroup's segment descriptors
+  MergeLds<D, G> rec[NS];          // wave records of each segment
+  float q[NS][G][D];               // queries of each segment's group
+  uint8_t zb[kMaxWgSpanRows];      // zoom head bits of each span row of the share, in segment order
+  int2 zmeta[kMaxWgSpanRows];      // basis metadata of the rows with zoom bits
+  int4 zit[kMaxWgSpanRows];        // zoomed spans: (head bits | kCachedBit, basis offset / 8, rank | count << 8, segment | bg << 8)
+  int ustart[kMaxWgSpanRows + 1];  // their first work unit
+  int red[kWaves][2];
+};
+
+// Span rows [k0, k0 + rows) of one (b, g): routing scores and zoom decisions
+// (mask, and the head bits and basis metadata of row k at zb[rb + k - k0]),
+// and the summary entries of the rows each head does not zoom, folded into the
+// wave's record of segment s.
+// Rows per row slot per round of the planned kernel's streaming.  One round's
+// loads are issued together and consumed before the next round: the stage
+// registers are not carried across loop iterations (a carried stage makes the
+// compiler copy it at the loop head, which waits for every load in flight).
+#ifndef SEKV_PLAN_ROWS
+#define SEKV_PLAN_ROWS 2
+#endif
+
+template <int G, bool ROUTED = false>
+__host__ __device__ constexpr int plan_rows() {
+  return G == 1 ? SEKV_PLAN_ROWS : G == 2 ? 2 : 1;
+}
+
+// Double-buffered rounds of one wave: round j starts at row first + j * step,
+// for the rounds that start before `end`.  The next round's loads are issued
+// before the current round is consumed; scheduling barriers keep the compiler
+// from moving them below the consumption, and the loop runs over pairs of
+// rounds with no early exit and no conditional load, so that neither buffer is
+// copied at the loop head and every wait covers one round only.  The load past
+// the last round reads rows clamped into the segment (the loaders clamp rows
+// at or beyond `end`): L2 hits, never consumed.
+template <class Buf, class Load, class Consume>
+__device__ __forceinline__ void stream_rounds(int first, int end, int step, Load load, Consume consume) {
+  if (first >= end) return;
+  const int n = (end - first + step - 1) / step;
+  Buf A, B;
+  load(A, first);
+  int bs = first, i = 0;
+  for (; i + 2 <= n; i += 2) {
+    load(B, bs + step);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(A, bs);
+    load(A, bs + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(B, bs + step);
+    bs += 2 * step;
+  }
+  if (i < n) consume(A, bs);
+}
+
+// One row's entry added to a running softmax record (logit lg in log2 units,
+// -inf for no entry).
+template <typename T, int EPL>
+__device__ __forceinline__ void online_add(float& m, float& l, float (&acc)[EPL], float lg, const Raw<T>& v) {
+  const float mn = fmaxf(m, lg);
+  const float ms = (mn == kNegInf) ? 0.f : mn;
+  const float sc = fast_exp2(m - ms), p = fast_exp2(lg - ms);
+  l = l * sc + p;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sc + p * v.get(e);
+  m = mn;
+}
+
+// 16-byte piece at a byte offset from a base shared by the wave: the address is
+// a scalar base plus a 32-bit lane offset.
+template <typename T>
+__device__ __forceinline__ void load_at(Raw<T>& r, const T* base, uint32_t off) {
+  r.load(reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off));
+}
+template <typename X>
+__device__ __forceinline__ X load_off(const X* base, uint32_t off) {
+  return *reinterpret_cast<const X*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// Span rows [k0, k0 + rows) of one (b, g): routing scores and zoom decisions
+// (the head bits and basis metadata of row k at zb / zmeta[rb + k - k0]; the
+// mask is written from them after the streaming), and the summary entries of
+// the rows each head does not zoom, folded into the wave's record of segment s.
+// One round of span rows: the key and value pieces of U rows per row slot,
+// and, in lane l < RPW * U, ln|S| and the basis metadata of row l of the round
+// (one load each for the whole round).
+template <typename T, int U>
+struct SpanRound {
+  Raw<T> k[U], v[U];
+  Raw<T> kr[U];      // with a routing projection: piece of the routing summary
+  uint32_t zsel[U];  // under the budget cap: zoom bit of each head
+  float ls;
+  int2 meta;
+};
+
+template <int D, typename T, int G, bool ROUTED, bool CAPPED, int NS>
+__device__ void plan_span_rows(const DecodeArgs& a, int4 sg, int s, int rb, PlanSmem<D, G, NS>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr int U = plan_rows<G, ROUTED>();
+  constexpr int RR = RPW * U;  // rows per wave per round
+  static_assert(RR <= 64, "one lane per row of a round");
+  constexpr int STEP = kWaves * RR;
+  constexpr uint32_t ROWB = D * sizeof(T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const int bg = sg.x;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const float c2 = kLog2e * rsqrtf((float)D);
+  const float inv_sqrt_d = rsqrtf((float)D);
+  SoftState<G> st;
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = kNegInf;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  const int k0 = sg.y;
+  const int k1 = k0 + sg.z;
+  // bases of this (b, g): uniform over the wave
+  const T* Kb = reinterpret_cast<const T*>(a.kbar) + (size_t)bg * a.m_max * D;
+  const T* Vb = reinterpret_cast<const T*>(a.vbar) + (size_t)bg * a.m_max * D;
+  const float* lS = a.logS + (size_t)b * a.m_max;
+  const int2* Mb = a.smeta + (size_t)bg * a.m_max;
+  const T* Rb = ROUTED ? reinterpret_cast<const T*>(a.Kr) + (size_t)bg * a.m_max * a.dr : nullptr;
+  const uint32_t sub_off = sub * 16u;
+  auto load = [&](SpanRound<T, U>& rd, int bs) {
+    // the round's ln|S| and metadata first: the row loop needs them early
+    {
+      const int kl = bs + (lane < RR ? lane : 0);
+      const uint32_t kc = (uint32_t)(kl < k1 ? kl : k0);
+      rd.ls = load_off(lS, kc * 4u);
+      rd.meta = load_off(Mb, kc * 8u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = bs + u * RPW + slot;
+      const uint32_t kk = (uint32_t)(k < k1 ? k : k0);
+      load_at(rd.k[u], Kb, kk * ROWB + sub_off);
+      load_at(rd.v[u], Vb, kk * ROWB + sub_off);
+      if (ROUTED) {
+        const uint32_t sp = sub * EPL < a.dr ? sub_off : 0u;  // lanes beyond d' load piece 0 (unused)
+        load_at(rd.kr[u], Rb, kk * (uint32_t)a.dr * (uint32_t)sizeof(T) + sp);
+      }
+      if (CAPPED) {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          bits |= (a.mask[((size_t)b * a.Hq + g * G + h) * a.m_max + kk] != 0 ? 1u : 0u) << h;
+        rd.zsel[u] = bits;
+      }
+    }
+  };
+  constexpr bool QLDS = G >= 4 && !ROUTED;
+  float qr[QLDS ? 1 : G][EPL];
+  float qpr[ROUTED ? G : 1][EPL];  // projected query piece (routing projection), zero beyond d'
+  const float inv_sqrt_dr = ROUTED ? rsqrtf((float)a.dr) : 0.f;
+  auto consume = [&](const SpanRound<T, U>& rd, int bs) {
+    uint32_t zbu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float nrm = 0.f;
+      if (!ROUTED) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) nrm += rd.k[u].get(e) * rd.k[u].get(e);
+        nrm = group_sum<LPR>(nrm);
+      }
+      const float ls = __shfl(rd.ls, u * RPW + slot, 64);
+      const int k = bs + u * RPW + slot;
+      const bool ok = k < k1;
+      uint32_t zbits = 0u;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float qh[EPL];
+        if constexpr (QLDS) {
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(qh + e) = *reinterpret_cast<const float4*>(&sh.q[s][h][sub * EPL + e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qh[e] = qr[h][e];
+        }
+        Raw<T> kx = rd.k[u], vx = rd.v[u];  // per head, so that their unpacking is not hoisted out of the loop
+        if (G > 1) {
+          keep_packed(kx);
+          keep_packed(vx);
+        }
+        float dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dp += qh[e] * kx.get(e);
+        dp = group_sum<LPR>(dp);
+        float score;
+        if (ROUTED) {
+          float dq = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dq += qpr[ROUTED ? h : 0][e] * rd.kr[u].get(e);
+          score = group_sum<LPR>(dq) * inv_sqrt_dr + ls;
+        } else {
+          score = (nrm > 0.f ? dp * rsqrtf(nrm) * inv_sqrt_d : 0.f) + ls;
+        }
+        const bool zoom = CAPPED ? ((rd.zsel[u] >> h) & 1u) != 0u : (double)score > a.theta[g * G + h];
+        if (zoom) zbits |= 1u << h;
+        online_add<T, EPL>(st.m[h], st.l[h], acc[h], (ok && !zoom) ? dp * c2 + ls * kLog2e : kNegInf, vx);
+      }
+      zbu[u] = zbits;
+    }
+    // zoom bookkeeping after the round: head bits from the first lane of each
+    // row slot, the metadata of every row from the lane that loaded it
+    if (sub == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = bs + u * RPW + slot;
+        if (k < k1) sh.zb[rb + k - k0] = (uint8_t)zbu[u];
+      }
+    }
+    if (lane < RR && bs + lane < k1) sh.zmeta[rb + bs + lane - k0] = rd.meta;
+  };
+  const int first = k0 + wave * RR;
+  if (first < k1) {
+    if constexpr (!QLDS) load_q<D, G, T>(a, b, g, sub, qr);
+    if constexpr (ROUTED) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bool in = sub * EPL < a.dr;
+        const float* src = a.qp + ((size_t)b * a.Hq + g * G + h) * a.dr + (in ? sub * EPL : 0);
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) Elem<float>::load16(src + e, qpr[h] + e);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qpr[h][e] = in ? qpr[h][e] : 0.f;
+      }
+    }
+    stream_rounds<SpanRound<T, U>>(first, k1, STEP, load, consume);
+  }
+  slots_to_lds<D, G, EPL, LPR>(st, acc, sh.rec[s], lane, wave, slot, sub);
+}
+
+// Anchor rows [r0, r0 + rows) of one (b, g), exact entries, folded into the
+// wave's record of segment s.
+template <int D, typename T, int G, int NS>
+__device__ void plan_anchor_rows(const DecodeArgs& a, int4 sg, int s, PlanSmem<D, G, NS>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPW = Gm::RPW;
+  constexpr int U = plan_rows<G>();
+  constexpr int STEP = kWaves * RPW * U;
+  constexpr uint32_t ROWB = D * sizeof(T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const int bg = sg.x & 0x7fffffff;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const float c2 = kLog2e * rsqrtf((float)D);
+  SoftState<G> st;
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = kNegInf;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  const int r0 = sg.y;
+  const int r1 = r0 + sg.z;
+  const T* Kb = reinterpret_cast<const T*>(a.KA) + (size_t)bg * a.na_max * D;
+  const T* Vb = reinterpret_cast<const T*>(a.VA) + (size_t)bg * a.na_max * D;
+  const uint32_t sub_off = sub * 16u;
+  auto load = [&](Stage<T, U>& sgs, int bs) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = bs + u * RPW + slot;
+      const uint32_t rr = (uint32_t)(row < r1 ? row : r0);
+      load_at(sgs.k[u], Kb, rr * ROWB + sub_off);
+      load_at(sgs.v[u], Vb, rr * ROWB + sub_off);
+    }
+  };
+  constexpr bool QLDS = G >= 4;
+  float qr[QLDS ? 1 : G][EPL];
+  auto consume = [&](const Stage<T, U>& sgs, int bs) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = bs + u * RPW + slot < r1;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float qh[EPL];
+        if constexpr (QLDS) {
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(qh + e) = *reinterpret_cast<const float4*>(&sh.q[s][h][sub * EPL + e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) qh[e] = qr[h][e];
+        }
+        Raw<T> kx = sgs.k[u], vx = sgs.v[u];
+        if (G > 1) {
+          keep_packed(kx);
+          keep_packed(vx);
+        }
+        float dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dp += qh[e] * kx.get(e);
+        dp = group_sum<LPR>(dp);
+        online_add<T, EPL>(st.m[h], st.l[h], acc[h], ok ? dp * c2 : kNegInf, vx);
+      }
+    }
+  };
+  const int first = r0 + wave * RPW * U;
+  if (first < r1) {
+    if constexpr (!QLDS) load_q<D, G, T>(a, b, g, sub, qr);
+    stream_rounds<Stage<T, U>>(first, r1, STEP, load, consume);
+  }
+  slots_to_lds<D, G, EPL, LPR>(st, acc, sh.rec[s], lane, wave, slot, sub);
+}
+
+// Zoom phase of a share: the zoomed spans of its R span rows (zoom bits in
+// zb, in segment order) compacted in row order, cut into token-tile units
+// spread over the waves (wave w takes units w, w + 4, ...), each folded into
+// the wave's record of its segment.
+template <int D, typename T, int G, int NS>
+__device__ void plan_zoom(const DecodeArgs& a, int nseg, int R, PlanSmem<D, G, NS>& sh) {
+  using Gm = Geo<D, T>;
+  constexpr int EPL = Gm::EPL, TILE = Gm::TILE, LPR = Gm::LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = lane / LPR, tg = lane % LPR;
+  // thread i takes rows 2i and 2i + 1 (R <= kMaxWgSpanRows = 2 * kThreads)
+  static_assert(kMaxWgSpanRows == 2 * kThreads, "two span rows per thread in the compaction");
+  int cnt = 0, tiles = 0;
+  uint32_t hb2[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int j = 2 * (int)threadIdx.x + e;
+    hb2[e] = j < R ? sh.zb[j] : 0u;
+    if (hb2[e]) {
+      ++cnt;
+      tiles += ((int)((uint32_t)sh.zmeta[j].y >> 8) + TILE - 1) / TILE;
+    }
+  }
+  // exclusive scan of (cnt, tiles) over the workgroup
+  int ic = cnt, it = tiles;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int yc = __shfl_up(ic, sft, 64), yt = __shfl_up(it, sft, 64);
+    if (lane >= sft) {
+      ic += yc;
+      it += yt;
+    }
+  }
+  if (lane == 63) {
+    sh.red[wave][0] = ic;
+    sh.red[wave][1] = it;
+  }
+  __syncthreads();
+  int pc = ic - cnt, pt = it - tiles, zc = 0, units = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) {
+      pc += sh.red[w][0];
+      pt += sh.red[w][1];
+    }
+    zc += sh.red[w][0];
+    units += sh.red[w][1];
+  }
+  if (zc == 0) return;  // uniform over the workgroup
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (!hb2[e]) continue;
+    const int j = 2 * (int)threadIdx.x + e;
+    // the segment of span row j
+    int s = 0, rs = 0, k = 0, bg = 0;
+    {
+      int acc = 0;
+      for (int t = 0; t < nseg; ++t) {
+        const int4 sg = sh.seg[t];
+        if (sg.x < 0) continue;
+        if (j >= acc && j < acc + sg.z) {
+          s = t;
+          rs = acc;
+          k = sg.y + j - acc;
+          bg = sg.x;
+        }
+        acc += sg.z;
+      }
+    }
+    (void)rs;
+    int off8 = sh.zmeta[j].x;
+    uint32_t bits = hb2[e];
+    if (a.cslot) {  // host-resident bases with a device cache: use the cached copy if any
+      const int cs = a.cslot[(size_t)bg * a.m_max + k];
+      if (cs >= 0) {
+        off8 = cs;
+        bits |= kCachedBit;
+      }
+    }
+    sh.zit[pc] = make_int4((int)bits, off8, sh.zmeta[j].y, s | (bg << 8));
+    sh.ustart[pc] = pt;
+    pt += ((int)((uint32_t)sh.zmeta[j].y >> 8) + TILE - 1) / TILE;
+    ++pc;
+  }
+  if (threadIdx.x == 0) sh.ustart[zc] = units;
+  __syncthreads();
+
+  const float c2 = kLog2e * rsqrtf((float)D);
+  const T* src = reinterpret_cast<const T*>(a.bases);
+  struct UnitRef {
+    const T* base;
+    uint32_t hb;
+    int r, cnt, t0, s, bg;
+  };
+  auto unit_ref = [&](int u, int j) -> UnitRef {
+    const int4 itm = sh.zit[j];
+    const uint32_t hb = (uint32_t)__builtin_amdgcn_readfirstlane(itm.x);
+    const uint32_t iz = (uint32_t)__builtin_amdgcn_readfirstlane(itm.z);
+    const uint32_t off8 = (uint32_t)__builtin_amdgcn_readfirstlane(itm.y);
+    const int sw = __builtin_amdgcn_readfirstlane(itm.w);
+    const T* from = (hb & kCachedBit) ? reinterpret_cast<const T*>(a.cache) : src;
+    return {from + ((int64_t)off8 << 3), hb & 0xffu, (int)(iz & 0xffu), (int)(iz >> 8),
+            __builtin_amdgcn_readfirstlane((u - sh.ustart[j]) * TILE), sw & 0xff, sw >> 8};
+  };
+  if constexpr (G == 1) {
+    // one head: the query slice and a running softmax in registers, folded
+    // into the wave's record of a segment when the units move to the next one
+    int cur = -1;
+    float m = kNegInf, l = 0.f, acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    auto qget = [&](int, int e) { return sh.q[cur][0][tg * EPL + e]; };
+    auto sink = [&](int, float sm, float sl, const float (&o)[EPL]) { lse_merge<EPL>(m, l, acc, sm, sl, o); };
+    auto begin = [&](int s) {
+      if (cur >= 0) fold_record<D, G, EPL>(sh.rec[cur], wave, 0, lane, rg, tg, m, l, acc);
+      cur = s;
+      m = kNegInf;
+      l = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    };
+    int j = 0;
+#pragma unroll 1
+    for (int u = wave; u < units; u += kWaves) {
+      while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
+      const UnitRef x = unit_ref(u, j);
+      if (x.s != cur) begin(x.s);
+      if constexpr (kPairUnits) {
+        // two units of rank <= RBATCH / 2 (this one and the wave's next, of the
+        // same segment) fit the registers of one full-rank unit: one round of loads
+        constexpr int NP = Gm::RB / 2;
+        const int u2 = u + kWaves;
+        if (x.r <= NP * Gm::RPW && u2 < units) {
+          int j2 = j;
+          while (sh.ustart[j2 + 1] <= u2) ++j2;
+          const UnitRef y = unit_ref(u2, j2);
+          if (y.r <= NP * Gm::RPW && y.s == x.s) {
+            UnitRows<T, NP> X, Y;
+            const int cx8 = (x.cnt + 7) & ~7, cy8 = (y.cnt + 7) & ~7;
+            const int tx = x.t0 + tg * EPL, ty = y.t0 + tg * EPL;
+            unit_rows_load<D, T, NP>(X, x.base, cx8, x.r, tx < cx8 ? tx : x.t0, rg, tg);
+            unit_rows_load<D, T, NP>(Y, y.base, cy8, y.r, ty < cy8 ? ty : y.t0, rg, tg);
+            unit_rows_attend<D, T, NP>(X, x.cnt, x.r, tx, qget, sink, c2, rg);
+            unit_rows_attend<D, T, NP>(Y, y.cnt, y.r, ty, qget, sink, c2, rg);
+            u = u2;
+            j = j2;
+            continue;
+          }
+        }
+      }
+      zoom_unit<D, T, G>(x.base, x.cnt, x.r, x.t0, x.hb, qget, sink, c2, rg, tg);
+    }
+    if (cur >= 0) fold_record<D, G, EPL>(sh.rec[cur], wave, 0, lane, rg, tg, m, l, acc);
+  } else {
+    // several heads: queries from LDS, each head's pieces folded into the wave's records
+    int j = 0;
+#pragma unroll 1
+    for (int u = wave; u < units; u += kWaves) {
+      while (sh.ustart[j + 1] <= u) ++j;
+      const UnitRef x = unit_ref(u, j);
+      const int s = x.s;
+      zoom_unit<D, T, G>(x.base, x.cnt, x.r, x.t0, x.hb,
+                         [&](int h, int e) { return sh.q[s][h][tg * EPL + e]; },
+                         [&](int h, float sm, float sl, const float (&o)[EPL]) {
+                           fold_record<D, G, EPL>(sh.rec[s], wave, h, lane, rg, tg, sm, sl, o);
+                         },
+                         c2, rg, tg);
+    }
+  }
+}
+
+// The zoom mask of the span rows of a share, from the head bits in LDS: one
+// byte per (head, row), written after the streaming so that no store sits
+// between the pipelined loads.
+template <int D, int G, int NS>
+__device__ void plan_write_mask(const DecodeArgs& a, int nseg, PlanSmem<D, G, NS>& sh) {
+  int rb = 0;
+#pragma unroll 1
+  for (int s = 0; s < nseg; ++s) {
+    const int4 sg = sh.seg[s];
+    const int x = __builtin_amdgcn_readfirstlane(sg.x), k0 = __builtin_amdgcn_readfirstlane(sg.y),
+              n = __builtin_amdgcn_readfirstlane(sg.z);
+    if (x < 0) continue;
+    const int b = x / a.Hkv, g = x % a.Hkv;
+    for (int idx = threadIdx.x; idx < G * n; idx += kThreads) {
+      const int h = idx / n, k = idx % n;
+      a.mask[((size_t)b * a.Hq + g * G + h) * a.m_max + k0 + k] = (sh.zb[rb + k] >> h) & 1u;
+    }
+    rb += n;
+  }
+}
+
+template <int D, typename T, int G, bool ROUTED, bool CAPPED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1 ? 3 : 1))) void k_planned(DecodeArgs a) {
+  constexpr int NS = wg_segments(G);
+  __shared__ PlanSmem<D, G, NS> sh;
+  // the segment descriptors, read before any store (scalar loads), kept in LDS
+  int4 sgs[NS];
+  const int4* segs = a.wsegs + (size_t)blockIdx.x * NS;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) sgs[s] = segs[s];
+  int nseg = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) nseg += (nseg == s && sgs[s].z > 0) ? 1 : 0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sh.seg[s] = sgs[s];
+  }
+  // the queries of every segment's group, loaded at the start (one round trip
+  // shared with the first streaming round) and written to LDS when needed: at
+  // once for wide groups, which stream with the queries in LDS, and before the
+  // zoom phase for narrow ones
+  constexpr int QN = (NS * G * D + kThreads - 1) / kThreads;
+  float qv[QN];
+#pragma unroll
+  for (int i = 0; i < QN; ++i) {
+    const int idx = (int)threadIdx.x + i * kThreads;
+    const int sidx = idx / (G * D);
+    const float* src = a.q;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int bg = sgs[t].x & 0x7fffffff;
+      if (t == sidx) src = a.q + ((size_t)(bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G) * D;
+    }
+    qv[i] = sidx < nseg ? src[idx % (G * D)] : 0.f;
+  }
+  auto fill_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int idx = (int)threadIdx.x + i * kThreads;
+      if (idx < NS * G * D) (&sh.q[0][0][0])[idx] = qv[i];
+    }
+  };
+  if constexpr (G >= 4) fill_q();
+  __syncthreads();
+  // 1. span segments
+  int R = 0;
+#pragma unroll 1
+  for (int s = 0; s < nseg; ++s) {
+    const int4 v = sh.seg[s];
+    const int4 sg = make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                              __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+    if (sg.x < 0) continue;
+    plan_span_rows<D, T, G, ROUTED, CAPPED, NS>(a, sg, s, R, sh);
+    R += sg.z;
+  }
+  // 2. their zoomed spans
+  if (R > 0) {
+    if constexpr (G < 4) fill_q();
+    __syncthreads();  // zoom bits, wave records and queries complete
+    plan_zoom<D, T, G, NS>(a, nseg, R, sh);
+  }
+  // 3. anchor segments
+#pragma unroll 1
+  for (int s = 0; s < nseg; ++s) {
+    const int4 v = sh.seg[s];
+    const int4 sg = make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                              __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+    if (sg.x >= 0) continue;
+    plan_anchor_rows<D, T, G, NS>(a, sg, s, sh);
+  }
+  __syncthreads();
+  if (!CAPPED && R > 0) plan_write_mask<D, G, NS>(a, nseg, sh);
+#pragma unroll 1
+  for (int s = 0; s < nseg; ++s) {
+    const int4 v = sh.seg[s];
+    const int x = __builtin_amdgcn_readfirstlane(v.x), w = __builtin_amdgcn_readfirstlane(v.w);
+    const int bg = x & 0x7fffffff;
+    store_partial<D, G>(sh.rec[s], a, bg / a.Hkv, bg % a.Hkv, w);
+  }
+}
+
 // ------------------------------------------------------------------ kernels
 
+// Span tasks of the staged path (MODE 1) and of the routing-scores pass (MODE
+// 2); the grid covers the span tasks only.
 template <int D, typename T, int G, int MODE, bool ROUTED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1 && MODE == 0 ? 3 : 1))) void k_route(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_route(DecodeArgs a) {
   __shared__ Smem<D, G> sh;
   const int4 task = a.tasks[blockIdx.x];
-  if (task.x < 0) {  // anchor tasks: MODE 0 only (the attend kernel runs them otherwise)
-    if (MODE == 0) anchor_task<D, T, G>(a, task, sh);
-    return;
-  }
+  if (task.x < 0) return;
   span_task<D, T, G, MODE, ROUTED>(a, (int)blockIdx.x, task, sh);
 }
 
@@ -1074,6 +1649,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, hq = bh % a.Hq;
   const int g = hq / a.G;
+  // the slot count first, before any store, so that it is a scalar load
+  const int np = a.parts_n[(size_t)b * a.Hkv + g];
   if (a.mask_h) {
     // the zoom mask back to host memory (the device basis cache predicts the
     // next step from it), spread over the grid; 16-byte pieces when aligned
@@ -1088,7 +1665,6 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
     }
     for (int64_t i = i0 + tid; i < n; i += nth) a.mask_h[i] = a.mask[i];
   }
-  const int np = a.parts_n[(size_t)b * a.Hkv + g];
   const int pg = threadIdx.x / C4, c4 = threadIdx.x % C4;
   float M = kNegInf, L = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1318,13 +1894,19 @@ void launch_t(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s)
   if (grid <= 0) return;
   const dim3 gd(grid), bd(kThreads);
   if (which == 0 && a.dr > 0) {
-    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0, true>), gd, bd, 0, s, a);
-    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, true>), gd, bd, 0, s, a);
+    if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, true>), gd, bd, 0, s, a);
     else hipLaunchKernelGGL((k_route<D, T, G, 2, true>), gd, bd, 0, s, a);
   } else if (which == 0) {
-    if (mode == 0) hipLaunchKernelGGL((k_route<D, T, G, 0, false>), gd, bd, 0, s, a);
-    else if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, false>), gd, bd, 0, s, a);
+    if (mode == 1) hipLaunchKernelGGL((k_route<D, T, G, 1, false>), gd, bd, 0, s, a);
     else hipLaunchKernelGGL((k_route<D, T, G, 2, false>), gd, bd, 0, s, a);
+  } else if (which == 2) {
+    if (a.dr > 0) {
+      if (a.capped) hipLaunchKernelGGL((k_planned<D, T, G, true, true>), gd, bd, 0, s, a);
+      else hipLaunchKernelGGL((k_planned<D, T, G, true, false>), gd, bd, 0, s, a);
+    } else {
+      if (a.capped) hipLaunchKernelGGL((k_planned<D, T, G, false, true>), gd, bd, 0, s, a);
+      else hipLaunchKernelGGL((k_planned<D, T, G, false, false>), gd, bd, 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((k_attend<D, T, G>), gd, bd, 0, s, a);
   }
@@ -1383,6 +1965,10 @@ void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArg
 
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
   launch_variant(1, d, kv_bf16, 0, grid, a, s);
+}
+
+void launch_decode_planned(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s) {
+  launch_variant(2, d, kv_bf16, 0, grid, a, s);
 }
 
 void launch_decode_qproj(int d, const DecodeArgs& a, hipStream_t s) {

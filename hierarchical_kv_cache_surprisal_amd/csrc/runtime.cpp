@@ -64,6 +64,30 @@ struct LayerSched {
   uint64_t calls = 0, reads = 0;
   std::vector<double> est;        // zoomed spans per call, per row
   std::vector<double> est_plan;   // the estimates the current tables were planned from
+
+  // Segment lists of the planned kernel (DEVICE bases, HOST bases read in
+  // place): one list of at most wg_segments(G) segments per workgroup, cut from
+  // the predicted cost of every row.  The prediction is the zoom mask of an
+  // earlier call, read back without a sync.
+  bool wvalid = false;
+  std::vector<int4> wsegs;         // [n_wg * wg_segments(G)]
+  int n_wg = 0;
+  std::vector<int32_t> wparts;     // [B*Hkv] partial slots of each (sequence, kv head)
+  int w_max_parts = 0;
+  int4* wsegs_d = nullptr;
+  int4* wsegs_pin = nullptr;
+  size_t wsegs_cap = 0;
+  int32_t* wparts_d = nullptr;
+  int32_t* wparts_pin = nullptr;
+  std::vector<int32_t> plan_m, plan_na;  // span and anchor counts the lists were cut for
+  std::vector<float> zprob;              // [B*Hkv*m_max] zoom frequency (any head of the group), running mean
+  std::vector<float> zunits;             // [B*Hkv] expected zoom units per row from zprob
+  std::vector<float> zunits_plan;        // ... when the lists were cut
+  int zsamples = 0;                      // masks seen
+  uint8_t* mask_pin = nullptr;           // pinned copy of the last zoom mask [B*Hq*m_max]
+  size_t mask_cap = 0;
+  hipEvent_t mev = nullptr;              // recorded after that copy
+  bool mpending = false;
 };
 
 // Device cache of one layer's host-resident bases: a ring region of the
@@ -324,6 +348,12 @@ void free_layer(LayerState& L) {
   hfree(L.sched.parts_pin);
   hfree(L.sched.stat_pin);
   if (L.sched.ev) (void)hipEventDestroy(L.sched.ev);
+  dfree(L.sched.wsegs_d);
+  dfree(L.sched.wparts_d);
+  hfree(L.sched.wsegs_pin);
+  hfree(L.sched.wparts_pin);
+  hfree(L.sched.mask_pin);
+  if (L.sched.mev) (void)hipEventDestroy(L.sched.mev);
   L = LayerState();
 }
 
@@ -439,6 +469,7 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   HIPCHK(c, hipMemcpy(L.na_l_d, L.na_l.data(), (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice));
 
   HIPCHK(c, hipEventCreateWithFlags(&L.sched.ev, hipEventDisableTiming));
+  HIPCHK(c, hipEventCreateWithFlags(&L.sched.mev, hipEventDisableTiming));
   L.sched.est.assign((size_t)B * Hkv, 0.0);
   HIPCHK(c, hipMemset(L.kbar, 0, rows_m * d * c->esz));
   HIPCHK(c, hipMemset(L.vbar, 0, rows_m * d * c->esz));
@@ -756,6 +787,219 @@ sekv_status finish_sched(sekv_ctx* c, int layer, hipStream_t stream, bool captur
   HIPCHK(c, hipEventRecord(S.ev, stream));
   S.stat_tasks.assign(S.tasks.begin(), S.tasks.begin() + S.n_span_tasks);
   S.pending = true;
+  return SEKV_OK;
+}
+
+// Segment lists of the planned kernel.  The work of a layer-step is the
+// sequence "span rows of (b, g), anchor rows of (b, g)" over (b, g) in order.
+// Each row costs the bytes it streams (summaries or anchor keys and values).
+// A span adds, for each of its token-tile units, the unit's bases and a fixed
+// cost (its latency), times the span's zoom frequency over recent calls: the
+// zoom sets move from call to call (spans near the threshold flip with the
+// query), so a share is charged its expected zoom work plus z standard
+// deviations of it.  The sequence is cut into shares of at most `budget`, each
+// a list of at most wg_segments(G) segments and kMaxWgSpanRows span rows;
+// every segment gets the next partial slot of its (b, g).  Returns the number
+// of shares.
+int plan_lists(sekv_ctx* c, LayerState& L, double budget, bool commit) {
+  LayerSched& S = L.sched;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv, d = c->cfg.d_head;
+  const int NS = wg_segments(c->G), mm = c->m_max;
+  // costs in bytes of anchor streaming: a span row, which also routes, takes
+  // about twice as long as an anchor row (per-workgroup timings on the 128K
+  // benchmark layer); a token-tile unit costs its bases plus a fixed amount for
+  // its dependent round of loads (tuned on the same layer)
+  const double row = 2.0 * d * (double)c->esz;
+  const double span_row = row * env_int("SEKV_SPAN_COST", 200, 50, 1000) / 100.0;
+  const double unit_cost = env_int("SEKV_UNIT_COST", 6144, 0, 1 << 24);
+  const double zdev = env_int("SEKV_ZOOM_DEV", 150, 0, 1000) / 100.0;
+  std::vector<int4> segs;
+  std::vector<int32_t> parts(BH, 0);
+  std::vector<int4> cur;
+  int span_rows = 0, nwg = 0;
+  double mean = 0.0, var = 0.0;
+  auto cost = [&]() { return mean + zdev * std::sqrt(var); };
+  auto close_wg = [&]() {
+    if (cur.empty()) return;
+    if (commit) {
+      for (auto& x : cur) segs.push_back(x);
+      for (int i = (int)cur.size(); i < NS; ++i) segs.push_back(make_int4(0, 0, 0, 0));
+    }
+    cur.clear();
+    span_rows = 0;
+    mean = var = 0.0;
+    ++nwg;
+  };
+  for (int bg = 0; bg < BH; ++bg) {
+    const int m = c->m_b[bg / Hkv], na = L.na_l[bg / Hkv];
+    for (int k = 0; k < m;) {
+      if ((int)cur.size() == NS || span_rows >= kMaxWgSpanRows) close_wg();
+      int n = 0;
+      while (k < m && span_rows < kMaxWgSpanRows) {
+        const float pz = S.zprob[(size_t)bg * mm + k];
+        double zm = 0.0, zv = 0.0;
+        if (pz > 0.f) {
+          const int cnt = c->mcount[bg / Hkv][k], r = L.rank_h[(size_t)bg * mm + k];
+          const double work = 2.0 * (pad8(cnt) + d) * r * c->esz + ((cnt + d - 1) / d) * unit_cost;
+          zm = pz * work;
+          zv = pz * (1.0 - pz) * work * work;
+        }
+        const double m2 = mean + span_row + zm, v2 = var + zv;
+        if (n > 0 || !cur.empty()) {
+          // the row goes to the next share when it would take this one over budget
+          if (m2 + zdev * std::sqrt(v2) > budget && cost() > 0.5 * budget) break;
+        }
+        mean = m2;
+        var = v2;
+        ++k;
+        ++n;
+        ++span_rows;
+      }
+      if (n > 0) cur.push_back(make_int4(bg, k - n, n, parts[bg]++));
+      if (k < m) close_wg();
+    }
+    for (int r = 0; r < na;) {
+      if ((int)cur.size() == NS) close_wg();
+      int n = (int)std::floor((budget - cost()) / row);
+      if (n < 1) {
+        if (!cur.empty()) {
+          close_wg();
+          continue;
+        }
+        n = 1;
+      }
+      n = std::min(n, na - r);
+      mean += n * row;
+      cur.push_back(make_int4(bg | (int)0x80000000u, r, n, parts[bg]++));
+      r += n;
+      if (r < na) close_wg();
+    }
+  }
+  close_wg();
+  if (commit) {
+    S.wsegs.swap(segs);
+    S.wparts.swap(parts);
+    S.n_wg = nwg;
+    S.w_max_parts = 1;
+    for (int bg = 0; bg < BH; ++bg) S.w_max_parts = std::max(S.w_max_parts, S.wparts[bg]);
+  } else {
+    int mp = 1;
+    for (int bg = 0; bg < BH; ++bg) mp = std::max(mp, parts[bg]);
+    if (mp > kMaxParts) return INT32_MAX;  // too many slots for one (b, g): a larger budget is needed
+  }
+  return nwg;
+}
+
+// Refresh the segment lists of a layer before a planned launch on `stream`
+// (see prepare_sched for the protocol: nothing changes during a capture, and
+// the lists are replaced only when no mask copy is in flight).
+sekv_status prepare_plan(sekv_ctx* c, int layer, hipStream_t stream, bool capturing) {
+  LayerState& L = c->layers[layer];
+  LayerSched& S = L.sched;
+  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads, BH = B * Hkv, G = c->G;
+  const int d = c->cfg.d_head, mm = c->m_max;
+  const size_t rows = (size_t)BH * mm;
+  if (capturing) {
+    if (!S.wvalid) return fail(c, SEKV_ERR_STATE, "decode a layer once before capturing it into a graph");
+    return SEKV_OK;
+  }
+  bool replan = !S.wvalid || S.plan_m != c->m_b || S.plan_na != L.na_l || S.zprob.size() != rows;
+  if (S.zprob.size() != rows) {
+    S.zprob.assign(rows, 0.f);
+    S.zsamples = 0;
+  }
+  if (S.mpending && hipEventQuery(S.mev) == hipSuccess) {
+    // the zoom mask of an earlier call (union over each group's heads) into
+    // the running zoom frequency of every span: the mean of the first masks,
+    // then an exponential average
+    S.mpending = false;
+    const float w = 1.f / (float)std::min(S.zsamples + 1, 8);
+    S.zsamples++;
+    S.zunits.assign(BH, 0.f);
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < Hkv; ++g) {
+        float eu = 0.f;
+        for (int k = 0; k < c->m_b[b]; ++k) {
+          uint8_t z = 0;
+          for (int h = g * G; h < (g + 1) * G; ++h) z |= S.mask_pin[((size_t)b * Hq + h) * mm + k] ? 1 : 0;
+          float& p = S.zprob[((size_t)b * Hkv + g) * mm + k];
+          p += w * ((float)z - p);
+          eu += p * (float)((c->mcount[b][k] + d - 1) / d);
+        }
+        S.zunits[b * Hkv + g] = eu;
+      }
+    // replan while the frequencies settle, then only when the expected zoom
+    // work of the rows moved: steady zoom keeps the lists, and with them the
+    // order of the merges, from call to call
+    double moved = 0.0, tot = 0.0;
+    for (int bg = 0; bg < BH; ++bg) {
+      const double p0 = bg < (int)S.zunits_plan.size() ? S.zunits_plan[bg] : 0.0;
+      moved += std::fabs(S.zunits[bg] - p0);
+      tot += p0;
+    }
+    replan |= S.zsamples <= 4 || moved > 0.15 * tot + 2.0;
+  }
+  if (!replan || S.mpending) return SEKV_OK;
+  // the smallest budget that cuts the work into at most fill_tasks shares,
+  // bracketed around the mean share of the expected work
+  double total = 0.0;
+  {
+    const double row = 2.0 * d * (double)c->esz;
+    for (int bg = 0; bg < BH; ++bg) {
+      const int b = bg / Hkv;
+      total += (double)c->m_b[b] * 2.0 * row + (double)L.na_l[b] * row;
+      if (bg < (int)S.zunits.size()) total += S.zunits[bg] * 16384.0;
+    }
+  }
+  const int nw = c->fill_tasks;
+  double lo = 0.25 * total / nw, hi = 2.0 * total / nw + 1.0;
+  while (plan_lists(c, L, hi, false) > nw) hi *= 2.0;
+  for (int it = 0; it < 16 && hi - lo > 0.005 * hi; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (plan_lists(c, L, mid, false) > nw) lo = mid;
+    else hi = mid;
+  }
+  plan_lists(c, L, hi, true);
+  if (S.w_max_parts > kMaxParts) return fail(c, SEKV_ERR_STATE, "too many partial slots per head");
+  S.zunits_plan = S.zunits;
+  S.plan_m = c->m_b;
+  S.plan_na = L.na_l;
+  const size_t nrec = S.wsegs.size();
+  if (nrec > S.wsegs_cap) {
+    dfree(S.wsegs_d);
+    hfree(S.wsegs_pin);
+    S.wsegs_cap = 0;
+    TRY(dalloc(c, &S.wsegs_d, nrec * sizeof(int4)));
+    TRY(halloc(c, &S.wsegs_pin, nrec * sizeof(int4)));
+    S.wsegs_cap = nrec;
+  }
+  if (!S.wparts_d) {
+    TRY(dalloc(c, &S.wparts_d, (size_t)BH * 4));
+    TRY(halloc(c, &S.wparts_pin, (size_t)BH * 4));
+  }
+  std::memcpy(S.wsegs_pin, S.wsegs.data(), nrec * sizeof(int4));
+  std::memcpy(S.wparts_pin, S.wparts.data(), (size_t)BH * 4);
+  HIPCHK(c, hipMemcpyAsync(S.wsegs_d, S.wsegs_pin, nrec * sizeof(int4), hipMemcpyHostToDevice, stream));
+  HIPCHK(c, hipMemcpyAsync(S.wparts_d, S.wparts_pin, (size_t)BH * 4, hipMemcpyHostToDevice, stream));
+  S.wvalid = true;
+  return SEKV_OK;
+}
+
+// After a planned launch: copy the zoom mask back for the next plan, if no
+// copy is in flight.
+sekv_status finish_plan(sekv_ctx* c, int layer, const uint8_t* mask, hipStream_t stream, bool capturing) {
+  LayerSched& S = c->layers[layer].sched;
+  if (capturing || S.mpending) return SEKV_OK;
+  const size_t n = (size_t)c->cfg.batch * c->cfg.n_q_heads * c->m_max;
+  if (n > S.mask_cap) {
+    hfree(S.mask_pin);
+    S.mask_cap = 0;
+    TRY(halloc(c, &S.mask_pin, n));
+    S.mask_cap = n;
+  }
+  HIPCHK(c, hipMemcpyAsync(S.mask_pin, mask, n, hipMemcpyDeviceToHost, stream));
+  HIPCHK(c, hipEventRecord(S.mev, stream));
+  S.mpending = true;
   return SEKV_OK;
 }
 
@@ -1338,6 +1582,13 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
   a.q = q;
   a.out = out;
   a.mask = zoom_mask ? zoom_mask : c->mask_d;
+  if (!staged(c)) {
+    // the planned kernel: its segment lists and their partial slots
+    TRY(prepare_plan(c, layer, stream, capturing));
+    a.wsegs = L.sched.wsegs_d;
+    a.parts_n = L.sched.wparts_d;
+    a.max_parts = L.sched.w_max_parts;
+  }
   if (capturing && (size_t)a.B * a.Hq * a.max_parts > c->parts_cap)
     return fail(c, SEKV_ERR_STATE, "partial buffers would grow during graph capture: decode once first");
   TRY(ensure_parts(c, (size_t)a.B * a.Hq * a.max_parts));
@@ -1378,7 +1629,7 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
     // the pinned host store over the link, or from its device cache), and the
     // anchor tasks
     if (host_store(c)) a.bases = L.bases_hd;
-    launch_decode_route(0, a.n_tasks, d, c->bf16, a, stream);
+    launch_decode_planned(L.sched.n_wg, d, c->bf16, a, stream);
     HIPCHK(c, hipGetLastError());
   } else {
     // HOST home: learn the zoom list, fetch the bases, then the zoomed segment
@@ -1421,6 +1672,7 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
       TRY(cache_prefetch(c, nxt));
     }
   }
+  if (!staged(c)) return finish_plan(c, layer, a.mask, stream, capturing);
   return finish_sched(c, layer, stream, capturing);
 }
 

@@ -15,6 +15,12 @@ constexpr int kMaxParts = 512;  // split-K partial slots per (sequence, query he
 constexpr int kCombineThreads = 512;
 constexpr int kMaxSpanChunk = 256;  // span rows per span task
 
+// Planned layer-step kernel: every workgroup runs a short list of segments
+// (runs of span rows or anchor rows of one (sequence, kv head)), at most
+// wg_segments(G) of them, holding at most kMaxWgSpanRows span rows in all.
+constexpr int kMaxWgSpanRows = 512;
+__host__ __device__ constexpr int wg_segments(int G) { return G == 1 ? 4 : (G <= 4 ? 2 : 1); }
+
 // Every packed basis block starts on a multiple of 8 elements (16 bytes for
 // bf16), so wide loads stay aligned.
 __host__ __device__ inline int64_t pad8(int64_t x) { return (x + 7) & ~int64_t(7); }
@@ -52,6 +58,9 @@ struct DecodeArgs {
   int32_t* zcnt;          // [n_span_tasks] zoomed spans of each span task in the last call (statistics)
   float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
   float* part_acc;        // [B][Hq][max_parts][d]
+  // planned kernel: segments of workgroup i at wsegs[i * wg_segments(G) ..], each
+  // (bg | anchors << 31, first row, rows, partial slot); rows = 0 ends a list
+  const int4* wsegs;
   int n_zoom_wgs;          // host store: fetched groups at the front of the attend grid
   // host fetch path: flat list (bg | head bits << 24, span, basis offset / 8, rank | count << 8)
   int4* zlist;
@@ -68,16 +77,18 @@ struct DecodeArgs {
   int32_t budget[kMaxHq]; // most zoomed spans per (sequence, query head); < 0: no cap
 };
 
-// mode 0 (DEVICE bases): span tasks with their zoomed spans in place, and the
-// anchor tasks, grid = tasks.  mode 1 (HOST bases): span tasks, zoomed spans
-// to the flat list, grid = span tasks.  mode 2: routing scores of the span
-// tasks only, grid = span tasks
+// mode 1 (staged HOST bases): span tasks, zoomed spans to the flat list, grid
+// = span tasks.  mode 2: routing scores of the span tasks only, grid = span
+// tasks
 void launch_decode_route(int mode, int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
 // the route (which = 0) and attend (which = 1) kernels of one (head dim, KV dtype)
 void decode_variant_d128_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
 void decode_variant_d128_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
 void decode_variant_d64_bf16(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
 void decode_variant_d64_f32(int which, int mode, int grid, const DecodeArgs& a, hipStream_t s);
+// the planned layer-step kernel (DEVICE bases, and HOST bases read in place):
+// one workgroup per segment list, grid = lists
+void launch_decode_planned(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
 // HOST bases: n_zoom_wgs workgroups for the fetched groups, then the anchor
 // tasks; grid = n_zoom_wgs + anchor tasks
 void launch_decode_attend(int grid, int d, int kv_bf16, const DecodeArgs& a, hipStream_t s);
