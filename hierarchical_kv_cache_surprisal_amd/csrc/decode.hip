@@ -498,7 +498,9 @@ __device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int
     }
     const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
     a.part_acc[slot * D + j] = A;
-    if (j == 0) reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(M, L);
+    if (j == 0) {
+      reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(M, L);
+    }
   }
 }
 
@@ -509,7 +511,9 @@ __device__ void store_empty(const DecodeArgs& a, int b, int g, int part) {
     const int h = idx / D, j = idx % D;
     const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
     a.part_acc[slot * D + j] = 0.f;
-    if (j == 0) reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(kNegInf, 0.f);
+    if (j == 0) {
+      reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(kNegInf, 0.f);
+    }
   }
 }
 
@@ -801,10 +805,12 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
   const float inv_sqrt_d = rsqrtf((float)D);
   SoftState<G> st;
   float acc[G][EPL];
+  float zcl[G];  // zoomed spans per head among this lane's rows (first lane of each row slot)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     st.m[h] = kNegInf;
     st.l[h] = 0.f;
+    zcl[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
@@ -930,6 +936,8 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
         if (k < k1) {
           sh.zb[k - k0] = (uint8_t)zbits[u];
           if (zbits[u]) sh.zmeta[k - k0] = sg.meta[u];
+#pragma unroll
+          for (int h = 0; h < G; ++h) zcl[h] += (float)((zbits[u] >> h) & 1u);
         }
       }
     }
@@ -964,6 +972,16 @@ __device__ void span_task(const DecodeArgs& a, int t, int4 task, Smem<D, G>& sh)
     }
   }
   if (SCORES) return;
+  if (a.zcount) {
+    // the layer's zoom counters: this wave's zoomed spans of each head
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float z = wave_sum(zcl[h]);
+      if (lane == 0 && z > 0.f)
+        __hip_atomic_fetch_add(a.zcount + (size_t)b * a.Hq + g * G + h, (unsigned long long)z, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   slots_to_lds<D, G, EPL, LPR>(st, acc, sh.ml, lane, wave, slot, sub);
   __syncthreads();  // zoom bits and records complete
 
@@ -1018,6 +1036,7 @@ struct PlanSmem {
   int4 zit[kMaxWgSpanRows];        // zoomed spans: (head bits | kCachedBit, basis offset / 8, rank | count << 8, segment | bg << 8)
   int ustart[kMaxWgSpanRows + 1];  // their first work unit
   int red[kWaves][2];
+  int zcnt[NS][G];                 // spans each head zoomed in each segment
 };
 
 // Span rows [k0, k0 + rows) of one (b, g): routing scores and zoom decisions
@@ -1402,6 +1421,10 @@ __device__ void plan_zoom(const DecodeArgs& a, int nseg, int R, PlanSmem<D, G, N
       }
     }
     sh.zit[pc] = make_int4((int)bits, off8, sh.zmeta[j].y, s | (bg << 8));
+    // the segment's zoom counts (its slot reports them to the combine)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if ((hb2[e] >> h) & 1u) atomicAdd(&sh.zcnt[s][h], 1);
     sh.ustart[pc] = pt;
     pt += ((int)((uint32_t)sh.zmeta[j].y >> 8) + TILE - 1) / TILE;
     ++pc;
@@ -1427,28 +1450,18 @@ __device__ void plan_zoom(const DecodeArgs& a, int nseg, int R, PlanSmem<D, G, N
             __builtin_amdgcn_readfirstlane((u - sh.ustart[j]) * TILE), sw & 0xff, sw >> 8};
   };
   if constexpr (G == 1) {
-    // one head: the query slice and a running softmax in registers, folded
-    // into the wave's record of a segment when the units move to the next one
-    int cur = -1;
-    float m = kNegInf, l = 0.f, acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    auto qget = [&](int, int e) { return sh.q[cur][0][tg * EPL + e]; };
-    auto sink = [&](int, float sm, float sl, const float (&o)[EPL]) { lse_merge<EPL>(m, l, acc, sm, sl, o); };
-    auto begin = [&](int s) {
-      if (cur >= 0) fold_record<D, G, EPL>(sh.rec[cur], wave, 0, lane, rg, tg, m, l, acc);
-      cur = s;
-      m = kNegInf;
-      l = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    };
+    // one head: each unit's piece folded into the wave's record of its segment
+    // (LDS), so that no running record stays in registers across the units
     int j = 0;
 #pragma unroll 1
     for (int u = wave; u < units; u += kWaves) {
       while (sh.ustart[j + 1] <= u) ++j;  // units are visited in increasing order
       const UnitRef x = unit_ref(u, j);
-      if (x.s != cur) begin(x.s);
+      const int s = x.s;
+      auto qget = [&](int, int e) { return sh.q[s][0][tg * EPL + e]; };
+      auto sink = [&](int, float sm, float sl, const float (&o)[EPL]) {
+        fold_record<D, G, EPL>(sh.rec[s], wave, 0, lane, rg, tg, sm, sl, o);
+      };
       if constexpr (kPairUnits) {
         // two units of rank <= RBATCH / 2 (this one and the wave's next, of the
         // same segment) fit the registers of one full-rank unit: one round of loads
@@ -1474,7 +1487,6 @@ __device__ void plan_zoom(const DecodeArgs& a, int nseg, int R, PlanSmem<D, G, N
       }
       zoom_unit<D, T, G>(x.base, x.cnt, x.r, x.t0, x.hb, qget, sink, c2, rg, tg);
     }
-    if (cur >= 0) fold_record<D, G, EPL>(sh.rec[cur], wave, 0, lane, rg, tg, m, l, acc);
   } else {
     // several heads: queries from LDS, each head's pieces folded into the wave's records
     int j = 0;
@@ -1530,6 +1542,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1
 #pragma unroll
     for (int s = 0; s < NS; ++s) sh.seg[s] = sgs[s];
   }
+  if (threadIdx.x < NS * G) (&sh.zcnt[0][0])[threadIdx.x] = 0;
   // the queries of every segment's group, loaded at the start (one round trip
   // shared with the first streaming round) and written to LDS when needed: at
   // once for wide groups, which stream with the queries in LDS, and before the
@@ -1591,6 +1604,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1
     const int x = __builtin_amdgcn_readfirstlane(v.x), w = __builtin_amdgcn_readfirstlane(v.w);
     const int bg = x & 0x7fffffff;
     store_partial<D, G>(sh.rec[s], a, bg / a.Hkv, bg % a.Hkv, w);
+  }
+  // the layer's zoom counters: atomic adds whose result is not used, so no
+  // round trip before the workgroup ends
+  if (a.zcount && (int)threadIdx.x < nseg * G) {
+    const int s = threadIdx.x / G, h = threadIdx.x % G;
+    const int z = sh.zcnt[s][h];
+    const int bg = sh.seg[s].x & 0x7fffffff;
+    if (z > 0)
+      __hip_atomic_fetch_add(a.zcount + (size_t)(bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G + h, (unsigned long long)z,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1670,6 +1693,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)bh * a.max_parts;
   const float4* pa = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * a.max_parts * D) + c4;
+
   // the slot loads are bounded by the buffer (max_parts), not by np, so the
   // first batch is in flight together with the load of np; slots >= np are
   // loaded but never merged
@@ -1704,6 +1728,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   }
   ga_s[pg][c4] = A;
   __syncthreads();
+  if (a.zcount && bh == 0 && threadIdx.x == 0)  // the layer's call counter (the attention kernel adds the spans)
+    __hip_atomic_fetch_add(a.zcount + (size_t)a.B * a.Hq, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (threadIdx.x < C4) {
     float Mg = kNegInf;
     for (int q = 0; q < PG; ++q) Mg = fmaxf(Mg, gm_s[q]);

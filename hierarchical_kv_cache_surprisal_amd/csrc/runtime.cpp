@@ -146,6 +146,7 @@ struct LayerState {
   uint64_t seed = 0;
   LayerCache lc;                   // device cache of its host-resident bases
   LayerSched sched;
+  unsigned long long* zcount_d = nullptr;  // [B*Hq + 1] zoom counters (spans per (b, h) over calls; calls)
 };
 
 // Routing projection of one layer (set before the layer's layout exists).
@@ -328,6 +329,16 @@ void free_layer_cache(LayerCache& C) {
   C = LayerCache();
 }
 
+// A layer's stored bases are about to change: drop its device cache, whose
+// copies would go stale, once no decode and no prefetch copy that may read
+// the store or the cache is still in flight.
+hipError_t invalidate_layer_cache(LayerState& L) {
+  if (!L.lc.init) return hipSuccess;
+  const hipError_t e = hipDeviceSynchronize();
+  free_layer_cache(L.lc);
+  return e;
+}
+
 void free_layer(LayerState& L) {
   free_layer_cache(L.lc);
   dfree(L.kbar);
@@ -348,6 +359,7 @@ void free_layer(LayerState& L) {
   hfree(L.sched.parts_pin);
   hfree(L.sched.stat_pin);
   if (L.sched.ev) (void)hipEventDestroy(L.sched.ev);
+  dfree(L.zcount_d);
   dfree(L.sched.wsegs_d);
   dfree(L.sched.wparts_d);
   hfree(L.sched.wsegs_pin);
@@ -467,6 +479,11 @@ sekv_status alloc_layer(sekv_ctx* c, int layer, const std::vector<int32_t>& rank
   TRY(dalloc(c, &L.smeta_d, rows_m * sizeof(int2)));
   TRY(dalloc(c, &L.na_l_d, (size_t)B * sizeof(int32_t)));
   HIPCHK(c, hipMemcpy(L.na_l_d, L.na_l.data(), (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice));
+  {
+    const size_t nz = (size_t)B * c->cfg.n_q_heads + 1;
+    TRY(dalloc(c, &L.zcount_d, nz * sizeof(unsigned long long)));
+    HIPCHK(c, hipMemset(L.zcount_d, 0, nz * sizeof(unsigned long long)));
+  }
 
   HIPCHK(c, hipEventCreateWithFlags(&L.sched.ev, hipEventDisableTiming));
   HIPCHK(c, hipEventCreateWithFlags(&L.sched.mev, hipEventDisableTiming));
@@ -1475,8 +1492,7 @@ sekv_status sekv_build(sekv_ctx* c, int32_t layer, const float* H, const void* K
   for (int i = 0; i < 5; ++i) {
     sv.problems = c->prob_d[i];
     sv.n_problems = c->n_prob[i];
-    launch_svd(cmax[i], d, c->bf16, sv, stream);
-    HIPCHK(c, hipGetLastError());
+    HIPCHK(c, launch_svd(cmax[i], d, c->bf16, sv, stream));
   }
   // 5. HOST home: move the store to pinned memory
   if (host_store(c)) {
@@ -1594,6 +1610,7 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
   TRY(ensure_parts(c, (size_t)a.B * a.Hq * a.max_parts));
   a.part_ml = c->part_ml;
   a.part_acc = c->part_acc;
+  a.zcount = L.zcount_d;
   c->stats.decode_calls++;
   const int d = c->cfg.d_head;
   if (a.dr > 0) {
@@ -1801,6 +1818,7 @@ sekv_status sekv_import_head(sekv_ctx* c, int32_t layer, int32_t b, int32_t g, c
   if (basis_elems != he)
     return fail(c, SEKV_ERR_INVALID, "basis_elems " + std::to_string(basis_elems) + " != layout " + std::to_string(he));
   const size_t es = c->esz;
+  HIPCHK(c, invalidate_layer_cache(L));
   if (m) {
     HIPCHK(c, hipMemcpy((char*)L.kbar + bg * mm * d * es, kbar, (size_t)m * d * es, hipMemcpyHostToDevice));
     HIPCHK(c, hipMemcpy((char*)L.vbar + bg * mm * d * es, vbar, (size_t)m * d * es, hipMemcpyHostToDevice));
@@ -2115,8 +2133,7 @@ sekv_status sekv_resegment_window(sekv_ctx* c, hipStream_t stream) {
       HIPCHK(c, hipMemcpy(prob_t, probs[i].data(), probs[i].size() * 4, hipMemcpyHostToDevice));
       sv.problems = prob_t;
       sv.n_problems = (int)(probs[i].size() / 3);
-      launch_svd(cmax[i], d, c->bf16, sv, stream);
-      HIPCHK(c, hipGetLastError());
+      HIPCHK(c, launch_svd(cmax[i], d, c->bf16, sv, stream));
       HIPCHK(c, hipStreamSynchronize(stream));  // prob_t is reused by the next bucket
     }
     // 7. the new store: each head's old spans, then its new ones
@@ -2439,6 +2456,9 @@ sekv_status sekv_apply_rank_gates(sekv_ctx* c, int32_t layer, int32_t b, int32_t
       }
     }
   }
+  // the gated factors replace the stored ones: cached copies of this layer's
+  // bases go, and no prefetch copy may read a half-gated span
+  HIPCHK(c, invalidate_layer_cache(L));
   float* g_d = nullptr;
   const size_t ng = (size_t)m * d;
   TRY(dalloc(c, &g_d, 2 * ng * sizeof(float)));
@@ -2461,6 +2481,24 @@ sekv_status sekv_apply_rank_gates(sekv_ctx* c, int32_t layer, int32_t b, int32_t
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   dfree(g_d);
   if (e != hipSuccess) return fail(c, SEKV_ERR_HIP, std::string("rank gates: ") + hipGetErrorString(e));
+  return SEKV_OK;
+}
+
+sekv_status sekv_get_zoom_counts(sekv_ctx* c, int32_t layer, uint64_t* counts, uint64_t* calls, int32_t reset) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(c, SEKV_ERR_INVALID, "layer " + std::to_string(layer) + " out of range");
+  LayerState& L = c->layers[layer];
+  if (!L.zcount_d) return fail(c, SEKV_ERR_STATE, "layer has no layout");
+  const size_t n = (size_t)c->cfg.batch * c->cfg.n_q_heads;
+  std::vector<unsigned long long> h(n + 1);
+  HIPCHK(c, hipDeviceSynchronize());  // every decode call that updates the counters has finished
+  HIPCHK(c, hipMemcpy(h.data(), L.zcount_d, (n + 1) * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+  if (counts)
+    for (size_t i = 0; i < n; ++i) counts[i] = h[i];
+  if (calls) *calls = h[n];
+  if (reset) HIPCHK(c, hipMemset(L.zcount_d, 0, (n + 1) * sizeof(unsigned long long)));
   return SEKV_OK;
 }
 

@@ -58,6 +58,8 @@ struct DecodeArgs {
   int32_t* zcnt;          // [n_span_tasks] zoomed spans of each span task in the last call (statistics)
   float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
   float* part_acc;        // [B][Hq][max_parts][d]
+  unsigned long long* zcount;  // the layer's counters: [B*Hq] zoomed spans per (sequence, query head)
+                               // summed over calls (atomic adds), then [B*Hq] the number of calls (or NULL)
   // planned kernel: segments of workgroup i at wsegs[i * wg_segments(G) ..], each
   // (bg | anchors << 31, first row, rows, partial slot); rows = 0 ends a list
   const int4* wsegs;
@@ -194,6 +196,7 @@ struct SvdArgs {
 };
 // cmax: 16, 32, 64 or 128 member rows (one-sided Jacobi on the rows),
 // or 0 for taller spans (fp64 Gram, Cholesky, Jacobi on the triangular factor)
-void launch_svd(int cmax, int d, int kv_bf16, const SvdArgs& a, hipStream_t s);
+// returns the launch error, or the refusal of the kernel's LDS attribute
+hipError_t launch_svd(int cmax, int d, int kv_bf16, const SvdArgs& a, hipStream_t s);
 
 }  // namespace sekv

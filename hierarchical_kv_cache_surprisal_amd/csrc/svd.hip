@@ -353,55 +353,49 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   store_a_from_rows<D, T, ROWS, XS>(a, p, src, Xr, Rr, XS, sig, order);
 }
 
+// The kernels take more than 64 KB of dynamic LDS, which needs the attribute
+// set on the current device before the launch (a build-time call, not timed):
+// a refusal is returned instead of surfacing later as a launch failure.
 template <int D, typename T, int PMAX>
-void launch_rows(const SvdArgs& a, hipStream_t s) {
+hipError_t launch_rows(const SvdArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * (PMAX + 16) * (D + kVecPad);
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr = true;
-  }
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(kSvdThreads), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int D, typename T>
-void launch_tall(const SvdArgs& a, hipStream_t s) {
+hipError_t launch_tall(const SvdArgs& a, hipStream_t s) {
   // max(packed fp64 Gram + 16 staged rows, fp32 rows of R + 16 staged rows)
   const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * D;
   const size_t rows = sizeof(float) * (D + 16) * (D + kVecPad);
   const size_t lds = gram > rows ? gram : rows;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr = true;
-  }
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_svd_tall<D, T>), dim3(a.n_problems), dim3(kSvdThreads), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int D, typename T>
-void launch_svd_t(int cmax, const SvdArgs& a, hipStream_t s) {
+hipError_t launch_svd_t(int cmax, const SvdArgs& a, hipStream_t s) {
   switch (cmax) {
-    case 16: launch_rows<D, T, 16>(a, s); break;
-    case 32: launch_rows<D, T, 32>(a, s); break;
-    case 64: launch_rows<D, T, 64>(a, s); break;
-    case 128: launch_rows<D, T, 128>(a, s); break;
-    default: launch_tall<D, T>(a, s); break;
+    case 16: return launch_rows<D, T, 16>(a, s);
+    case 32: return launch_rows<D, T, 32>(a, s);
+    case 64: return launch_rows<D, T, 64>(a, s);
+    case 128: return launch_rows<D, T, 128>(a, s);
+    default: return launch_tall<D, T>(a, s);
   }
 }
 
 }  // namespace
 
-void launch_svd(int cmax, int d, int kv_bf16, const SvdArgs& a, hipStream_t s) {
-  if (a.n_problems <= 0) return;
-  if (d == 128) {
-    if (kv_bf16) launch_svd_t<128, bf16_t>(cmax, a, s);
-    else launch_svd_t<128, float>(cmax, a, s);
-  } else {
-    if (kv_bf16) launch_svd_t<64, bf16_t>(cmax, a, s);
-    else launch_svd_t<64, float>(cmax, a, s);
-  }
+hipError_t launch_svd(int cmax, int d, int kv_bf16, const SvdArgs& a, hipStream_t s) {
+  if (a.n_problems <= 0) return hipSuccess;
+  if (d == 128) return kv_bf16 ? launch_svd_t<128, bf16_t>(cmax, a, s) : launch_svd_t<128, float>(cmax, a, s);
+  return kv_bf16 ? launch_svd_t<64, bf16_t>(cmax, a, s) : launch_svd_t<64, float>(cmax, a, s);
 }
 
 }  // namespace sekv

@@ -31,7 +31,8 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_import_spans", "sekv_import_layout", "sekv_import_head", "sekv_export_head",
             "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
             "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window",
-            "sekv_set_basis_cache", "sekv_reserve_spans", "sekv_append_surprisal", "sekv_resegment_window"]
+            "sekv_set_basis_cache", "sekv_reserve_spans", "sekv_append_surprisal", "sekv_resegment_window",
+            "sekv_get_zoom_counts"]
 
 
 class SekvError(RuntimeError):
@@ -97,6 +98,7 @@ def load_library(path: str = LIB_PATH):
         "sekv_import_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_export_route_summary": (I32, [P, I32, I32, I32, P]),
         "sekv_apply_rank_gates": (I32, [P, I32, I32, I32, C.POINTER(C.c_float), C.POINTER(C.c_float), P]),
+        "sekv_get_zoom_counts": (I32, [P, I32, C.POINTER(C.c_uint64), C.POINTER(C.c_uint64), I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -304,6 +306,44 @@ def sekv_apply_rank_gates(ctx, layer: int, b: int, g: int, gate_k=None, gate_v=N
            ctx)
 
 
+def sekv_get_zoom_counts(ctx, layer: int, n: int, reset: bool = False):
+    """(counts uint64 [n] = [B * H_q], calls) of one layer."""
+    counts = np.zeros(n, np.uint64)
+    calls = np.zeros(1, np.uint64)
+    u64 = C.POINTER(C.c_uint64)
+    _check(load_library().sekv_get_zoom_counts(ctx, layer, counts.ctypes.data_as(u64), calls.ctypes.data_as(u64),
+                                               1 if reset else 0), ctx)
+    return counts, int(calls[0])
+
+
+# ----------------------------------------------------------------------------- argument checks
+
+def _check_tensor(t, name: str, dtype, numel: int, device: int, optional: bool = False):
+    """Raise ValueError unless t is a contiguous tensor of `dtype` with exactly
+    `numel` elements on cuda:`device`: the library reads and writes that many
+    elements through the raw pointer."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device.index != device:
+        raise ValueError(f"{name} must be on cuda:{device}, not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, not {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_host(a, name: str, n: int):
+    if a is None or np.asarray(a).size != n:
+        raise ValueError(f"{name} must hold {n} entries")
+
+
 # ----------------------------------------------------------------------------- convenience object
 
 class Context:
@@ -317,6 +357,7 @@ class Context:
         dt = {"f32": SEKV_F32, "bf16": SEKV_BF16}[kv_dtype]
         home = {"host": SEKV_BASES_HOST, "device": SEKV_BASES_DEVICE,
                 "host_staged": SEKV_BASES_HOST_STAGED}[basis_home]
+        self.device = device
         self.ptr = sekv_create(n_layers, batch, n_ctx, n_q_heads, n_kv_heads, d_head, dt, local_window,
                                home, device)
 
@@ -335,7 +376,17 @@ class Context:
     def storage_dtype(self):
         return np.float32 if self.kv_dtype == "f32" else np.uint16
 
+    @property
+    def kv_torch_dtype(self):
+        import torch
+        return torch.float32 if self.kv_dtype == "f32" else torch.bfloat16
+
     def build(self, layer, H, K, V, alpha, rank_choices, rank_seed, stream=None):
+        import torch
+        _check_tensor(H, "H", torch.float32, self.B * self.n, self.device)
+        kv = self.B * self.Hkv * self.n * self.d
+        _check_tensor(K, "K", self.kv_torch_dtype, kv, self.device)
+        _check_tensor(V, "V", self.kv_torch_dtype, kv, self.device)
         sekv_build(self.ptr, layer, H, K, V, alpha, rank_choices, rank_seed, stream)
 
     def spans(self, b):
@@ -345,12 +396,24 @@ class Context:
         return sekv_get_spans(self.ptr, 0)[3]
 
     def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None, budget=None):
+        import torch
+        qn = self.B * self.Hq * self.d
+        _check_tensor(q, "q", torch.float32, qn, self.device)
+        _check_tensor(out, "out", torch.float32, qn, self.device)
+        if zoom_mask is not None:
+            _check_tensor(zoom_mask, "zoom_mask", torch.uint8, self.B * self.Hq * self.m_max(), self.device)
+        _check_host(tau, "tau", self.Hq)
+        if budget is not None:
+            _check_host(budget, "budget", self.Hq)
         if budget is None:
             sekv_decode_attn(self.ptr, layer, q, tau, out, zoom_mask, stream)
         else:
             sekv_decode_attn_budget(self.ptr, layer, q, tau, budget, out, zoom_mask, stream)
 
     def route_scores(self, layer, q, scores, stream=None):
+        import torch
+        _check_tensor(q, "q", torch.float32, self.B * self.Hq * self.d, self.device)
+        _check_tensor(scores, "scores", torch.float32, self.B * self.Hq * self.m_max(), self.device)
         sekv_route_scores(self.ptr, layer, q, scores, stream)
 
     def bases_layout(self, layer, b, g):
@@ -379,6 +442,12 @@ class Context:
         return sekv_get_stats(self.ptr)
 
     def append_tokens(self, layer, K_new, V_new, stream=None):
+        n_new = int(K_new.shape[2]) if K_new is not None and K_new.dim() == 4 else -1
+        if n_new < 0:
+            raise ValueError("K_new must be [B][H_kv][n_new][d]")
+        kv = self.B * self.Hkv * n_new * self.d
+        _check_tensor(K_new, "K_new", self.kv_torch_dtype, kv, self.device)
+        _check_tensor(V_new, "V_new", self.kv_torch_dtype, kv, self.device)
         sekv_append_tokens(self.ptr, layer, K_new, V_new, stream)
 
     def set_basis_cache(self, nbytes):
@@ -405,6 +474,11 @@ class Context:
     def export_route_summary(self, layer, b, g, d_route):
         m = len(self.spans(b)[0])
         return sekv_export_route_summary(self.ptr, layer, b, g, m, d_route, self.storage_dtype)
+
+    def zoom_counts(self, layer, reset=False):
+        """(counts [B][H_q] uint64, calls): spans zoomed per (sequence, query head) of a layer."""
+        counts, calls = sekv_get_zoom_counts(self.ptr, layer, self.B * self.Hq, reset)
+        return counts.reshape(self.B, self.Hq), calls
 
     def apply_rank_gates(self, layer, b, g, gate_k=None, gate_v=None, stream=None):
         sekv_apply_rank_gates(self.ptr, layer, b, g, gate_k, gate_v, stream)

@@ -244,8 +244,9 @@ sekv_status sekv_import_layout(sekv_ctx* ctx, int32_t layer, const int32_t* rank
  *   bases host KV dtype, packed as described at sekv_get_bases_layout,
  *   basis_elems elements.
  * The layer needs a layout (sekv_build or sekv_import_layout) and the ranks
- * must equal that layout's; imports are synchronous.  The layer is decodable
- * once every (b, g) has artefacts (all of them, after a build).
+ * must equal that layout's; imports are synchronous, and drop the layer's
+ * device basis cache (after a device synchronisation).  The layer is
+ * decodable once every (b, g) has artefacts (all of them, after a build).
  * Errors: INVALID, STATE (no layout), OOM, HIP. */
 sekv_status sekv_import_head(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, const void* kbar,
                              const void* vbar, const void* KA, const void* VA, const int32_t* rank,
@@ -372,8 +373,10 @@ sekv_status sekv_export_route_summary(const sekv_ctx* ctx, int32_t layer, int32_
  *   gate_k, gate_v host float32 [m][d] (entries i >= rank[k] ignored), each in
  *   [0, 1]; either may be NULL (that factor is left alone).
  * Works on device and host basis stores; synchronises `stream` before it
- * returns.  Errors: STATE (head has no artefacts), INVALID (gate outside
- * [0, 1] or NaN), OOM, HIP. */
+ * returns.  A device basis cache of the layer (sekv_set_basis_cache) is
+ * dropped first, after a device synchronisation, so that no cached copy of an
+ * ungated factor is read afterwards.  Errors: STATE (head has no artefacts),
+ * INVALID (gate outside [0, 1] or NaN), OOM, HIP. */
 sekv_status sekv_apply_rank_gates(sekv_ctx* ctx, int32_t layer, int32_t b, int32_t g, const float* gate_k,
                                   const float* gate_v, hipStream_t stream);
 
@@ -396,6 +399,23 @@ typedef struct sekv_stats {
 } sekv_stats;
 
 sekv_status sekv_get_stats(const sekv_ctx* ctx, sekv_stats* out);
+
+/* Per-(layer, query head) zoom counters [summary page, section 3.4 and Figures
+ * 5-6, which read router health from the zoom rate of every (layer, head)].
+ *   counts host uint64 [B][H_q] (or NULL): spans zoomed by each (sequence, query
+ *          head) of `layer`, summed over the layer's decode calls since its
+ *          layout was made (sekv_build, sekv_import_layout) or since the last
+ *          reset; a span zoomed by several query heads of a group counts for
+ *          each of them.
+ *   calls  host uint64 (or NULL): the number of those decode calls.
+ *   reset  nonzero: zero both counters after reading.
+ * The counters live on the device and are advanced by the combine kernel of
+ * every decode call (graph replays included, no host synchronisation); the
+ * zoom rate of a head is counts / (calls * m) with m the sequence's span count.
+ * This call synchronises the device.  Errors: INVALID (layer out of range),
+ * STATE (layer has no layout), HIP. */
+sekv_status sekv_get_zoom_counts(sekv_ctx* ctx, int32_t layer, uint64_t* counts, uint64_t* calls,
+                                 int32_t reset);
 
 #ifdef __cplusplus
 }

@@ -101,3 +101,26 @@ def test_pack_unpack_roundtrip():
     AK, BKt, AV, BVt = unpack_bases(flat, art.mcount, art.rank, "f32", 64)
     for k in range(art.m):
         assert np.array_equal(AK[k], art.AK[k]) and np.array_equal(BVt[k], art.BVt[k])
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The Context wrapper checks dtype, device and size of every device buffer the
+    library would read or write through a raw pointer, and the host arrays'
+    lengths, and raises ValueError before any call into the library."""
+    import torch
+    from hierarchical_kv_cache_surprisal_amd import sekv
+    ctx = object.__new__(sekv.Context)  # no library context: the checks come first
+    ctx.B, ctx.Hq, ctx.Hkv, ctx.L, ctx.n, ctx.d, ctx.kv_dtype, ctx.device = 1, 4, 2, 1, 64, 64, "bf16", 0
+    ctx.ptr = None
+    cpu_q = torch.zeros(1, 4, 64)
+    with pytest.raises(ValueError, match="cuda"):
+        ctx.decode_attn(0, cpu_q, np.zeros(4, np.float32), cpu_q)
+    with pytest.raises(ValueError, match="cuda"):
+        ctx.build(0, torch.zeros(1, 64), torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16),
+                  torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16), 1.0, (8,), 1)
+    with pytest.raises(ValueError, match="K_new"):
+        ctx.append_tokens(0, torch.zeros(3), torch.zeros(3))
+    with pytest.raises(ValueError, match="torch tensor"):
+        sekv._check_tensor(np.zeros(4), "x", torch.float32, 4, 0)
+    with pytest.raises(ValueError, match="entries"):
+        sekv._check_host(np.zeros(3), "tau", 4)

@@ -209,6 +209,53 @@ def test_layer_128k_sampled_heads_graph_replay():
         assert int(masks[t][:, :, :m].max()) <= 1
 
 
+def eager_decode(ctx, layer, q_steps_dev, taus, out_steps, mask_steps):
+    stream = torch.cuda.current_stream()
+    for o in out_steps:
+        o.zero_()
+    for m in mask_steps:
+        m.fill_(7)
+    for t in range(len(q_steps_dev)):
+        ctx.decode_attn(layer, q_steps_dev[t], taus, out_steps[t], mask_steps[t], stream)
+    torch.cuda.synchronize()
+
+
+def test_layer_128k_host_bases_in_place_and_cached():
+    """The benchmark's layer with its bases in pinned host memory (the pages' CPU
+    tier): zoomed spans read in place over the host link (decode replayed from a
+    captured graph), then through a device basis cache with prefetch (eager,
+    repeated so that cached and uncached spans are both read).  Sampled heads
+    compared with the oracle on the GPU's own artefacts."""
+    s = synth.spec("layers32_128k")
+    layer = 12
+    ctx = _ctx(s, "host", L=1)
+    H = synth.surprisal_batch(s)
+    K, V = synth.kv_layer(s, layer, device=DEV)
+    ctx.build(0, torch.from_numpy(H).to(DEV), K, V, s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    del K, V
+    rates = synth.zoom_targets(s, layer)
+    heads = sorted({int(np.argmax(rates)), 5})
+    seg = gpu_segmentation(ctx, 0)
+    arts = {(0, g): gpu_artefacts(ctx, s, 0, 0, g, seg) for g in heads}
+    steps = 3
+    q_np = np.stack([synth.queries(s, layer, t).numpy().astype(np.float64) for t in range(steps)])
+    q_dev = [torch.from_numpy(q_np[t].astype(np.float32)).to(DEV) for t in range(steps)]
+    taus = taus_for_workload(s, ctx, 0, q_dev, rates, arts, q_np)
+    m_max = ctx.m_max()
+    outs = [torch.zeros(s.B, s.Hq, s.d, device=DEV) for _ in range(steps)]
+    masks = [torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV) for _ in range(steps)]
+    graph_decode(ctx, 0, q_dev, taus, outs, masks)
+    worst, nz = compare_sampled(s, q_np, taus, arts, outs, masks)
+    assert nz > 0
+    ctx.set_basis_cache(256 << 20)
+    for rep in range(3):
+        eager_decode(ctx, 0, q_dev, taus, outs, masks)
+        compare_sampled(s, q_np, taus, arts, outs, masks)
+    st = ctx.stats()
+    assert st["cache_zoomed"] > 0 and st["cache_hits"] > 0, st
+
+
 @pytest.mark.parametrize("rate", [0.01, 0.05, 0.15, 0.30])
 def test_gqa_batch8_128k_zoom_sweep(rate, _gqa_layer):
     """32 query heads on 8 kv heads, batch 8 at n = 131072, ranks 8..64: sampled
@@ -244,7 +291,8 @@ def _gqa_layer():
     del ctx
 
 
-@pytest.mark.parametrize("alpha,rank", [(0.5, 8), (1.0, 16), (2.0, 32)])
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 2.0])
+@pytest.mark.parametrize("rank", [8, 16, 32])
 def test_prefill_builder_128k(alpha, rank):
     """Builder stress: 32 kv heads x 131072 tokens, three-level surprisal spikes, planted
     rank 6-24 span structure; alpha in {0.5, 1, 2} and rank budgets {8, 16, 32}."""

@@ -670,6 +670,72 @@ def test_basis_cache_prefetch_decode(cache_kb, L, mask_offset):
     _decode_compare(s, ctx, arts, 0, 1, taus)
 
 
+def test_basis_cache_then_rank_gates_and_reimport():
+    """Host-resident bases with a device cache: after decodes that fill the cache,
+    soft rank gates (then a re-import of the ungated artefacts) rewrite the
+    store; the next decodes must follow the rewritten factors, not the cached
+    copies of the old ones."""
+    s = _small_bf16().replace(Hq=4, Hkv=4, steps=3)
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    import copy
+    plain = copy.deepcopy(arts)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.1, 0.3, 0.6, 0.05]), s.B)
+    ctx = _ctx(s, "host")
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    ctx.set_basis_cache(4 << 20)
+    for _ in range(2):
+        _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    assert ctx.stats()["cache_hits"] > 0
+    rng = np.random.default_rng(33)
+    for g in range(s.Hkv):
+        a = arts[(0, g)]
+        gk = rng.uniform(0.0, 1.0, (a.m, s.d)).astype(np.float32)
+        gv = rng.uniform(0.0, 1.0, (a.m, s.d)).astype(np.float32)
+        ctx.apply_rank_gates(0, 0, g, gk, gv)
+        a.AK = [O.apply_rank_gates(a.AK[k], gk[k].astype(np.float64), s.kv_dtype) for k in range(a.m)]
+        a.AV = [O.apply_rank_gates(a.AV[k], gv[k].astype(np.float64), s.kv_dtype) for k in range(a.m)]
+    for _ in range(2):
+        _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    # back to the ungated factors by re-import, with the cache warm again
+    T.import_oracle_layer(ctx, 0, segs, plain, s.B, s.Hkv, s.d, s.kv_dtype, set_spans=False, set_layout=False)
+    for _ in range(2):
+        _decode_compare(s, ctx, plain, 0, s.steps, taus)
+
+
+@pytest.mark.parametrize("home", ["device", "host_staged"])
+def test_zoom_counts_match_oracle_masks(home):
+    """Per-(layer, query head) zoom counters: after several decode calls on the
+    oracle's artefacts (a ragged GQA batch, so that heads of a group differ), the
+    counters equal the oracle's zoom masks summed over the calls, head by head;
+    the call count follows; a reset empties both."""
+    s = _gqa_small()
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    qs = _q_steps(s, 0, s.steps)
+    taus = T.thresholds_for(qs, arts, s.G, np.array([0.05, 0.15, 0.3, 0.6, 0.05, 0.02, 1.0, 0.1]), s.B)
+    ctx = _ctx(s, home)
+    T.import_oracle_layer(ctx, 0, segs, arts, s.B, s.Hkv, s.d, s.kv_dtype)
+    counts, calls = ctx.zoom_counts(0)
+    assert calls == 0 and int(counts.sum()) == 0
+    reps = 2
+    for _ in range(reps):
+        _decode_compare(s, ctx, arts, 0, s.steps, taus)
+    expect = np.zeros((s.B, s.Hq), np.int64)
+    for t in range(s.steps):
+        for b in range(s.B):
+            for h in range(s.Hq):
+                _, z, _ = O.decode_head(qs[t, b, h], float(taus[h]), arts[(b, h // s.G)])
+                expect[b, h] += reps * int(z.sum())
+    counts, calls = ctx.zoom_counts(0, reset=True)
+    assert calls == reps * s.steps
+    assert np.array_equal(counts.astype(np.int64), expect), (counts, expect)
+    assert expect.sum() > 0 and len(np.unique(expect)) > 2
+    counts, calls = ctx.zoom_counts(0)
+    assert calls == 0 and int(counts.sum()) == 0
+
+
 # ============================================================================ window re-segmentation
 
 def _export_arts(ctx, s, layer, W=None, dr=0):
