@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 # (source, object name, extra defines): decode.hip builds once per route/attend
 # kernel variant and once for the rest, so the variants compile in parallel
 SOURCES = [("runtime.cpp", "runtime", []), ("decode.hip", "decode", []), ("build.hip", "build", []),
-           ("svd.hip", "svd", [])] + \
+           ("svd.hip", "svd", []), ("noalloc.hip", "noalloc", [])] + \
           [("decode.hip", f"decode_v{i}", [f"-DSEKV_DECODE_VARIANT={i}"]) for i in range(4)]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

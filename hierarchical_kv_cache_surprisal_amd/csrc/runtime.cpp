@@ -1309,6 +1309,11 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
     s = fail(c, SEKV_ERR_HIP, "hipStreamCreate(side)");
   if (s == SEKV_OK && hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming) != hipSuccess)
     s = fail(c, SEKV_ERR_HIP, "hipEventCreate");
+  if (s == SEKV_OK) {
+    // the device address of this GPU's scratch array of sekv_decode_attn_noalloc
+    const hipError_t e = noalloc_scratch_init(k.device);
+    if (e != hipSuccess) s = fail(c, SEKV_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  }
   if (s != SEKV_OK) {
     g_create_err = c->err;
     sekv_destroy(c);
@@ -1706,6 +1711,63 @@ sekv_status sekv_decode_attn_budget(sekv_ctx* c, int32_t layer, const float* q, 
                                     const int32_t* budget, float* out, uint8_t* zoom_mask, hipStream_t stream) {
   if (c && !budget) return fail(c, SEKV_ERR_INVALID, "budget is NULL");
   return decode_step(c, layer, q, tau, budget, out, zoom_mask, stream);
+}
+
+static_assert(kNoAllocScratchBytes == SEKV_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the library");
+
+sekv_status sekv_decode_attn_noalloc(sekv_ctx* c, int32_t layer, const float* q, const float* tau, float* out,
+                                     uint8_t* zoom_mask, hipStream_t stream) {
+  if (!c) return fail(nullptr, SEKV_ERR_INVALID, "NULL context");
+  DevGuard dg(c->cfg.device);
+  TRY(check_layer(c, layer));
+  if (!q || !out) return fail(c, SEKV_ERR_INVALID, "NULL q or out");
+  if (staged(c)) return fail(c, SEKV_ERR_STATE, "staged host bases allocate staging: use sekv_decode_attn");
+  if (c->cache_d && c->cfg.basis_home == SEKV_BASES_HOST)
+    return fail(c, SEKV_ERR_STATE, "a basis cache refills itself: use sekv_decode_attn");
+  LayerState& L = c->layers[layer];
+  LayerSched& S = L.sched;
+  // the layer's segment lists as the last sekv_decode_attn left them; they
+  // must still cover every span and anchor row
+  if (!S.valid || !S.wvalid || S.anchors_changed || S.plan_m != c->m_b || S.plan_na != L.na_l)
+    return fail(c, SEKV_ERR_STATE, "no current work schedule: decode this layer once with sekv_decode_attn");
+  DecodeArgs a;
+  fill_decode_geometry(c, L, a);
+  TRY(thetas(c, tau, a));
+  for (int h = 0; h < kMaxHq; ++h) a.budget[h] = -1;
+  // scratch: partials, projected queries, and the zoom mask when the caller passes none
+  const int d = c->cfg.d_head;
+  auto up = [](size_t n) { return (n + 255) & ~size_t(255); };
+  const size_t slots = (size_t)a.B * a.Hq * S.w_max_parts;
+  const size_t ml_b = up(slots * 2 * sizeof(float)), acc_b = up(slots * d * sizeof(float));
+  const size_t qp_b = a.dr > 0 ? up((size_t)a.B * a.Hq * a.dr * sizeof(float)) : 0;
+  const size_t mask_b = zoom_mask ? 0 : up((size_t)a.B * a.Hq * a.m_max);
+  const size_t need = ml_b + acc_b + qp_b + mask_b;
+  if (need > kNoAllocScratchBytes)
+    return fail(c, SEKV_ERR_INVALID, "decode needs " + std::to_string(need) + " scratch bytes, more than the " +
+                                         std::to_string(kNoAllocScratchBytes) + " of sekv_decode_attn_noalloc");
+  char* base = static_cast<char*>(noalloc_scratch(c->cfg.device));
+  if (!base) return fail(c, SEKV_ERR_STATE, "scratch address of this device not initialised");
+  a.part_ml = reinterpret_cast<float*>(base);
+  a.part_acc = reinterpret_cast<float*>(base + ml_b);
+  if (a.dr > 0) a.qp = reinterpret_cast<float*>(base + ml_b + acc_b);
+  a.mask = zoom_mask ? zoom_mask : reinterpret_cast<uint8_t*>(base + ml_b + acc_b + qp_b);
+  a.q = q;
+  a.out = out;
+  a.wsegs = S.wsegs_d;
+  a.parts_n = S.wparts_d;
+  a.max_parts = S.w_max_parts;
+  a.zcount = L.zcount_d;
+  if (host_store(c)) a.bases = L.bases_hd;
+  c->stats.decode_calls++;
+  if (a.dr > 0) {
+    launch_decode_qproj(d, a, stream);
+    HIPCHK(c, hipGetLastError());
+  }
+  launch_decode_planned(S.n_wg, d, c->bf16, a, stream);
+  HIPCHK(c, hipGetLastError());
+  launch_decode_combine(d, a, stream);
+  HIPCHK(c, hipGetLastError());
+  return SEKV_OK;
 }
 
 sekv_status sekv_route_scores(sekv_ctx* c, int32_t layer, const float* q, float* scores, hipStream_t stream) {

@@ -102,6 +102,17 @@ void launch_decode_qproj(int d, const DecodeArgs& a, hipStream_t s);
 // scores (mode 2) into mask, one workgroup each, grid = B * Hq
 void launch_decode_select(const DecodeArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- no-alloc decode
+
+// Bytes of the per-device scratch array of sekv_decode_attn_noalloc (split-K
+// partials, and the zoom mask when the caller passes none).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // SEKV_NOALLOC_SCRATCH_BYTES of sekv.h
+// Look up the device address of that array on `device`, which must be the
+// current device; once per device, later calls return at once.
+hipError_t noalloc_scratch_init(int device);
+// The address found by noalloc_scratch_init (NULL before it succeeded).
+void* noalloc_scratch(int device);
+
 // ---------------------------------------------------------------- build
 
 struct SegmentArgs {

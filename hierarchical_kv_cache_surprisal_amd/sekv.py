@@ -32,7 +32,7 @@ EXPORTED = ["sekv_create", "sekv_destroy", "sekv_last_error", "sekv_build", "sek
             "sekv_get_stats", "sekv_set_routing", "sekv_import_route_summary",
             "sekv_export_route_summary", "sekv_apply_rank_gates", "sekv_append_tokens", "sekv_get_window",
             "sekv_set_basis_cache", "sekv_reserve_spans", "sekv_append_surprisal", "sekv_resegment_window",
-            "sekv_get_zoom_counts"]
+            "sekv_get_zoom_counts", "sekv_decode_attn_noalloc"]
 
 
 class SekvError(RuntimeError):
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH):
         "sekv_get_bases_layout": (I32, [P, I32, I32, I32, pI32, pI64, pI64]),
         "sekv_decode_attn": (I32, [P, I32, P, C.POINTER(C.c_float), P, P, P]),
         "sekv_decode_attn_budget": (I32, [P, I32, P, C.POINTER(C.c_float), pI32, P, P, P]),
+        "sekv_decode_attn_noalloc": (I32, [P, I32, P, C.POINTER(C.c_float), P, P, P]),
         "sekv_route_scores": (I32, [P, I32, P, P, P]),
         "sekv_zoom_fetch": (I32, [P, I32, pI32, pI32, P, P]),
         "sekv_import_spans": (I32, [P, I32, I32, pI32, pI32, I32, pI32]),
@@ -194,6 +195,12 @@ def sekv_decode_attn_budget(ctx, layer: int, q, tau, budget, out, zoom_mask=None
     k = np.ascontiguousarray(budget, dtype=np.int32)
     _check(load_library().sekv_decode_attn_budget(ctx, layer, _dptr(q), t.ctypes.data_as(C.POINTER(C.c_float)),
                                                   _i32(k), _dptr(out), _dptr(zoom_mask), _stream(stream)), ctx)
+
+
+def sekv_decode_attn_noalloc(ctx, layer: int, q, tau, out, zoom_mask=None, stream=None):
+    t = np.ascontiguousarray(tau, dtype=np.float32)
+    _check(load_library().sekv_decode_attn_noalloc(ctx, layer, _dptr(q), t.ctypes.data_as(C.POINTER(C.c_float)),
+                                                   _dptr(out), _dptr(zoom_mask), _stream(stream)), ctx)
 
 
 def sekv_route_scores(ctx, layer: int, q, scores, stream=None):
@@ -395,7 +402,7 @@ class Context:
     def m_max(self):
         return sekv_get_spans(self.ptr, 0)[3]
 
-    def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None, budget=None):
+    def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None, budget=None, noalloc=False):
         import torch
         qn = self.B * self.Hq * self.d
         _check_tensor(q, "q", torch.float32, qn, self.device)
@@ -405,7 +412,11 @@ class Context:
         _check_host(tau, "tau", self.Hq)
         if budget is not None:
             _check_host(budget, "budget", self.Hq)
-        if budget is None:
+        if noalloc:
+            if budget is not None:
+                raise ValueError("the entry point that allocates nothing takes no budget")
+            sekv_decode_attn_noalloc(self.ptr, layer, q, tau, out, zoom_mask, stream)
+        elif budget is None:
             sekv_decode_attn(self.ptr, layer, q, tau, out, zoom_mask, stream)
         else:
             sekv_decode_attn_budget(self.ptr, layer, q, tau, budget, out, zoom_mask, stream)

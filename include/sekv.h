@@ -191,6 +191,29 @@ sekv_status sekv_decode_attn_budget(sekv_ctx* ctx, int32_t layer, const float* q
                                     const int32_t* budget, float* out, uint8_t* zoom_mask,
                                     hipStream_t stream);
 
+/* sekv_decode_attn for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, with the split-K partials, the projected queries and (when
+ * zoom_mask is NULL) the zoom mask in a device array of
+ * SEKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends.  Calls no hipMalloc, hipFree or other allocating routine, and
+ * no host synchronisation.  Arguments and result as sekv_decode_attn.
+ * It runs the layer's work schedule as the last sekv_decode_attn on that
+ * layer left it (it does not refine the schedule): decode the layer once with
+ * sekv_decode_attn first, and again after appending tokens or re-segmenting.
+ * Every call on one GPU shares that GPU's scratch array: calls that overlap
+ * in time on one GPU (other streams, other contexts, other threads) race and
+ * corrupt each other's results; serialise them on one stream.
+ * DEVICE and HOST bases only (staged bases and the basis cache allocate).
+ * Errors: STATE (layer not built, no current schedule, HOST_STAGED bases or a
+ * basis cache), INVALID (bad arguments, or a decode that needs more scratch
+ * than SEKV_NOALLOC_SCRATCH_BYTES: B*H_q*slots*(2+d)*4 bytes of partials,
+ * slots <= 512, plus B*H_q*d_r*4 and B*H_q*m_max, each rounded up to 256),
+ * HIP. */
+#define SEKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+sekv_status sekv_decode_attn_noalloc(sekv_ctx* ctx, int32_t layer, const float* q, const float* tau,
+                                     float* out, uint8_t* zoom_mask, hipStream_t stream);
+
 /* Stage-1 routing scores only [eq. (5) with the identity projection]:
  *   scores dev float32 [B][H_q][m_max] = q.kbar/(|kbar| sqrt(d)) + ln|S|
  * (ln|S| alone when kbar = 0).  Entries beyond a sequence's m are untouched.
