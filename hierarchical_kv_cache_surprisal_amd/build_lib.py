@@ -27,6 +27,10 @@ SOURCES = [("runtime.cpp", "runtime", []), ("decode.hip", "decode", []), ("build
            ("svd.hip", "svd", []), ("noalloc.hip", "noalloc", [])] + \
           [("decode.hip", f"decode_v{i}", [f"-DSEKV_DECODE_VARIANT={i}"]) for i in range(4)]
 
+# the benchmark's streaming-read reference: a library of its own, outside the SeKV API
+BENCH_SOURCES = [("bench_read.hip", "bench_read", [])]
+BENCH_OUT = os.path.join(PKG, "libsekv_bench.so")
+
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("SEKV_ARCH", "gfx950")
 
@@ -52,18 +56,24 @@ def _compile(job) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {out}")
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = SOURCES + BENCH_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], OUT, verbose)
+    _link(objs[len(SOURCES):], BENCH_OUT, verbose)
     return OUT
 
 

@@ -229,11 +229,12 @@ sekv_status sekv_route_scores(sekv_ctx* ctx, int32_t layer, const float* q, floa
  *           mask of the group's zooming query heads in bits 24..31 (bit i =
  *           query head g*G+i).  Each span id at most once per (b, g).
  *   counts  host int32 [B*H_kv]
- * The copies are issued on `side` (runs of adjacent spans coalesced into one
- * hipMemcpyAsync each), followed by the upload of the staging table, and
- * `done` (may be NULL) is recorded on `side` after the last copy.  The staging
- * table describes exactly these spans until the next fetch; the decode entry
- * point calls this itself.  The host arrays may be reused after `done`.
+ * The copy is one kernel on `side` that reads the mapped pinned store (runs of
+ * adjacent spans coalesced, cut into pieces of at most 32768 elements, one
+ * workgroup each), followed by the upload of the staging table, and `done`
+ * (may be NULL) is recorded on `side` after it.  The staging table describes
+ * exactly these spans until the next fetch; the decode entry point calls this
+ * itself.  The host arrays may be reused after `done`.
  * Errors: STATE (DEVICE bases, layer not built), INVALID (bad id, duplicate),
  * OOM (staging too small), HIP. */
 sekv_status sekv_zoom_fetch(sekv_ctx* ctx, int32_t layer, const int32_t* entries,
@@ -410,7 +411,7 @@ typedef struct sekv_stats {
   uint64_t fetch_calls;           /* sekv_zoom_fetch calls */
   uint64_t spans_fetched;         /* (b, g, span) bases copied to staging */
   uint64_t bytes_fetched;         /* bytes copied host -> staging */
-  uint64_t memcpy_calls;          /* copy calls issued by fetches (a staged fetch: one per run; a cache prefetch: one kernel) */
+  uint64_t memcpy_calls;          /* copy launches issued by fetches (one kernel per staged fetch or cache prefetch) */
   int64_t device_resident_bytes;  /* anchors + summaries (+ routing summaries) + tables (+ bases if DEVICE) */
   int64_t host_basis_bytes;       /* pinned store (HOST) */
   int64_t full_kv_bytes;          /* 2 * L * B * H_kv * n * d * elem: the full cache */
