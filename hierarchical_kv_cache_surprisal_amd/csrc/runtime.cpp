@@ -238,6 +238,7 @@ struct sekv_ctx {
   sekv_stats stats{};
   int anchor_chunk = 256, span_chunk = 64;
   int fill_tasks = 768;           // route workgroups that fill the GPU once (three per CU)
+  bool fill_fixed = false;        // fill_tasks given by the environment: used as is
 };
 
 namespace {
@@ -912,7 +913,8 @@ int plan_lists(sekv_ctx* c, LayerState& L, double budget, bool commit) {
     }
     for (int r = 0; r < na;) {
       if ((int)cur.size() == NS) close_wg();
-      int n = (int)std::floor((budget - cost()) / row);
+      // (clamped before the conversion: a large budget must not overflow int)
+      int n = (int)std::min(std::floor((budget - cost()) / row), (double)(na - r));
       if (n < 1) {
         if (!cur.empty()) {
           close_wg();
@@ -1003,13 +1005,27 @@ sekv_status prepare_plan(sekv_ctx* c, int layer, hipStream_t stream, bool captur
       if (bg < (int)S.zunits.size()) total += S.zunits[bg] * 16384.0;
     }
   }
-  const int nw = c->fill_tasks;
+  // one wave of workgroups: three per CU, or two for large one-head layers
+  // (measured on MI355X: the 128K layers of 32 heads take 33.9 against 34.8 us
+  // per layer-step at two per CU; the 32K layer and the grouped-query batch are
+  // faster at three)
+  int nw = c->fill_tasks;
+  if (!c->fill_fixed && c->G == 1 && total > 64e6) nw = c->fill_tasks * 2 / 3;
   double lo = 0.25 * total / nw, hi = 2.0 * total / nw + 1.0;
-  while (plan_lists(c, L, hi, false) > nw) hi *= 2.0;
-  for (int it = 0; it < 16 && hi - lo > 0.005 * hi; ++it) {
-    const double mid = 0.5 * (lo + hi);
-    if (plan_lists(c, L, mid, false) > nw) lo = mid;
-    else hi = mid;
+  // the share count falls as the budget grows, down to a floor set by the
+  // per-share row and segment limits; when that floor is above nw no budget
+  // reaches nw, and the plan takes the floor (a second wave of workgroups)
+  int n_hi = plan_lists(c, L, hi, false);
+  for (int it = 0; it < 40 && n_hi > nw; ++it) {
+    hi *= 2.0;
+    n_hi = plan_lists(c, L, hi, false);
+  }
+  if (n_hi <= nw) {
+    for (int it = 0; it < 16 && hi - lo > 0.005 * hi; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (plan_lists(c, L, mid, false) > nw) lo = mid;
+      else hi = mid;
+    }
   }
   plan_lists(c, L, hi, true);
   if (S.w_max_parts > kMaxParts) return fail(c, SEKV_ERR_STATE, "too many partial slots per head");
@@ -1336,8 +1352,10 @@ sekv_status sekv_create(const sekv_config* cfg, sekv_ctx** out) {
   c->anchor_chunk = env_int("SEKV_ANCHOR_CHUNK", 256, 16, 1 << 20);
   {
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->cfg.device) == hipSuccess && cus > 0)
-      c->fill_tasks = 3 * cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->cfg.device) == hipSuccess && cus > 0) {
+      c->fill_tasks = env_int("SEKV_FILL_TASKS", 3 * cus, 64, 1 << 16);
+      c->fill_fixed = std::getenv("SEKV_FILL_TASKS") != nullptr;
+    }
   }
   c->span_chunk = env_int("SEKV_SPAN_CHUNK", 64, 8, 1024);
   sekv_status s = dalloc(c, &c->zcounter_d, 4);

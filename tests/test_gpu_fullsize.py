@@ -274,6 +274,31 @@ def test_gqa_batch8_128k_zoom_sweep(rate, _gqa_layer):
     assert nz > 0
 
 
+def test_gqa_plan_floor_above_the_workgroup_target(_gqa_layer, monkeypatch):
+    """A workgroup target below what the per-share limits allow: 64 workgroups,
+    against at least 448 shares for 64 (sequence, kv head) rows of about 3500 spans
+    each (at most 512 span rows per share).  The planner settles for the smallest
+    plan the limits allow (a second wave of workgroups) instead of searching for a
+    budget that does not exist, and the decode matches the oracle on the sampled
+    heads.  The context reads the target when it is created."""
+    s, _, _, arts = _gqa_layer
+    monkeypatch.setenv("SEKV_FILL_TASKS", "64")
+    ctx, H, K, V = build_gpu_layer(s)
+    del K, V
+    torch.cuda.empty_cache()
+    steps = 2
+    q_np = np.stack([synth.queries(s, 0, 200 + t).numpy().astype(np.float64) for t in range(steps)])
+    q_dev = [torch.from_numpy(q_np[t].astype(np.float32)).to(DEV) for t in range(steps)]
+    taus = taus_for_workload(s, ctx, 0, q_dev, np.full(s.Hq, 0.05), arts, q_np)
+    m_max = ctx.m_max()
+    outs = [torch.zeros(s.B, s.Hq, s.d, device=DEV) for _ in range(steps)]
+    masks = [torch.full((s.B, s.Hq, m_max), 7, dtype=torch.uint8, device=DEV) for _ in range(steps)]
+    eager_decode(ctx, 0, q_dev, taus, outs, masks)
+    worst, nz = compare_sampled(s, q_np, taus, arts, outs, masks)
+    assert nz > 0
+    ctx.close()
+
+
 @pytest.fixture(scope="module")
 def _gqa_layer():
     s = synth.spec("gqa_batch8_128k")
