@@ -46,9 +46,13 @@ __device__ __forceinline__ float jacobi_tol(int p) {
 
 // One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
 // of the workgroup; each disjoint pair of a round gets 2 * kSvdThreads / PMAX
-// threads.
+// threads.  The squared norms of the vectors (nrm, LDS, p entries) are computed
+// at the start of every sweep and carried through its rotations: a rotation
+// that zeroes x_i . x_j = g with tangent t maps |x_i|^2 to |x_i|^2 - t g and
+// |x_j|^2 to |x_j|^2 + t g, so a round needs one dot product per pair, not
+// three.
 template <int D, int PMAX>
-__device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
+__device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, float* nrm) {
   constexpr int TPP = 2 * kSvdThreads / PMAX;
   constexpr int EPT = D / TPP;  // elements of a vector per thread of its pair group
   static_assert(D % TPP == 0, "pair groups must tile the vector length");
@@ -57,6 +61,16 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
   if (p < 2) return;
   for (int sweep = 0; sweep < 40; ++sweep) {
     if (threadIdx.x == 0) *s_rot = 0;
+    for (int i = pi; i < p; i += kSvdThreads / TPP) {
+      float sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const float x = Xv[i * XS + li + k * TPP];
+        sq += x * x;
+      }
+      sq = group_sum<TPP>(sq);
+      if (li == 0) nrm[i] = sq;
+    }
     __syncthreads();
     for (int t = 0; t < pe - 1; ++t) {
       int i = -1, j = -1;
@@ -70,23 +84,21 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
         }
       }
       const bool act = i >= 0 && i < p && j < p;
-      // the pair's elements stay in registers from the dot products to the rotation
+      // the pair's elements stay in registers from the dot product to the rotation
       float u[EPT], v[EPT];
       float al = 0.f, be = 0.f, ga = 0.f;
       float* xi = Xv + (act ? i : 0) * XS + li;
       float* xj = Xv + (act ? j : 0) * XS + li;
       if (act) {
+        al = nrm[i];
+        be = nrm[j];
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
           u[k] = xi[k * TPP];
           v[k] = xj[k * TPP];
-          al += u[k] * u[k];
-          be += v[k] * v[k];
           ga += u[k] * v[k];
         }
       }
-      al = group_sum<TPP>(al);
-      be = group_sum<TPP>(be);
       ga = group_sum<TPP>(ga);
       if (act && al > 0.f && be > 0.f && fabsf(ga) > tol * sqrtf(al) * sqrtf(be)) {
         const float zeta = (be - al) / (2.f * ga);
@@ -100,7 +112,11 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot) {
           xi[k * TPP] = cs * u[k] - sn * v[k];
           xj[k * TPP] = sn * u[k] + cs * v[k];
         }
-        if (li == 0) *s_rot = 1;
+        if (li == 0) {
+          *s_rot = 1;
+          nrm[i] = al - tt * ga;
+          nrm[j] = be + tt * ga;
+        }
       }
       __syncthreads();
     }
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
     X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
   }
   __syncthreads();
-  jacobi_sweeps<D, PMAX>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot);
+  jacobi_sweeps<D, PMAX>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot, sig);
   __syncthreads();
   rank_by_norm(X, XS, D, p.c, p.r, sig, order);
 
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
     Rr[row * XS + col] = rv[u];
   }
   __syncthreads();
-  jacobi_sweeps<D, D>(Rr, XS, D, jacobi_tol<T>(D), &s_rot);
+  jacobi_sweeps<D, D>(Rr, XS, D, jacobi_tol<T>(D), &s_rot, sig);
   __syncthreads();
   rank_by_norm(Rr, XS, D, D, p.r, sig, order);
 
