@@ -1666,7 +1666,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   constexpr int NT = kCombineThreads;
   constexpr int C4 = D / 4;
   constexpr int PG = NT / C4;
-  constexpr int UN = 8;
+#ifndef SEKV_COMBINE_UN
+#define SEKV_COMBINE_UN 8
+#endif
+  constexpr int UN = SEKV_COMBINE_UN;
   __shared__ float gm_s[PG], gl_s[PG];
   __shared__ float4 ga_s[PG][C4];
   const int bh = blockIdx.x;

@@ -12,7 +12,10 @@ constexpr int kMaxBg = 512;       // sequences x kv heads supported by the decod
 constexpr int kThreads = 256;     // 4 wave64 per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxParts = 512;  // split-K partial slots per (sequence, query head)
-constexpr int kCombineThreads = 512;
+#ifndef SEKV_COMBINE_THREADS
+#define SEKV_COMBINE_THREADS 256
+#endif
+constexpr int kCombineThreads = SEKV_COMBINE_THREADS;
 constexpr int kMaxSpanChunk = 256;  // span rows per span task
 
 // Planned layer-step kernel: every workgroup runs a short list of segments
