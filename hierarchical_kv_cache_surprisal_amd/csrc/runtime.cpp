@@ -864,7 +864,7 @@ int plan_lists(sekv_ctx* c, LayerState& L, double budget, bool commit) {
   // its dependent round of loads (tuned on the same layer)
   const double row = 2.0 * d * (double)c->esz;
   const double span_row = row * env_int("SEKV_SPAN_COST", 200, 50, 1000) / 100.0;
-  const double unit_cost = env_int("SEKV_UNIT_COST", 6144, 0, 1 << 24);
+  const double unit_cost = env_int("SEKV_UNIT_COST", 12288, 0, 1 << 24);
   const double zdev = env_int("SEKV_ZOOM_DEV", 150, 0, 1000) / 100.0;
   std::vector<int4> segs;
   std::vector<int32_t> parts(BH, 0);
