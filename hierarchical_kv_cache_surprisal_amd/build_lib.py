@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 # (source, object name, extra defines): decode.hip builds once per route/attend
 # kernel variant and once for the rest, so the variants compile in parallel
-SOURCES = [("runtime.cpp", "runtime", []), ("decode.hip", "decode", []), ("build.hip", "build", []),
+SOURCES = [("runtime.cpp", "runtime", []), ("plan.cpp", "plan", []), ("decode.hip", "decode", []), ("build.hip", "build", []),
            ("svd.hip", "svd", []), ("noalloc.hip", "noalloc", [])] + \
           [("decode.hip", f"decode_v{i}", [f"-DSEKV_DECODE_VARIANT={i}"]) for i in range(4)]
 

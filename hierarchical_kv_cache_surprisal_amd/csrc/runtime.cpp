@@ -5,6 +5,7 @@
 // partials, arrival tickets), the zoom fetch path (pinned tables, device
 // staging, a side stream) and launches the HIP kernels.
 #include "sekv.h"
+#include "plan.h"
 #include "sekv_internal.h"
 
 #include <algorithm>
@@ -843,105 +844,37 @@ sekv_status finish_sched(sekv_ctx* c, int layer, hipStream_t stream, bool captur
   return SEKV_OK;
 }
 
-// Segment lists of the planned kernel.  The work of a layer-step is the
-// sequence "span rows of (b, g), anchor rows of (b, g)" over (b, g) in order.
-// Each row costs the bytes it streams (summaries or anchor keys and values).
-// A span adds, for each of its token-tile units, the unit's bases and a fixed
-// cost (its latency), times the span's zoom frequency over recent calls: the
-// zoom sets move from call to call (spans near the threshold flip with the
-// query), so a share is charged its expected zoom work plus z standard
-// deviations of it.  The sequence is cut into shares of at most `budget`, each
-// a list of at most wg_segments(G) segments and kMaxWgSpanRows span rows;
-// every segment gets the next partial slot of its (b, g).  Returns the number
-// of shares.
-int plan_lists(sekv_ctx* c, LayerState& L, double budget, bool commit) {
+// Inputs of the planner (plan.h) for one layer: the span table, ranks and
+// zoom frequencies, and the cost knobs (environment overrides for tuning:
+// SEKV_SPAN_COST in percent of an anchor row, SEKV_UNIT_COST in bytes,
+// SEKV_ZOOM_DEV in hundredths).  The costs were tuned on the 128K benchmark
+// layer: a span row, which also routes, takes about twice as long as an anchor
+// row, and a token-tile unit costs its bases plus 12 KB for its dependent
+// round of loads.  `cnt` holds the per-sequence span-count pointers.
+PlanInput plan_input(sekv_ctx* c, LayerState& L, std::vector<const int32_t*>& cnt) {
   LayerSched& S = L.sched;
-  const int B = c->cfg.batch, Hkv = c->cfg.n_kv_heads, BH = B * Hkv, d = c->cfg.d_head;
-  const int NS = wg_segments(c->G), mm = c->m_max;
-  // costs in bytes of anchor streaming: a span row, which also routes, takes
-  // about twice as long as an anchor row (per-workgroup timings on the 128K
-  // benchmark layer); a token-tile unit costs its bases plus a fixed amount for
-  // its dependent round of loads (tuned on the same layer)
-  const double row = 2.0 * d * (double)c->esz;
-  const double span_row = row * env_int("SEKV_SPAN_COST", 200, 50, 1000) / 100.0;
-  const double unit_cost = env_int("SEKV_UNIT_COST", 12288, 0, 1 << 24);
-  const double zdev = env_int("SEKV_ZOOM_DEV", 150, 0, 1000) / 100.0;
-  std::vector<int4> segs;
-  std::vector<int32_t> parts(BH, 0);
-  std::vector<int4> cur;
-  int span_rows = 0, nwg = 0;
-  double mean = 0.0, var = 0.0;
-  auto cost = [&]() { return mean + zdev * std::sqrt(var); };
-  auto close_wg = [&]() {
-    if (cur.empty()) return;
-    if (commit) {
-      for (auto& x : cur) segs.push_back(x);
-      for (int i = (int)cur.size(); i < NS; ++i) segs.push_back(make_int4(0, 0, 0, 0));
-    }
-    cur.clear();
-    span_rows = 0;
-    mean = var = 0.0;
-    ++nwg;
-  };
-  for (int bg = 0; bg < BH; ++bg) {
-    const int m = c->m_b[bg / Hkv], na = L.na_l[bg / Hkv];
-    for (int k = 0; k < m;) {
-      if ((int)cur.size() == NS || span_rows >= kMaxWgSpanRows) close_wg();
-      int n = 0;
-      while (k < m && span_rows < kMaxWgSpanRows) {
-        const float pz = S.zprob[(size_t)bg * mm + k];
-        double zm = 0.0, zv = 0.0;
-        if (pz > 0.f) {
-          const int cnt = c->mcount[bg / Hkv][k], r = L.rank_h[(size_t)bg * mm + k];
-          const double work = 2.0 * (pad8(cnt) + d) * r * c->esz + ((cnt + d - 1) / d) * unit_cost;
-          zm = pz * work;
-          zv = pz * (1.0 - pz) * work * work;
-        }
-        const double m2 = mean + span_row + zm, v2 = var + zv;
-        if (n > 0 || !cur.empty()) {
-          // the row goes to the next share when it would take this one over budget
-          if (m2 + zdev * std::sqrt(v2) > budget && cost() > 0.5 * budget) break;
-        }
-        mean = m2;
-        var = v2;
-        ++k;
-        ++n;
-        ++span_rows;
-      }
-      if (n > 0) cur.push_back(make_int4(bg, k - n, n, parts[bg]++));
-      if (k < m) close_wg();
-    }
-    for (int r = 0; r < na;) {
-      if ((int)cur.size() == NS) close_wg();
-      // (clamped before the conversion: a large budget must not overflow int)
-      int n = (int)std::min(std::floor((budget - cost()) / row), (double)(na - r));
-      if (n < 1) {
-        if (!cur.empty()) {
-          close_wg();
-          continue;
-        }
-        n = 1;
-      }
-      n = std::min(n, na - r);
-      mean += n * row;
-      cur.push_back(make_int4(bg | (int)0x80000000u, r, n, parts[bg]++));
-      r += n;
-      if (r < na) close_wg();
-    }
-  }
-  close_wg();
-  if (commit) {
-    S.wsegs.swap(segs);
-    S.wparts.swap(parts);
-    S.n_wg = nwg;
-    S.w_max_parts = 1;
-    for (int bg = 0; bg < BH; ++bg) S.w_max_parts = std::max(S.w_max_parts, S.wparts[bg]);
-  } else {
-    int mp = 1;
-    for (int bg = 0; bg < BH; ++bg) mp = std::max(mp, parts[bg]);
-    if (mp > kMaxParts) return INT32_MAX;  // too many slots for one (b, g): a larger budget is needed
-  }
-  return nwg;
+  const int B = c->cfg.batch;
+  cnt.resize(B);
+  for (int b = 0; b < B; ++b) cnt[b] = c->mcount[b].data();
+  PlanInput in;
+  in.B = B;
+  in.Hkv = c->cfg.n_kv_heads;
+  in.d = c->cfg.d_head;
+  in.esz = c->esz;
+  in.m_max = c->m_max;
+  in.segs_per_share = wg_segments(c->G);
+  in.max_span_rows = kMaxWgSpanRows;
+  in.max_parts = kMaxParts;
+  in.m = c->m_b.data();
+  in.na = L.na_l.data();
+  in.count = cnt.data();
+  in.rank = L.rank_h.data();
+  in.zprob = S.zprob.data();
+  in.zunits = S.zunits.empty() ? nullptr : S.zunits.data();
+  in.span_cost = env_int("SEKV_SPAN_COST", 200, 50, 1000) / 100.0;
+  in.unit_cost = env_int("SEKV_UNIT_COST", 12288, 0, 1 << 24);
+  in.zdev = env_int("SEKV_ZOOM_DEV", 150, 0, 1000) / 100.0;
+  return in;
 }
 
 // Refresh the segment lists of a layer before a planned launch on `stream`
@@ -994,40 +927,23 @@ sekv_status prepare_plan(sekv_ctx* c, int layer, hipStream_t stream, bool captur
     replan |= S.zsamples <= 4 || moved > 0.15 * tot + 2.0;
   }
   if (!replan || S.mpending) return SEKV_OK;
-  // the smallest budget that cuts the work into at most fill_tasks shares,
-  // bracketed around the mean share of the expected work
-  double total = 0.0;
-  {
-    const double row = 2.0 * d * (double)c->esz;
-    for (int bg = 0; bg < BH; ++bg) {
-      const int b = bg / Hkv;
-      total += (double)c->m_b[b] * 2.0 * row + (double)L.na_l[b] * row;
-      if (bg < (int)S.zunits.size()) total += S.zunits[bg] * 16384.0;
-    }
-  }
-  // one wave of workgroups: three per CU, or two for large one-head layers
-  // (measured on MI355X: the 128K layers of 32 heads take 33.9 against 34.8 us
-  // per layer-step at two per CU; the 32K layer and the grouped-query batch are
-  // faster at three)
+  // the smallest budget that cuts the work into at most the target number of
+  // shares: one wave of workgroups, three per CU, or two for large one-head
+  // layers (measured on MI355X: the 128K layers of 32 heads take 33.9 against
+  // 34.8 us per layer-step at two per CU; the 32K layer and the grouped-query
+  // batch are faster at three)
+  std::vector<const int32_t*> cnt;
+  const PlanInput in = plan_input(c, L, cnt);
   int nw = c->fill_tasks;
-  if (!c->fill_fixed && c->G == 1 && total > 64e6) nw = c->fill_tasks * 2 / 3;
-  double lo = 0.25 * total / nw, hi = 2.0 * total / nw + 1.0;
-  // the share count falls as the budget grows, down to a floor set by the
-  // per-share row and segment limits; when that floor is above nw no budget
-  // reaches nw, and the plan takes the floor (a second wave of workgroups)
-  int n_hi = plan_lists(c, L, hi, false);
-  for (int it = 0; it < 40 && n_hi > nw; ++it) {
-    hi *= 2.0;
-    n_hi = plan_lists(c, L, hi, false);
-  }
-  if (n_hi <= nw) {
-    for (int it = 0; it < 16 && hi - lo > 0.005 * hi; ++it) {
-      const double mid = 0.5 * (lo + hi);
-      if (plan_lists(c, L, mid, false) > nw) lo = mid;
-      else hi = mid;
-    }
-  }
-  plan_lists(c, L, hi, true);
+  if (!c->fill_fixed && c->G == 1 && plan_expected_bytes(in) > 64e6) nw = c->fill_tasks * 2 / 3;
+  PlanOut po;
+  plan_shares(in, nw, &po);
+  S.wsegs.resize(po.segs.size());
+  for (size_t i = 0; i < po.segs.size(); ++i)
+    S.wsegs[i] = make_int4(po.segs[i].x, po.segs[i].y, po.segs[i].z, po.segs[i].w);
+  S.wparts.swap(po.parts);
+  S.n_wg = po.n_shares;
+  S.w_max_parts = po.max_parts;
   if (S.w_max_parts > kMaxParts) return fail(c, SEKV_ERR_STATE, "too many partial slots per head");
   S.zunits_plan = S.zunits;
   S.plan_m = c->m_b;
