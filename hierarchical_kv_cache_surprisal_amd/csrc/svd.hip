@@ -13,15 +13,18 @@
 // rows (streamed again from X), so J is never stored.
 //
 // Tall spans (c > 128): the d x d Gram matrix X^T X is accumulated in fp64
-// (upper triangle, packed), factored by Cholesky (R^T R, semidefinite pivots
+// on the matrix cores (upper triangle, packed), factored by Cholesky (R^T R, semidefinite pivots
 // dropped) and one-sided Jacobi orthogonalises the rows of R (R = J N with
 // orthogonal rows n_i, so R^T R = N^T N and the right singular vectors of X
 // are the normalised n_i); sigma_i = |n_i| and A = X V_r is streamed from X.
 // fp64 for the Gram and the factorisation keeps the squared condition number
 // away from fp32 rounding.
 //
-// Rotations are applied to disjoint pairs in parallel (round-robin tournament
-// ordering), one group of 512/PMAX threads per pair.  Neither path keeps the
+// The two products that are matrix products, the Gram and A = X V_r, run on
+// the matrix cores (fp64 and fp32 MFMA).  The rotations are plane updates of
+// two vectors at a time and stay on the vector ALUs: they are applied to
+// disjoint pairs in parallel (round-robin tournament ordering), one group of
+// 512/PMAX threads per pair.  Neither path keeps the
 // rotations, so a workgroup needs about 78 KB of LDS and two fit on a CU.
 #include "sekv_device.h"
 
@@ -35,6 +38,10 @@ constexpr int kSvdThreads = 512;  // 8 waves per workgroup
 // their row; rows of neighbouring pairs then start 8 banks apart and a
 // half-wave's 32 reads hit 32 different banks (with D + 1, about 11).
 constexpr int kVecPad = 8;
+
+// Matrix-core accumulator tiles (one 16 x 16 tile: 4 values per lane).
+typedef float flt4 __attribute__((ext_vector_type(4)));
+typedef double dbl4 __attribute__((ext_vector_type(4)));
 
 // Rotation threshold: a pair is rotated while |x_i . x_j| > tol |x_i| |x_j|.
 // fp32 storage: p ulps of fp32; bf16 storage: 1e-4, far below the storage
@@ -173,14 +180,27 @@ __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt
 
 // ---------------------------------------------------------------- short spans
 
-// A^T [r][c8] = (X V_r)^T from the original rows of X (streamed ROWS at a time
+// A^T [r][c8] = (X V_r)^T from the original rows of X (streamed 16 at a time
 // through Xr), with V_i = Vt[order[kk]] / sig[order[kk]]; zero beyond c.
-template <int D, typename T, int ROWS, int XS>
+// A block of 16 rows times 16 ranks is one fp32 matrix-core product over the
+// D columns (v_mfma_f32_16x16x4f32, fp32 products and sums like the scalar
+// dot products): wave w takes ranks 16w .. 16w + 15 (r <= D <= 8 * 16).
+// Operand lanes: A[m][k] = X[m][e0 + k] and B[k][n] = V[n][e0 + k] in lane
+// m + 16k (resp. n + 16k); the result D[4 (l / 16) + i][l % 16] in lane l.
+template <int D, typename T, int XS>
 __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src, float* Xr, const float* Vt,
                                   int VS, const float* sig, const int* order) {
+  constexpr int ROWS = 16;
   T* At = block_ptr<T, D>(a, p, false);
   const int c8 = (int)pad8(p.c);
   const int r = p.r;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kk = wave * 16 + (lane & 15);  // this lane's rank in the B operand and the result
+  const bool wact = wave * 16 < r;         // uniform over the wave
+  const int vi = (kk < r) ? order[kk] : 0;
+  const float si = (kk < r) ? sig[vi] : 0.f;
+  const float* vrow = Vt + vi * VS + (lane >> 4);
+  const float* xrow = Xr + (lane & 15) * XS + (lane >> 4);
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < ROWS * D; idx += kSvdThreads) {
@@ -188,17 +208,18 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
       Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * r; idx += kSvdThreads) {
-      const int t = idx % ROWS, kk = idx / ROWS;
-      if (t0 + t >= p.c) continue;
-      const int i = order[kk];
-      const float si = sig[i];
-      float s = 0.f;
-      if (si > 0.f) {
-        for (int e = 0; e < D; ++e) s += Xr[t * XS + e] * Vt[i * VS + e];
-        s /= si;
+    if (wact) {
+      flt4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int e0 = 0; e0 < D; e0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[e0], kk < r ? vrow[e0] : 0.f, acc, 0, 0, 0);
+      if (kk < r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 4 * (lane >> 4) + i;
+          if (t < p.c) At[(size_t)kk * c8 + t] = Elem<T>::from_f(si > 0.f ? acc[i] / si : 0.f);
+        }
       }
-      At[(size_t)kk * c8 + t0 + t] = Elem<T>::from_f(s);
     }
   }
   for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kSvdThreads) {
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
     const float s = sig[i];
     Bt[idx] = Elem<T>::from_f(s > 0.f ? X[i * XS + e] / s : 0.f);
   }
-  store_a_from_rows<D, T, ROWS, XS>(a, p, src, Xr, X, XS, sig, order);
+  store_a_from_rows<D, T, XS>(a, p, src, Xr, X, XS, sig, order);
 }
 
 // ---------------------------------------------------------------- tall spans
@@ -253,10 +274,13 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   extern __shared__ double smd[];
   constexpr int XS = D + kVecPad;  // float vector stride
   constexpr int ROWS = 16;        // X rows staged per step
-  constexpr int NB = D / 8;       // 8-column Gram blocks per row of blocks
+  constexpr int GS = D + 16;      // staging row stride: the 4 row groups of a tile read distinct banks
+  constexpr int GT = D / 16;      // 16 x 16 Gram tiles per side
+  constexpr int NT = GT * (GT + 1) / 2;
+  constexpr int TPW = (NT + 7) / 8;  // upper-triangle tiles per wave
   constexpr int NP = D * (D + 1) / 2;
   double* Gp = smd;                                       // [NP] packed upper Gram, then R
-  float* Xs = reinterpret_cast<float*>(smd + NP);         // [ROWS][D]
+  float* Xs = reinterpret_cast<float*>(smd + NP);         // [ROWS][GS]
   __shared__ float sig[D];
   __shared__ int order[D];
   __shared__ int s_rot;
@@ -265,45 +289,52 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
 
-  // 1. Gram matrix in fp64: 4 x 8 blocks (rows 4 bi.., columns 8 bj..) that
-  // reach the upper triangle; 32 fp64 accumulators per thread keep two
-  // workgroups per CU
-  const int bi = threadIdx.x / NB, bj = threadIdx.x % NB;
-  const bool gact = bi < 2 * NB && bj * 8 + 7 >= bi * 4;
-  double gacc[4][8];
+  // 1. Gram matrix in fp64 on the matrix cores: tile (I, J), I <= J, of
+  // G = X^T X accumulates v_mfma_f64_16x16x4f64 over 4 staged rows at a time
+  // (A[m][k] = X[k][16 I + m] and B[k][n] = X[k][16 J + n] in lane m + 16 k,
+  // resp. n + 16 k; exact fp64 products of the stored values, fp64 sums).
+  // Wave w takes tiles w, w + 8, ...
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ti[TPW], tj[TPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < TPW; ++u) {
+    int q = wave + 8 * u, I = 0;
+    while (I < GT && q >= GT - I) {
+      q -= GT - I;
+      ++I;
+    }
+    ti[u] = I;
+    tj[u] = I + q;  // I == GT: no tile (q >= NT)
+  }
+  dbl4 gacc[TPW];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) gacc[u][v] = 0.0;
+  for (int u = 0; u < TPW; ++u) gacc[u] = dbl4{0.0, 0.0, 0.0, 0.0};
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     for (int idx = threadIdx.x; idx < ROWS * D; idx += kSvdThreads) {
       const int t = idx / D, e = idx % D;
-      Xs[idx] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
+      Xs[t * GS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
     __syncthreads();
-    if (gact) {
-      for (int t = 0; t < ROWS; ++t) {
-        double xa[4], xb[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) xa[u] = (double)Xs[t * D + bi * 4 + u];
+    for (int k0 = 0; k0 < ROWS; k0 += 4) {
+      const float* xr = Xs + (k0 + (lane >> 4)) * GS + (lane & 15);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) xb[v] = (double)Xs[t * D + bj * 8 + v];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 8; ++v) gacc[u][v] = fma(xa[u], xb[v], gacc[u][v]);
-      }
+      for (int u = 0; u < TPW; ++u)
+        if (ti[u] < GT)  // uniform over the wave
+          gacc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xr[16 * ti[u]], (double)xr[16 * tj[u]], gacc[u],
+                                                         0, 0, 0);
     }
     __syncthreads();
   }
-  if (gact) {
+  // the fp64 result is row-interleaved: lane l holds G[16 I + l / 16 + 4 i][16 J + l % 16], i < 4
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < TPW; ++u) {
+    if (ti[u] >= GT) continue;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int gi = bi * 4 + u, gj = bj * 8 + v;
-        if (gj >= gi) Gp[upk<D>(gi, gj)] = gacc[u][v];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int gi = 16 * ti[u] + (lane >> 4) + 4 * i, gj = 16 * tj[u] + (lane & 15);
+      if (gj >= gi) Gp[upk<D>(gi, gj)] = gacc[u][i];
+    }
   }
   __syncthreads();
 
@@ -366,7 +397,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   }
   // 5. A = X V_r, streamed from X through the staging rows
   float* Xr = Rr + D * XS;  // [ROWS][XS], after the rows of R
-  store_a_from_rows<D, T, ROWS, XS>(a, p, src, Xr, Rr, XS, sig, order);
+  store_a_from_rows<D, T, XS>(a, p, src, Xr, Rr, XS, sig, order);
 }
 
 // The kernels take more than 64 KB of dynamic LDS, which needs the attribute
@@ -385,7 +416,7 @@ hipError_t launch_rows(const SvdArgs& a, hipStream_t s) {
 template <int D, typename T>
 hipError_t launch_tall(const SvdArgs& a, hipStream_t s) {
   // max(packed fp64 Gram + 16 staged rows, fp32 rows of R + 16 staged rows)
-  const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * D;
+  const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * (D + 16);
   const size_t rows = sizeof(float) * (D + 16) * (D + kVecPad);
   const size_t lds = gram > rows ? gram : rows;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
