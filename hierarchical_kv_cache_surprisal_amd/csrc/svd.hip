@@ -79,17 +79,16 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
       if (li == 0) nrm[i] = sq;
     }
     __syncthreads();
-    for (int t = 0; t < pe - 1; ++t) {
-      int i = -1, j = -1;
-      if (pi < pe / 2) {
-        if (pi == 0) {
-          i = pe - 1;
-          j = t;
-        } else {
-          i = (t + pi) % (pe - 1);
-          j = (t - pi + pe - 1) % (pe - 1);
-        }
-      }
+    // round t pairs (pe - 1, t) in group 0 and ((t + pi) mod (pe - 1),
+    // (t - pi) mod (pe - 1)) in group pi > 0: both indices advance by one per
+    // round, so they are carried instead of recomputed with two modulos
+    const int pm = pe - 1;
+    int ia = pi == 0 ? pm : pi;
+    int ja = pi == 0 ? 0 : pm - pi;
+    for (int t = 0; t < pm; ++t) {
+      const int i = pi < pe / 2 ? ia : -1, j = pi < pe / 2 ? ja : -1;
+      if (pi != 0) ia = ia + 1 == pm ? 0 : ia + 1;
+      ja = ja + 1 == pm ? 0 : ja + 1;
       const bool act = i >= 0 && i < p && j < p;
       // the pair's elements stay in registers from the dot product to the rotation
       float u[EPT], v[EPT];
@@ -107,12 +106,18 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
         }
       }
       ga = group_sum<TPP>(ga);
-      if (act && al > 0.f && be > 0.f && fabsf(ga) > tol * sqrtf(al) * sqrtf(be)) {
-        const float zeta = (be - al) / (2.f * ga);
+      // (the threshold test needs no correctly rounded square roots)
+      if (act && al > 0.f && be > 0.f &&
+          fabsf(ga) > tol * __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be)) {
+        // the angle needs no correctly rounded division: v_rcp_f32 and
+        // v_rsq_f32 (1 ulp) keep cs^2 + sn^2 = 1 to a few ulps, and a pair left
+        // slightly off orthogonal is rotated again in a later round
+        const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
         const float az = fabsf(zeta);
-        const float tt = (az > 1e15f) ? 0.5f / zeta
-                                     : copysignf(1.f, zeta) / (az + sqrtf(1.f + zeta * zeta));
-        const float cs = 1.f / sqrtf(1.f + tt * tt);
+        const float tt = (az > 1e15f) ? 0.5f * __builtin_amdgcn_rcpf(zeta)
+                                     : copysignf(__builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(1.f + zeta * zeta)),
+                                                 zeta);
+        const float cs = __builtin_amdgcn_rsqf(1.f + tt * tt);
         const float sn = cs * tt;
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
