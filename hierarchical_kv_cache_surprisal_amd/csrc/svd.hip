@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   __shared__ float sig[D];
   __shared__ int order[D];
   __shared__ int s_rot;
-  __shared__ double s_rkk, s_tol;
+  __shared__ double s_tol;
 
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
@@ -343,30 +343,39 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   }
   __syncthreads();
 
-  // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped
+  // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped.  One
+  // barrier per column: column kc's pass subtracts g_ki g_kj / g_kk from the
+  // trailing entries (i, j), kc < i <= j, with row kc as the previous passes
+  // left it, and scales row kc - 1 to R (nothing reads it any more).  Thread t
+  // takes column kc + 1 + ... = t mod D and every TPC-th row of it, so no
+  // index is divided per entry.
   if (threadIdx.x == 0) {
     double mx = 0.0;
     for (int i = 0; i < D; ++i) mx = fmax(mx, Gp[upk<D>(i, i)]);
     s_tol = mx * (double)D * 4.440892098500626e-16;
   }
   __syncthreads();
-  const double tolc = s_tol;
-  for (int kc = 0; kc < D; ++kc) {
-    if (threadIdx.x == 0) {
+  {
+    constexpr int TPC = kSvdThreads / D;  // threads per column
+    static_assert(kSvdThreads % D == 0, "whole columns per thread group");
+    const double tolc = s_tol;
+    const int col = threadIdx.x % D, ph = threadIdx.x / D;
+    double prev = 0.0;  // the pivot of the previous column, as this thread read it
+    for (int kc = 0; kc <= D; ++kc) {
+      // scale row kc - 1 (its pivot was read at the previous column)
+      if (kc > 0 && ph == 0 && col >= kc - 1) {
+        const int q = upk<D>(kc - 1, col);
+        const double r = prev > tolc ? sqrt(prev) : 0.0;
+        Gp[q] = r > 0.0 ? (col == kc - 1 ? r : Gp[q] / r) : 0.0;
+      }
+      if (kc == D) break;
       const double piv = Gp[upk<D>(kc, kc)];
-      s_rkk = piv > tolc ? sqrt(piv) : 0.0;
-    }
-    __syncthreads();
-    const double rkk = s_rkk;
-    for (int j = kc + threadIdx.x; j < D; j += kSvdThreads) {
-      const int q = upk<D>(kc, j);
-      Gp[q] = rkk > 0.0 ? (j == kc ? rkk : Gp[q] / rkk) : 0.0;
-    }
-    __syncthreads();
-    const int w = D - kc - 1;
-    for (int idx = threadIdx.x; idx < w * w; idx += kSvdThreads) {
-      const int i = kc + 1 + idx / w, j = kc + 1 + idx % w;
-      if (j >= i) Gp[upk<D>(i, j)] -= Gp[upk<D>(kc, i)] * Gp[upk<D>(kc, j)];
+      if (piv > tolc && col > kc) {
+        const double gj = Gp[upk<D>(kc, col)] / piv;
+        for (int i = kc + 1 + ph; i <= col; i += TPC) Gp[upk<D>(i, col)] -= Gp[upk<D>(kc, i)] * gj;
+      }
+      prev = piv;
+      __syncthreads();
     }
     __syncthreads();
   }
