@@ -13,8 +13,9 @@
 // rows (streamed again from X), so J is never stored.
 //
 // Tall spans (c > 128): the d x d Gram matrix X^T X is accumulated in fp64
-// on the matrix cores (upper triangle, packed), factored by Cholesky (R^T R, semidefinite pivots
-// dropped) and one-sided Jacobi orthogonalises the rows of R (R = J N with
+// on the matrix cores (the upper triangle of 16 x 16 tiles), factored by a
+// blocked Cholesky (R^T R, semidefinite pivots dropped, the trailing updates
+// on the matrix cores) and one-sided Jacobi orthogonalises the rows of R (R = J N with
 // orthogonal rows n_i, so R^T R = N^T N and the right singular vectors of X
 // are the normalised n_i); sigma_i = |n_i| and A = X V_r is streamed from X.
 // fp64 for the Gram and the factorisation keeps the squared condition number
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
 
 // ---------------------------------------------------------------- tall spans
 
-// Packed upper triangle of a D x D symmetric matrix: (i, j), j >= i.
-template <int D>
-__device__ __forceinline__ int upk(int i, int j) {
-  return i * D - (i * (i - 1)) / 2 + (j - i);
+// Upper-triangle tiles of a GT x GT grid of 16 x 16 tiles: (I, J), J >= I.
+template <int GT>
+__device__ __forceinline__ int utile(int I, int J) {
+  return I * GT - (I * (I - 1)) / 2 + (J - I);
 }
 
 template <int D, typename T>
@@ -283,9 +284,10 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   constexpr int GT = D / 16;      // 16 x 16 Gram tiles per side
   constexpr int NT = GT * (GT + 1) / 2;
   constexpr int TPW = (NT + 7) / 8;  // upper-triangle tiles per wave
-  constexpr int NP = D * (D + 1) / 2;
-  double* Gp = smd;                                       // [NP] packed upper Gram, then R
-  float* Xs = reinterpret_cast<float*>(smd + NP);         // [ROWS][GS]
+  // the Gram, then R, as NT row-major 16 x 16 fp64 tiles (the diagonal
+  // tiles whole); the staged rows of X share the space before the tiles exist
+  double* Tt = smd;                                       // [NT][16][16]
+  float* Xs = reinterpret_cast<float*>(smd);              // [ROWS][GS]
   __shared__ float sig[D];
   __shared__ int order[D];
   __shared__ int s_rot;
@@ -332,52 +334,89 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
     __syncthreads();
   }
   // the fp64 result is row-interleaved: lane l holds G[16 I + l / 16 + 4 i][16 J + l % 16], i < 4
+  // (the staging rows are dead: the loop ended with a barrier)
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     if (ti[u] >= GT) continue;
+    double* tile = Tt + utile<GT>(ti[u], tj[u]) * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = 16 * ti[u] + (lane >> 4) + 4 * i, gj = 16 * tj[u] + (lane & 15);
-      if (gj >= gi) Gp[upk<D>(gi, gj)] = gacc[u][i];
-    }
+    for (int i = 0; i < 4; ++i) tile[((lane >> 4) + 4 * i) * 16 + (lane & 15)] = gacc[u][i];
   }
   __syncthreads();
 
-  // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped.  One
-  // barrier per column: column kc's pass subtracts g_ki g_kj / g_kk from the
-  // trailing entries (i, j), kc < i <= j, with row kc as the previous passes
-  // left it, and scales row kc - 1 to R (nothing reads it any more).  Thread t
-  // takes column kc + 1 + ... = t mod D and every TPC-th row of it, so no
-  // index is divided per entry.
+  // 2. Cholesky G = R^T R (upper R in place), pivots below tol dropped,
+  // blocked by tiles (right-looking): for each block row kb, wave 0 factors
+  // the diagonal tile; the panel tiles (kb, J > kb) are solved with R_kk^T,
+  // one thread per column; the trailing tiles (I, J), kb < I <= J, take
+  // X_I^T X_J off with v_mfma_f64_16x16x4f64 (the panel's negated transpose
+  // as the A operand).  Three barriers per block row.
   if (threadIdx.x == 0) {
     double mx = 0.0;
-    for (int i = 0; i < D; ++i) mx = fmax(mx, Gp[upk<D>(i, i)]);
+    for (int i = 0; i < D; ++i) mx = fmax(mx, Tt[utile<GT>(i >> 4, i >> 4) * 256 + (i & 15) * 17]);
     s_tol = mx * (double)D * 4.440892098500626e-16;
   }
   __syncthreads();
   {
-    constexpr int TPC = kSvdThreads / D;  // threads per column
-    static_assert(kSvdThreads % D == 0, "whole columns per thread group");
     const double tolc = s_tol;
-    const int col = threadIdx.x % D, ph = threadIdx.x / D;
-    double prev = 0.0;  // the pivot of the previous column, as this thread read it
-    for (int kc = 0; kc <= D; ++kc) {
-      // scale row kc - 1 (its pivot was read at the previous column)
-      if (kc > 0 && ph == 0 && col >= kc - 1) {
-        const int q = upk<D>(kc - 1, col);
-        const double r = prev > tolc ? sqrt(prev) : 0.0;
-        Gp[q] = r > 0.0 ? (col == kc - 1 ? r : Gp[q] / r) : 0.0;
+    for (int kb = 0; kb < GT; ++kb) {
+      double* A = Tt + utile<GT>(kb, kb) * 256;
+      // (a) the diagonal tile: unblocked, its upper triangle only
+      if (wave == 0) {
+        const int j = lane & 15, i0 = lane >> 4;
+        for (int k = 0; k < 16; ++k) {
+          const double piv = A[k * 17];
+          const double r = piv > tolc ? sqrt(piv) : 0.0;
+          wave_lds_sync();  // every lane has read the pivot before it is rewritten
+          if (lane < 16 && j >= k) A[k * 16 + j] = r > 0.0 ? (j == k ? r : A[k * 16 + j] / r) : 0.0;
+          wave_lds_sync();
+          const double rkj = A[k * 16 + j];
+          for (int i = k + 1 + i0; i <= j; i += 4) A[i * 16 + j] -= A[k * 16 + i] * rkj;
+          wave_lds_sync();
+        }
       }
-      if (kc == D) break;
-      const double piv = Gp[upk<D>(kc, kc)];
-      if (piv > tolc && col > kc) {
-        const double gj = Gp[upk<D>(kc, col)] / piv;
-        for (int i = kc + 1 + ph; i <= col; i += TPC) Gp[upk<D>(i, col)] -= Gp[upk<D>(kc, i)] * gj;
+      __syncthreads();
+      // (b) panel tiles: X = R_kk^-T B, column by column (a dropped pivot gives a zero row)
+      const int npan = 16 * (GT - 1 - kb);
+      for (int c = threadIdx.x; c < npan; c += kSvdThreads) {
+        double* bp = Tt + utile<GT>(kb, kb + 1 + (c >> 4)) * 256 + (c & 15);
+        double x[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          double v = bp[k * 16];
+#pragma unroll
+          for (int m = 0; m < k; ++m) v -= A[m * 16 + k] * x[m];
+          const double r = A[k * 17];
+          x[k] = r > 0.0 ? v / r : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) bp[k * 16] = x[k];
       }
-      prev = piv;
+      __syncthreads();
+      // (c) trailing tiles, wave w taking tiles w, w + 8, ... of the triangle
+      const int nt = GT - 1 - kb;
+      for (int q = wave; q < nt * (nt + 1) / 2; q += kSvdThreads / 64) {
+        int I = 0, rr = q;
+        while (rr >= nt - I) {
+          rr -= nt - I;
+          ++I;
+        }
+        const int TI = kb + 1 + I, TJ = TI + rr;
+        const double* pI = Tt + utile<GT>(kb, TI) * 256;
+        const double* pJ = Tt + utile<GT>(kb, TJ) * 256;
+        double* C = Tt + utile<GT>(TI, TJ) * 256;
+        dbl4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = C[((lane >> 4) + 4 * i) * 16 + (lane & 15)];
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int e = (k0 + (lane >> 4)) * 16 + (lane & 15);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-pI[e], pJ[e], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C[((lane >> 4) + 4 * i) * 16 + (lane & 15)] = acc[i];
+      }
       __syncthreads();
     }
-    __syncthreads();
   }
 
   // 3. rows of R in fp32 (through registers: they overwrite the packed factor)
@@ -387,7 +426,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   for (int u = 0; u < PER; ++u) {
     const int idx = threadIdx.x + u * kSvdThreads;
     const int row = idx / D, col = idx % D;
-    rv[u] = col >= row ? (float)Gp[upk<D>(row, col)] : 0.f;
+    rv[u] = col >= row ? (float)Tt[utile<GT>(row >> 4, col >> 4) * 256 + (row & 15) * 16 + (col & 15)] : 0.f;
   }
   __syncthreads();
   float* Rr = reinterpret_cast<float*>(smd);  // [D][XS]: vector row = row `row` of R
@@ -429,8 +468,9 @@ hipError_t launch_rows(const SvdArgs& a, hipStream_t s) {
 
 template <int D, typename T>
 hipError_t launch_tall(const SvdArgs& a, hipStream_t s) {
-  // max(packed fp64 Gram + 16 staged rows, fp32 rows of R + 16 staged rows)
-  const size_t gram = sizeof(double) * (D * (D + 1) / 2) + sizeof(float) * 16 * (D + 16);
+  // max(fp64 Gram tiles or the 16 staged rows they replace, fp32 rows of R + 16 staged rows)
+  const size_t tiles = sizeof(double) * 256 * ((D / 16) * (D / 16 + 1) / 2), stage = sizeof(float) * 16 * (D + 16);
+  const size_t gram = tiles > stage ? tiles : stage;
   const size_t rows = sizeof(float) * (D + 16) * (D + kVecPad);
   const size_t lds = gram > rows ? gram : rows;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_tall<D, T>),
