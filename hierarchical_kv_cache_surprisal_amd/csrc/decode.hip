@@ -1084,16 +1084,32 @@ __device__ __forceinline__ void stream_rounds(int first, int end, int step, Load
 }
 
 // One row's entry added to a running softmax record (logit lg in log2 units,
-// -inf for no entry).
+// -inf for no entry).  The record's reference m moves only when a logit of
+// the wave exceeds it by more than kSlack: the weights then stay below
+// 2^kSlack, and a row that moves no reference (the common case, decided for
+// the whole wave) costs one exp2 and the accumulation, without the rescale of
+// the accumulator.  The record keeps its meaning (each entry weighted by
+// 2^(logit - m)), so the merges and acc / l are unchanged; m lies at most
+// kSlack below the largest logit folded in.
+constexpr float kSlack = 8.f;
+
 template <typename T, int EPL>
 __device__ __forceinline__ void online_add(float& m, float& l, float (&acc)[EPL], float lg, const Raw<T>& v) {
-  const float mn = fmaxf(m, lg);
-  const float ms = (mn == kNegInf) ? 0.f : mn;
-  const float sc = fast_exp2(m - ms), p = fast_exp2(lg - ms);
-  l = l * sc + p;
+  if (__builtin_amdgcn_ballot_w64(lg > m + kSlack) != 0) {
+    const float mn = fmaxf(m, lg);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float sc = fast_exp2(m - ms), p = fast_exp2(lg - ms);
+    l = l * sc + p;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sc + p * v.get(e);
-  m = mn;
+    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sc + p * v.get(e);
+    m = mn;
+    return;
+  }
+  // m = -inf here only with lg = -inf (no entry yet, none now)
+  const float p = fast_exp2(lg - ((m == kNegInf) ? 0.f : m));
+  l += p;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] += p * v.get(e);
 }
 
 // 16-byte piece at a byte offset from a base shared by the wave: the address is
