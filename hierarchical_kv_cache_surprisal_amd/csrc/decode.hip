@@ -480,9 +480,11 @@ __device__ void slots_to_lds(SoftState<G>& st, float (&acc)[G][EPL], MergeLds<D,
   }
 }
 
-// Merge the per-wave records into one partial per head and store it in `part`.
+// Merge the per-wave records into one partial per head and store it in `part`,
+// with the head's count of zoomed spans zc[h] (none: 0) for the zoom counters.
 template <int D, int G>
-__device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int b, int g, int part) {
+__device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int b, int g, int part,
+                              const int* zc = nullptr) {
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, j = idx % D;
     float M = kNegInf;
@@ -498,9 +500,7 @@ __device__ void store_partial(const MergeLds<D, G>& ml, const DecodeArgs& a, int
     }
     const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
     a.part_acc[slot * D + j] = A;
-    if (j == 0) {
-      reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(M, L);
-    }
+    if (j == 0) reinterpret_cast<float4*>(a.part_ml)[slot] = make_float4(M, L, zc ? (float)zc[h] : 0.f, 0.f);
   }
 }
 
@@ -511,9 +511,7 @@ __device__ void store_empty(const DecodeArgs& a, int b, int g, int part) {
     const int h = idx / D, j = idx % D;
     const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.max_parts + part;
     a.part_acc[slot * D + j] = 0.f;
-    if (j == 0) {
-      reinterpret_cast<float2*>(a.part_ml)[slot] = make_float2(kNegInf, 0.f);
-    }
+    if (j == 0) reinterpret_cast<float4*>(a.part_ml)[slot] = make_float4(kNegInf, 0.f, 0.f, 0.f);
   }
 }
 
@@ -1620,17 +1618,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 1
     const int4 v = sh.seg[s];
     const int x = __builtin_amdgcn_readfirstlane(v.x), w = __builtin_amdgcn_readfirstlane(v.w);
     const int bg = x & 0x7fffffff;
-    store_partial<D, G>(sh.rec[s], a, bg / a.Hkv, bg % a.Hkv, w);
-  }
-  // the layer's zoom counters: atomic adds whose result is not used, so no
-  // round trip before the workgroup ends
-  if (a.zcount && (int)threadIdx.x < nseg * G) {
-    const int s = threadIdx.x / G, h = threadIdx.x % G;
-    const int z = sh.zcnt[s][h];
-    const int bg = sh.seg[s].x & 0x7fffffff;
-    if (z > 0)
-      __hip_atomic_fetch_add(a.zcount + (size_t)(bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G + h, (unsigned long long)z,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // each segment's zoom counts travel with its partials to the combine,
+    // which adds them to the layer's counters (no atomics, no round trip)
+    store_partial<D, G>(sh.rec[s], a, bg / a.Hkv, bg % a.Hkv, w, sh.zcnt[s]);
   }
 }
 
@@ -1687,7 +1677,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
 #define SEKV_COMBINE_UN 8
 #endif
   constexpr int UN = SEKV_COMBINE_UN;
-  __shared__ float gm_s[PG], gl_s[PG];
+  __shared__ float gm_s[PG], gl_s[PG], gz_s[PG];
   __shared__ float4 ga_s[PG][C4];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, hq = bh % a.Hq;
@@ -1708,17 +1698,25 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
     }
     for (int64_t i = i0 + tid; i < n; i += nth) a.mask_h[i] = a.mask[i];
   }
+  // the layer's zoom counters of this (sequence, query head), and the call
+  // counter (with bh = 0): read here, with the first batch of slots, and
+  // rewritten at the end; only this workgroup touches them in this launch
+  unsigned long long zc0 = 0ull, calls0 = 0ull;
+  if (a.zcount && threadIdx.x == 0) {
+    if (a.zparts) zc0 = a.zcount[bh];
+    if (bh == 0) calls0 = a.zcount[(size_t)a.B * a.Hq];
+  }
   const int pg = threadIdx.x / C4, c4 = threadIdx.x % C4;
-  float M = kNegInf, L = 0.f;
+  float M = kNegInf, L = 0.f, Z = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)bh * a.max_parts;
+  const float4* pml = reinterpret_cast<const float4*>(a.part_ml) + (size_t)bh * a.max_parts;
   const float4* pa = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * a.max_parts * D) + c4;
 
   // the slot loads are bounded by the buffer (max_parts), not by np, so the
   // first batch is in flight together with the load of np; slots >= np are
   // loaded but never merged
   for (int p0 = pg; p0 < a.max_parts; p0 += UN * PG) {
-    float2 ml[UN];
+    float4 ml[UN];
     float4 v[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
@@ -1733,6 +1731,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
         const float ms = (mn == kNegInf) ? 0.f : mn;
         const float x = fast_exp2(M - ms), y = fast_exp2(ml[u].x - ms);
         L = L * x + ml[u].y * y;
+        Z += ml[u].z;  // whole counts, exact in fp32
         A.x = A.x * x + v[u].x * y;
         A.y = A.y * x + v[u].y * y;
         A.z = A.z * x + v[u].z * y;
@@ -1745,11 +1744,18 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(DecodeArgs a) {
   if (c4 == 0) {
     gm_s[pg] = M;
     gl_s[pg] = L;
+    gz_s[pg] = Z;
   }
   ga_s[pg][c4] = A;
   __syncthreads();
-  if (a.zcount && bh == 0 && threadIdx.x == 0)  // the layer's call counter (the attention kernel adds the spans)
-    __hip_atomic_fetch_add(a.zcount + (size_t)a.B * a.Hq, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.zcount && threadIdx.x == 0) {
+    if (a.zparts) {
+      float z = 0.f;
+      for (int q = 0; q < PG; ++q) z += gz_s[q];
+      a.zcount[bh] = zc0 + (unsigned long long)z;
+    }
+    if (bh == 0) a.zcount[(size_t)a.B * a.Hq] = calls0 + 1ull;
+  }
   if (threadIdx.x < C4) {
     float Mg = kNegInf;
     for (int q = 0; q < PG; ++q) Mg = fmaxf(Mg, gm_s[q]);

@@ -543,7 +543,7 @@ sekv_status ensure_parts(sekv_ctx* c, size_t slots) {
   dfree(c->part_ml);
   dfree(c->part_acc);
   c->parts_cap = 0;
-  TRY(dalloc(c, &c->part_ml, slots * 2 * sizeof(float)));
+  TRY(dalloc(c, &c->part_ml, slots * 4 * sizeof(float)));
   TRY(dalloc(c, &c->part_acc, slots * c->cfg.d_head * sizeof(float)));
   c->parts_cap = slots;
   return SEKV_OK;
@@ -1584,6 +1584,7 @@ sekv_status decode_step(sekv_ctx* c, int32_t layer, const float* q, const float*
     // the planned kernel: its segment lists and their partial slots
     TRY(prepare_plan(c, layer, stream, capturing));
     a.wsegs = L.sched.wsegs_d;
+    a.zparts = 1;
     a.parts_n = L.sched.wparts_d;
     a.max_parts = L.sched.w_max_parts;
   }
@@ -1715,7 +1716,7 @@ sekv_status sekv_decode_attn_noalloc(sekv_ctx* c, int32_t layer, const float* q,
   const int d = c->cfg.d_head;
   auto up = [](size_t n) { return (n + 255) & ~size_t(255); };
   const size_t slots = (size_t)a.B * a.Hq * S.w_max_parts;
-  const size_t ml_b = up(slots * 2 * sizeof(float)), acc_b = up(slots * d * sizeof(float));
+  const size_t ml_b = up(slots * 4 * sizeof(float)), acc_b = up(slots * d * sizeof(float));
   const size_t qp_b = a.dr > 0 ? up((size_t)a.B * a.Hq * a.dr * sizeof(float)) : 0;
   const size_t mask_b = zoom_mask ? 0 : up((size_t)a.B * a.Hq * a.m_max);
   const size_t need = ml_b + acc_b + qp_b + mask_b;
@@ -1731,6 +1732,7 @@ sekv_status sekv_decode_attn_noalloc(sekv_ctx* c, int32_t layer, const float* q,
   a.q = q;
   a.out = out;
   a.wsegs = S.wsegs_d;
+  a.zparts = 1;
   a.parts_n = S.wparts_d;
   a.max_parts = S.w_max_parts;
   a.zcount = L.zcount_d;

@@ -59,10 +59,13 @@ struct DecodeArgs {
   const int32_t* parts_n; // [B*Hkv] partial slots used by each (sequence, kv head)
   int max_parts;          // partial slots per (sequence, query head) in the buffers below
   int32_t* zcnt;          // [n_span_tasks] zoomed spans of each span task in the last call (statistics)
-  float* part_ml;         // [B][Hq][max_parts][2] (running max in log2 units, sum)
+  float* part_ml;         // [B][Hq][max_parts][4] (running max in log2 units, sum, zoomed spans, unused)
   float* part_acc;        // [B][Hq][max_parts][d]
   unsigned long long* zcount;  // the layer's counters: [B*Hq] zoomed spans per (sequence, query head)
-                               // summed over calls (atomic adds), then [B*Hq] the number of calls (or NULL)
+                               // summed over calls, then the number of calls (or NULL); the combine
+                               // kernel counts the call
+  int zparts;             // 1: the spans come with the partials (planned kernel) and the combine adds
+                          // them; 0: the route kernel adds them (atomics)
   // planned kernel: segments of workgroup i at wsegs[i * wg_segments(G) ..], each
   // (bg | anchors << 31, first row, rows, partial slot); rows = 0 ends a list
   const int4* wsegs;

@@ -207,7 +207,7 @@ sekv_status sekv_decode_attn_budget(sekv_ctx* ctx, int32_t layer, const float* q
  * DEVICE and HOST bases only (staged bases and the basis cache allocate).
  * Errors: STATE (layer not built, no current schedule, HOST_STAGED bases or a
  * basis cache), INVALID (bad arguments, or a decode that needs more scratch
- * than SEKV_NOALLOC_SCRATCH_BYTES: B*H_q*slots*(2+d)*4 bytes of partials,
+ * than SEKV_NOALLOC_SCRATCH_BYTES: B*H_q*slots*(4+d)*4 bytes of partials,
  * slots <= 512, plus B*H_q*d_r*4 and B*H_q*m_max, each rounded up to 256),
  * HIP. */
 #define SEKV_NOALLOC_SCRATCH_BYTES (16u << 20)
