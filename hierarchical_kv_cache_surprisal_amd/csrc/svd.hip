@@ -107,12 +107,15 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
         }
       }
       ga = group_sum<TPP>(ga);
-      // (the threshold test needs no correctly rounded square roots)
+      // The threshold test needs no correctly rounded square roots, and the
+      // angle no correctly rounded division: v_rcp_f32 and v_rsq_f32 (1 ulp)
+      // keep cs^2 + sn^2 = 1 to a few ulps, and a pair left slightly off
+      // orthogonal is rotated again in a later round.  These instructions take
+      // denormal inputs as zero, so a pair is rotated only when |x_i . x_j| is
+      // at least 1e-37: 1 / (2 x_i . x_j) is then finite, and zeta is never
+      // 0 * inf (vectors this small are zero for the factors).
       if (act && al > 0.f && be > 0.f &&
-          fabsf(ga) > tol * __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be)) {
-        // the angle needs no correctly rounded division: v_rcp_f32 and
-        // v_rsq_f32 (1 ulp) keep cs^2 + sn^2 = 1 to a few ulps, and a pair left
-        // slightly off orthogonal is rotated again in a later round
+          fabsf(ga) > fmaxf(1e-37f, tol * __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be))) {
         const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
         const float az = fabsf(zeta);
         const float tt = (az > 1e15f) ? 0.5f * __builtin_amdgcn_rcpf(zeta)

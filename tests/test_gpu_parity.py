@@ -248,6 +248,28 @@ def test_small_bf16_build_parity():
     _check_build(s, ctx, segs, arts, 0, H, K, V)
 
 
+@pytest.mark.parametrize("rho", [(0, 0), (4, 4)])
+@pytest.mark.parametrize("d", [128, 64])
+def test_build_low_rank_long_spans(d, rho):
+    """Spans of up to 179 members with no noise: with no planted factors the rows
+    of a span are identical (rank 1 exactly, in bf16 too), so the Gram of every
+    tall span is singular and the blocked Cholesky drops all pivots but one, in
+    its diagonal tiles and in its panels; with rank-4 factors the bf16 rounding
+    leaves singular values near 4e-4 of the largest (tiny pivots kept).  The GPU
+    build must match the oracle's spans and anchors bit for bit, and its
+    truncated SVD (ranks up to 32, above the true rank) must reach the
+    Eckart-Young bound: zero singular values give zero factor columns."""
+    s = _small_bf16().replace(n=4096, Hq=4, Hkv=4, d=d, noise=0.0, rho=rho, spikes=((0.004, 6.0),))
+    H, K, V = _inputs(s)
+    segs, arts = _oracle_layer(s, H, K, V)
+    _check_margins(s, H, segs)
+    assert int(np.sum(segs[0].mcount > 128)) >= 3, "the workload must have tall spans"
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    _check_build(s, ctx, segs, arts, 0, H, K, V)
+
+
 # ============================================================================ GQA, ragged batch
 
 def _gqa_small():
