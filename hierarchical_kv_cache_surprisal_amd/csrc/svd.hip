@@ -123,11 +123,19 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
                                                  zeta);
         const float cs = __builtin_amdgcn_rsqf(1.f + tt * tt);
         const float sn = cs * tt;
+        // all of x_i, then all of x_j: consecutive stores to one row pair up
+        // into ds_write2 (interleaved with the other row's, which the compiler
+        // must assume may alias, they stay single)
+        float nu[EPT], nv[EPT];
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
-          xi[k * TPP] = cs * u[k] - sn * v[k];
-          xj[k * TPP] = sn * u[k] + cs * v[k];
+          nu[k] = cs * u[k] - sn * v[k];
+          nv[k] = sn * u[k] + cs * v[k];
         }
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) xi[k * TPP] = nu[k];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) xj[k * TPP] = nv[k];
         if (li == 0) {
           *s_rot = 1;
           nrm[i] = al - tt * ga;
