@@ -400,7 +400,12 @@ class Context:
         return sekv_get_spans(self.ptr, b)
 
     def m_max(self):
-        return sekv_get_spans(self.ptr, 0)[3]
+        # the size query alone (no span tables copied): every decode call checks
+        # the mask's size with it
+        lib = load_library()
+        m, na, mm = C.c_int32(), C.c_int32(), C.c_int32()
+        _check(lib.sekv_get_spans(self.ptr, 0, C.byref(m), C.byref(na), C.byref(mm), None, None, None), self.ptr)
+        return mm.value
 
     def decode_attn(self, layer, q, tau, out, zoom_mask=None, stream=None, budget=None, noalloc=False):
         import torch
