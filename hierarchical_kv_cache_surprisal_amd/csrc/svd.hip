@@ -24,8 +24,9 @@
 // The two products that are matrix products, the Gram and A = X V_r, run on
 // the matrix cores (fp64 and fp32 MFMA).  The rotations are plane updates of
 // two vectors at a time and stay on the vector ALUs: they are applied to
-// disjoint pairs in parallel (round-robin tournament ordering), one group of
-// 512/PMAX threads per pair.  Neither path keeps the
+// disjoint pairs in parallel (round-robin tournament ordering), a group of 8
+// threads per pair (tall spans with d = 64: 16), one wave per 16 members of a
+// short span's bucket and 8 waves for tall spans.  Neither path keeps the
 // rotations, so a workgroup needs about 78 KB of LDS and two fit on a CU.
 #include "sekv_device.h"
 
@@ -33,7 +34,13 @@ namespace sekv {
 
 namespace {
 
-constexpr int kSvdThreads = 512;  // 8 waves per workgroup
+constexpr int kSvdThreads = 512;  // 8 waves per workgroup (tall spans, and short spans of up to 128 members)
+
+// Threads of a short-span workgroup for at most PMAX members: 8 per pair of a
+// round (PMAX / 2 pairs), so that a pair's dot product is a sum over 8 lanes
+// and every vector element is touched by one thread; spans of at most 16
+// members take one wave, with no workgroup barrier to wait for.
+constexpr int rows_threads(int pmax) { return pmax >= 128 ? kSvdThreads : 4 * pmax; }
 // Row stride of the fp32 vectors in LDS: D + 8 floats.  In a Jacobi round on
 // 128 vectors each pair has 8 threads, which read 8 consecutive elements of
 // their row; rows of neighbouring pairs then start 8 banks apart and a
@@ -53,15 +60,15 @@ __device__ __forceinline__ float jacobi_tol(int p) {
 }
 
 // One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
-// of the workgroup; each disjoint pair of a round gets 2 * kSvdThreads / PMAX
+// of the workgroup (NT); each disjoint pair of a round gets 2 * NT / PMAX
 // threads.  The squared norms of the vectors (nrm, LDS, p entries) are computed
 // at the start of every sweep and carried through its rotations: a rotation
 // that zeroes x_i . x_j = g with tangent t maps |x_i|^2 to |x_i|^2 - t g and
 // |x_j|^2 to |x_j|^2 + t g, so a round needs one dot product per pair, not
 // three.
-template <int D, int PMAX>
+template <int D, int PMAX, int NT = kSvdThreads>
 __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, float* nrm) {
-  constexpr int TPP = 2 * kSvdThreads / PMAX;
+  constexpr int TPP = 2 * NT / PMAX;
   constexpr int EPT = D / TPP;  // elements of a vector per thread of its pair group
   static_assert(D % TPP == 0, "pair groups must tile the vector length");
   const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
@@ -69,7 +76,7 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
   if (p < 2) return;
   for (int sweep = 0; sweep < 40; ++sweep) {
     if (threadIdx.x == 0) *s_rot = 0;
-    for (int i = pi; i < p; i += kSvdThreads / TPP) {
+    for (int i = pi; i < p; i += NT / TPP) {
       float sq = 0.f;
 #pragma unroll
       for (int k = 0; k < EPT; ++k) {
@@ -151,14 +158,15 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
 }
 
 // sigma_i = |v_i| for p vectors, and order[kk] = index of the kk-th largest (kk < r).
+template <int NT = kSvdThreads>
 __device__ void rank_by_norm(const float* Xv, int XS, int len, int p, int r, float* sig, int* order) {
-  for (int i = threadIdx.x; i < p; i += kSvdThreads) {
+  for (int i = threadIdx.x; i < p; i += NT) {
     float s = 0.f;
     for (int e = 0; e < len; ++e) s += Xv[i * XS + e] * Xv[i * XS + e];
     sig[i] = sqrtf(s);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < p; i += kSvdThreads) {
+  for (int i = threadIdx.x; i < p; i += NT) {
     const float si = sig[i];
     int rk = 0;
     for (int j = 0; j < p; ++j) rk += (sig[j] > si || (sig[j] == si && j < i)) ? 1 : 0;
@@ -201,10 +209,11 @@ __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt
 // through Xr), with V_i = Vt[order[kk]] / sig[order[kk]]; zero beyond c.
 // A block of 16 rows times 16 ranks is one fp32 matrix-core product over the
 // D columns (v_mfma_f32_16x16x4f32, fp32 products and sums like the scalar
-// dot products): wave w takes ranks 16w .. 16w + 15 (r <= D <= 8 * 16).
+// dot products): wave w takes ranks 16w .. 16w + 15 (r <= 16 NT / 64: the
+// workgroup has a wave for every 16 ranks).
 // Operand lanes: A[m][k] = X[m][e0 + k] and B[k][n] = V[n][e0 + k] in lane
 // m + 16k (resp. n + 16k); the result D[4 (l / 16) + i][l % 16] in lane l.
-template <int D, typename T, int XS>
+template <int D, typename T, int XS, int NT = kSvdThreads>
 __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src, float* Xr, const float* Vt,
                                   int VS, const float* sig, const int* order) {
   constexpr int ROWS = 16;
@@ -220,7 +229,7 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
   const float* xrow = Xr + (lane & 15) * XS + (lane >> 4);
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * D; idx += kSvdThreads) {
+    for (int idx = threadIdx.x; idx < ROWS * D; idx += NT) {
       const int t = idx / D, e = idx % D;
       Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
@@ -239,14 +248,16 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
       }
     }
   }
-  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += kSvdThreads) {
+  for (int idx = threadIdx.x; idx < r * (c8 - p.c); idx += NT) {
     const int kk = idx / (c8 - p.c), t = p.c + idx % (c8 - p.c);
     At[(size_t)kk * c8 + t] = Elem<T>::from_f(0.f);
   }
 }
 
 template <int D, typename T, int PMAX>
-__global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
+__global__ __launch_bounds__(rows_threads(PMAX)) void k_svd_rows(SvdArgs a) {
+  constexpr int NT = rows_threads(PMAX);
+  static_assert(16 * (NT / 64) >= PMAX, "a wave for every 16 ranks of the A product (r <= PMAX)");
   extern __shared__ float smem[];
   constexpr int XS = D + kVecPad;
   constexpr int ROWS = 16;
@@ -258,24 +269,24 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_rows(SvdArgs a) {
 
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
-  for (int idx = threadIdx.x; idx < p.c * D; idx += kSvdThreads) {
+  for (int idx = threadIdx.x; idx < p.c * D; idx += NT) {
     const int t = idx / D, e = idx % D;
     X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
   }
   __syncthreads();
-  jacobi_sweeps<D, PMAX>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot, sig);
+  jacobi_sweeps<D, PMAX, NT>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot, sig);
   __syncthreads();
-  rank_by_norm(X, XS, D, p.c, p.r, sig, order);
+  rank_by_norm<NT>(X, XS, D, p.c, p.r, sig, order);
 
   // B^T rows: the chosen orthogonal rows, normalised
   T* Bt = block_ptr<T, D>(a, p, true);
-  for (int idx = threadIdx.x; idx < p.r * D; idx += kSvdThreads) {
+  for (int idx = threadIdx.x; idx < p.r * D; idx += NT) {
     const int kk = idx / D, e = idx % D;
     const int i = order[kk];
     const float s = sig[i];
     Bt[idx] = Elem<T>::from_f(s > 0.f ? X[i * XS + e] / s : 0.f);
   }
-  store_a_from_rows<D, T, XS>(a, p, src, Xr, X, XS, sig, order);
+  store_a_from_rows<D, T, XS, NT>(a, p, src, Xr, X, XS, sig, order);
 }
 
 // ---------------------------------------------------------------- tall spans
@@ -473,7 +484,7 @@ hipError_t launch_rows(const SvdArgs& a, hipStream_t s) {
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_svd_rows<D, T, PMAX>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(kSvdThreads), lds, s, a);
+  hipLaunchKernelGGL((k_svd_rows<D, T, PMAX>), dim3(a.n_problems), dim3(rows_threads(PMAX)), lds, s, a);
   return hipGetLastError();
 }
 
