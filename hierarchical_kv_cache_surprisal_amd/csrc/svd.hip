@@ -37,10 +37,11 @@ namespace {
 constexpr int kSvdThreads = 512;  // 8 waves per workgroup (tall spans, and short spans of up to 128 members)
 
 // Threads of a short-span workgroup for at most PMAX members: 8 per pair of a
-// round (PMAX / 2 pairs), so that a pair's dot product is a sum over 8 lanes
-// and every vector element is touched by one thread; spans of at most 16
-// members take one wave, with no workgroup barrier to wait for.
-constexpr int rows_threads(int pmax) { return pmax >= 128 ? kSvdThreads : 4 * pmax; }
+// round (PMAX / 2 pairs), so that a pair's dot product is a sum over 8 lanes;
+// spans of at most 16 members take one wave.  (4 threads per pair took 40 to 50%
+// longer for the buckets of 32 to 128 members, 16 per pair 9 to 14% longer.)
+constexpr int rows_threads(int pmax) { return pmax >= 128 ? kSvdThreads : (4 * pmax < 64 ? 64 : 4 * pmax); }
+
 // Row stride of the fp32 vectors in LDS: D + 8 floats.  In a Jacobi round on
 // 128 vectors each pair has 8 threads, which read 8 consecutive elements of
 // their row; rows of neighbouring pairs then start 8 banks apart and a
@@ -209,8 +210,8 @@ __device__ __forceinline__ T* block_ptr(const SvdArgs& a, const Prob& p, bool bt
 // through Xr), with V_i = Vt[order[kk]] / sig[order[kk]]; zero beyond c.
 // A block of 16 rows times 16 ranks is one fp32 matrix-core product over the
 // D columns (v_mfma_f32_16x16x4f32, fp32 products and sums like the scalar
-// dot products): wave w takes ranks 16w .. 16w + 15 (r <= 16 NT / 64: the
-// workgroup has a wave for every 16 ranks).
+// dot products): wave w takes ranks 16w .. 16w + 15, then 16 (w + NT / 64) ..,
+// and so on.
 // Operand lanes: A[m][k] = X[m][e0 + k] and B[k][n] = V[n][e0 + k] in lane
 // m + 16k (resp. n + 16k); the result D[4 (l / 16) + i][l % 16] in lane l.
 template <int D, typename T, int XS, int NT = kSvdThreads>
@@ -221,11 +222,6 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
   const int c8 = (int)pad8(p.c);
   const int r = p.r;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kk = wave * 16 + (lane & 15);  // this lane's rank in the B operand and the result
-  const bool wact = wave * 16 < r;         // uniform over the wave
-  const int vi = (kk < r) ? order[kk] : 0;
-  const float si = (kk < r) ? sig[vi] : 0.f;
-  const float* vrow = Vt + vi * VS + (lane >> 4);
   const float* xrow = Xr + (lane & 15) * XS + (lane >> 4);
   for (int t0 = 0; t0 < p.c; t0 += ROWS) {
     __syncthreads();
@@ -234,7 +230,11 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
       Xr[t * XS + e] = (t0 + t < p.c) ? Elem<T>::to_f(src[(size_t)(t0 + t) * D + e]) : 0.f;
     }
     __syncthreads();
-    if (wact) {
+    for (int k0 = wave * 16; k0 < r; k0 += NT / 4) {  // uniform over the wave
+      const int kk = k0 + (lane & 15);  // this lane's rank in the B operand and the result
+      const int vi = (kk < r) ? order[kk] : 0;
+      const float si = (kk < r) ? sig[vi] : 0.f;
+      const float* vrow = Vt + vi * VS + (lane >> 4);
       flt4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int e0 = 0; e0 < D; e0 += 4)
@@ -257,7 +257,7 @@ __device__ void store_a_from_rows(const SvdArgs& a, const Prob& p, const T* src,
 template <int D, typename T, int PMAX>
 __global__ __launch_bounds__(rows_threads(PMAX)) void k_svd_rows(SvdArgs a) {
   constexpr int NT = rows_threads(PMAX);
-  static_assert(16 * (NT / 64) >= PMAX, "a wave for every 16 ranks of the A product (r <= PMAX)");
+  static_assert(NT % 64 == 0 && (2 * NT) % PMAX == 0, "whole waves, whole pair groups");
   extern __shared__ float smem[];
   constexpr int XS = D + kVecPad;
   constexpr int ROWS = 16;
