@@ -608,8 +608,11 @@ def single_layer(dev, stream, args, steps=64):
     return e
 
 
-# one-sided Jacobi sweeps per span matrix, measured in a diagnostic build of the
-# builder (mean over every span of the 128K workload at the bf16 rotation threshold)
+# one-sided Jacobi sweeps per span matrix under the plain stopping rule (a sweep
+# with no rotation), measured in a diagnostic build of the builder (mean over every
+# span of the 128K workload at the bf16 rotation threshold).  The builder stops
+# earlier where the kept rank is below the span's size, so the FLOP rate below is
+# the plain rule's work over the measured time (an equivalent rate).
 JACOBI_SWEEPS = 8.6
 
 
@@ -650,7 +653,8 @@ def builder_runs(dev, stream, alphas=(0.5, 1.0, 2.0), ranks=(8, 16, 32)):
     del K, V
     torch.cuda.empty_cache()
     out["note"] = (f"one build of 131072 tokens x {s.Hkv} kv heads (K and V), bases in pinned host memory; "
-                   f"nominal FLOP = {JACOBI_SWEEPS} sweeps x 6pq(q-1)/2 per span matrix (p = 128, q = min(c, 128)) "
+                   f"nominal FLOP = {JACOBI_SWEEPS} sweeps (the plain stopping rule's mean; the builder stops earlier "
+                   f"for ranks below the span size) x 6pq(q-1)/2 per span matrix (p = 128, q = min(c, 128)) "
                    f"plus 2cd^2 for the Gram of spans longer than 128")
     return out
 

@@ -7,8 +7,9 @@
 // every rank gate on).
 //
 // Short spans (c <= 128): one-sided Jacobi (Hestenes) on the c rows of X held
-// in LDS: plane rotations of row pairs until all pairs are orthogonal,
-// X = J X' with orthogonal rows x'_i.  Then sigma_i = |x'_i|,
+// in LDS: plane rotations of row pairs until the pairs that involve the r
+// largest rows are orthogonal, X = J X' with rows x'_i (the r largest orthogonal
+// to each other and to the rest).  Then sigma_i = |x'_i|,
 // V_i = x'_i / sigma_i, and A = U_r Sigma_r = X V_r is formed from the original
 // rows (streamed again from X), so J is never stored.
 //
@@ -60,23 +61,45 @@ __device__ __forceinline__ float jacobi_tol(int p) {
   return sizeof(T) == 2 ? 1e-4f : (float)(p + (p & 1)) * 1.1920929e-7f;
 }
 
+// Stopping bound.  Only the r largest singular triplets are kept (the
+// truncation of eq. (6)), so the sweeps end after one in which no pair that
+// involves one of the r largest vectors (by norm at the sweep's start) was
+// further than this from orthogonal, even if pairs of smaller vectors were
+// still rotated.  Such a pair was then rotated to orthogonal in that sweep, and
+// what later rotations of the sweep leave of it is of second order (stop^2).
+// bf16 storage: 1e-2 (second-order effects of 1e-4 against the 2^-9 rounding of
+// the stored factors); fp32 storage: the rotation threshold, so that with
+// r >= p the rule is the plain one (stop after a sweep with no rotation).
+template <typename T>
+__device__ __forceinline__ float jacobi_stop(int p) {
+  return sizeof(T) == 2 ? 1e-2f : jacobi_tol<T>(p);
+}
+
 // One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
 // of the workgroup (NT); each disjoint pair of a round gets 2 * NT / PMAX
 // threads.  The squared norms of the vectors (nrm, LDS, p entries) are computed
 // at the start of every sweep and carried through its rotations: a rotation
 // that zeroes x_i . x_j = g with tangent t maps |x_i|^2 to |x_i|^2 - t g and
 // |x_j|^2 to |x_j|^2 + t g, so a round needs one dot product per pair, not
-// three.
+// three.  The sweeps end after one with no rotation, or with no pair above the
+// stopping bound `stop` among the pairs that involve one of the r largest
+// vectors (marked in topf, LDS, p entries, at every sweep's start).  s_flag
+// (LDS, 2 entries): a rotation happened; such a pair was seen.
 template <int D, int PMAX, int NT = kSvdThreads>
-__device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, float* nrm) {
+__device__ void jacobi_sweeps(float* Xv, int XS, int p, int r, float tol, float stop, int* s_flag, float* nrm,
+                              int* topf) {
   constexpr int TPP = 2 * NT / PMAX;
   constexpr int EPT = D / TPP;  // elements of a vector per thread of its pair group
   static_assert(D % TPP == 0, "pair groups must tile the vector length");
   const int pi = threadIdx.x / TPP, li = threadIdx.x % TPP;
   const int pe = p + (p & 1);
   if (p < 2) return;
+  const bool all_top = r >= p;  // uniform
   for (int sweep = 0; sweep < 40; ++sweep) {
-    if (threadIdx.x == 0) *s_rot = 0;
+    if (threadIdx.x == 0) {
+      s_flag[0] = 0;
+      s_flag[1] = 0;
+    }
     for (int i = pi; i < p; i += NT / TPP) {
       float sq = 0.f;
 #pragma unroll
@@ -88,6 +111,19 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
       if (li == 0) nrm[i] = sq;
     }
     __syncthreads();
+    if (!all_top) {
+      // the r largest norms at the sweep's start (ties to the lower index)
+      for (int i = threadIdx.x; i < p; i += NT) {
+        const float ni = nrm[i];
+        int rk = 0;
+        for (int j = 0; j < p; ++j) {
+          const float nj = nrm[j];
+          rk += (nj > ni || (nj == ni && j < i)) ? 1 : 0;
+        }
+        topf[i] = rk < r ? 1 : 0;
+      }
+      __syncthreads();
+    }
     // round t pairs (pe - 1, t) in group 0 and ((t + pi) mod (pe - 1),
     // (t - pi) mod (pe - 1)) in group pi > 0: both indices advance by one per
     // round, so they are carried instead of recomputed with two modulos
@@ -122,8 +158,10 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
       // denormal inputs as zero, so a pair is rotated only when |x_i . x_j| is
       // at least 1e-37: 1 / (2 x_i . x_j) is then finite, and zeta is never
       // 0 * inf (vectors this small are zero for the factors).
-      if (act && al > 0.f && be > 0.f &&
-          fabsf(ga) > fmaxf(1e-37f, tol * __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be))) {
+      const float sab = __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be);
+      if (act && li == 0 && al > 0.f && be > 0.f && fabsf(ga) > stop * sab && (all_top || topf[i] || topf[j]))
+        s_flag[1] = 1;
+      if (act && al > 0.f && be > 0.f && fabsf(ga) > fmaxf(1e-37f, tol * sab)) {
         const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
         const float az = fabsf(zeta);
         const float tt = (az > 1e15f) ? 0.5f * __builtin_amdgcn_rcpf(zeta)
@@ -145,16 +183,16 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, float tol, int* s_rot, f
 #pragma unroll
         for (int k = 0; k < EPT; ++k) xj[k * TPP] = nv[k];
         if (li == 0) {
-          *s_rot = 1;
+          s_flag[0] = 1;
           nrm[i] = al - tt * ga;
           nrm[j] = be + tt * ga;
         }
       }
       __syncthreads();
     }
-    const int rot = *s_rot;
+    const int rot = s_flag[0], big = s_flag[1];
     __syncthreads();
-    if (!rot) break;
+    if (!rot || !big) break;
   }
 }
 
@@ -265,7 +303,7 @@ __global__ __launch_bounds__(rows_threads(PMAX)) void k_svd_rows(SvdArgs a) {
   float* Xr = smem + PMAX * XS;    // [ROWS][XS]: original rows, for A
   __shared__ float sig[PMAX];
   __shared__ int order[PMAX];
-  __shared__ int s_rot;
+  __shared__ int s_flag[2];
 
   const Prob p = load_prob(a, a.Hkv);
   const T* src = reinterpret_cast<const T*>(p.which ? a.V : a.K) + ((size_t)p.bg * a.n + p.ms) * D;
@@ -274,7 +312,8 @@ __global__ __launch_bounds__(rows_threads(PMAX)) void k_svd_rows(SvdArgs a) {
     X[t * XS + e] = Elem<T>::to_f(src[(size_t)t * D + e]);
   }
   __syncthreads();
-  jacobi_sweeps<D, PMAX, NT>(X, XS, p.c, jacobi_tol<T>(p.c), &s_rot, sig);
+  // (order is free until the sweeps end: it holds the marks of the largest vectors)
+  jacobi_sweeps<D, PMAX, NT>(X, XS, p.c, p.r, jacobi_tol<T>(p.c), jacobi_stop<T>(p.c), s_flag, sig, order);
   __syncthreads();
   rank_by_norm<NT>(X, XS, D, p.c, p.r, sig, order);
 
@@ -297,8 +336,9 @@ __device__ __forceinline__ int utile(int I, int J) {
   return I * GT - (I * (I - 1)) / 2 + (J - I);
 }
 
+// (at most 128 VGPRs: two workgroups of 8 waves per CU)
 template <int D, typename T>
-__global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
+__global__ __launch_bounds__(kSvdThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_svd_tall(SvdArgs a) {
   extern __shared__ double smd[];
   constexpr int XS = D + kVecPad;  // float vector stride
   constexpr int ROWS = 16;        // X rows staged per step
@@ -312,7 +352,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
   float* Xs = reinterpret_cast<float*>(smd);              // [ROWS][GS]
   __shared__ float sig[D];
   __shared__ int order[D];
-  __shared__ int s_rot;
+  __shared__ int s_flag[2];
   __shared__ double s_tol;
 
   const Prob p = load_prob(a, a.Hkv);
@@ -459,7 +499,7 @@ __global__ __launch_bounds__(kSvdThreads) void k_svd_tall(SvdArgs a) {
     Rr[row * XS + col] = rv[u];
   }
   __syncthreads();
-  jacobi_sweeps<D, D>(Rr, XS, D, jacobi_tol<T>(D), &s_rot, sig);
+  jacobi_sweeps<D, D>(Rr, XS, D, p.r, jacobi_tol<T>(D), jacobi_stop<T>(D), s_flag, sig, order);
   __syncthreads();
   rank_by_norm(Rr, XS, D, D, p.r, sig, order);
 
