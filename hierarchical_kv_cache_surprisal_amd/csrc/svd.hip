@@ -66,13 +66,16 @@ __device__ __forceinline__ float jacobi_tol(int p) {
 // involves one of the r largest vectors (by norm at the sweep's start) was
 // further than this from orthogonal, even if pairs of smaller vectors were
 // still rotated.  Such a pair was then rotated to orthogonal in that sweep, and
-// what later rotations of the sweep leave of it is of second order (stop^2).
-// bf16 storage: 1e-2 (second-order effects of 1e-4 against the 2^-9 rounding of
-// the stored factors); fp32 storage: the rotation threshold, so that with
-// r >= p the rule is the plain one (stop after a sweep with no rotation).
+// the later rotations of the sweep leave of it about p stop^2 at most.  bf16
+// storage: 3e-3, which leaves the kept factors orthonormal to about 1e-3, below
+// the 2^-9 rounding of their storage, even for spans whose singular values all
+// lie in one tight cluster (with 1e-2 such spans stopped after their first
+// sweep, 1e-2 from orthonormal).  fp32 storage: the
+// rotation threshold, so that with r >= p the rule is the plain one (stop after
+// a sweep with no rotation).
 template <typename T>
 __device__ __forceinline__ float jacobi_stop(int p) {
-  return sizeof(T) == 2 ? 1e-2f : jacobi_tol<T>(p);
+  return sizeof(T) == 2 ? 3e-3f : jacobi_tol<T>(p);
 }
 
 // One-sided Jacobi on p vectors (length D, stride XS), in place.  All threads
@@ -130,6 +133,9 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, int r, float tol, float 
     const int pm = pe - 1;
     int ia = pi == 0 ? pm : pi;
     int ja = pi == 0 ? 0 : pm - pi;
+    // this thread's pair group has seen a pair above the stopping bound that
+    // involves a marked vector (once set, the test and its mark reads are skipped)
+    bool big = false;
     for (int t = 0; t < pm; ++t) {
       const int i = pi < pe / 2 ? ia : -1, j = pi < pe / 2 ? ja : -1;
       if (pi != 0) ia = ia + 1 == pm ? 0 : ia + 1;
@@ -159,8 +165,7 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, int r, float tol, float 
       // at least 1e-37: 1 / (2 x_i . x_j) is then finite, and zeta is never
       // 0 * inf (vectors this small are zero for the factors).
       const float sab = __builtin_amdgcn_sqrtf(al) * __builtin_amdgcn_sqrtf(be);
-      if (act && li == 0 && al > 0.f && be > 0.f && fabsf(ga) > stop * sab && (all_top || topf[i] || topf[j]))
-        s_flag[1] = 1;
+      if (!big && act && fabsf(ga) > stop * sab) big = all_top || topf[i] != 0 || topf[j] != 0;
       if (act && al > 0.f && be > 0.f && fabsf(ga) > fmaxf(1e-37f, tol * sab)) {
         const float zeta = (be - al) * __builtin_amdgcn_rcpf(2.f * ga);
         const float az = fabsf(zeta);
@@ -190,9 +195,11 @@ __device__ void jacobi_sweeps(float* Xv, int XS, int p, int r, float tol, float 
       }
       __syncthreads();
     }
-    const int rot = s_flag[0], big = s_flag[1];
+    if (__builtin_amdgcn_ballot_w64(big) != 0 && (threadIdx.x & 63) == 0) s_flag[1] = 1;
     __syncthreads();
-    if (!rot || !big) break;
+    const int rot = s_flag[0], any_big = s_flag[1];
+    __syncthreads();
+    if (!rot || !any_big) break;
   }
 }
 
