@@ -270,6 +270,47 @@ def test_build_low_rank_long_spans(d, rho):
     _check_build(s, ctx, segs, arts, 0, H, K, V)
 
 
+def _clustered_kv(s, H, seed):
+    """K and V whose span matrices have all their singular values in one tight
+    cluster (1 + 1e-3 i, i < min(c, d), times 4, before the bf16 rounding of the
+    storage): random orthonormal left and right factors per span; anchor rows
+    are plain Gaussian."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(2):
+        X = rng.standard_normal((s.B, s.Hkv, s.n, s.d))
+        for b in range(s.B):
+            seg = O.segment(H[b], s.alpha, s.w)
+            for g in range(s.Hkv):
+                for k0, c in zip(seg.mstart, seg.mcount):
+                    q = min(int(c), s.d)
+                    U = np.linalg.qr(rng.standard_normal((int(c), q)))[0]
+                    W = np.linalg.qr(rng.standard_normal((s.d, q)))[0].T
+                    X[b, g, k0:k0 + c] = 4.0 * (U * (1.0 + 1e-3 * np.arange(q))) @ W
+        out.append(torch.from_numpy(X.astype(np.float32)).to(torch.bfloat16))
+    return out
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_build_clustered_spectra(d):
+    """Spans whose singular values all lie in one tight cluster, short and tall
+    (up to 179 members): the worst case for stopping the rotations once the
+    pairs that involve the r largest vectors are nearly orthogonal, since every
+    direction is then almost as large as the kept ones.  The GPU build must
+    match the oracle's spans and anchors bit for bit and reach the same
+    Eckart-Young and singular-value bounds as on the benchmark's spans."""
+    s = _small_bf16().replace(n=4096, Hq=4, Hkv=4, d=d, spikes=((0.004, 6.0),))
+    H = synth.surprisal_batch(s)
+    K, V = _clustered_kv(s, H, seed=11)
+    segs, arts = _oracle_layer(s, H, K, V)
+    _check_margins(s, H, segs)
+    assert int(np.sum(segs[0].mcount > 128)) >= 3, "the workload must have tall spans"
+    ctx = _ctx(s, "device")
+    ctx.build(0, torch.from_numpy(H).to(DEV), K.to(DEV), V.to(DEV), s.alpha, s.rank_choices, s.rank_seed)
+    torch.cuda.synchronize()
+    _check_build(s, ctx, segs, arts, 0, H, K, V)
+
+
 # ============================================================================ GQA, ragged batch
 
 def _gqa_small():
