@@ -272,7 +272,7 @@ def test_build_low_rank_long_spans(d, rho):
 
 def _clustered_kv(s, H, seed):
     """K and V whose span matrices have all their singular values in one tight
-    cluster (1 + 1e-3 i, i < min(c, d), times 4, before the bf16 rounding of the
+    cluster (1 + 1e-3 i, i < min(c, d), times 4, before any bf16 rounding of the
     storage): random orthonormal left and right factors per span; anchor rows
     are plain Gaussian."""
     rng = np.random.default_rng(seed)
@@ -287,19 +287,21 @@ def _clustered_kv(s, H, seed):
                     U = np.linalg.qr(rng.standard_normal((int(c), q)))[0]
                     W = np.linalg.qr(rng.standard_normal((s.d, q)))[0].T
                     X[b, g, k0:k0 + c] = 4.0 * (U * (1.0 + 1e-3 * np.arange(q))) @ W
-        out.append(torch.from_numpy(X.astype(np.float32)).to(torch.bfloat16))
+        t = torch.from_numpy(X.astype(np.float32))
+        out.append(t.to(torch.bfloat16) if s.kv_dtype == "bf16" else t)
     return out
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_build_clustered_spectra(d):
+@pytest.mark.parametrize("kv_dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_build_clustered_spectra(kv_dtype, d):
     """Spans whose singular values all lie in one tight cluster, short and tall
     (up to 179 members): the worst case for stopping the rotations once the
     pairs that involve the r largest vectors are nearly orthogonal, since every
     direction is then almost as large as the kept ones.  The GPU build must
     match the oracle's spans and anchors bit for bit and reach the same
-    Eckart-Young and singular-value bounds as on the benchmark's spans."""
-    s = _small_bf16().replace(n=4096, Hq=4, Hkv=4, d=d, spikes=((0.004, 6.0),))
+    Eckart-Young and singular-value bounds as on the benchmark's spans (fp32:
+    also orthonormal B^T to 1e-4)."""
+    s = _small_bf16().replace(n=4096, Hq=4, Hkv=4, d=d, kv_dtype=kv_dtype, spikes=((0.004, 6.0),))
     H = synth.surprisal_batch(s)
     K, V = _clustered_kv(s, H, seed=11)
     segs, arts = _oracle_layer(s, H, K, V)
