@@ -933,9 +933,15 @@ sekv_status prepare_plan(sekv_ctx* c, int layer, hipStream_t stream, bool captur
   // 34.8 us per layer-step at two per CU; the 32K layer and the grouped-query
   // batch are faster at three)
   std::vector<const int32_t*> cnt;
-  const PlanInput in = plan_input(c, L, cnt);
+  PlanInput in = plan_input(c, L, cnt);
   int nw = c->fill_tasks;
-  if (!c->fill_fixed && c->G == 1 && plan_expected_bytes(in) > 64e6) nw = c->fill_tasks * 2 / 3;
+  if (!c->fill_fixed && c->G == 1 && plan_expected_bytes(in) > 64e6) {
+    nw = c->fill_tasks * 2 / 3;
+    // and half the cushion of zoom work per share: 32.1 against 32.4 us per
+    // 128K layer-step (0.5 to 1 standard deviation: 32.1 to 32.2 us; 0 and 3:
+    // 32.4 and 33.2 us); the grouped-query batch is 3 to 5% slower with it
+    in.zdev = env_int("SEKV_ZOOM_DEV", 75, 0, 1000) / 100.0;
+  }
   PlanOut po;
   plan_shares(in, nw, &po);
   S.wsegs.resize(po.segs.size());
